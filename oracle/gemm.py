@@ -1,0 +1,65 @@
+"""Block-scaled FP8 grouped GEMM (test infrastructure only).
+
+Operands are E4M3FN codes with fp32 scales: A per 1x128 tile, B per 128x128
+block (news.qq.com/rain/a/20241229A05OQF00, section FP8 低精度训练 ›
+细粒度量化).  Products are accumulated in high precision (same article,
+提高累加精度, which keeps the MMA partials in FP32).  For every 128-wide K
+block the partial dot product is taken exactly and multiplied by the product
+of the two block scales; the oracle adds the blocks in float64.  With E4M3
+operands each 128-term partial is exact in float64, so the result is the
+exact value up to float64 rounding of the scaled sums.  The output is then
+rounded once to bf16, the storage format of the GEMM outputs.
+
+B is stored [G, N, K] (K contiguous), B's scales [G, N/128, K/128].
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .formats import e4m3_decode, bf16_round
+
+TILE = 128
+
+
+def block_scaled_matmul(qA, sA, qB, sB) -> np.ndarray:
+    """One group: qA [m, K] codes, sA [m, K/128]; qB [N, K] codes, sB [N/128, K/128].
+
+    C[i, n] = sum_kb sA[i, kb] * sB[n // 128, kb] * sum_{k in kb} A[i, k] B[n, k]
+    """
+    qA = np.asarray(qA)
+    m, K = qA.shape
+    N = qB.shape[0]
+    nkb = K // TILE
+    A = e4m3_decode(qA)
+    B = e4m3_decode(qB)
+    sA64 = np.asarray(sA, dtype=np.float32).astype(np.float64)
+    sBn = np.repeat(np.asarray(sB, dtype=np.float32).astype(np.float64), TILE, axis=0)  # [N, nkb]
+    C = np.zeros((m, N), dtype=np.float64)
+    for kb in range(nkb):
+        ks = slice(kb * TILE, (kb + 1) * TILE)
+        part = A[:, ks] @ B[:, ks].T                       # exact
+        C += (sA64[:, kb][:, None] * sBn[:, kb][None, :]) * part
+    return C
+
+
+def grouped_gemm(qA, sA, qB_groups, sB_groups, offsets) -> np.ndarray:
+    """Grouped form: rows offsets[g]:offsets[g+1] of A use group g's B.
+
+    qB_groups / sB_groups: indexable by group (array [G, N, K] or a list).
+    Returns float64 [M_total, N] (not yet rounded).
+    """
+    offsets = np.asarray(offsets, dtype=np.int64)
+    G = len(offsets) - 1
+    M = int(offsets[-1])
+    N = qB_groups[0].shape[0]
+    C = np.zeros((M, N), dtype=np.float64)
+    for g in range(G):
+        r0, r1 = int(offsets[g]), int(offsets[g + 1])
+        if r1 > r0:
+            C[r0:r1] = block_scaled_matmul(qA[r0:r1], sA[r0:r1], qB_groups[g], sB_groups[g])
+    return C
+
+
+def to_bf16(C: np.ndarray) -> np.ndarray:
+    """Storage rounding of GEMM outputs (bf16, ties to even), as float64 values."""
+    return bf16_round(C)

@@ -1,0 +1,97 @@
+// Shared helpers of the HIP sources: error reporting, argument checks and
+// the device-side number-format codecs.  gfx950 (CDNA4, wave64) only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include <algorithm>
+
+#include "moe_fp8.h"
+
+namespace moe {
+
+// ---- host-side error reporting -------------------------------------------
+void set_error(const char* fmt, ...) __attribute__((format(printf, 1, 2)));
+void clear_error();
+
+#define MOE_REQUIRE(cond, code, ...)        \
+  do {                                      \
+    if (!(cond)) {                          \
+      ::moe::set_error(__VA_ARGS__);        \
+      return (code);                        \
+    }                                       \
+  } while (0)
+
+#define MOE_INVALID(cond, ...) MOE_REQUIRE(cond, MOE_ERR_INVALID, __VA_ARGS__)
+#define MOE_UNSUPPORTED(cond, ...) MOE_REQUIRE(cond, MOE_ERR_UNSUPPORTED, __VA_ARGS__)
+
+// Check the launch that was just enqueued.
+int check_launch(const char* what);
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+constexpr int kWave = 64;
+
+// ---- device-side codecs ----------------------------------------------------
+
+// bf16 bits -> fp32 (exact)
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) {
+  return __uint_as_float(h << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).  The gfx950
+// conversion v_cvt_pk_bf16_f32 was checked bit-identical, over every finite
+// fp32 input, to the bit-level rule "add 0x7FFF + lsb, keep the high half".
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  return f32x2_to_bf16x2(f, 0.0f) & 0xFFFFu;
+}
+
+// fp32 -> OCP E4M3FN codes: round to nearest even, saturate to +-448, keep
+// the sign of zero.  Inputs are clamped to [-448, 448] (the sign of zero
+// survives the clamp) and converted by v_cvt_pk_fp8_f32, which was checked
+// bit-identical, over every fp32 input in [-448, 448], to the format's
+// rounding rule: subnormal grid 2^-9 below 2^-6, else 3 mantissa bits with
+// round-half-even on the dropped bits.
+__device__ __forceinline__ float e4m3_clamp(float v) {
+  return __builtin_amdgcn_fmed3f(v, -448.0f, 448.0f);
+}
+// two codes in the low 16 bits (a: byte 0, b: byte 1)
+__device__ __forceinline__ uint32_t f32x2_to_e4m3x2(float a, float b) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(a), e4m3_clamp(b), 0, false) & 0xFFFFu;
+}
+// four codes in one word (a: byte 0 ... d: byte 3)
+__device__ __forceinline__ uint32_t f32x4_to_e4m3x4(float a, float b, float c, float d) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(a), e4m3_clamp(b), 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(c), e4m3_clamp(d), lo, true);
+}
+__device__ __forceinline__ uint32_t f32_to_e4m3(float v) { return f32x2_to_e4m3x2(v, v) & 0xFFu; }
+
+// Lanes 4k..4k+3 of a quad: lane 4k receives the values of lanes 4k+1..4k+3
+// (DPP quad_perm; other lanes receive values they do not use).
+__device__ __forceinline__ float quad_lane1(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x55, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float quad_lane2(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xAA, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float quad_lane3(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xFF, 0xF, 0xF, true));
+}
+
+// Wave-wide butterfly reductions (wave64).
+__device__ __forceinline__ float wave_max_xor(float v, int width) {
+  for (int o = 1; o < width; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+}  // namespace moe

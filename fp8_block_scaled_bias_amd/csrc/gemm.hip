@@ -1,0 +1,635 @@
+// Block-scaled FP8 grouped GEMM on gfx950 FP8 MFMA, with an optional fused
+// SwiGLU + 1x128 requantisation epilogue.
+//
+// Method: news.qq.com/rain/a/20241229A05OQF00, section FP8 低精度训练 -
+// activations carry one fp32 scale per 1x128 tile and weights one per
+// 128x128 block (细粒度量化), and MMA partial results are promoted to FP32
+// accumulators at a fixed K interval (提高累加精度).
+//
+// gfx950 design
+//  * One v_mfma_f32_16x16x128_f8f6f4 covers exactly one 128-wide K block of
+//    a 16x16 output tile, so its result P is that block's partial sum.  It is
+//    issued with a zero accumulator and promoted at once:
+//        acc += (sA[row, kb] * sB[nblk, kb]) * P      (one FMA per output)
+//    The MFMA's own 128-term sum is not fp32-exact (it is the hardware's
+//    limited-precision dot product, the effect the 128-element promotion
+//    interval is there to bound); everything after it is fp32.
+//  * Both operands are K-contiguous, so a lane feeds the MFMA 32 bytes of one
+//    A row and one B row; A and B use the same K order inside a block, which
+//    is all a dot product needs.
+//  * Workgroup tile BM x 256 (4 waves), K step 128.  Tiles of A (BM x 128 B),
+//    B (256 x 128 B) and A's scales (one fp32 per row) are copied global ->
+//    LDS with global_load_lds_dwordx4 / _dword (no VGPR staging) into a ring
+//    of STAGES buffers, so STAGES-1 K blocks are in flight while one is
+//    consumed.  The copies are issued from inline asm and their completion is
+//    tracked with explicit vmcnt waits plus a workgroup barrier per K block.
+//  * LDS rows are 128 B with the 16 B chunk index XOR-swizzled (swz below),
+//    so the rows read by one ds_read_b128 phase hit distinct bank groups.
+//  * Ragged groups: the host launches an upper bound of M tiles per N tile;
+//    each workgroup finds its (group, row block) from group_offsets with a
+//    block-wide scan.  Rows past a group's end are clamped on load and masked
+//    on store (an output row depends only on its own A row).
+//  * Tile order is XCD-aware: consecutive tile ids go to the same XCD (the
+//    hardware deals workgroups round-robin over 8 XCDs), and ids run
+//    group-major with M tiles fastest, so the workgroups running together on
+//    one XCD share each weight tile across all row blocks of an expert and
+//    each A tile across several N tiles, in that XCD's L2.
+//  * Epilogues: bf16 (round to nearest even) through an LDS-staged, coalesced
+//    store; or SwiGLU: the 256 columns are 128 gate + 128 up columns of the
+//    same h block, h = silu(g) * u is formed in fp32 from the fp32
+//    accumulators (g and u are never stored) and quantised 1x128 to E4M3.
+#include "common.h"
+
+namespace moe {
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int GM_THREADS = 256;
+constexpr int BN = 256;
+
+struct GemmArgs {
+  const uint8_t* A;
+  const float* A_scale;
+  const int32_t* a_row_index;
+  const uint8_t* B;
+  const float* B_scale;
+  const int32_t* offs;
+  int G;
+  int64_t N;       // columns of B's groups (2I for SwiGLU)
+  int64_t K;
+  int64_t ntiles;  // N tiles of 256 (SwiGLU: I / 128)
+  int64_t I;       // SwiGLU: h width
+  uint16_t* C;     // bf16 out [M_total, N]
+  uint8_t* Hq;     // SwiGLU out [M_total, I]
+  float* Hs;       // SwiGLU scales [M_total, I/128]
+};
+
+// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt bits [3:0] and
+// [15:14]; expcnt = 7 and lgkmcnt = 15 mean "no wait").
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__device__ __forceinline__ void barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Asynchronous global -> LDS copies.  Lane i's bytes land at lds + i*size;
+// lds must be wave-uniform.  No VGPR is written.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ v4f mfma_fp8_block(const v8i& a, const v8i& b) {
+  const v4f zero = {0.f, 0.f, 0.f, 0.f};
+  // cbsz = blgp = 0: both operands FP8 E4M3; no E8M0 block scaling.
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, 0, 0, 0);
+}
+
+// LDS tile layout: 128 B rows; 16 B chunk c of row r is stored in slot
+// c ^ swz(r).  swz keeps any 8 consecutive rows in distinct slots (one
+// 8-lane phase of a 32-bank LDS) and the 8 even and 8 odd rows of any 16
+// consecutive rows in distinct slots (one 16-lane phase of a 64-bank LDS).
+__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
+// 32 bytes of row `row` (K half h = lane/16) from a swizzled 128 B-row tile.
+__device__ __forceinline__ v8i lds_frag(const uint8_t* tile, int row, int h) {
+  const int sw = swz(row);
+  const uint4 lo = *reinterpret_cast<const uint4*>(tile + row * 128 + (((2 * h) ^ sw) << 4));
+  const uint4 hi = *reinterpret_cast<const uint4*>(tile + row * 128 + (((2 * h + 1) ^ sw) << 4));
+  v8i r;
+  r[0] = lo.x; r[1] = lo.y; r[2] = lo.z; r[3] = lo.w;
+  r[4] = hi.x; r[5] = hi.y; r[6] = hi.z; r[7] = hi.w;
+  return r;
+}
+
+constexpr int MAXG = 1024;  // groups the LDS tile tables hold
+
+template <int BM, int WAVES_M, int STAGES, bool SWIGLU, bool GATHER>
+struct Cfg {
+  static constexpr int WAVES_N = 4 / WAVES_M;
+  static constexpr int WTM = BM / WAVES_M;
+  static constexpr int WTN = BN / WAVES_N;  // B tile rows a wave multiplies
+  static constexpr int SI = WTM / 16;
+  static constexpr int SJ = WTN / 16;
+  static constexpr int A_BYTES = BM * 128;
+  static constexpr int B_BYTES = BN * 128;
+  static constexpr int S_BYTES = 256 * 4;
+  static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
+  static constexpr int A_LOADS = BM / 32;  // dwordx4 copies per wave per step
+  static constexpr int B_LOADS = 8;
+  static constexpr int LOADS = A_LOADS + B_LOADS + 1 + (GATHER ? 1 : 0);
+  static constexpr int OFF_PREF = STAGES * STAGE;            // int [MAXG + 1]
+  static constexpr int OFF_OFFS = OFF_PREF + (MAXG + 1) * 4;  // int [MAXG + 1]
+  static constexpr int OFF_RIDX = OFF_OFFS + (MAXG + 1) * 4;  // int [2][256]
+  static constexpr int OFF_AMAX = OFF_RIDX + 2 * 256 * 4;     // float [BM][WAVES_N]
+  static constexpr int LDS = OFF_AMAX + (SWIGLU ? BM * WAVES_N * 4 : 0);
+  static_assert(WTN <= 128 || SWIGLU, "a wave's columns must lie in one 128-column block");
+  static_assert(BM <= 128, "scale slots BM, BM+1 carry the weight scales");
+  static_assert(LDS <= 160 * 1024, "LDS budget");
+};
+
+// Uniform description of one output tile.
+struct Tile {
+  int g, m0, m1;
+  int64_t nt;
+};
+
+// Tile id L -> (group, rows, N tile).  Ids run group-major, then N tile,
+// then M tile (M fastest), so the workgroups that run together on one XCD
+// cover all row blocks of one expert against a few weight tiles.
+// s_pref[g] = M tiles of groups < g (empty groups repeat the prefix; the
+// largest g with s_pref[g] * ntiles <= L is the non-empty group holding L).
+__device__ __forceinline__ Tile decode_tile(const int* s_pref, const int* s_offs, int G,
+                                            int64_t ntiles, int64_t L, int bm) {
+  int lo = 0, hi = G;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if ((int64_t)s_pref[mid] * ntiles <= L) lo = mid;
+    else hi = mid;
+  }
+  Tile t;
+  const int cnt = s_pref[lo + 1] - s_pref[lo];
+  const int64_t rem = L - (int64_t)s_pref[lo] * ntiles;
+  t.g = lo;
+  t.nt = rem / cnt;
+  const int mi = (int)(rem - t.nt * cnt);
+  t.m0 = s_offs[lo] + mi * bm;
+  t.m1 = s_offs[lo + 1];
+  return t;
+}
+
+// Persistent kernel: one workgroup per CU walks its share of the tiles
+// (XCD-local, see decode_tile).  The copies of K block kb of the current or
+// a later tile ("steps") are issued STAGES-1 steps ahead of the step being
+// multiplied, across tile boundaries, so a tile's first K blocks load while
+// the previous tile finishes.  With GATHER, the A row indices of the next
+// tile are copied into LDS one tile ahead (every step of a tile repeats that
+// copy, so the table a new tile reads was written by a copy that has already
+// been waited for).
+template <int BM, int WAVES_M, int STAGES, bool SWIGLU, bool GATHER>
+__global__ __launch_bounds__(GM_THREADS, 1) void grouped_gemm_kernel(GemmArgs args) {
+  using C_ = Cfg<BM, WAVES_M, STAGES, SWIGLU, GATHER>;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[C_::LDS];
+  __shared__ int s_red[4];
+  __shared__ int s_carry;
+  int* s_pref = reinterpret_cast<int*>(smem + C_::OFF_PREF);
+  int* s_offs = reinterpret_cast<int*>(smem + C_::OFF_OFFS);
+  int* s_ridx = reinterpret_cast<int*>(smem + C_::OFF_RIDX);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wv / C_::WAVES_N, wn = wv % C_::WAVES_N;
+  const int G = args.G;
+  const int64_t K = args.K, N = args.N, ntiles = args.ntiles;
+  const int64_t nkb = K >> 7;
+
+  // ---- group tables: offsets and exclusive prefix of M tiles per group ----
+  for (int g = tid; g <= G; g += GM_THREADS) s_offs[g] = args.offs[g];
+  if (tid == 0) {
+    s_carry = 0;
+    s_pref[0] = 0;
+  }
+  __syncthreads();
+  for (int g0 = 0; g0 < G; g0 += GM_THREADS) {
+    const int g = g0 + tid;
+    const int cnt = g < G ? (s_offs[g + 1] - s_offs[g] + BM - 1) / BM : 0;
+    int v = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int n = __shfl_up(v, o, 64);
+      if (lane >= o) v += n;
+    }
+    if (lane == 63) s_red[wv] = v;
+    __syncthreads();
+    int add = s_carry;
+    for (int w = 0; w < wv; ++w) add += s_red[w];
+    if (g < G) s_pref[g + 1] = add + v;
+    __syncthreads();
+    if (tid == GM_THREADS - 1) s_carry = add + v;
+    __syncthreads();
+  }
+  const int64_t total = (int64_t)s_pref[G] * ntiles;
+  // this workgroup's tiles: XCD x owns ids [x*chunk, (x+1)*chunk); its
+  // workgroups (blocks x, x+8, ...) take every (gridDim/8)-th of them
+  const int xcd = blockIdx.x & 7, jw = blockIdx.x >> 3, nper = gridDim.x >> 3;
+  const int64_t chunk = (total + 7) >> 3;
+  const int64_t tlo = xcd * chunk, thi = min(total, tlo + chunk);
+  const int64_t L0 = tlo + jw;
+  if (L0 >= thi) return;
+  const int64_t my_n = (thi - L0 + nper - 1) / nper;
+  const int64_t nsteps = my_n * nkb;
+
+  auto tile_of = [&](int64_t ord) {
+    Tile t = decode_tile(s_pref, s_offs, G, ntiles, L0 + ord * nper, BM);
+    t.g = __builtin_amdgcn_readfirstlane(t.g);
+    t.m0 = __builtin_amdgcn_readfirstlane(t.m0);
+    t.m1 = __builtin_amdgcn_readfirstlane(t.m1);
+    t.nt = __builtin_amdgcn_readfirstlane((int)t.nt);
+    return t;
+  };
+
+  // ---- issue side: per-lane copy sources of the tile being issued ----
+  // copy instruction q covers tile rows 8q..8q+7: lane -> row 8q + lane/8,
+  // LDS slot lane%8, so it fetches global chunk (lane%8) ^ swz(row) with
+  // swz(row) = (lane/8) ^ (q & 1).
+  const int chunk0 = (lane & 7) ^ (lane >> 3);
+  const int chunk1 = chunk0 ^ 1;
+  const uint8_t* a_src[C_::A_LOADS];
+  const uint8_t* b_src0 = nullptr;
+  const uint8_t* b_src1 = nullptr;
+  bool b_tail = false;
+  const float* s_src = nullptr;
+  const int32_t* r_src = nullptr;  // row-index copy source (next tile)
+
+  auto row_src = [&](const Tile& t, int64_t ord, int row) -> int64_t {
+    if (GATHER) return (int64_t)s_ridx[(ord & 1) * 256 + row];
+    return (int64_t)min(t.m0 + row, t.m1 - 1);
+  };
+  auto setup_issue = [&](int64_t ord) {
+    const Tile t = tile_of(ord);
+#pragma unroll
+    for (int qi = 0; qi < C_::A_LOADS; ++qi) {
+      const int q = wv * C_::A_LOADS + qi;
+      const int row = 8 * q + (lane >> 3);
+      a_src[qi] = args.A + row_src(t, ord, row) * K + ((q & 1) ? chunk1 : chunk0) * 16;
+    }
+    int64_t brow0;
+    if (SWIGLU) brow0 = ((wv < 2) ? 0 : args.I) + 128 * t.nt + 64 * (wv & 1) + (lane >> 3);
+    else brow0 = 256 * t.nt + 64 * wv + (lane >> 3);
+    const uint8_t* b_row = args.B + ((int64_t)t.g * N + min<int64_t>(brow0, N - 1)) * K;
+    b_src0 = b_row + chunk0 * 16;
+    b_src1 = b_row + chunk1 * 16;
+    b_tail = (brow0 - (lane >> 3)) + 64 > N;  // wave-uniform
+    const int srow = 64 * wv + lane;
+    if (srow < BM) {
+      s_src = args.A_scale + row_src(t, ord, srow) * nkb;
+    } else {
+      const int b = srow & 1;
+      const int64_t nb = SWIGLU ? (b ? (args.I >> 7) + t.nt : t.nt)
+                                : min<int64_t>(2 * t.nt + b, (N >> 7) - 1);
+      s_src = args.B_scale + ((int64_t)t.g * (N >> 7) + nb) * nkb;
+    }
+    if (GATHER) {
+      const Tile tn = (ord + 1 < my_n) ? tile_of(ord + 1) : t;
+      r_src = args.a_row_index + min(tn.m0 + min(64 * wv + lane, BM - 1), tn.m1 - 1);
+    }
+  };
+
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+  const int nkb32 = (int)nkb;
+  const int64_t K8 = 8 * K;
+  // issue position (tile ordinal, K block, ring slot), advanced per step
+  int iss_ord = 0, iss_kb = 0, iss_slot = 0;
+  // One step's copies, split so they can be spread over the MFMA loop:
+  // issue_begin() sets up the step (new tile: per-lane sources), issue_op(k)
+  // issues copy k of LOADS, issue_end() advances the issue position.  A wave
+  // that issues into a saturated memory pipeline stalls; spread between
+  // MFMAs, those stalls overlap the matrix pipe's work.
+  uint32_t iss_st = 0;
+  int64_t iss_ko = 0;
+  auto issue_begin = [&]() {
+    if (iss_kb == 0) setup_issue(iss_ord);
+    iss_st = lds0 + (uint32_t)iss_slot * C_::STAGE;
+    iss_ko = (int64_t)iss_kb * 128;
+  };
+  auto issue_op = [&](int k) {
+    if (k < C_::A_LOADS) {
+      dma16(a_src[k] + iss_ko, iss_st + (wv * C_::A_LOADS + k) * 1024);
+    } else if (k < C_::A_LOADS + C_::B_LOADS) {
+      const int qi = k - C_::A_LOADS;
+      dma16(((qi & 1) ? b_src1 : b_src0) + (b_tail ? 0 : qi * K8) + iss_ko,
+            iss_st + C_::A_BYTES + (wv * 8 + qi) * 1024);
+    } else if (k == C_::A_LOADS + C_::B_LOADS) {
+      dma4(s_src + iss_kb, iss_st + C_::A_BYTES + C_::B_BYTES + wv * 256);
+    } else {
+      dma4(r_src, lds0 + C_::OFF_RIDX + (uint32_t)(((iss_ord + 1) & 1) * 1024 + wv * 256));
+    }
+  };
+  auto issue_end = [&]() {
+    if (++iss_kb == nkb32) {
+      iss_kb = 0;
+      ++iss_ord;
+    }
+    if (++iss_slot == STAGES) iss_slot = 0;
+  };
+  auto issue_step = [&]() {
+    issue_begin();
+#pragma unroll
+    for (int k = 0; k < C_::LOADS; ++k) issue_op(k);
+    issue_end();
+  };
+
+  // ---- prologue: row indices of the first tile, then STAGES-1 steps ----
+  if (GATHER) {
+    const Tile t0 = tile_of(0);
+    dma4(args.a_row_index + min(t0.m0 + min(64 * wv + lane, BM - 1), t0.m1 - 1),
+         lds0 + C_::OFF_RIDX + wv * 256);
+    wait_vmcnt<0>();
+    barrier();
+  }
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s) {
+    if (s < nsteps) {
+      if (GATHER && iss_kb == 0 && iss_ord > 0) {
+        // short K: this tile's row-index table was copied by a step issued
+        // just before; drain before reading it
+        wait_vmcnt<0>();
+        barrier();
+      }
+      issue_step();
+    }
+  }
+
+  v4f acc[C_::SI][C_::SJ];
+#pragma unroll
+  for (int i = 0; i < C_::SI; ++i)
+#pragma unroll
+    for (int j = 0; j < C_::SJ; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  const int h = lane >> 4;
+  constexpr int WHN = 128 / C_::WAVES_N;  // SwiGLU: h columns per wave
+  constexpr int SJH = C_::SJ / 2;
+  // B tile row of this lane for column subtile j
+  auto b_row_of = [&](int j) -> int {
+    if (SWIGLU) return (j < SJH ? wn * WHN + 16 * j : 128 + wn * WHN + 16 * (j - SJH)) + (lane & 15);
+    return wn * C_::WTN + 16 * j + (lane & 15);
+  };
+
+  const int nsteps32 = (int)nsteps;
+  int c_ord = 0, c_kb = 0, slot = 0;  // consume position
+  for (int c = 0; c < nsteps32; ++c) {
+    const int after = min(STAGES - 2, nsteps32 - 1 - c);
+    if (STAGES >= 4 && after >= 2) wait_vmcnt<(STAGES >= 4 ? 2 : 0) * C_::LOADS>();
+    else if (after >= 1) wait_vmcnt<C_::LOADS>();
+    else wait_vmcnt<0>();
+    barrier();
+    const bool do_issue = c + STAGES - 1 < nsteps32;
+    if (do_issue) {
+      if (GATHER && nkb32 < STAGES - 1 && iss_kb == 0) {
+        // short K: the last copy of the next tile's row indices may still be
+        // in flight; drain before reading the table
+        wait_vmcnt<0>();
+        barrier();
+      }
+      issue_begin();
+    }
+
+    const uint8_t* tA = smem + slot * C_::STAGE;
+    const uint8_t* tB = tA + C_::A_BYTES;
+    const float* tS = reinterpret_cast<const float*>(tB + C_::B_BYTES);
+    float sc0[C_::SI][4], sc1[C_::SI][4];  // sc1: SwiGLU up half
+    {
+      const float sb0 = SWIGLU ? tS[BM] : tS[BM + ((wn * C_::WTN) >> 7)];
+      const float sb1 = tS[BM + 1];
+#pragma unroll
+      for (int i = 0; i < C_::SI; ++i) {
+        const float4 v = *reinterpret_cast<const float4*>(tS + wm * C_::WTM + i * 16 + 4 * h);
+        const float sa[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          sc0[i][r] = sa[r] * sb0;
+          sc1[i][r] = SWIGLU ? sa[r] * sb1 : 0.f;
+        }
+      }
+    }
+    v8i a[C_::SI];
+#pragma unroll
+    for (int i = 0; i < C_::SI; ++i) a[i] = lds_frag(tA, wm * C_::WTM + i * 16 + (lane & 15), h);
+    // software pipeline over column subtiles: the MFMAs of subtile j and the
+    // LDS read of j+1 are issued before the promotion FMAs of subtile j-1
+    v8i bcur = lds_frag(tB, b_row_of(0), h);
+    v4f pprev[C_::SI];
+#pragma unroll
+    for (int j = 0; j < C_::SJ; ++j) {
+      v8i bnext = bcur;
+      if (j + 1 < C_::SJ) bnext = lds_frag(tB, b_row_of(j + 1), h);
+      v4f pcur[C_::SI];
+#pragma unroll
+      for (int i = 0; i < C_::SI; ++i) pcur[i] = mfma_fp8_block(a[i], bcur);
+      if (do_issue) {
+        // copies k in [j*LOADS/SJ, (j+1)*LOADS/SJ) of the step STAGES-1 ahead
+#pragma unroll
+        for (int k = (j * C_::LOADS) / C_::SJ; k < ((j + 1) * C_::LOADS) / C_::SJ; ++k) issue_op(k);
+      }
+      if (j > 0) {
+        const bool up = SWIGLU && (j - 1) >= SJH;
+#pragma unroll
+        for (int i = 0; i < C_::SI; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            acc[i][j - 1][r] = fmaf(up ? sc1[i][r] : sc0[i][r], pprev[i][r], acc[i][j - 1][r]);
+      }
+#pragma unroll
+      for (int i = 0; i < C_::SI; ++i) pprev[i] = pcur[i];
+      bcur = bnext;
+    }
+    if (do_issue) issue_end();
+    {
+      const bool up = SWIGLU && (C_::SJ - 1) >= SJH;
+#pragma unroll
+      for (int i = 0; i < C_::SI; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          acc[i][C_::SJ - 1][r] =
+              fmaf(up ? sc1[i][r] : sc0[i][r], pprev[i][r], acc[i][C_::SJ - 1][r]);
+    }
+
+    const int ct = c_ord;
+    const bool tile_done = (c_kb == nkb32 - 1);
+    if (++slot == STAGES) slot = 0;
+    if (++c_kb == nkb32) {
+      c_kb = 0;
+      ++c_ord;
+    }
+    if (!tile_done) continue;
+
+    // ---- epilogue of tile ct (from registers) ----
+    const Tile t = tile_of(ct);
+    if (!SWIGLU) {
+      // bf16 (round to nearest even); the 4 lanes of a quad hold 4
+      // consecutive columns of a row, lane 4k stores them as one 8-byte word
+#pragma unroll
+      for (int i = 0; i < C_::SI; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int64_t row = (int64_t)t.m0 + wm * C_::WTM + i * 16 + 4 * h + r;
+          const bool ok = row < t.m1 && (lane & 3) == 0;
+#pragma unroll
+          for (int j = 0; j < C_::SJ; ++j) {
+            const float v0 = acc[i][j][r];
+            const float v1 = quad_lane1(v0), v2 = quad_lane2(v0), v3 = quad_lane3(v0);
+            const int64_t col = 256 * t.nt + wn * C_::WTN + j * 16 + (lane & 15);
+            if (ok && col < N)
+              *reinterpret_cast<uint2*>(args.C + row * N + col) =
+                  make_uint2(f32x2_to_bf16x2(v0, v1), f32x2_to_bf16x2(v2, v3));
+          }
+        }
+    } else {
+      // h = silu(g) * u per (row, h column): gate subtile j pairs with up
+      // subtile j + SJ/2 in this lane's registers.  exp and the reciprocal
+      // use the hardware v_exp_f32 / v_rcp_f32 (a few ulp; h feeds a 3-bit
+      // mantissa code).
+      float* s_amax = reinterpret_cast<float*>(smem + C_::OFF_AMAX);
+#pragma unroll
+      for (int i = 0; i < C_::SI; ++i)
+#pragma unroll
+        for (int j = 0; j < SJH; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float g = acc[i][j][r], u = acc[i][j + SJH][r];
+            const float e = __builtin_amdgcn_exp2f(g * -1.4426950408889634f);
+            const float a = g * __builtin_amdgcn_rcpf(1.0f + e);
+            acc[i][j][r] = a * u;
+          }
+#pragma unroll
+      for (int i = 0; i < C_::SI; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float m = 0.f;
+#pragma unroll
+          for (int j = 0; j < SJH; ++j) m = fmaxf(m, fabsf(acc[i][j][r]));
+#pragma unroll
+          for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+          if ((lane & 15) == 0) s_amax[(wm * C_::WTM + i * 16 + 4 * h + r) * C_::WAVES_N + wn] = m;
+        }
+      barrier();
+#pragma unroll
+      for (int i = 0; i < C_::SI; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int trow = wm * C_::WTM + i * 16 + 4 * h + r;
+          float amax = 0.f;
+#pragma unroll
+          for (int w = 0; w < C_::WAVES_N; ++w) amax = fmaxf(amax, s_amax[trow * C_::WAVES_N + w]);
+          const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
+          const float inv = 1.0f / sc;
+          const int64_t row = (int64_t)t.m0 + trow;
+          const bool ok = row < t.m1;
+#pragma unroll
+          for (int j = 0; j < SJH; ++j) {
+            const float v0 = acc[i][j][r] * inv;
+            const float v1 = quad_lane1(v0), v2 = quad_lane2(v0), v3 = quad_lane3(v0);
+            const int64_t col = 128 * t.nt + wn * WHN + 16 * j + (lane & 15);
+            if (ok && (lane & 3) == 0)
+              *reinterpret_cast<uint32_t*>(args.Hq + row * args.I + col) =
+                  f32x4_to_e4m3x4(v0, v1, v2, v3);
+          }
+          if (ok && wn == 0 && (lane & 15) == 0) args.Hs[row * (args.I >> 7) + t.nt] = sc;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < C_::SI; ++i)
+#pragma unroll
+      for (int j = 0; j < C_::SJ; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+  }
+}
+
+int num_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+template <int BM, int WAVES_M, int STAGES, bool SWIGLU>
+int launch(const GemmArgs& a, hipStream_t st) {
+  const int grid = std::max(8, (num_cus() / 8) * 8);
+  if (a.a_row_index)
+    grouped_gemm_kernel<BM, WAVES_M, STAGES, SWIGLU, true><<<dim3(grid), dim3(GM_THREADS), 0, st>>>(a);
+  else
+    grouped_gemm_kernel<BM, WAVES_M, STAGES, SWIGLU, false><<<dim3(grid), dim3(GM_THREADS), 0, st>>>(a);
+  return MOE_OK;
+}
+
+template <bool SWIGLU>
+int dispatch(const GemmArgs& a, int64_t M_total, hipStream_t st) {
+  // rows per group decide the M tile: 128 for prefill-sized groups, 32 when
+  // groups hold a handful of rows (decode), 64 in between
+  const int64_t avg = M_total / a.G;
+  if (avg >= 96) return launch<128, 2, 3, SWIGLU>(a, st);
+  if (avg >= 40) return launch<64, 1, 3, SWIGLU>(a, st);
+  return launch<32, 1, 4, SWIGLU>(a, st);
+}
+
+int validate_common(const char* who, const uint8_t* A, const float* A_scale, const uint8_t* B,
+                    const float* B_scale, const int32_t* group_offsets, int32_t G,
+                    int64_t M_total, int64_t N, int64_t K) {
+  MOE_INVALID(G >= 1, "%s: G=%d must be >= 1", who, (int)G);
+  MOE_UNSUPPORTED(G <= MAXG, "%s: G=%d > %d groups is not supported", who, (int)G, MAXG);
+  MOE_INVALID(M_total >= 0 && M_total < (1ll << 31), "%s: M_total=%lld out of range", who,
+              (long long)M_total);
+  MOE_INVALID(N > 0 && N % 128 == 0, "%s: N=%lld must be a positive multiple of 128", who,
+              (long long)N);
+  MOE_INVALID(K > 0 && K % 128 == 0, "%s: K=%lld must be a positive multiple of 128", who,
+              (long long)K);
+  if (M_total == 0) return MOE_OK;
+  MOE_INVALID(A && A_scale && B && B_scale && group_offsets, "%s: null pointer", who);
+  MOE_INVALID(((uintptr_t)A & 15) == 0 && ((uintptr_t)B & 15) == 0 &&
+                  ((uintptr_t)A_scale & 3) == 0 && ((uintptr_t)B_scale & 3) == 0,
+              "%s: A and B must be 16-byte aligned, scales 4-byte aligned", who);
+  return MOE_OK;
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" int grouped_fp8_gemm(const uint8_t* A, const float* A_scale, const int32_t* a_row_index,
+                                const uint8_t* B, const float* B_scale,
+                                const int32_t* group_offsets, int32_t G, int64_t M_total, int64_t N,
+                                int64_t K, void* C_bf16, void* stream) {
+  clear_error();
+  int rc = validate_common("grouped_fp8_gemm", A, A_scale, B, B_scale, group_offsets, G, M_total,
+                           N, K);
+  if (rc != MOE_OK || M_total == 0) return rc;
+  MOE_INVALID(C_bf16 && ((uintptr_t)C_bf16 & 15) == 0,
+              "grouped_fp8_gemm: C must be non-null and 16-byte aligned");
+  GemmArgs a{};
+  a.A = A; a.A_scale = A_scale; a.a_row_index = a_row_index; a.B = B; a.B_scale = B_scale;
+  a.offs = group_offsets; a.G = G; a.N = N; a.K = K; a.ntiles = ceil_div(N, BN); a.I = 0;
+  a.C = static_cast<uint16_t*>(C_bf16);
+  rc = dispatch<false>(a, M_total, as_stream(stream));
+  if (rc != MOE_OK) return rc;
+  return check_launch("grouped_fp8_gemm");
+}
+
+extern "C" int grouped_fp8_gemm_swiglu(const uint8_t* A, const float* A_scale,
+                                       const int32_t* a_row_index, const uint8_t* B,
+                                       const float* B_scale, const int32_t* group_offsets,
+                                       int32_t G, int64_t M_total, int64_t I, int64_t K,
+                                       uint8_t* H_e4m3, float* H_scale, void* stream) {
+  clear_error();
+  MOE_INVALID(I > 0 && I % 128 == 0, "grouped_fp8_gemm_swiglu: I=%lld must be a positive "
+              "multiple of 128", (long long)I);
+  int rc = validate_common("grouped_fp8_gemm_swiglu", A, A_scale, B, B_scale, group_offsets, G,
+                           M_total, 2 * I, K);
+  if (rc != MOE_OK || M_total == 0) return rc;
+  MOE_INVALID(H_e4m3 && H_scale && ((uintptr_t)H_e4m3 & 15) == 0,
+              "grouped_fp8_gemm_swiglu: H must be non-null and 16-byte aligned");
+  GemmArgs a{};
+  a.A = A; a.A_scale = A_scale; a.a_row_index = a_row_index; a.B = B; a.B_scale = B_scale;
+  a.offs = group_offsets; a.G = G; a.N = 2 * I; a.K = K; a.ntiles = I / 128; a.I = I;
+  a.Hq = H_e4m3; a.Hs = H_scale;
+  rc = dispatch<true>(a, M_total, as_stream(stream));
+  if (rc != MOE_OK) return rc;
+  return check_launch("grouped_fp8_gemm_swiglu");
+}

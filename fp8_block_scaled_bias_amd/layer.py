@@ -1,0 +1,210 @@
+"""DeepSeekMoE layer forward composed from the C-ABI calls.
+
+The steps, in the order the method applies them (aliyun study note
+developer.aliyun.com/article/1776647 section 2.2; news.qq.com/rain/a/
+20241229A05OQF00 sections DeepSeekMoE 架构, 无额外损耗的负载均衡 and
+FP8 低精度训练):
+
+  1. moe_route         sigmoid scores + selection bias, 4-of-8-group top-8
+  2. fp8_quant_1x128   x -> E4M3 with 1x128 scales
+  3. moe_permute       expert-major dispatch order (no copy: GEMM 1 gathers)
+  4. grouped_fp8_gemm_swiglu
+                       gate+up of the 256 routed experts and the shared one,
+                       SwiGLU and 1x128 requantisation in the epilogue (the
+                       unfused form - grouped_fp8_gemm to bf16, then
+                       fp8_quant_1x128 mode 1 - is kept behind fused=False)
+  5. grouped_fp8_gemm  down projection
+  6. moe_combine       gate-weighted sum of routed outputs + shared output
+  7. moe_bias_update   (optional) aux-loss-free bias step for the next batch
+
+torch is only used to hold device memory and to name the stream; every step
+runs in the library's HIP kernels.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import torch
+
+from . import _lib as L
+
+
+@dataclasses.dataclass(frozen=True)
+class LayerShape:
+    H: int
+    E: int
+    n_group: int
+    topk_group: int
+    k: int
+    I: int
+    n_shared: int = 1
+
+    @property
+    def G(self):
+        return self.E + self.n_shared
+
+
+class Buffers:
+    """Device buffers of one forward at T tokens (reused across calls)."""
+
+    def __init__(self, shape: LayerShape, T: int, device="cuda"):
+        s = shape
+        R = T * s.k + s.n_shared * T
+        dev = torch.device(device)
+        u8, i32, f32, bf = torch.uint8, torch.int32, torch.float32, torch.bfloat16
+        self.T, self.R = T, R
+        self.topk_idx = torch.empty((T, s.k), dtype=i32, device=dev)
+        self.topk_w = torch.empty((T, s.k), dtype=f32, device=dev)
+        self.counts = torch.empty((s.E,), dtype=i32, device=dev)
+        self.route_ws_bytes = max(16, L.moe_route_workspace_bytes(T, s.H, s.E))
+        self.route_ws = torch.empty((self.route_ws_bytes,), dtype=u8, device=dev)
+        self.xq = torch.empty((T, s.H), dtype=u8, device=dev)
+        self.xs = torch.empty((T, s.H // 128), dtype=f32, device=dev)
+        self.offsets = torch.empty((s.G + 1,), dtype=i32, device=dev)
+        self.perm_src = torch.empty((max(R, 1),), dtype=i32, device=dev)
+        self.inv_perm = torch.empty((max(T * s.k, 1),), dtype=i32, device=dev)
+        self.perm_ws_bytes = max(16, L.moe_permute_workspace_bytes(T, s.k, s.E))
+        self.perm_ws = torch.empty((self.perm_ws_bytes,), dtype=u8, device=dev)
+        self._hgu = None
+        self._dev = dev
+        self._shape = s
+        self.hq = torch.empty((R, s.I), dtype=u8, device=dev)
+        self.hs = torch.empty((R, s.I // 128), dtype=f32, device=dev)
+        self.d = torch.empty((R, s.H), dtype=bf, device=dev)
+        self.y = torch.empty((T, s.H), dtype=bf, device=dev)
+
+    @property
+    def hgu(self):
+        """bf16 gate+up output of the unfused path (allocated on first use)."""
+        if self._hgu is None:
+            self._hgu = torch.empty((self.R, 2 * self._shape.I), dtype=torch.bfloat16,
+                                    device=self._dev)
+        return self._hgu
+
+
+class MoELayer:
+    """One MoE layer on one GPU: router state and FP8 expert weights.
+
+    Weights are E4M3 with 128x128 scales:
+      w_gu [G, 2I, H] (rows [0, I) gate, [I, 2I) up), w_gu_s [G, 2I/128, H/128]
+      w_dn [G, H, I],                                  w_dn_s [G, H/128, I/128]
+    Group E (the last) is the shared expert.
+    """
+
+    def __init__(self, shape: LayerShape, centroids, bias, w_gu, w_gu_s, w_dn, w_dn_s):
+        self.shape = shape
+        self.centroids = centroids
+        self.bias = bias
+        self.w_gu, self.w_gu_s, self.w_dn, self.w_dn_s = w_gu, w_gu_s, w_dn, w_dn_s
+        self._bufs = {}
+
+    @staticmethod
+    def empty_weights(shape: LayerShape, device="cuda"):
+        s = shape
+        dev = torch.device(device)
+        return (torch.empty((s.G, 2 * s.I, s.H), dtype=torch.uint8, device=dev),
+                torch.empty((s.G, 2 * s.I // 128, s.H // 128), dtype=torch.float32, device=dev),
+                torch.empty((s.G, s.H, s.I), dtype=torch.uint8, device=dev),
+                torch.empty((s.G, s.H // 128, s.I // 128), dtype=torch.float32, device=dev))
+
+    @staticmethod
+    def quantize_into(w_f32, out_q, out_s, stream=None):
+        """128x128 block quantisation of fp32 weights [G', N, K] into E4M3 + scales."""
+        G, N, K = w_f32.shape
+        L.fp8_quant_128x128(w_f32, G, N, K, out_q, out_s, stream)
+
+    @classmethod
+    def from_fp32_experts(cls, shape: LayerShape, centroids, bias, gu_fp32, dn_fp32,
+                          device="cuda"):
+        """Build a layer from per-expert fp32 weights, quantised on the GPU.
+
+        gu_fp32 / dn_fp32: iterables of (expert, array [2I, H] / [H, I]) covering
+        every group 0..G-1 (G-1 is the shared expert).  Each array is copied
+        to the GPU and quantised in 128x128 blocks by fp8_quant_128x128.
+        """
+        w_gu, w_gu_s, w_dn, w_dn_s = cls.empty_weights(shape, device)
+        stream = torch.cuda.current_stream()
+        for src, q, s in ((gu_fp32, w_gu, w_gu_s), (dn_fp32, w_dn, w_dn_s)):
+            for e, arr in src:
+                t = torch.from_numpy(arr).to(device)
+                cls.quantize_into(t[None], q[e:e + 1], s[e:e + 1], stream)
+                stream.synchronize()
+        return cls(shape, centroids, bias, w_gu, w_gu_s, w_dn, w_dn_s)
+
+    def buffers(self, T: int) -> Buffers:
+        b = self._bufs.get(T)
+        if b is None:
+            b = self._bufs[T] = Buffers(self.shape, T, self.centroids.device)
+        return b
+
+    def forward(self, x_bf16: torch.Tensor, bufs: Buffers | None = None, stream=None,
+                update_bias: bool = False, gamma: float = 0.001,
+                fused: bool = True, events: dict | None = None) -> torch.Tensor:
+        """One layer forward.  `events`, if given, maps a step name ("route",
+        "quant", "permute", "gate_up", "down", "combine", "bias") to a list
+        that receives a (start, end) pair of torch.cuda.Event recorded on the
+        launch stream around that step."""
+        s = self.shape
+        T = x_bf16.shape[0]
+        b = bufs or self.buffers(T)
+        R = b.R
+        if events is not None:
+            return self._forward_timed(x_bf16, b, stream, update_bias, gamma, fused, events)
+        L.moe_route(x_bf16, T, s.H, self.centroids, self.bias, s.E, s.n_group, s.topk_group,
+                    s.k, b.topk_idx, b.topk_w, b.counts, b.route_ws, b.route_ws_bytes, stream)
+        L.fp8_quant_1x128(x_bf16, T, s.H, s.H, 0, b.xq, b.xs, stream)
+        L.moe_permute(b.topk_idx, b.counts, T, s.k, s.E, s.n_shared, b.offsets, b.perm_src,
+                      b.inv_perm, None, None, s.H, None, None, b.perm_ws, b.perm_ws_bytes,
+                      stream)
+        if fused:
+            L.grouped_fp8_gemm_swiglu(b.xq, b.xs, b.perm_src, self.w_gu, self.w_gu_s, b.offsets,
+                                      s.G, R, s.I, s.H, b.hq, b.hs, stream)
+        else:
+            L.grouped_fp8_gemm(b.xq, b.xs, b.perm_src, self.w_gu, self.w_gu_s, b.offsets, s.G,
+                               R, 2 * s.I, s.H, b.hgu, stream)
+            L.fp8_quant_1x128(b.hgu, R, s.I, 2 * s.I, 1, b.hq, b.hs, stream)
+        L.grouped_fp8_gemm(b.hq, b.hs, None, self.w_dn, self.w_dn_s, b.offsets, s.G, R, s.H,
+                           s.I, b.d, stream)
+        shared = b.d[T * s.k:T * s.k + T] if s.n_shared else None
+        L.moe_combine(b.d, b.inv_perm, b.topk_w, shared, T, s.k, s.H, b.y, stream)
+        if update_bias:
+            L.moe_bias_update(b.counts, self.bias, s.E, gamma, stream)
+        return b.y
+
+    def _forward_timed(self, x_bf16, b, stream, update_bias, gamma, fused, events):
+        s = self.shape
+        T, R = x_bf16.shape[0], b.R
+        st = stream if stream is not None else torch.cuda.current_stream()
+
+        def timed(name, fn):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            fn()
+            e1.record(st)
+            events.setdefault(name, []).append((e0, e1))
+
+        timed("route", lambda: L.moe_route(
+            x_bf16, T, s.H, self.centroids, self.bias, s.E, s.n_group, s.topk_group, s.k,
+            b.topk_idx, b.topk_w, b.counts, b.route_ws, b.route_ws_bytes, st))
+        timed("quant", lambda: L.fp8_quant_1x128(x_bf16, T, s.H, s.H, 0, b.xq, b.xs, st))
+        timed("permute", lambda: L.moe_permute(
+            b.topk_idx, b.counts, T, s.k, s.E, s.n_shared, b.offsets, b.perm_src, b.inv_perm,
+            None, None, s.H, None, None, b.perm_ws, b.perm_ws_bytes, st))
+        if fused:
+            timed("gate_up", lambda: L.grouped_fp8_gemm_swiglu(
+                b.xq, b.xs, b.perm_src, self.w_gu, self.w_gu_s, b.offsets, s.G, R, s.I, s.H,
+                b.hq, b.hs, st))
+        else:
+            timed("gate_up", lambda: L.grouped_fp8_gemm(
+                b.xq, b.xs, b.perm_src, self.w_gu, self.w_gu_s, b.offsets, s.G, R, 2 * s.I,
+                s.H, b.hgu, st))
+            timed("swiglu", lambda: L.fp8_quant_1x128(b.hgu, R, s.I, 2 * s.I, 1, b.hq, b.hs, st))
+        timed("down", lambda: L.grouped_fp8_gemm(
+            b.hq, b.hs, None, self.w_dn, self.w_dn_s, b.offsets, s.G, R, s.H, s.I, b.d, st))
+        shared = b.d[T * s.k:T * s.k + T] if s.n_shared else None
+        timed("combine", lambda: L.moe_combine(b.d, b.inv_perm, b.topk_w, shared, T, s.k, s.H,
+                                               b.y, st))
+        if update_bias:
+            timed("bias", lambda: L.moe_bias_update(b.counts, self.bias, s.E, gamma, st))
+        return b.y

@@ -1,0 +1,249 @@
+/*
+ * moe_fp8.h - C ABI of libmoe_fp8.so, the DeepSeekMoE layer forward on
+ * MI355X (gfx950).
+ *
+ * The layer follows the DeepSeek-V3 pages:
+ *   - sigmoid gating with a per-expert bias used only to choose experts
+ *     (aliyun study note developer.aliyun.com/article/1776647, section 2.2;
+ *     news.qq.com/rain/a/20241229A05OQF00, section 无额外损耗的负载均衡);
+ *   - 1 shared + 256 routed experts, 8 routed per token, at most 4 nodes per
+ *     token (news.qq.com article, sections DeepSeekMoE 架构 and 节点限制路由);
+ *   - FP8 GEMMs with 1x128 activation tiles, 128x128 weight blocks and
+ *     high-precision accumulation (news.qq.com article, section FP8 低精度训练,
+ *     items 细粒度量化 and 提高累加精度).
+ *
+ * Conventions shared by every call:
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The
+ *     library never allocates, frees or keeps a pointer after the call.
+ *   - Layouts are row-major and dense unless a leading dimension is given.
+ *     "bf16" buffers hold raw bfloat16 bit patterns (uint16).  "e4m3" buffers
+ *     hold OCP E4M3FN bytes.  Scales are fp32.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Work is enqueued asynchronously on it; the caller keeps every buffer
+ *     alive until the stream has finished.  No call synchronises the host.
+ *   - Arguments are validated on the host before anything is launched.  On
+ *     error nothing is launched, the return value is negative and
+ *     moe_last_error() describes it.  Faults inside kernels surface at the
+ *     caller's next synchronisation, as for any HIP kernel.
+ *   - Outputs are fully overwritten, never accumulated into.  Inputs and
+ *     outputs must not alias (except where a call says "in place").
+ *   - A zero-sized problem (T == 0, M_total == 0) is a successful no-op that
+ *     still writes the outputs that do not depend on it (counts, offsets).
+ *   - NaN or Inf inputs give unspecified results.
+ */
+#ifndef MOE_FP8_H
+#define MOE_FP8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+#define MOE_OK               0
+#define MOE_ERR_INVALID     -1  /* null pointer, bad shape or parameter      */
+#define MOE_ERR_UNSUPPORTED -2  /* valid but outside what the kernels handle */
+#define MOE_ERR_HIP         -3  /* a HIP launch or API call failed            */
+#define MOE_ERR_WORKSPACE   -4  /* workspace too small                        */
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* moe_last_error(void);
+
+/* Library version string. */
+const char* moe_version(void);
+
+/*
+ * moe_route - router: sigmoid scores, selection bias, group-limited top-k.
+ *
+ * Follows the aliyun study note, section 2.2 (sigmoid gate per expert, a bias
+ * per expert that shifts only the choice), and the news.qq.com article,
+ * sections DeepSeekMoE 架构 (top-8 of 256) and 节点限制路由 (at most 4 nodes;
+ * here: groups).  Gating stays in high precision (same article,
+ * 选择性高精度): logits are computed with fp32 accumulation of exact
+ * products (bf16 x times a three-piece bf16 split of the fp32 centroids).
+ *
+ * For each token t:
+ *   l[e]  = sum_h x[t,h] * centroids[e,h]
+ *   s[e]  = 1 / (1 + exp(-l[e]))               (fp32)
+ *   s'[e] = s[e] + bias[e]                     (fp32, used to choose only)
+ *   experts form n_group contiguous groups of E/n_group; a group's score is
+ *   the sum of its two largest s'; the topk_group best groups are kept; the
+ *   k largest s' among the kept experts are chosen; ties go to the lower
+ *   index; ids are written in ascending order;
+ *   w[j]  = s[e_j] / sum_j' s[e_j']            (unbiased scores, fp32)
+ *   expert_counts[e] = number of tokens that chose e (overwritten).
+ *
+ * x_bf16          [T, H] bf16
+ * centroids       [E, H] fp32
+ * bias            [E] fp32
+ * topk_idx  (out) [T, k] int32, ascending per row
+ * topk_w    (out) [T, k] fp32, each row sums to 1
+ * expert_counts (out) [E] int32
+ * workspace       device scratch of at least moe_route_workspace_bytes(T, H, E)
+ *                 bytes (partial logits); contents on entry are ignored.
+ * Requirements: H % 128 == 0; 2 <= E <= 256; E % n_group == 0; the group
+ * size E/n_group is 4 times a power of two (4 .. 256); 1 <= topk_group <=
+ * n_group; 1 <= k <= 8; k <= topk_group * E / n_group.
+ */
+size_t moe_route_workspace_bytes(int64_t T, int64_t H, int32_t E);
+int moe_route(const void* x_bf16, int64_t T, int64_t H,
+              const float* centroids, const float* bias,
+              int32_t E, int32_t n_group, int32_t topk_group, int32_t k,
+              int32_t* topk_idx, float* topk_w, int32_t* expert_counts,
+              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * moe_bias_update - aux-loss-free balancing step, in place.
+ *
+ * aliyun study note section 2.2 (overloaded experts' bias goes down,
+ * underloaded goes up, no loss term) and news.qq.com article section
+ * 无额外损耗的负载均衡 (update speed gamma = 0.001).  With total = sum_e
+ * counts[e]: bias[e] -= gamma if counts[e]*E > total; bias[e] += gamma if
+ * counts[e]*E < total; unchanged otherwise.  fp32 arithmetic; integer test.
+ *
+ * expert_counts [E] int32 (e.g. the output of moe_route for this batch)
+ * bias          [E] fp32, updated in place
+ * Requirements: 1 <= E <= 1024.
+ */
+int moe_bias_update(const int32_t* expert_counts, float* bias, int32_t E,
+                    float gamma, void* stream);
+
+/*
+ * moe_permute - dispatch: expert-contiguous order of the token-expert
+ * assignments (the all-to-all dispatch of the news.qq.com article, section
+ * DualPipe 流水线并行, done inside one GPU).
+ *
+ * Rows of expert e are the assignments (t, j) with topk_idx[t,j] == e in
+ * ascending (t, j) order; the n_shared shared expert(s) follow, one block of
+ * T rows each in token order.  R = T*k + n_shared*T.
+ *
+ * topk_idx       [T, k] int32, values in [0, E)
+ * expert_counts  [E] int32, the histogram of topk_idx (as moe_route writes)
+ * offsets  (out) [E + n_shared + 1] int32: exclusive prefix sum of group sizes
+ * perm_src (out) [R] int32: token of each row
+ * inv_perm (out) [T*k] int32: row of assignment (t, j) at t*k + j
+ * xq, xs         optional [T, H] e4m3 and [T, H/128] fp32; when a_out is not
+ *                NULL, a_out[r] = xq[perm_src[r]] and a_scale_out[r] =
+ *                xs[perm_src[r]] ([R, H] e4m3, [R, H/128] fp32).
+ * workspace      at least moe_permute_workspace_bytes(T, k, E) bytes.
+ * Requirements: 1 <= k <= 8; 1 <= E <= 4096; n_shared in {0, 1};
+ * H % 128 == 0 when gathering.  topk_idx and expert_counts must be consistent.
+ */
+size_t moe_permute_workspace_bytes(int64_t T, int32_t k, int32_t E);
+int moe_permute(const int32_t* topk_idx, const int32_t* expert_counts,
+                int64_t T, int32_t k, int32_t E, int32_t n_shared,
+                int32_t* offsets, int32_t* perm_src, int32_t* inv_perm,
+                const uint8_t* xq, const float* xs, int64_t H,
+                uint8_t* a_out, float* a_scale_out,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fp8_quant_1x128 - fine-grained activation quantisation (news.qq.com
+ * article, section FP8 低精度训练 › 细粒度量化: 1x128 tiles for activations).
+ *
+ * For each row m and 128-column tile j of the output:
+ *   v     = mode 0: in[m, j*128 + c]
+ *           mode 1: silu(g) * u with g = in[m, j*128 + c], u = in[m, K + j*128 + c]
+ *                   evaluated in fp32 as a = g / (1 + exp(-g)); v = a * u
+ *   amax  = max_c |v|;  s = amax / 448 (fp32), or 1 if amax == 0
+ *   out   = E4M3FN(v / s): correctly rounded fp32 division, round to nearest
+ *           even, saturate to +-448, sign of zero kept
+ *   scales[m, j] = s
+ *
+ * in_bf16  [M, ld_in] bf16; mode 0 needs ld_in >= K, mode 1 needs ld_in >= 2K
+ * out_e4m3 [M, K] e4m3;  scales [M, K/128] fp32
+ * Requirements: K % 128 == 0, ld_in % 8 == 0, mode in {0, 1}.
+ */
+int fp8_quant_1x128(const void* in_bf16, int64_t M, int64_t K, int64_t ld_in,
+                    int32_t mode, uint8_t* out_e4m3, float* scales, void* stream);
+
+/*
+ * fp8_quant_128x128 - weight quantisation in 128x128 blocks (aliyun study
+ * note section 4.1; news.qq.com article section 细粒度量化).  Same scale and
+ * rounding rule as fp8_quant_1x128, with amax taken over each block.
+ *
+ * w_f32    [G, N, K] fp32;  out_e4m3 [G, N, K];  scales [G, N/128, K/128]
+ * Requirements: N % 128 == 0, K % 128 == 0.
+ */
+int fp8_quant_128x128(const float* w_f32, int64_t G, int64_t N, int64_t K,
+                      uint8_t* out_e4m3, float* scales, void* stream);
+
+/*
+ * grouped_fp8_gemm - block-scaled FP8 grouped GEMM with FP32 accumulation
+ * (news.qq.com article, section FP8 低精度训练, items 细粒度量化 and
+ * 提高累加精度).
+ *
+ * For group g, rows r in [group_offsets[g], group_offsets[g+1]):
+ *   C[r, n] = bf16( sum_kb  sa[r, kb] * B_scale[g, n/128, kb]
+ *                           * sum_{k in block kb} a[r, k] * B[g, n, k] )
+ * where a[r, :] = A[src(r), :], sa[r, :] = A_scale[src(r), :], and
+ * src(r) = a_row_index[r] if a_row_index is not NULL, else r.  Each 128-wide
+ * K block is one FP8 MFMA partial in FP32 that is scaled and added to an FP32
+ * total; the total is rounded to bf16 (nearest even) once.
+ *
+ * A        [rows_A, K] e4m3 (rows_A = M_total when a_row_index is NULL)
+ * A_scale  [rows_A, K/128] fp32
+ * a_row_index  [M_total] int32 or NULL
+ * B        [G, N, K] e4m3 (each group's matrix stored N x K, K contiguous)
+ * B_scale  [G, N/128, K/128] fp32
+ * group_offsets [G+1] int32 on the device, non-decreasing, [0] == 0,
+ *          [G] == M_total (read by the kernels, never by the host)
+ * C  (out) [M_total, N] bf16
+ * Requirements: N % 128 == 0, K % 128 == 0, G >= 1 (more than 1024 groups returns
+ * MOE_ERR_UNSUPPORTED).
+ */
+int grouped_fp8_gemm(const uint8_t* A, const float* A_scale, const int32_t* a_row_index,
+                     const uint8_t* B, const float* B_scale,
+                     const int32_t* group_offsets, int32_t G, int64_t M_total,
+                     int64_t N, int64_t K, void* C_bf16, void* stream);
+
+/*
+ * grouped_fp8_gemm_swiglu - the gate+up GEMM of the experts with SwiGLU and
+ * 1x128 requantisation fused into its epilogue (news.qq.com article, section
+ * FP8 低精度训练: FP8 GEMM with fine-grained scales and FP32 accumulation,
+ * activations kept in FP8; the SwiGLU form is this layer's expert FFN).
+ *
+ * B holds each group's fused weight [2I, K]: rows [0, I) gate, [I, 2I) up.
+ * For row r of group g and column c < I, with the FP32 totals
+ *   gt = sum_kb sa[r,kb] * B_scale[g, c/128, kb]     * sum_k a[r,k] B[g, c, k]
+ *   ut = sum_kb sa[r,kb] * B_scale[g, (I+c)/128, kb] * sum_k a[r,k] B[g, I+c, k]
+ * (accumulated as in grouped_fp8_gemm but never rounded to bf16 or stored):
+ *   h = (gt / (1 + exp(-gt))) * ut  in fp32, then per 128 columns of h
+ *   s = amax/448 (1 if 0), H_e4m3[r, c] = E4M3(h / s), H_scale[r, c/128] = s.
+ *
+ * A, A_scale, a_row_index, B_scale, group_offsets: as grouped_fp8_gemm with
+ * N = 2I.  H_e4m3 (out) [M_total, I] e4m3; H_scale (out) [M_total, I/128].
+ * Requirements: I % 128 == 0, K % 128 == 0, 1 <= G <= 1024.
+ */
+int grouped_fp8_gemm_swiglu(const uint8_t* A, const float* A_scale,
+                            const int32_t* a_row_index, const uint8_t* B,
+                            const float* B_scale, const int32_t* group_offsets,
+                            int32_t G, int64_t M_total, int64_t I, int64_t K,
+                            uint8_t* H_e4m3, float* H_scale, void* stream);
+
+/*
+ * moe_combine - weighted combine plus shared expert (news.qq.com article,
+ * section DeepSeekMoE 架构: shared experts are always on, routed experts are
+ * weighted by their gates).
+ *
+ *   y[t, :] = bf16( sum_{j<k} w[t, j] * D[inv_perm[t*k + j], :] + S[t, :] )
+ * accumulated in fp32 in slot order j = 0..k-1, then S added.
+ *
+ * expert_out_bf16 D [R, H] bf16 (R >= T*k)
+ * inv_perm        [T*k] int32
+ * topk_w          [T, k] fp32
+ * shared_out_bf16 S [T, H] bf16, or NULL for no shared expert
+ * y_bf16    (out) [T, H] bf16
+ * Requirements: 1 <= k <= 8, H % 8 == 0.
+ */
+int moe_combine(const void* expert_out_bf16, const int32_t* inv_perm,
+                const float* topk_w, const void* shared_out_bf16,
+                int64_t T, int32_t k, int64_t H, void* y_bf16, void* stream);
+
+#ifdef __cplusplus
+}  /* extern "C" */
+#endif
+
+#endif /* MOE_FP8_H */

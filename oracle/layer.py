@@ -42,6 +42,13 @@ class ExpertWeights:
         self._gu = lru_cache(maxsize=None)(lambda e: quant_128x128(fp32_gu(e)))
         self._dn = lru_cache(maxsize=None)(lambda e: quant_128x128(fp32_dn(e)))
 
+    def prefetch(self, experts, threads: int = 8):
+        """Quantise the given experts' weights ahead of use, on a thread pool."""
+        from concurrent.futures import ThreadPoolExecutor
+        experts = sorted(set(int(e) for e in experts))
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(lambda e: (self.gu(e), self.dn(e)), experts))
+
     def gu(self, e):
         return self._gu(e)
 
@@ -50,7 +57,9 @@ class ExpertWeights:
 
 
 def layer(x_bits, centroids, bias, wts: ExpertWeights, n_group, topk_group, k, I,
-          n_shared: int = 1):
+          n_shared: int = 1, fused: bool = True):
+    """fused=True: SwiGLU reads the gate/up sums in FP32 (never stored);
+    fused=False: they are stored as bf16 first."""
     T, H = x_bits.shape
     E = centroids.shape[0]
     assert n_shared in (0, 1)
@@ -62,7 +71,9 @@ def layer(x_bits, centroids, bias, wts: ExpertWeights, n_group, topk_group, k, I
     G = E + n_shared
     gu = [wts.gu(g) for g in range(G)]
     dn = [wts.dn(g) for g in range(G)]
-    Hgu = to_bf16(grouped_gemm(A, sA, [q for q, _ in gu], [s for _, s in gu], offsets))
+    Hgu = grouped_gemm(A, sA, [q for q, _ in gu], [s for _, s in gu], offsets)
+    if not fused:
+        Hgu = to_bf16(Hgu)
     Hq, Hs, h = swiglu_quant(Hgu, I)
     D = to_bf16(grouped_gemm(Hq, Hs, [q for q, _ in dn], [s for _, s in dn], offsets))
     shared = D[T * k:T * k + T] if n_shared else None
@@ -72,22 +83,27 @@ def layer(x_bits, centroids, bias, wts: ExpertWeights, n_group, topk_group, k, I
                 inv_perm=inv_perm, Hgu=Hgu, Hq=Hq, Hs=Hs, h=h, D=D, y=y, y64=y64)
 
 
-def expert_ffn(xq_row, xs_row, wts: ExpertWeights, e: int, I: int):
+def expert_ffn(xq_row, xs_row, wts: ExpertWeights, e: int, I: int, fused: bool = True):
     """One expert on quantised rows: gate+up GEMM, SwiGLU+requant, down GEMM."""
     qgu, sgu = wts.gu(e)
     qdn, sdn = wts.dn(e)
-    hgu = bf16_round(block_scaled_matmul(xq_row, xs_row, qgu, sgu))
+    hgu = block_scaled_matmul(xq_row, xs_row, qgu, sgu)
+    if not fused:
+        hgu = bf16_round(hgu)
     hq, hs, _ = swiglu_quant(hgu, I)
     return bf16_round(block_scaled_matmul(hq, hs, qdn, sdn))
 
 
 def layer_tokens(x_bits, centroids, bias, wts: ExpertWeights, n_group, topk_group, k, I,
-                 tokens, n_shared: int = 1):
+                 tokens, n_shared: int = 1, fused: bool = True):
     """Direct per-token form for the given token indices.
 
     Routing of a token only depends on that token (the counts are not an
     input of the forward), so the routes of a subset equal those of the full
-    batch.  Returns dict(idx, w32, margin, y (bf16 values), y64).
+    batch.  Each expert is evaluated on the sampled tokens that chose it (its
+    rows are independent of one another), then every token's output is the
+    sum over its slots in slot order plus the shared expert(s).
+    Returns dict(idx, w32, margin, y (bf16 values), y64).
     """
     tokens = np.asarray(tokens, dtype=np.int64)
     E = centroids.shape[0]
@@ -96,12 +112,19 @@ def layer_tokens(x_bits, centroids, bias, wts: ExpertWeights, n_group, topk_grou
     idx, w, margin = select(s, sb, n_group, topk_group, k)
     w32 = w.astype(np.float32)
     xq, xsc = quant_1x128(bf16_value_from_bits(xs_bits).astype(np.float32))
+    n = len(tokens)
     H = x_bits.shape[1]
-    y64 = np.zeros((len(tokens), H), dtype=np.float64)
-    for i in range(len(tokens)):
+    out = {}                                   # (token row, slot) -> expert output
+    for e in sorted(set(idx.ravel().tolist())):
+        rows, slots = np.nonzero(idx == e)
+        d = expert_ffn(xq[rows], xsc[rows], wts, e, I, fused)
+        for r, j, dr in zip(rows, slots, d):
+            out[(int(r), int(j))] = dr
+    shared = [expert_ffn(xq, xsc, wts, E + sh, I, fused) for sh in range(n_shared)]
+    y64 = np.zeros((n, H), dtype=np.float64)
+    for i in range(n):
         for j in range(k):
-            d = expert_ffn(xq[i:i + 1], xsc[i:i + 1], wts, int(idx[i, j]), I)
-            y64[i] += np.float64(w32[i, j]) * d[0]
+            y64[i] += np.float64(w32[i, j]) * out[(i, j)]
         for sh in range(n_shared):
-            y64[i] += expert_ffn(xq[i:i + 1], xsc[i:i + 1], wts, E + sh, I)[0]
+            y64[i] += shared[sh][i]
     return dict(idx=idx, w32=w32, margin=margin, y=bf16_round(y64), y64=y64)

@@ -7,9 +7,14 @@ silu(g) = g / (1 + exp(-g)).  h is then quantised in 1x128 tiles like any
 activation (news.qq.com/rain/a/20241229A05OQF00, section FP8 低精度训练 ›
 细粒度量化, and 低精度存储和通信 for keeping activations in FP8).
 
-g and u are the bf16 values stored by the first GEMM.  h decides E4M3 codes,
-so it is evaluated in fp32, the kernel's precision, in this order:
-t = exp(-g); d = 1 + t; a = g / d; h = a * u.
+Two readings of where g and u come from are supported:
+* unfused - the first GEMM stores bf16 g and u, which SwiGLU reads back;
+* fused   - g and u are never stored: SwiGLU reads the first GEMM's FP32
+  totals (the pages keep MMA results in FP32 and store activations in FP8 or
+  BF16 only; g and u are not stored at all in this form).  The oracle takes
+  the fp32 rounding of the exact sums.
+Either way h decides E4M3 codes, so it is evaluated in fp32, the kernel's
+precision, in this order: t = exp(-g); d = 1 + t; a = g / d; h = a * u.
 """
 from __future__ import annotations
 
@@ -28,9 +33,11 @@ def silu_mul_fp32(g: np.ndarray, u: np.ndarray) -> np.ndarray:
 
 
 def swiglu_quant(hgu: np.ndarray, I: int):
-    """hgu: bf16-valued [M, 2I] -> (codes uint8 [M, I], scales fp32 [M, I/128], h fp32)."""
+    """hgu [M, 2I]: bf16 values (unfused) or exact float64 sums (fused; rounded
+    to fp32 here, ties to even).  Returns (codes uint8 [M, I], scales fp32
+    [M, I/128], h fp32)."""
     hgu = np.asarray(hgu, dtype=np.float64)
-    g = hgu[:, :I].astype(np.float32)   # exact: bf16 values
+    g = hgu[:, :I].astype(np.float32)
     u = hgu[:, I:2 * I].astype(np.float32)
     h = silu_mul_fp32(g, u)
     q, s = quant_1x128(h)

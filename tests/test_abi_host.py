@@ -1,0 +1,108 @@
+"""Host-only checks of the C ABI: the library loads, exports every function
+that include/moe_fp8.h declares, and rejects bad arguments with the
+documented codes before launching anything (no GPU needed: every call here
+fails validation or is a zero-sized no-op, so no HIP API is reached)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+from fp8_block_scaled_bias_amd import _lib as L
+
+HEADER = os.path.join(ROOT, "include", "moe_fp8.h")
+FAKE = ctypes.c_void_p(4096)  # never dereferenced: validation fails first
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", src, flags=re.M)
+    return sorted(set(n for n in names if n not in ("defined",)))
+
+
+def test_library_exports_every_declared_function():
+    lib = L.lib()
+    names = header_functions()
+    assert "grouped_fp8_gemm" in names and "moe_route" in names and len(names) >= 11
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in L.SIGNATURES, n
+    assert set(L.SIGNATURES) == set(names)
+    assert L.version().startswith("moe_fp8")
+
+
+def rc(name, *args):
+    return getattr(L.lib(), name)(*args)
+
+
+def test_quant_validation():
+    assert rc("fp8_quant_1x128", FAKE, 4, 100, 100, 0, FAKE, FAKE, None) == L.MOE_ERR_INVALID
+    assert "K=100" in L.last_error()
+    assert rc("fp8_quant_1x128", FAKE, 4, 128, 128, 2, FAKE, FAKE, None) == L.MOE_ERR_INVALID
+    assert rc("fp8_quant_1x128", FAKE, 4, 128, 128, 1, FAKE, FAKE, None) == L.MOE_ERR_INVALID
+    assert "ld_in" in L.last_error()
+    assert rc("fp8_quant_1x128", None, 4, 128, 128, 0, FAKE, FAKE, None) == L.MOE_ERR_INVALID
+    assert rc("fp8_quant_1x128", ctypes.c_void_p(4100), 4, 128, 128, 0, FAKE, FAKE, None) == L.MOE_ERR_INVALID
+    assert "aligned" in L.last_error()
+    assert rc("fp8_quant_1x128", None, 0, 128, 128, 0, None, None, None) == L.MOE_OK
+    assert rc("fp8_quant_128x128", FAKE, 2, 100, 128, FAKE, FAKE, None) == L.MOE_ERR_INVALID
+    assert rc("fp8_quant_128x128", None, 0, 128, 128, None, None, None) == L.MOE_OK
+
+
+def test_gemm_validation():
+    f = lambda G, M, N, K, A=FAKE: rc("grouped_fp8_gemm", A, FAKE, None, FAKE, FAKE, FAKE, G, M, N, K, FAKE, None)
+    assert f(0, 10, 128, 128) == L.MOE_ERR_INVALID
+    assert f(5000, 10, 128, 128) == L.MOE_ERR_UNSUPPORTED   # more groups than the LDS tables hold
+    assert f(4, 10, 100, 128) == L.MOE_ERR_INVALID and "N=100" in L.last_error()
+    assert f(4, 10, 128, 200) == L.MOE_ERR_INVALID and "K=200" in L.last_error()
+    assert f(4, -1, 128, 128) == L.MOE_ERR_INVALID
+    assert f(4, 10, 128, 128, A=None) == L.MOE_ERR_INVALID
+    assert f(4, 0, 128, 128, A=None) == L.MOE_OK          # empty problem is a no-op
+
+
+def test_route_validation():
+    def f(T=64, H=256, E=16, ng=4, tg=2, k=4, ws=FAKE, wsb=1 << 30):
+        return rc("moe_route", FAKE, T, H, FAKE, FAKE, E, ng, tg, k, FAKE, FAKE, FAKE, ws, wsb, None)
+    assert f(H=200) == L.MOE_ERR_INVALID
+    assert f(E=18, ng=4) == L.MOE_ERR_INVALID and "n_group" in L.last_error()
+    assert f(tg=5) == L.MOE_ERR_INVALID
+    assert f(k=9) == L.MOE_ERR_INVALID                       # k > topk_group * group size
+    assert f(E=512, ng=8, tg=4, k=8) == L.MOE_ERR_UNSUPPORTED
+    assert f(E=256, ng=8, tg=4, k=16) == L.MOE_ERR_UNSUPPORTED
+    assert f(E=24, ng=4, tg=2, k=4) == L.MOE_ERR_UNSUPPORTED  # group size 6
+    assert f(E=16, ng=16, tg=2, k=2) == L.MOE_ERR_INVALID      # group size 1: no top-2 sum
+    assert f(wsb=16) == L.MOE_ERR_WORKSPACE
+    assert f(ws=None) == L.MOE_ERR_WORKSPACE
+
+
+def test_route_group_size_two_is_valid_shape():
+    # E=16 in 8 groups has group size 2: valid, but 2 is not 4 * 2^n
+    assert rc("moe_route", FAKE, 8, 256, FAKE, FAKE, 16, 8, 2, 4, FAKE, FAKE, FAKE, FAKE, 1 << 30,
+              None) == L.MOE_ERR_UNSUPPORTED
+
+
+def test_permute_and_combine_and_bias_validation():
+    p = lambda T=10, k=8, E=256, ns=1, ws=FAKE, wsb=1 << 20: rc(
+        "moe_permute", FAKE, FAKE, T, k, E, ns, FAKE, FAKE, FAKE, None, None, 7168, None, None,
+        ws, wsb, None)
+    assert p(k=9) == L.MOE_ERR_INVALID
+    assert p(ns=2) == L.MOE_ERR_INVALID
+    assert p(E=5000) == L.MOE_ERR_INVALID
+    assert p(wsb=8) == L.MOE_ERR_WORKSPACE
+    c = lambda T=4, k=8, H=7168: rc("moe_combine", FAKE, FAKE, FAKE, None, T, k, H, FAKE, None)
+    assert c(H=7) == L.MOE_ERR_INVALID
+    assert c(k=0) == L.MOE_ERR_INVALID
+    assert c(T=0) == L.MOE_OK
+    assert rc("moe_bias_update", FAKE, FAKE, 0, ctypes.c_float(0.001), None) == L.MOE_ERR_INVALID
+    assert rc("moe_bias_update", None, FAKE, 256, ctypes.c_float(0.001), None) == L.MOE_ERR_INVALID
+
+
+def test_workspace_sizes():
+    assert L.moe_permute_workspace_bytes(16384, 8, 256) == 256 * 256 * 4
+    assert L.moe_permute_workspace_bytes(0, 8, 256) == 0
+    # router: partial logits [splits, T, E] fp32; at least one split
+    assert L.moe_route_workspace_bytes(16384, 7168, 256) == 16384 * 256 * 4
+    b = L.moe_route_workspace_bytes(128, 7168, 256)
+    assert b % (128 * 256 * 4) == 0 and b >= 128 * 256 * 4

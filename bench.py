@@ -73,7 +73,43 @@ def touched_experts(layer, T):
     return int((cnt > 0).sum().item())
 
 
-def cpu_baseline(cfg, n_tokens=4):
+def copy_probe(gib=1, reps=5):
+    """A plain device-to-device copy of `gib` GiB (torch's copy kernel):
+    the practical HBM ceiling, and the reference dispatch that scales the
+    FETCH_SIZE / WRITE_SIZE counters of a profiled run to bytes."""
+    import torch
+    n = gib << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    return {"bytes_per_copy": 2 * n, "ms": ms, "GB_s": 2 * n / (ms * 1e-3) / 1e9}
+
+
+def gemm_source_digest():
+    import hashlib
+    p = os.path.join(ROOT, "fp8_block_scaled_bias_amd", "csrc", "gemm.hip")
+    with open(p, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+# HBM traffic of the gate+up kernel at T=16384, from two rocprofv3 --pmc runs
+# (FETCH_SIZE, WRITE_SIZE) of this script, each scaled by the same counter on
+# the 1 GiB copy probe.  Valid only for the kernel source with this digest.
+GATE_UP_TRAFFIC = {"gemm_src": "3a3544bd06e733ce",
+                   # FETCH_SIZE 6,871,815 KiB x 2.000 + WRITE_SIZE 322,852 KiB x 1.000
+                   "bytes": 6871815 * 1024 * 2 + 322852 * 1024}
+
+
+def cpu_baseline(cfg, n_tokens=32):
     """The FP64 oracle on a bounded sample: the layer output of the first
     n_tokens tokens of the same batch (their routes, the weights of every
     expert they touch, and the shared expert), one BLAS thread."""
@@ -124,6 +160,8 @@ def main():
     layer = build_layer(cfg)
     x = x_device(cfg)
 
+    cp = copy_probe()
+    log(f"[bench] copy probe: {cp['GB_s']:.0f} GB/s")
     log(f"[bench] prefill T={cfg.T}: warmup {args.warmup}, steps {args.steps}")
     wall, per = run_steps(layer, x, args.steps, args.warmup, update_bias=True)
     ms = wall / args.steps * 1e3
@@ -148,6 +186,9 @@ def main():
     dgbs = dbytes / (dms * 1e-3) / 1e9
     log(f"[bench] decode per-kernel ms: " + ", ".join(f"{k} {v:.3f}" for k, v in dper.items()))
 
+    traffic = None
+    if GATE_UP_TRAFFIC and GATE_UP_TRAFFIC["gemm_src"] == gemm_source_digest():
+        traffic = GATE_UP_TRAFFIC["bytes"]
     out = {
         "metric": METRIC,
         "value": cfg.T / (ms * 1e-3),
@@ -171,10 +212,12 @@ def main():
         "per_kernel_ms": per,
         "roofline": {"bound": "mfma", "kernel": "grouped_fp8_gemm_swiglu (gate+up)",
                      "achieved": achieved_gu, "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved_gu / FP8_PEAK_TFLOPS, "traffic": None},
+                     "frac": achieved_gu / FP8_PEAK_TFLOPS, "traffic": traffic,
+                     "algorithmic_flop_per_launch": flops_gu, "avg_launch_ms": gu_ms},
         "decode": {"T": dcfg.T, "ms_per_step": dms, "touched_experts": touched,
                    "algorithmic_bytes": dbytes, "GB_s": dgbs, "frac_hbm_peak": dgbs / HBM_PEAK_GBS,
                    "per_kernel_ms": dper},
+        "copy_probe": cp,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg)

@@ -1,120 +1,42 @@
-// Block-scaled FP8 grouped GEMM on gfx950 FP8 MFMA, with an optional fused
-// SwiGLU + 1x128 requantisation epilogue.
+// Block-scaled FP8 grouped GEMM for small and medium groups (row tiles of
+// 32, 64 or 128), with an optional fused SwiGLU + 1x128 requantisation
+// epilogue, and the host entry points that choose between it and the
+// 256x256-tile kernel of gemm_wide.hip.
 //
 // Method: news.qq.com/rain/a/20241229A05OQF00, section FP8 低精度训练 -
 // activations carry one fp32 scale per 1x128 tile and weights one per
-// 128x128 block (细粒度量化), and MMA partial results are promoted to FP32
-// accumulators at a fixed K interval (提高累加精度).
+// 128x128 block (细粒度量化), and MMA partial results are accumulated in FP32
+// at a fixed K interval (提高累加精度).
 //
 // gfx950 design
 //  * One v_mfma_f32_16x16x128_f8f6f4 covers exactly one 128-wide K block of
 //    a 16x16 output tile, so its result P is that block's partial sum.  It is
 //    issued with a zero accumulator and promoted at once:
 //        acc += (sA[row, kb] * sB[nblk, kb]) * P      (one FMA per output)
-//    The MFMA's own 128-term sum is not fp32-exact (it is the hardware's
+//    The MFMA's own 128-term sum is not fp32-exact (the hardware's
 //    limited-precision dot product, the effect the 128-element promotion
-//    interval is there to bound); everything after it is fp32.
-//  * Both operands are K-contiguous, so a lane feeds the MFMA 32 bytes of one
-//    A row and one B row; A and B use the same K order inside a block, which
-//    is all a dot product needs.
+//    interval bounds); everything after it is fp32.
 //  * Workgroup tile BM x 256 (4 waves), K step 128.  Tiles of A (BM x 128 B),
 //    B (256 x 128 B) and A's scales (one fp32 per row) are copied global ->
 //    LDS with global_load_lds_dwordx4 / _dword (no VGPR staging) into a ring
 //    of STAGES buffers, so STAGES-1 K blocks are in flight while one is
 //    consumed.  The copies are issued from inline asm and their completion is
 //    tracked with explicit vmcnt waits plus a workgroup barrier per K block.
-//  * LDS rows are 128 B with the 16 B chunk index XOR-swizzled (swz below),
-//    so the rows read by one ds_read_b128 phase hit distinct bank groups.
-//  * Ragged groups: the host launches an upper bound of M tiles per N tile;
-//    each workgroup finds its (group, row block) from group_offsets with a
-//    block-wide scan.  Rows past a group's end are clamped on load and masked
-//    on store (an output row depends only on its own A row).
-//  * Tile order is XCD-aware: consecutive tile ids go to the same XCD (the
-//    hardware deals workgroups round-robin over 8 XCDs), and ids run
-//    group-major with M tiles fastest, so the workgroups running together on
-//    one XCD share each weight tile across all row blocks of an expert and
-//    each A tile across several N tiles, in that XCD's L2.
-//  * Epilogues: bf16 (round to nearest even) through an LDS-staged, coalesced
-//    store; or SwiGLU: the 256 columns are 128 gate + 128 up columns of the
-//    same h block, h = silu(g) * u is formed in fp32 from the fp32
-//    accumulators (g and u are never stored) and quantised 1x128 to E4M3.
-#include "common.h"
+//  * Persistent: one workgroup per CU walks an XCD-local range of the tile
+//    list (see decode_tile); rows past a group's end are clamped on load and
+//    masked on store (an output row depends only on its own A row).
+//  * Epilogues: bf16 (round to nearest even), four lanes' columns packed into
+//    one 8-byte store; or SwiGLU: the 256 columns are 128 gate + 128 up
+//    columns of the same h block, h = silu(g) * u is formed in fp32 from the
+//    fp32 accumulators (g and u are never stored) and quantised 1x128 to E4M3.
+#include "gemm_common.h"
 
 namespace moe {
+namespace gemm {
 namespace {
-
-typedef int v8i __attribute__((ext_vector_type(8)));
-typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int GM_THREADS = 256;
 constexpr int BN = 256;
-
-struct GemmArgs {
-  const uint8_t* A;
-  const float* A_scale;
-  const int32_t* a_row_index;
-  const uint8_t* B;
-  const float* B_scale;
-  const int32_t* offs;
-  int G;
-  int64_t N;       // columns of B's groups (2I for SwiGLU)
-  int64_t K;
-  int64_t ntiles;  // N tiles of 256 (SwiGLU: I / 128)
-  int64_t I;       // SwiGLU: h width
-  uint16_t* C;     // bf16 out [M_total, N]
-  uint8_t* Hq;     // SwiGLU out [M_total, I]
-  float* Hs;       // SwiGLU scales [M_total, I/128]
-};
-
-// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt bits [3:0] and
-// [15:14]; expcnt = 7 and lgkmcnt = 15 mean "no wait").
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-__device__ __forceinline__ void barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// Asynchronous global -> LDS copies.  Lane i's bytes land at lds + i*size;
-// lds must be wave-uniform.  No VGPR is written.
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds)
-               : "memory", "m0");
-}
-__device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds)
-               : "memory", "m0");
-}
-
-__device__ __forceinline__ v4f mfma_fp8_block(const v8i& a, const v8i& b) {
-  const v4f zero = {0.f, 0.f, 0.f, 0.f};
-  // cbsz = blgp = 0: both operands FP8 E4M3; no E8M0 block scaling.
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, 0, 0, 0);
-}
-
-// LDS tile layout: 128 B rows; 16 B chunk c of row r is stored in slot
-// c ^ swz(r).  swz keeps any 8 consecutive rows in distinct slots (one
-// 8-lane phase of a 32-bank LDS) and the 8 even and 8 odd rows of any 16
-// consecutive rows in distinct slots (one 16-lane phase of a 64-bank LDS).
-__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
-
-// 32 bytes of row `row` (K half h = lane/16) from a swizzled 128 B-row tile.
-__device__ __forceinline__ v8i lds_frag(const uint8_t* tile, int row, int h) {
-  const int sw = swz(row);
-  const uint4 lo = *reinterpret_cast<const uint4*>(tile + row * 128 + (((2 * h) ^ sw) << 4));
-  const uint4 hi = *reinterpret_cast<const uint4*>(tile + row * 128 + (((2 * h + 1) ^ sw) << 4));
-  v8i r;
-  r[0] = lo.x; r[1] = lo.y; r[2] = lo.z; r[3] = lo.w;
-  r[4] = hi.x; r[5] = hi.y; r[6] = hi.z; r[7] = hi.w;
-  return r;
-}
-
-constexpr int MAXG = 1024;  // groups the LDS tile tables hold
 
 template <int BM, int WAVES_M, int STAGES, bool SWIGLU, bool GATHER>
 struct Cfg {
@@ -139,36 +61,6 @@ struct Cfg {
   static_assert(BM <= 128, "scale slots BM, BM+1 carry the weight scales");
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
-
-// Uniform description of one output tile.
-struct Tile {
-  int g, m0, m1;
-  int64_t nt;
-};
-
-// Tile id L -> (group, rows, N tile).  Ids run group-major, then N tile,
-// then M tile (M fastest), so the workgroups that run together on one XCD
-// cover all row blocks of one expert against a few weight tiles.
-// s_pref[g] = M tiles of groups < g (empty groups repeat the prefix; the
-// largest g with s_pref[g] * ntiles <= L is the non-empty group holding L).
-__device__ __forceinline__ Tile decode_tile(const int* s_pref, const int* s_offs, int G,
-                                            int64_t ntiles, int64_t L, int bm) {
-  int lo = 0, hi = G;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if ((int64_t)s_pref[mid] * ntiles <= L) lo = mid;
-    else hi = mid;
-  }
-  Tile t;
-  const int cnt = s_pref[lo + 1] - s_pref[lo];
-  const int64_t rem = L - (int64_t)s_pref[lo] * ntiles;
-  t.g = lo;
-  t.nt = rem / cnt;
-  const int mi = (int)(rem - t.nt * cnt);
-  t.m0 = s_offs[lo] + mi * bm;
-  t.m1 = s_offs[lo + 1];
-  return t;
-}
 
 // Persistent kernel: one workgroup per CU walks its share of the tiles
 // (XCD-local, see decode_tile).  The copies of K block kb of the current or
@@ -196,30 +88,7 @@ __global__ __launch_bounds__(GM_THREADS, 1) void grouped_gemm_kernel(GemmArgs ar
   const int64_t nkb = K >> 7;
 
   // ---- group tables: offsets and exclusive prefix of M tiles per group ----
-  for (int g = tid; g <= G; g += GM_THREADS) s_offs[g] = args.offs[g];
-  if (tid == 0) {
-    s_carry = 0;
-    s_pref[0] = 0;
-  }
-  __syncthreads();
-  for (int g0 = 0; g0 < G; g0 += GM_THREADS) {
-    const int g = g0 + tid;
-    const int cnt = g < G ? (s_offs[g + 1] - s_offs[g] + BM - 1) / BM : 0;
-    int v = cnt;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int n = __shfl_up(v, o, 64);
-      if (lane >= o) v += n;
-    }
-    if (lane == 63) s_red[wv] = v;
-    __syncthreads();
-    int add = s_carry;
-    for (int w = 0; w < wv; ++w) add += s_red[w];
-    if (g < G) s_pref[g + 1] = add + v;
-    __syncthreads();
-    if (tid == GM_THREADS - 1) s_carry = add + v;
-    __syncthreads();
-  }
+  build_group_tables<GM_THREADS, BM>(args.offs, G, s_offs, s_pref, s_red, &s_carry);
   const int64_t total = (int64_t)s_pref[G] * ntiles;
   // this workgroup's tiles: XCD x owns ids [x*chunk, (x+1)*chunk); its
   // workgroups (blocks x, x+8, ...) take every (gridDim/8)-th of them
@@ -504,6 +373,7 @@ __global__ __launch_bounds__(GM_THREADS, 1) void grouped_gemm_kernel(GemmArgs ar
           for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
           if ((lane & 15) == 0) s_amax[(wm * C_::WTM + i * 16 + 4 * h + r) * C_::WAVES_N + wn] = m;
         }
+      wait_lgkm0();
       barrier();
 #pragma unroll
       for (int i = 0; i < C_::SI; ++i)
@@ -536,6 +406,8 @@ __global__ __launch_bounds__(GM_THREADS, 1) void grouped_gemm_kernel(GemmArgs ar
   }
 }
 
+}  // namespace
+
 int num_cus() {
   static int cus[64] = {0};
   int dev = 0;
@@ -548,6 +420,8 @@ int num_cus() {
   }
   return cus[dev];
 }
+
+namespace {
 
 template <int BM, int WAVES_M, int STAGES, bool SWIGLU>
 int launch(const GemmArgs& a, hipStream_t st) {
@@ -564,6 +438,12 @@ int dispatch(const GemmArgs& a, int64_t M_total, hipStream_t st) {
   // rows per group decide the M tile: 128 for prefill-sized groups, 32 when
   // groups hold a handful of rows (decode), 64 in between
   const int64_t avg = M_total / a.G;
+  // the 256x256 kernel addresses a tile's output with 32-bit offsets
+  // (and takes an even number of at least 4 K blocks)
+  const int64_t nkb = a.K / 128;
+  const bool wide_ok = (SWIGLU ? a.I <= (1 << 22) : (a.N % 256 == 0 && a.N <= (1 << 21))) &&
+                       nkb >= 4 && nkb % 2 == 0;
+  if (avg >= 160 && wide_ok) return launch_wide(a, SWIGLU, st);
   if (avg >= 96) return launch<128, 2, 3, SWIGLU>(a, st);
   if (avg >= 40) return launch<64, 1, 3, SWIGLU>(a, st);
   return launch<32, 1, 4, SWIGLU>(a, st);
@@ -589,9 +469,11 @@ int validate_common(const char* who, const uint8_t* A, const float* A_scale, con
 }
 
 }  // namespace
+}  // namespace gemm
 }  // namespace moe
 
 using namespace moe;
+using namespace moe::gemm;
 
 extern "C" int grouped_fp8_gemm(const uint8_t* A, const float* A_scale, const int32_t* a_row_index,
                                 const uint8_t* B, const float* B_scale,

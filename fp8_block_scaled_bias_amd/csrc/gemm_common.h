@@ -1,0 +1,178 @@
+// Pieces shared by the two grouped FP8 GEMM kernels (gemm.hip: row tiles of
+// 32..128 for small and medium groups; gemm_wide.hip: 256x256 tiles for
+// large groups): arguments, the asynchronous global -> LDS copy, the FP8
+// MFMA block product, the swizzled LDS tile layout and the tile scheduler.
+//
+// Method: news.qq.com/rain/a/20241229A05OQF00, section FP8 低精度训练 -
+// activations carry one fp32 scale per 1x128 tile and weights one per
+// 128x128 block (细粒度量化); MMA results are accumulated in FP32 at a fixed
+// K interval (提高累加精度).
+#pragma once
+
+#include "common.h"
+
+namespace moe {
+namespace gemm {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int MAXG = 1024;  // groups the LDS tile tables hold
+
+struct GemmArgs {
+  const uint8_t* A;
+  const float* A_scale;
+  const int32_t* a_row_index;
+  const uint8_t* B;
+  const float* B_scale;
+  const int32_t* offs;
+  int G;
+  int64_t N;       // columns of B's groups (2I for SwiGLU)
+  int64_t K;
+  int64_t ntiles;  // N tiles of 256 (SwiGLU: I / 128)
+  int64_t I;       // SwiGLU: h width
+  uint16_t* C;     // bf16 out [M_total, N]
+  uint8_t* Hq;     // SwiGLU out [M_total, I]
+  float* Hs;       // SwiGLU scales [M_total, I/128]
+};
+
+// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt bits [3:0] and
+// [15:14]; expcnt = 7 and lgkmcnt = 15 mean "no wait").
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// s_waitcnt lgkmcnt(0) (LDS writes done before a barrier that publishes
+// them; gfx950 barriers do not wait for outstanding memory operations).
+__device__ __forceinline__ void wait_lgkm0() {
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
+}
+// s_waitcnt vmcnt(0) lgkmcnt(0)
+__device__ __forceinline__ void wait_vm_lgkm0() { __builtin_amdgcn_s_waitcnt(7 << 4); }
+
+// Workgroup barrier that does not drain outstanding global -> LDS copies
+// (the compiler's __syncthreads waits for every memory operation).
+__device__ __forceinline__ void barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Asynchronous global -> LDS copies.  Lane i's bytes land at lds + i*size;
+// lds must be wave-uniform.  No VGPR is written.
+// (lds is made wave-uniform explicitly: inside branches the compiler cannot
+// always prove it.)
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+  const uint32_t l = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(l)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
+  const uint32_t l = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(l)
+               : "memory", "m0");
+}
+
+// One 16x16 output block over one 128-wide K block: lane l supplies 32 bytes
+// of A row l%16 and of B row l%16 at K offset 32*(l/16); the result holds
+// rows 4*(l/16)..+3 of column l%16.  cbsz = blgp = 0: both operands E4M3,
+// no E8M0 block scaling.
+__device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b, const v4f& c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+__device__ __forceinline__ v4f mfma_fp8_block(const v8i& a, const v8i& b) {
+  const v4f zero = {0.f, 0.f, 0.f, 0.f};
+  return mfma_fp8(a, b, zero);
+}
+
+// LDS tile layout: 128 B rows; 16 B chunk c of row r is stored in slot
+// c ^ swz(r).  swz keeps any 8 consecutive rows in distinct slots (one
+// 8-lane phase of a 32-bank LDS) and the 8 even and 8 odd rows of any 16
+// consecutive rows in distinct slots (one 16-lane phase of a 64-bank LDS).
+__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
+// 32 bytes of row `row` (K half h = lane/16) from a swizzled 128 B-row tile.
+__device__ __forceinline__ v8i lds_frag(const uint8_t* tile, int row, int h) {
+  const int sw = swz(row);
+  const uint4 lo = *reinterpret_cast<const uint4*>(tile + row * 128 + (((2 * h) ^ sw) << 4));
+  const uint4 hi = *reinterpret_cast<const uint4*>(tile + row * 128 + (((2 * h + 1) ^ sw) << 4));
+  v8i r;
+  r[0] = lo.x; r[1] = lo.y; r[2] = lo.z; r[3] = lo.w;
+  r[4] = hi.x; r[5] = hi.y; r[6] = hi.z; r[7] = hi.w;
+  return r;
+}
+
+// Uniform description of one output tile.
+struct Tile {
+  int g, m0, m1;
+  int64_t nt;
+};
+
+// Tile id L -> (group, rows, N tile).  Ids run group-major, then N tile,
+// then M tile (M fastest), so the workgroups that run together on one XCD
+// cover all row blocks of one expert against a few weight tiles.
+// s_pref[g] = M tiles of groups < g (empty groups repeat the prefix; the
+// largest g with s_pref[g] * ntiles <= L is the non-empty group holding L).
+__device__ __forceinline__ Tile decode_tile(const int* s_pref, const int* s_offs, int G,
+                                            int64_t ntiles, int64_t L, int bm) {
+  int lo = 0, hi = G;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if ((int64_t)s_pref[mid] * ntiles <= L) lo = mid;
+    else hi = mid;
+  }
+  Tile t;
+  const int cnt = s_pref[lo + 1] - s_pref[lo];
+  const int64_t rem = L - (int64_t)s_pref[lo] * ntiles;
+  t.g = lo;
+  t.nt = rem / cnt;
+  const int mi = (int)(rem - t.nt * cnt);
+  t.m0 = s_offs[lo] + mi * bm;
+  t.m1 = s_offs[lo + 1];
+  return t;
+}
+
+// Group tables in LDS: s_offs[0..G] = group_offsets, s_pref[0..G] =
+// exclusive prefix of ceil(rows / BM) per group.  A block-wide scan; ends
+// with a barrier (all THREADS threads must call it).
+template <int THREADS, int BM>
+__device__ __forceinline__ void build_group_tables(const int32_t* offs, int G, int* s_offs,
+                                                   int* s_pref, int* s_red, int* s_carry) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  for (int g = tid; g <= G; g += THREADS) s_offs[g] = offs[g];
+  if (tid == 0) {
+    *s_carry = 0;
+    s_pref[0] = 0;
+  }
+  __syncthreads();
+  for (int g0 = 0; g0 < G; g0 += THREADS) {
+    const int g = g0 + tid;
+    const int cnt = g < G ? (s_offs[g + 1] - s_offs[g] + BM - 1) / BM : 0;
+    int v = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int n = __shfl_up(v, o, 64);
+      if (lane >= o) v += n;
+    }
+    if (lane == 63) s_red[wv] = v;
+    __syncthreads();
+    int add = *s_carry;
+    for (int w = 0; w < wv; ++w) add += s_red[w];
+    if (g < G) s_pref[g + 1] = add + v;
+    __syncthreads();
+    if (tid == THREADS - 1) *s_carry = add + v;
+    __syncthreads();
+  }
+}
+
+// Compute units of the current device (cached per device).
+int num_cus();
+
+// The 256x256-tile kernel for large groups (gemm_wide.hip).  Requires
+// N % 256 == 0 (plain) or I % 128 == 0 (SwiGLU), and K / 128 even and >= 4.
+int launch_wide(const GemmArgs& a, bool swiglu, hipStream_t st);
+
+}  // namespace gemm
+}  // namespace moe

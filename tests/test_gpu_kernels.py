@@ -282,16 +282,21 @@ def _gemm_gpu(qA, sA, rowidx, qB, sB, offsets, N, K):
 # fp32-exact; over 1M random E4M3 sums its error reached 2^-15.6 of the
 # absolute sum (mean 2^-19.4).  2^-14 keeps a 3x margin over that maximum.
 MFMA_BLOCK_REL = 2.0 ** -14
+PROMO_ROUNDINGS = 5
 
 
 def gemm_accumulation_bound(qA, sA, qB, sB, offsets, K):
     """Bound on |GPU fp32 total - exact| per output: each K block's MFMA
-    partial is off by at most MFMA_BLOCK_REL of its absolute sum, and the
-    K/128 fp32 promotion FMAs round at most once each relative to the running
-    total, which never exceeds S = sum_kb |sA sB| sum_k |a b|."""
+    partial is off by at most MFMA_BLOCK_REL of its absolute sum, and each of
+    the K/128 promotion steps rounds a few times relative to the running
+    total, which never exceeds S = sum_kb |sA sB| sum_k |a b|: the
+    zero-started form rounds the scale product and the FMA (2); the rescaled
+    form the two scale products and their quotient, the multiply and the
+    MFMA's add of the rescaled accumulator (4 on the sums' scale, 5 with the
+    final multiply).  PROMO_ROUNDINGS = 5 covers both."""
     qBabs = [np.asarray(q) & 0x7F for q in qB]
     S = OG.grouped_gemm(np.asarray(qA) & 0x7F, sA, qBabs, sB, offsets)
-    return (MFMA_BLOCK_REL + (K // 128) * 2.0 ** -24) * S
+    return (MFMA_BLOCK_REL + PROMO_ROUNDINGS * (K // 128 + 1) * 2.0 ** -24) * S
 
 
 @pytest.mark.parametrize("with_index", [False, True])
@@ -347,7 +352,28 @@ def test_gemm_integer_exact_many_tiles(mean_rows, G, N, K, with_index):
     assert np.array_equal(got, ref), int((got != ref).sum())
 
 
-@pytest.mark.parametrize("sizes,N,K", [([5, 0, 300, 129], 384, 1024), ([1000], 256, 7168)])
+# Large groups (256x256 tiles, taken for an even number of >= 4 K blocks):
+# every remainder class of the last M tile (1..64, 65..128, 129..192,
+# 193..256 rows), empty groups, 4 to 12 K blocks (tiles shorter and longer
+# than the copy pipeline's reach), with and without row gather.
+@pytest.mark.parametrize("K", [512, 1024, 1536])
+@pytest.mark.parametrize("with_index", [False, True])
+def test_gemm_integer_exact_wide(K, with_index):
+    sizes = [1000, 0, 170, 400, 256, 513, 65, 129, 200, 0, 700]
+    N = 512
+    rng = np.random.default_rng(K)
+    rows_src = 2222 if with_index else int(sum(sizes))
+    offsets, Mt, qA, sA, qB, sB = _int_gemm_case(sizes, N, K, rows_src, 31 + K)
+    rowidx = rng.integers(0, rows_src, Mt).astype(np.int32) if with_index else None
+    got = _gemm_gpu(qA, sA, rowidx, qB, sB, offsets, N, K)
+    qAr = qA[rowidx] if with_index else qA
+    sAr = sA[rowidx] if with_index else sA
+    ref = OG.to_bf16(OG.grouped_gemm(qAr, sAr, qB, sB, offsets))
+    assert np.array_equal(got, ref), int((got != ref).sum())
+
+
+@pytest.mark.parametrize("sizes,N,K", [([5, 0, 300, 129], 384, 1024), ([1000], 256, 7168),
+                                       ([700, 300, 0, 450], 512, 2048)])
 def test_gemm_random_within_one_ulp(sizes, N, K):
     G = len(sizes)
     offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
@@ -426,7 +452,9 @@ def check_fused_swiglu(q, s, exact, bound, I, what):
                                                   ([3, 40, 1], 384, 256, True),
                                                   ([1000], 128, 7168, False),
                                                   ([2500] * 12, 256, 384, True),
-                                                  ([6] * 200, 256, 256, True)])
+                                                  ([6] * 200, 256, 256, True),
+                                                  ([300, 0, 77, 513], 256, 512, True),
+                                                  ([600, 190], 384, 1024, False)])
 def test_gemm_swiglu_fused(sizes, I, K, with_index):
     G = len(sizes)
     offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)

@@ -35,10 +35,10 @@ SIGNATURES = {
                                    _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
     "fp8_quant_1x128": (ctypes.c_int, [_vp, _i64, _i64, _i64, _i32, _vp, _vp, _vp]),
     "fp8_quant_128x128": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _vp, _vp]),
-    "grouped_fp8_gemm": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64,
-                                        _vp, _vp]),
-    "grouped_fp8_gemm_swiglu": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _i64,
-                                               _i64, _vp, _vp, _vp]),
+    "grouped_fp8_gemm": (ctypes.c_int, [_vp, _vp, _vp, _i64, _vp, _vp, _vp, _i32, _i64, _i64,
+                                        _i64, _vp, _vp]),
+    "grouped_fp8_gemm_swiglu": (ctypes.c_int, [_vp, _vp, _vp, _i64, _vp, _vp, _vp, _i32, _i64,
+                                               _i64, _i64, _vp, _vp, _vp]),
     "moe_combine": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i32, _i64, _vp, _vp]),
 }
 
@@ -100,6 +100,13 @@ def _stream(stream):
     return stream.cuda_stream if isinstance(stream, torch.cuda.Stream) else stream
 
 
+def _rows(t):
+    """Rows of a 2-D operand (A of the grouped GEMMs)."""
+    if not isinstance(t, torch.Tensor) or t.dim() != 2:
+        raise TypeError("expected a 2-D torch.Tensor")
+    return int(t.shape[0])
+
+
 def _call(name, *args):
     rc = getattr(lib(), name)(*args)
     if rc != MOE_OK:
@@ -146,15 +153,15 @@ def fp8_quant_128x128(w_f32, G, N, K, out_e4m3, scales, stream=None):
 
 def grouped_fp8_gemm(A, A_scale, a_row_index, B, B_scale, group_offsets, G, M_total, N, K,
                      C_bf16, stream=None):
-    return _call("grouped_fp8_gemm", _dev(A), _dev(A_scale), _dev(a_row_index), _dev(B),
+    return _call("grouped_fp8_gemm", _dev(A), _dev(A_scale), _dev(a_row_index), _rows(A), _dev(B),
                  _dev(B_scale), _dev(group_offsets), G, M_total, N, K, _dev(C_bf16),
                  _stream(stream))
 
 
 def grouped_fp8_gemm_swiglu(A, A_scale, a_row_index, B, B_scale, group_offsets, G, M_total, I,
                             K, H_e4m3, H_scale, stream=None):
-    return _call("grouped_fp8_gemm_swiglu", _dev(A), _dev(A_scale), _dev(a_row_index), _dev(B),
-                 _dev(B_scale), _dev(group_offsets), G, M_total, I, K, _dev(H_e4m3),
+    return _call("grouped_fp8_gemm_swiglu", _dev(A), _dev(A_scale), _dev(a_row_index), _rows(A),
+                 _dev(B), _dev(B_scale), _dev(group_offsets), G, M_total, I, K, _dev(H_e4m3),
                  _dev(H_scale), _stream(stream))
 
 

@@ -123,7 +123,7 @@ __global__ __launch_bounds__(GM_THREADS, 1) void grouped_gemm_kernel(GemmArgs ar
   const int32_t* r_src = nullptr;  // row-index copy source (next tile)
 
   auto row_src = [&](const Tile& t, int64_t ord, int row) -> int64_t {
-    if (GATHER) return (int64_t)s_ridx[(ord & 1) * 256 + row];
+    if (GATHER) return (int64_t)min((uint32_t)s_ridx[(ord & 1) * 256 + row], (uint32_t)(args.A_rows - 1));
     return (int64_t)min(t.m0 + row, t.m1 - 1);
   };
   auto setup_issue = [&](int64_t ord) {
@@ -438,18 +438,21 @@ int dispatch(const GemmArgs& a, int64_t M_total, hipStream_t st) {
   // rows per group decide the M tile: 128 for prefill-sized groups, 32 when
   // groups hold a handful of rows (decode), 64 in between
   const int64_t avg = M_total / a.G;
-  // the 256x256 kernel addresses a tile's output with 32-bit offsets
-  // (and takes an even number of at least 4 K blocks)
+  // the 256x256 kernel addresses a tile's output, A and one group's B with
+  // 32-bit offsets, and takes an even number of at least 6 K blocks
   const int64_t nkb = a.K / 128;
+  const int64_t lim = (int64_t)1 << 32;
   const bool wide_ok = (SWIGLU ? a.I <= (1 << 22) : (a.N % 256 == 0 && a.N <= (1 << 21))) &&
-                       nkb >= 4 && nkb % 2 == 0;
+                       nkb >= 6 && nkb % 2 == 0 && a.K <= (1 << 20) && a.N * a.K < lim &&
+                       a.A_rows * a.K < lim;
   if (avg >= 160 && wide_ok) return launch_wide(a, SWIGLU, st);
   if (avg >= 96) return launch<128, 2, 3, SWIGLU>(a, st);
   if (avg >= 40) return launch<64, 1, 3, SWIGLU>(a, st);
   return launch<32, 1, 4, SWIGLU>(a, st);
 }
 
-int validate_common(const char* who, const uint8_t* A, const float* A_scale, const uint8_t* B,
+int validate_common(const char* who, const uint8_t* A, const float* A_scale,
+                    const int32_t* a_row_index, int64_t A_rows, const uint8_t* B,
                     const float* B_scale, const int32_t* group_offsets, int32_t G,
                     int64_t M_total, int64_t N, int64_t K) {
   MOE_INVALID(G >= 1, "%s: G=%d must be >= 1", who, (int)G);
@@ -461,6 +464,9 @@ int validate_common(const char* who, const uint8_t* A, const float* A_scale, con
   MOE_INVALID(K > 0 && K % 128 == 0, "%s: K=%lld must be a positive multiple of 128", who,
               (long long)K);
   if (M_total == 0) return MOE_OK;
+  MOE_INVALID(A_rows >= (a_row_index ? 1 : M_total) && A_rows < (1ll << 31),
+              "%s: A_rows=%lld must be in [%s, 2^31)", who, (long long)A_rows,
+              a_row_index ? "1" : "M_total");
   MOE_INVALID(A && A_scale && B && B_scale && group_offsets, "%s: null pointer", who);
   MOE_INVALID(((uintptr_t)A & 15) == 0 && ((uintptr_t)B & 15) == 0 &&
                   ((uintptr_t)A_scale & 3) == 0 && ((uintptr_t)B_scale & 3) == 0,
@@ -476,17 +482,18 @@ using namespace moe;
 using namespace moe::gemm;
 
 extern "C" int grouped_fp8_gemm(const uint8_t* A, const float* A_scale, const int32_t* a_row_index,
-                                const uint8_t* B, const float* B_scale,
+                                int64_t A_rows, const uint8_t* B, const float* B_scale,
                                 const int32_t* group_offsets, int32_t G, int64_t M_total, int64_t N,
                                 int64_t K, void* C_bf16, void* stream) {
   clear_error();
-  int rc = validate_common("grouped_fp8_gemm", A, A_scale, B, B_scale, group_offsets, G, M_total,
-                           N, K);
+  int rc = validate_common("grouped_fp8_gemm", A, A_scale, a_row_index, A_rows, B, B_scale,
+                           group_offsets, G, M_total, N, K);
   if (rc != MOE_OK || M_total == 0) return rc;
   MOE_INVALID(C_bf16 && ((uintptr_t)C_bf16 & 15) == 0,
               "grouped_fp8_gemm: C must be non-null and 16-byte aligned");
   GemmArgs a{};
-  a.A = A; a.A_scale = A_scale; a.a_row_index = a_row_index; a.B = B; a.B_scale = B_scale;
+  a.A = A; a.A_scale = A_scale; a.a_row_index = a_row_index; a.A_rows = A_rows;
+  a.B = B; a.B_scale = B_scale;
   a.offs = group_offsets; a.G = G; a.N = N; a.K = K; a.ntiles = ceil_div(N, BN); a.I = 0;
   a.C = static_cast<uint16_t*>(C_bf16);
   rc = dispatch<false>(a, M_total, as_stream(stream));
@@ -495,20 +502,21 @@ extern "C" int grouped_fp8_gemm(const uint8_t* A, const float* A_scale, const in
 }
 
 extern "C" int grouped_fp8_gemm_swiglu(const uint8_t* A, const float* A_scale,
-                                       const int32_t* a_row_index, const uint8_t* B,
+                                       const int32_t* a_row_index, int64_t A_rows, const uint8_t* B,
                                        const float* B_scale, const int32_t* group_offsets,
                                        int32_t G, int64_t M_total, int64_t I, int64_t K,
                                        uint8_t* H_e4m3, float* H_scale, void* stream) {
   clear_error();
   MOE_INVALID(I > 0 && I % 128 == 0, "grouped_fp8_gemm_swiglu: I=%lld must be a positive "
               "multiple of 128", (long long)I);
-  int rc = validate_common("grouped_fp8_gemm_swiglu", A, A_scale, B, B_scale, group_offsets, G,
-                           M_total, 2 * I, K);
+  int rc = validate_common("grouped_fp8_gemm_swiglu", A, A_scale, a_row_index, A_rows, B,
+                           B_scale, group_offsets, G, M_total, 2 * I, K);
   if (rc != MOE_OK || M_total == 0) return rc;
   MOE_INVALID(H_e4m3 && H_scale && ((uintptr_t)H_e4m3 & 15) == 0,
               "grouped_fp8_gemm_swiglu: H must be non-null and 16-byte aligned");
   GemmArgs a{};
-  a.A = A; a.A_scale = A_scale; a.a_row_index = a_row_index; a.B = B; a.B_scale = B_scale;
+  a.A = A; a.A_scale = A_scale; a.a_row_index = a_row_index; a.A_rows = A_rows;
+  a.B = B; a.B_scale = B_scale;
   a.offs = group_offsets; a.G = G; a.N = 2 * I; a.K = K; a.ntiles = I / 128; a.I = I;
   a.Hq = H_e4m3; a.Hs = H_scale;
   rc = dispatch<true>(a, M_total, as_stream(stream));

@@ -23,6 +23,7 @@ struct GemmArgs {
   const uint8_t* A;
   const float* A_scale;
   const int32_t* a_row_index;
+  int64_t A_rows;  // rows of A (gathered indices are clamped to A_rows - 1)
   const uint8_t* B;
   const float* B_scale;
   const int32_t* offs;
@@ -171,7 +172,8 @@ __device__ __forceinline__ void build_group_tables(const int32_t* offs, int G, i
 int num_cus();
 
 // The 256x256-tile kernel for large groups (gemm_wide.hip).  Requires
-// N % 256 == 0 (plain) or I % 128 == 0 (SwiGLU), and K / 128 even and >= 4.
+// N % 256 == 0 (plain) or I % 128 == 0 (SwiGLU), K / 128 even and >= 6, and
+// 32-bit copy offsets: N*K (one group's B) and A_rows*K below 2^32.
 int launch_wide(const GemmArgs& a, bool swiglu, hipStream_t st);
 
 }  // namespace gemm

@@ -27,13 +27,18 @@
 //
 // Pipeline: a step is 64 K (one v_mfma_f32_32x32x64_f8f6f4 per 32x32
 // block); a ring of 4 LDS stages (A 256 x 64 B, B 256 x 64 B) is filled
-// 3 steps ahead by global_load_lds_dwordx4 copies that each wave spreads over
-// its MFMAs; K-block scales come 4 steps ahead, the gathered row-index table
-// of a tile 7 steps ahead.  Each step waits (vmcnt) only for the copies of
-// the step it is about to use.
+// 3 steps ahead by buffer_load ... lds copies that each wave spreads over its
+// MFMAs; K-block scales come 4 steps ahead, the gathered row-index table of
+// a tile 7 steps ahead.  Copies address memory as a per-tile buffer resource
+// (SGPRs) + a per-tile lane offset (one VGPR) + the K position as the SGPR
+// soffset, which moves only the global address, never the LDS one; so a step
+// spends no vector instructions on addressing.  Every wave issues the same
+// number of copies per step, and each step waits (vmcnt) only for the copies
+// of the step it is about to use.
 //   step s: wait, barrier; per wave 8 MFMAs with the copies of step s+3
 //   interleaved; after the second step of a K block, the ratios of the next
 //   block; after the last step of a tile, the epilogue.
+// The steps away from a tile's first 4 and last 8 carry no run-time tests.
 // Waves whose 64 rows lie past the group's end skip their MFMAs (a ragged
 // last tile costs about half a tile when at most 128 rows remain).
 #include "gemm_common.h"
@@ -45,6 +50,7 @@ namespace gemm {
 namespace {
 
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef int v4i __attribute__((ext_vector_type(4)));
 
 constexpr int WT = 512;                  // 8 waves, 2 per SIMD
 constexpr int WBM = 256;                 // tile rows
@@ -69,23 +75,13 @@ static_assert(OFF_R % 16 == 0 && OFF_SC % 16 == 0 && SSLOT % 16 == 0, "float4 re
 // slots spread the rows over distinct banks.
 __device__ __forceinline__ int swz64(int row) { return ((row >> 1) & 3) ^ ((row >> 3) & 1); }
 
-// 32 bytes (chunks 2q, 2q+1, q = lane/32) of row `row` of a 64 B-row stage:
-// the A or B operand of one 32x32x64 MFMA for lane row `row`.
-__device__ __forceinline__ v8i lds_frag64(const uint8_t* tile, int row, int q) {
-  const int sw = swz64(row);
-  const uint4 lo = *reinterpret_cast<const uint4*>(tile + row * 64 + (((2 * q) ^ sw) << 4));
-  const uint4 hi = *reinterpret_cast<const uint4*>(tile + row * 64 + (((2 * q + 1) ^ sw) << 4));
-  v8i r;
-  r[0] = lo.x; r[1] = lo.y; r[2] = lo.z; r[3] = lo.w;
-  r[4] = hi.x; r[5] = hi.y; r[6] = hi.z; r[7] = hi.w;
-  return r;
-}
-
-// 32x32 output block over 64 K: lane l feeds row l%32 of A and of B (K bytes
-// 32*(l/32)..+31); result element r of lane l is row 8*(r/4) + 4*(l/32) +
-// r%4, column l%32.
-__device__ __forceinline__ v16f mfma32(const v8i& a, const v8i& b, const v16f& c) {
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+// 32x32 block over 64 K: lane l feeds row l%32 of x and of y (K bytes
+// 32*(l/32)..+31); result element r of lane l is x row 8*(r/4) + 4*(l/32) +
+// r%4 against y row l%32.  The kernel passes weights as x and tokens as y,
+// so a lane holds one token row and 16 output columns: 4 runs of 4
+// consecutive columns (r = 4g..4g+3 at column 8g + 4*(l/32)).
+__device__ __forceinline__ v16f mfma32(const v8i& x, const v8i& y, const v16f& c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x, y, c, 0, 0, 0, 0, 0, 0);
 }
 
 // Raw buffer resource over `bytes` bytes at p (gfx9 dword3: 32-bit data,
@@ -96,6 +92,33 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t out_rsrc(const void* p, uint32
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
 }
 
+// The same descriptor as four SGPRs, for the copies below (stride 0: the
+// range check is offset < bytes; loads past it return zeros).
+__device__ __forceinline__ v4i load_rsrc(const void* p, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  v4i r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+  r[3] = 0x00020000;
+  return r;
+}
+
+// Asynchronous copies into LDS.  Lane i's 16 (4) bytes come from buffer
+// offset voff + soff and land at m0 + i*16 (i*4); soff moves the global
+// address only.  m0 and soff must be wave-uniform (SGPRs).
+template <int IMM>
+__device__ __forceinline__ void copy16(const v4i& r, uint32_t voff, uint32_t soff, uint32_t m0b) {
+  asm volatile("s_add_u32 m0, %3, %4\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               ::"v"(voff), "s"(r), "s"(soff), "s"(m0b), "n"(IMM)
+               : "memory", "m0", "scc");
+}
+__device__ __forceinline__ void copy4(const v4i& r, uint32_t voff, uint32_t soff, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dword %0, %1, %2 offen lds"
+               ::"v"(voff), "s"(r), "s"(soff), "s"(m0)
+               : "memory", "m0");
+}
+
 // s_waitcnt vmcnt(N) lgkmcnt(0)
 template <int N>
 __device__ __forceinline__ void wait_vmcnt_lgkm0() {
@@ -103,14 +126,8 @@ __device__ __forceinline__ void wait_vmcnt_lgkm0() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
 }
 
-// Position of a step in this workgroup's step sequence: tile ordinal and
-// step within the tile (2 per K block).
-struct Cursor {
-  int ord, k;
-  __device__ __forceinline__ void next(int spt) {
-    if (++k == spt) { k = 0; ++ord; }
-  }
-};
+template <int V>
+using ic = std::integral_constant<int, V>;
 
 template <bool SWIGLU, bool GATHER>
 __global__ __launch_bounds__(WT, 1) void wide_gemm_kernel(GemmArgs args) {
@@ -129,10 +146,13 @@ __global__ __launch_bounds__(WT, 1) void wide_gemm_kernel(GemmArgs args) {
   const int wm = wv >> 1, wn = wv & 1;  // wave tile: rows 64*wm.., columns 128*wn..
   const int q = lane >> 5, l32 = lane & 31;
   const int G = args.G;
-  const int64_t K = args.K, N = args.N, ntiles = args.ntiles;
-  const int nkb = (int)(K >> 7);  // even, >= 4 (host)
-  const int spt = 2 * nkb;        // steps per tile, a multiple of 4
-  const int64_t nblk = N >> 7;
+  const int64_t N = args.N, ntiles = args.ntiles;
+  const uint32_t K = (uint32_t)args.K;
+  const int nkb = (int)(K >> 7);  // even, >= 6 (host)
+  const int spt = 2 * nkb;        // steps per tile, a multiple of 4, >= 12
+  const int nblk = (int)(N >> 7);
+  // copies per wave per step: 4 tile rows + 1 scale (+ 1 row-index table)
+  constexpr int NC = GATHER ? 6 : 5;
 
   build_group_tables<WT, WBM>(args.offs, G, s_offs, s_pref, s_red, &s_carry);
   const int64_t total = (int64_t)s_pref[G] * ntiles;
@@ -164,96 +184,111 @@ __global__ __launch_bounds__(WT, 1) void wide_gemm_kernel(GemmArgs args) {
   };
   int gh = __builtin_amdgcn_readfirstlane(decode_tile(s_pref, s_offs, G, ntiles, L0, WBM).g);
   // weight block (of 128 columns) of the tile's column half b
-  auto nblk_of = [&](const Tile& t, int b) -> int64_t {
-    return SWIGLU ? (b ? (args.I >> 7) + t.nt : t.nt) : 2 * t.nt + b;
+  auto nblk_of = [&](const Tile& t, int b) -> int {
+    return SWIGLU ? (b ? (int)(args.I >> 7) + (int)t.nt : (int)t.nt) : 2 * (int)t.nt + b;
   };
 
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
 
-  // ---- copy sources of one tile (per lane).  Tile copy instruction p
-  // (0..15) of a stage half covers rows 16p..16p+15: lane -> row 16p +
-  // lane/4, LDS slot lane%4, global chunk (lane%4) ^ swz64(row); wave wv
-  // issues p = 2wv, 2wv+1 for A and for B.  Scales: waves 0-3 copy sA of 64
-  // rows each, wave 4 the two sB of the tile.  Gathered A rows come from
-  // the tile's row-index table in LDS (buffer ord & 3).
+  // ---- copy sources of one tile.  Tile copy p (0..15) of a stage half
+  // covers rows 16p..16p+15: lane -> row 16p + lane/4, LDS slot lane%4,
+  // global chunk (lane%4) ^ swz64(row); wave wv issues p = 2wv, 2wv+1 for A
+  // and for B.  Scales: waves 0-3 copy sA of 64 rows each, waves 4-7 the two
+  // sB of the tile (the same bytes to the same place).  Gathered A rows come
+  // from the tile's row-index table in LDS (buffer ord & 3), clamped to A.
   struct Srcs {
-    const uint8_t* a0;
-    const uint8_t* a1;
-    const uint8_t* b0;  // B rows of p = 2wv; p = 2wv + 1 is 16 rows further
-    const float* sc;
+    v4i rb;                            // the group's B
+    uint32_t va0, va1, vb0, vb1, vs;  // lane offsets
+  };
+  // A and the scales are addressed whole (32-bit offsets: the host checks
+  // the sizes); only B's base moves with the tile's group
+  const uint32_t a_last = (uint32_t)(args.A_rows - 1);
+  const v4i ra = load_rsrc(args.A, (uint32_t)args.A_rows * K);
+  const v4i rs = wv < 4 ? load_rsrc(args.A_scale, (uint32_t)args.A_rows * (uint32_t)nkb * 4)
+                        : load_rsrc(args.B_scale, (uint32_t)(G * nblk * nkb * 4));
+  // source row of tile row `row` (gathered: from the table, clamped to A)
+  auto a_row = [&](const Tile& t, int ord, int row) -> uint32_t {
+    if (GATHER) return min((uint32_t)s_ridx[(ord & 3) * 256 + row], a_last);
+    return (uint32_t)min(t.m0 + row, t.m1 - 1);
   };
   auto make_srcs = [&](const Tile& t, int ord) {
     Srcs r;
-    const uint8_t* ap[2];
+    uint32_t va[2];
 #pragma unroll
     for (int pi = 0; pi < 2; ++pi) {
       const int row = 32 * wv + 16 * pi + (lane >> 2);
-      const int gch = (lane & 3) ^ swz64(row);
-      const int64_t ar = GATHER ? (int64_t)s_ridx[(ord & 3) * 256 + row] : (int64_t)min(t.m0 + row, t.m1 - 1);
-      ap[pi] = args.A + ar * K + gch * 16;
+      const uint32_t gch = (uint32_t)((lane & 3) ^ swz64(row));
+      va[pi] = a_row(t, ord, row) * K + gch * 16;
     }
-    r.a0 = ap[0];
-    r.a1 = ap[1];
+    r.va0 = va[0];
+    r.va1 = va[1];
+    r.rb = load_rsrc(args.B + ((int64_t)t.g * N) * K, (uint32_t)N * K);
     {
       const int row = 32 * wv + (lane >> 2);
-      const int gch = (lane & 3) ^ swz64(row);
-      int64_t n;
-      if (SWIGLU) n = (row < 128 ? 0 : args.I - 128) + 128 * t.nt + row;
-      else n = 256 * t.nt + row;
-      r.b0 = args.B + ((int64_t)t.g * N + n) * K + gch * 16;
+      const uint32_t gch = (uint32_t)((lane & 3) ^ swz64(row));
+      uint32_t n;
+      if (SWIGLU) n = (uint32_t)((row < 128 ? 0 : (int)args.I - 128) + 128 * (int)t.nt + row);
+      else n = (uint32_t)(256 * (int)t.nt + row);
+      r.vb0 = n * K + gch * 16;
+      r.vb1 = r.vb0 + 16 * K;
     }
-    if (wv < 4) {
-      const int row = 64 * wv + lane;
-      const int64_t ar = GATHER ? (int64_t)s_ridx[(ord & 3) * 256 + row] : (int64_t)min(t.m0 + row, t.m1 - 1);
-      r.sc = args.A_scale + ar * nkb;
-    } else {
-      r.sc = args.B_scale + ((int64_t)t.g * nblk + nblk_of(t, lane == 1)) * nkb;
-    }
+    if (wv < 4) r.vs = a_row(t, ord, 64 * wv + lane) * (uint32_t)nkb * 4;
+    else r.vs = (uint32_t)((t.g * nblk + nblk_of(t, lane == 1)) * nkb * 4);
     return r;
   };
-  const uint32_t m0_w = lds0 + (uint32_t)(2 * wv) * 1024;  // this wave's first copy slot
-  // tile copy op (0, 1: A rows p = 2wv, 2wv+1; 2, 3: B rows) of tile step kk into stage st
-  auto tile_op = [&](const Srcs& r, int op, int kk, int st) {
-    const uint32_t dst = m0_w + (uint32_t)st * STAGE + ((op & 2) ? A_BYTES : 0) + (op & 1) * 1024;
-    const int64_t ko = (int64_t)kk * 64;
-    const uint8_t* src = (op == 0) ? r.a0 : (op == 1) ? r.a1 : (op == 2) ? r.b0 : r.b0 + 16 * K;
-    dma16(src + ko, dst);
-  };
-  auto scale_op = [&](const Srcs& r, int kb, int gslot) {
-    const uint32_t ss = lds0 + OFF_SC + (uint32_t)gslot * SSLOT;
-    if (wv < 4) dma4(r.sc + kb, ss + wv * 256);
-    else if (wv == 4) dma4(r.sc + kb, ss + 1024);
-  };
-  // row-index table of a tile: waves 4-7, 64 rows each
+  // row-index table of a tile: slice wv & 3 (64 rows) from every wave
   auto table_src = [&](const Tile& t) -> const int32_t* {
-    return args.a_row_index + min(t.m0 + 64 * (wv - 4) + lane, t.m1 - 1);
+    return args.a_row_index + min(t.m0 + 64 * (wv & 3) + lane, t.m1 - 1);
   };
-  auto table_op = [&](const int32_t* src, int ord) {
-    dma4(src, lds0 + OFF_RIDX + (uint32_t)(((ord & 3) * 256 + 64 * (wv - 4)) * 4));
+  auto table_m0 = [&](int ord) -> uint32_t {
+    return (uint32_t)__builtin_amdgcn_readfirstlane(
+        (int)(lds0 + OFF_RIDX + (uint32_t)(((ord & 3) * 256 + 64 * (wv & 3)) * 4)));
   };
-  // copies per step of this wave in steady state (vmcnt bookkeeping)
-  const int n_step = 4 + (wv <= 4 ? 1 : 0) + (GATHER && wv >= 4 ? 1 : 0);
+  auto table_copy = [&](const int32_t* src, uint32_t m0) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(m0)
+                 : "memory", "m0");
+  };
+  // LDS destinations: this wave's first tile-copy slot, its scale slice
+  const uint32_t m0_w =
+      (uint32_t)__builtin_amdgcn_readfirstlane((int)(lds0 + (uint32_t)(2 * wv) * 1024));
+  const uint32_t sc_w = (uint32_t)__builtin_amdgcn_readfirstlane(
+      (int)(lds0 + OFF_SC + (wv < 4 ? (uint32_t)wv * 256 : 1024u)));
+  // tile copy op (0, 1: A rows p = 2wv, 2wv+1; 2, 3: B rows) into stage TST
+  auto tile_op = [&](auto TST_, const Srcs& r, int op, uint32_t so) __attribute__((always_inline)) {
+    constexpr int TST = decltype(TST_)::value;
+    if (op == 0) copy16<TST * STAGE>(ra, r.va0, so, m0_w);
+    else if (op == 1) copy16<TST * STAGE + 1024>(ra, r.va1, so, m0_w);
+    else if (op == 2) copy16<TST * STAGE + A_BYTES>(r.rb, r.vb0, so, m0_w);
+    else copy16<TST * STAGE + A_BYTES + 1024>(r.rb, r.vb1, so, m0_w);
+  };
+  auto scale_copy = [&](const Srcs& r, int kb, int gslot) __attribute__((always_inline)) {
+    copy4(rs, r.vs, (uint32_t)kb * 4, sc_w + (uint32_t)gslot * SSLOT);
+  };
 
   // ---- prologue: table of tile 0, then its first 3 steps and the scales
-  // of its first 2 K blocks; all waited for.
+  // of its first 3 K blocks; all waited for.
   Tile tc = tile_at(gh, 0);
-  const int32_t* tb_src = nullptr;
+  const int32_t* tb_c = nullptr;
+  const int32_t* tb_n = nullptr;
+  uint32_t tbm_c = 0, tbm_n = 0;
   if (GATHER) {
-    if (wv >= 4) {
-      tb_src = table_src(tc);
-      table_op(tb_src, 0);
-    }
+    tb_c = table_src(tc);
+    tbm_c = table_m0(0);
+    table_copy(tb_c, tbm_c);
     wait_vm_lgkm0();
     barrier();
   }
   Srcs cur = make_srcs(tc, 0);
+  Srcs nxt = cur;
 #pragma unroll
-  for (int kk = 0; kk < 3; ++kk)
-#pragma unroll
-    for (int op = 0; op < 4; ++op) tile_op(cur, op, kk, kk);
-  scale_op(cur, 0, 0);
-  scale_op(cur, 1, 1);
-  scale_op(cur, 2, 2);
+  for (int op = 0; op < 4; ++op) {
+    tile_op(ic<0>(), cur, op, 0);
+    tile_op(ic<1>(), cur, op, 64);
+    tile_op(ic<2>(), cur, op, 128);
+  }
+  scale_copy(cur, 0, 0);
+  scale_copy(cur, 1, 1);
+  scale_copy(cur, 2, 2);
   wait_vm_lgkm0();
   barrier();
 
@@ -288,8 +323,7 @@ __global__ __launch_bounds__(WT, 1) void wide_gemm_kernel(GemmArgs args) {
   auto b_roff = [&](int j) -> int { return SWIGLU ? (j < 2 ? 32 * j : 128 + 32 * (j - 2)) : 32 * j; };
   auto half_of = [&](int j) -> int { return SWIGLU ? (j >= 2) : wn; };
 
-  bool drain = false;  // stores pending: the next wait is for everything
-  int gh_n = gh;       // hint for decoding the next tile
+  int gh_n = gh;  // hint for decoding the next tile
   Tile tn = tc;
 
   for (int ord = 0; ord < my_n; ++ord) {
@@ -297,50 +331,70 @@ __global__ __launch_bounds__(WT, 1) void wide_gemm_kernel(GemmArgs args) {
     const bool wvalid = tc.m0 + 64 * wm < tc.m1;
     const int gbase = ord * nkb;  // global K-block index of this tile's kb 0
 
-    // one step k = k4 + U of this tile (stage U: tiles start at a multiple
-    // of 4 steps; K block k4/2 + U/2, ratio buffer (U/2) ^ 1 after it)
-    auto step = [&](auto U_, int k4) {
+    // One step k = k4 + U of this tile (stage U: tiles start at a multiple
+    // of 4 steps; K block k4/2 + U/2).  Phase PH: 0 the first 4 steps (k4 =
+    // 0), 1 the interior (4 <= k4 < spt - 8), 2 and 3 the last 8 (k4 = spt -
+    // 8, spt - 4; spt >= 12).  Every test below is decided by U and PH
+    // except the first step's wait for the previous epilogue's stores.
+    // After the last tile the copies still run (onto the last tile's own
+    // sources): every step then issues NC copies and one vmcnt suffices.
+    auto step = [&](auto U_, auto PH_, int k4) __attribute__((always_inline)) {
       constexpr int U = decltype(U_)::value;
+      constexpr int PH = decltype(PH_)::value;
       const int k = k4 + U;
       // copies of step k are done (those of the next two steps may still
-      // fly; after stores and at the end of the work, everything); then
-      // everyone is past the previous step
-      if (drain || (!has_next && k + 6 >= spt)) wait_vm_lgkm0();
-      else if (n_step == 4) wait_vmcnt_lgkm0<8>();
-      else if (n_step == 5) wait_vmcnt_lgkm0<10>();
-      else wait_vmcnt_lgkm0<12>();
-      drain = false;
+      // fly; after the epilogue's stores, everything); then everyone is
+      // past the previous step
+      if (PH == 0 && U == 0) wait_vm_lgkm0();
+      else wait_vmcnt_lgkm0<2 * NC>();
       barrier();
 
-      // ---- next tile's table (8 steps ahead) and decode
-      if (has_next) {
-        if (GATHER && k == spt - 8) {
-          tn = tile_at(gh_n, ord + 1);
-          if (wv >= 4) tb_src = table_src(tn);
+      // ---- next tile: decode (its table is copied from step spt-8 on) and
+      // copy sources (at step spt-5, when that table has landed)
+      if (PH == 2 && U == (GATHER ? 0 : 3)) {
+        tn = has_next ? tile_at(gh_n, ord + 1) : tc;
+        if (GATHER) {
+          tb_n = table_src(tn);
+          tbm_n = table_m0(ord + 1);
         }
-        if (!GATHER && k == spt - 5) tn = tile_at(gh_n, ord + 1);
       }
-      // ---- scales of the K block of step k+5 (re-copied: same data)
+      if (PH == 2 && U == 3) nxt = make_srcs(tn, ord + 1);
+      // ---- scales of the K block of step k+5 (re-copied: same data); in
+      // the last 5 steps, the next tile's first blocks
       {
+        constexpr bool NEXT = PH == 3 || (PH == 2 && U == 3);
         const int kb5 = (k + 5) >> 1;
-        if (kb5 < nkb) scale_op(cur, kb5, (gbase + kb5) & 3);
-        else if (has_next) scale_op(make_srcs(tn, ord + 1), kb5 - nkb, (gbase + kb5) & 3);
+        const int gslot = (gbase + kb5) & 3;
+        if (NEXT) scale_copy(nxt, kb5 - nkb, gslot);
+        else scale_copy(cur, kb5, gslot);
       }
       // ---- the current or next tile's row-index table (re-copied)
-      if (GATHER && wv >= 4 && (has_next || k + 8 < spt))
-        table_op(tb_src, (GATHER && has_next && k >= spt - 8) ? ord + 1 : ord);
-      // ---- tile copies of step k+3 ride between the MFMAs below
-      // (the last 3 steps copy the next tile's first steps; its sources are
-      // formed for those few steps only)
-      const bool t_cur = k + 3 < spt;
-      const bool do_t = t_cur || has_next;
-      const int kt = t_cur ? k + 3 : k + 3 - spt;
-      const Srcs ts = t_cur ? cur : make_srcs(tn, ord + 1);
+      if (GATHER) {
+        if (PH >= 2) table_copy(tb_n, tbm_n);
+        else table_copy(tb_c, tbm_c);
+      }
+      // ---- tile copies of step k+3 ride between the MFMAs below (the
+      // last 3 steps copy the next tile's first steps)
+      constexpr bool T_NEXT = PH == 3 && U >= 1;
+      const uint32_t so = (uint32_t)((T_NEXT ? k + 3 - spt : k + 3) * 64);
       constexpr int ST = U;                   // stage of step k
       constexpr int SOFF = (ST & 1) * STAGE;  // offset within the stage pair
       constexpr int TST = (U + 3) & 3;        // stage of step k+3
+      auto copies = [&](int op) __attribute__((always_inline)) {
+        if (T_NEXT) tile_op(ic<TST>(), nxt, op, so);
+        else tile_op(ic<TST>(), cur, op, so);
+      };
 
       const int kb = (k4 >> 1) + (U >> 1);
+      // rescale by S_kb-1 / S_kb in two halves: column blocks 2, 3 on the
+      // first step of K block kb (between the MFMAs of blocks 0, 1 and
+      // their own), blocks 0, 1 at the end of the step before; each step then
+      // carries half of the multiplies.  None before K block 1; none after
+      // the last block.
+      constexpr bool RESC_NOW = (U & 1) == 0 && !(PH == 0 && U == 0);
+      constexpr bool RESC_NEXT = (U & 1) == 1 && !(PH == 3 && U == 3);
+      // ratios S_kb / S_kb+1 after a K block's first step, but the last
+      constexpr bool RATIO = (U & 1) == 0 && !(PH == 3 && U == 2);
       if (wvalid) {
         const uint8_t* alo = pa_lo + (ST >= 2 ? 2 * STAGE : 0);
         const uint8_t* ahi = pa_hi + (ST >= 2 ? 2 * STAGE : 0);
@@ -351,51 +405,39 @@ __global__ __launch_bounds__(WT, 1) void wide_gemm_kernel(GemmArgs args) {
         for (int i = 0; i < 2; ++i) a[i] = read_frag(alo, ahi, SOFF + i * 32 * 64);
 #pragma unroll
         for (int j = 0; j < 4; ++j) b[j] = read_frag(blo, bhi, SOFF + b_roff(j) * 64);
-        // rescale by S_kb-1 / S_kb in two halves: column blocks 2, 3 here
-        // (first step of K block kb, between the MFMAs of blocks 0, 1 and
-        // their own), blocks 0, 1 at the end of the previous step; each step
-        // then carries half of the multiplies
-        float rr[2][16];
+        // the ratio of a (token row, column half) pair: one value per lane
+        // and row block
+        float rr[2];
         auto load_ratios = [&](int kbr, int hb) __attribute__((always_inline)) {
-          const float* rsh = s_r + (kbr & 1) * 512 + hb * 256 + wm * 64 + 4 * q;
-#pragma unroll
-          for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              const float4 v = *reinterpret_cast<const float4*>(rsh + 32 * i + 8 * g);
-              rr[i][4 * g] = v.x; rr[i][4 * g + 1] = v.y;
-              rr[i][4 * g + 2] = v.z; rr[i][4 * g + 3] = v.w;
-            }
+          const float* rsh = s_r + (kbr & 1) * 512 + hb * 256 + wm * 64 + l32;
+          rr[0] = rsh[0];
+          rr[1] = rsh[32];
         };
         auto rescale_block = [&](int j) __attribute__((always_inline)) {
 #pragma unroll
           for (int i = 0; i < 2; ++i)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] *= rr[i][r];
+            for (int r = 0; r < 16; ++r) acc[i][j][r] *= rr[i];
         };
-        const bool resc_now = (U & 1) == 0 && kb > 0;           // blocks 2, 3, ratio of kb
-        const bool resc_next = (U & 1) == 1 && kb + 1 < nkb;    // blocks 0, 1, ratio of kb+1
-        if (resc_now) load_ratios(kb, SWIGLU ? 1 : wn);
+        if (RESC_NOW) load_ratios(kb, SWIGLU ? 1 : wn);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          if (resc_now && j >= 2) rescale_block(j);
+          if (RESC_NOW && j >= 2) rescale_block(j);
 #pragma unroll
-          for (int i = 0; i < 2; ++i) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
-          if (do_t) tile_op(ts, j, kt, TST);
+          for (int i = 0; i < 2; ++i) acc[i][j] = mfma32(b[j], a[i], acc[i][j]);
+          copies(j);
         }
-        if (resc_next) {
+        if (RESC_NEXT) {
           load_ratios(kb + 1, SWIGLU ? 0 : wn);
           rescale_block(0);
           rescale_block(1);
         }
-      } else if (do_t) {
+      } else {
 #pragma unroll
-        for (int op = 0; op < 4; ++op) tile_op(ts, op, kt, TST);
+        for (int op = 0; op < 4; ++op) copies(op);
       }
 
-      // ---- after a K block's first step: ratios S_kb / S_kb+1 for the
-      // next block of the same tile (used from the next step on)
-      if ((U & 1) == 0 && kb + 1 < nkb) {
+      if (RATIO) {
         const float* sc0 = s_sc + ((gbase + kb) & 3) * (SSLOT / 4);
         const float* sc1 = s_sc + ((gbase + kb + 1) & 3) * (SSLOT / 4);
         const int row = tid & 255, b = tid >> 8;
@@ -404,80 +446,86 @@ __global__ __launch_bounds__(WT, 1) void wide_gemm_kernel(GemmArgs args) {
         s_r[((kb + 1) & 1) * 512 + b * 256 + row] = S0 / S1;
       }
     };
-    for (int k4 = 0; k4 < spt; k4 += 4) {
-      step(std::integral_constant<int, 0>(), k4);
-      step(std::integral_constant<int, 1>(), k4);
-      step(std::integral_constant<int, 2>(), k4);
-      step(std::integral_constant<int, 3>(), k4);
+    step(ic<0>(), ic<0>(), 0);
+    step(ic<1>(), ic<0>(), 0);
+    step(ic<2>(), ic<0>(), 0);
+    step(ic<3>(), ic<0>(), 0);
+    for (int k4 = 4; k4 < spt - 8; k4 += 4) {
+      step(ic<0>(), ic<1>(), k4);
+      step(ic<1>(), ic<1>(), k4);
+      step(ic<2>(), ic<1>(), k4);
+      step(ic<3>(), ic<1>(), k4);
     }
+    step(ic<0>(), ic<2>(), spt - 8);
+    step(ic<1>(), ic<2>(), spt - 8);
+    step(ic<2>(), ic<2>(), spt - 8);
+    step(ic<3>(), ic<2>(), spt - 8);
+    step(ic<0>(), ic<3>(), spt - 4);
+    step(ic<1>(), ic<3>(), spt - 4);
+    step(ic<2>(), ic<3>(), spt - 4);
+    step(ic<3>(), ic<3>(), spt - 4);
 
-    // ---- epilogue of tile ord: result = acc * S_last ----
+    // ---- epilogue of tile ord: result = acc * S_last.  Lane (q, l32) of
+    // wave (wm, wn) holds tile row wm*64 + 32i + l32 of row block i and, in
+    // column block j, the columns 8g + 4q + (0..3) for g = 0..3.
     const Tile t = tc;
     const float* scl = s_sc + ((gbase + nkb - 1) & 3) * (SSLOT / 4);
-    // lane row of element r of row block i: 32i + 8(r/4) + 4q + r%4
     if (wvalid) {
       const float sb[2] = {scl[256], scl[257]};
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 2; ++i) {
+        const float sa = scl[wm * 64 + 32 * i + l32];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const float4 v = *reinterpret_cast<const float4*>(scl + wm * 64 + 32 * i + 8 * g + 4 * q);
-          const float sa[4] = {v.x, v.y, v.z, v.w};
+        for (int j = 0; j < 4; ++j) {
+          const float S = sa * sb[half_of(j)];
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int p = 0; p < 4; ++p) acc[i][j][4 * g + p] *= sa[p] * sb[half_of(j)];
+          for (int r = 0; r < 16; ++r) acc[i][j][r] *= S;
         }
+      }
     }
     if (!SWIGLU) {
-      // bf16 (round to nearest even); lane 4k of a quad stores the 4
-      // consecutive columns of lanes 4k..4k+3 as one 8-byte word
+      // bf16 (round to nearest even): 4 consecutive columns per 8-byte store
       if (wvalid) {
         const uint32_t rowb = (uint32_t)N * 2;
         const __amdgpu_buffer_rsrc_t rs =
             out_rsrc(args.C + (int64_t)t.m0 * N, (uint32_t)min(t.m1 - t.m0, WBM) * rowb);
-        const int vb = (wm * 64 + 4 * q) * (int)rowb + (int)(256 * t.nt + wn * 128 + l32) * 2;
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < 2; ++i) {
+          const int vb = (wm * 64 + 32 * i + l32) * (int)rowb + (int)(256 * t.nt + wn * 128 + 4 * q) * 2;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
+          for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const float v0 = acc[i][j][r];
-              const float v1 = quad_lane1(v0), v2 = quad_lane2(v0), v3 = quad_lane3(v0);
-              const int so = (32 * i + 8 * (r >> 2) + (r & 3)) * (int)rowb + 64 * j;
-              if ((lane & 3) == 0) {
-                typedef uint32_t v2u __attribute__((ext_vector_type(2)));
-                const v2u w = {f32x2_to_bf16x2(v0, v1), f32x2_to_bf16x2(v2, v3)};
-                __builtin_amdgcn_raw_buffer_store_b64(w, rs, vb, so, 0);
-              }
+            for (int g = 0; g < 4; ++g) {
+              typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+              const v2u w = {f32x2_to_bf16x2(acc[i][j][4 * g], acc[i][j][4 * g + 1]),
+                             f32x2_to_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3])};
+              __builtin_amdgcn_raw_buffer_store_b64(w, rs, vb, (32 * j + 8 * g) * 2, 0);
             }
-          }
+        }
       }
     } else {
-      // h = silu(g) * u: gate block j pairs with up block j + 2 in this
-      // lane's registers; a row's 128 h columns are split over the two
-      // column waves, whose row maxima meet in LDS.
+      // h = silu(g) * u: gate block j pairs with up block j + 2.  A row's 128
+      // h columns of this N tile: 32 in each lane of the pair (q = 0, 1) of
+      // both column waves; the row maximum meets over the pair by a lane
+      // exchange and over the two waves in LDS.
+      float inv[2] = {1.f, 1.f};
       if (wvalid) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < 2; ++i) {
+          float m = 0.f;
 #pragma unroll
           for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const float g = acc[i][j][r], u = acc[i][j + 2][r];
               const float e = __builtin_amdgcn_exp2f(g * -1.4426950408889634f);
-              acc[i][j][r] = g * __builtin_amdgcn_rcpf(1.0f + e) * u;
+              const float h = g * __builtin_amdgcn_rcpf(1.0f + e) * u;
+              acc[i][j][r] = h;
+              m = fmaxf(m, fabsf(h));
             }
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            float m = fmaxf(fabsf(acc[i][0][r]), fabsf(acc[i][1][r]));
-#pragma unroll
-            for (int o = 1; o < 32; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-            if (l32 == 0) s_amax[(wm * 64 + 32 * i + 8 * (r >> 2) + 4 * q + (r & 3)) * 2 + wn] = m;
-          }
+          m = fmaxf(m, __shfl_xor(m, 32, 64));
+          s_amax[(wm * 64 + 32 * i + l32) * 2 + wn] = m;  // both lanes of the pair: same value
+        }
       }
       wait_lgkm0();
       barrier();
@@ -486,28 +534,26 @@ __global__ __launch_bounds__(WT, 1) void wide_gemm_kernel(GemmArgs args) {
         const uint32_t rows = (uint32_t)min(t.m1 - t.m0, WBM);
         const __amdgpu_buffer_rsrc_t rq = out_rsrc(args.Hq + (int64_t)t.m0 * I, rows * I);
         const __amdgpu_buffer_rsrc_t rsc = out_rsrc(args.Hs + (int64_t)t.m0 * hb, rows * hb * 4);
-        const int vq = (wm * 64 + 4 * q) * I + (int)(128 * t.nt) + wn * 64 + l32;
-        const int vs = ((wm * 64 + 4 * q) * hb + (int)t.nt) * 4;
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < 2; ++i) {
+          const int trow = wm * 64 + 32 * i + l32;
+          const float amax = fmaxf(s_amax[trow * 2], s_amax[trow * 2 + 1]);
+          const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
+          inv[i] = 1.0f / sc;
+          if (wn == 0 && q == 0)
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), rsc, (trow * hb + (int)t.nt) * 4, 0, 0);
+          const int vq = trow * I + (int)(128 * t.nt) + wn * 64 + 4 * q;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int rl = 32 * i + 8 * (r >> 2) + (r & 3);  // row in the wave's 64, less 4q
-            const int trow = wm * 64 + rl + 4 * q;
-            const float amax = fmaxf(s_amax[trow * 2], s_amax[trow * 2 + 1]);
-            const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
-            const float inv = 1.0f / sc;
+          for (int j = 0; j < 2; ++j)
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-              const float v0 = acc[i][j][r] * inv;
-              const float v1 = quad_lane1(v0), v2 = quad_lane2(v0), v3 = quad_lane3(v0);
-              if ((lane & 3) == 0)
-                __builtin_amdgcn_raw_buffer_store_b32(f32x4_to_e4m3x4(v0, v1, v2, v3), rq, vq,
-                                                      rl * I + 32 * j, 0);
+            for (int g = 0; g < 4; ++g) {
+              const v16f& h = acc[i][j];
+              __builtin_amdgcn_raw_buffer_store_b32(
+                  f32x4_to_e4m3x4(h[4 * g] * inv[i], h[4 * g + 1] * inv[i], h[4 * g + 2] * inv[i],
+                                  h[4 * g + 3] * inv[i]),
+                  rq, vq, 32 * j + 8 * g, 0);
             }
-            if (wn == 0 && l32 == 0)
-              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), rsc, vs, rl * hb * 4, 0);
-          }
+        }
       }
     }
 #pragma unroll
@@ -516,12 +562,14 @@ __global__ __launch_bounds__(WT, 1) void wide_gemm_kernel(GemmArgs args) {
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-    drain = true;  // the stores count in vmcnt and may finish out of order
-    if (has_next) {
-      tc = tn;
-      cur = make_srcs(tc, ord + 1);
-    }
+    // (the epilogue's stores count in vmcnt and may finish out of order:
+    // the next tile's first step waits for everything)
+    tc = tn;
+    cur = nxt;
+    tb_c = tb_n;
+    tbm_c = tbm_n;
   }
+  wait_vm_lgkm0();  // copies issued past the last tile land before the LDS is released
 }
 
 }  // namespace

@@ -183,9 +183,12 @@ int fp8_quant_128x128(const float* w_f32, int64_t G, int64_t N, int64_t K,
  * K block is one FP8 MFMA partial in FP32 that is scaled and added to an FP32
  * total; the total is rounded to bf16 (nearest even) once.
  *
- * A        [rows_A, K] e4m3 (rows_A = M_total when a_row_index is NULL)
- * A_scale  [rows_A, K/128] fp32
- * a_row_index  [M_total] int32 or NULL
+ * A        [A_rows, K] e4m3
+ * A_scale  [A_rows, K/128] fp32
+ * a_row_index  [M_total] int32 or NULL; entries should lie in [0, A_rows):
+ *          an entry outside it reads row A_rows - 1 (never memory past A)
+ * A_rows   rows of A and A_scale: >= M_total when a_row_index is NULL, >= 1
+ *          otherwise
  * B        [G, N, K] e4m3 (each group's matrix stored N x K, K contiguous)
  * B_scale  [G, N/128, K/128] fp32
  * group_offsets [G+1] int32 on the device, non-decreasing, [0] == 0,
@@ -195,7 +198,7 @@ int fp8_quant_128x128(const float* w_f32, int64_t G, int64_t N, int64_t K,
  * MOE_ERR_UNSUPPORTED).
  */
 int grouped_fp8_gemm(const uint8_t* A, const float* A_scale, const int32_t* a_row_index,
-                     const uint8_t* B, const float* B_scale,
+                     int64_t A_rows, const uint8_t* B, const float* B_scale,
                      const int32_t* group_offsets, int32_t G, int64_t M_total,
                      int64_t N, int64_t K, void* C_bf16, void* stream);
 
@@ -213,12 +216,12 @@ int grouped_fp8_gemm(const uint8_t* A, const float* A_scale, const int32_t* a_ro
  *   h = (gt / (1 + exp(-gt))) * ut  in fp32, then per 128 columns of h
  *   s = amax/448 (1 if 0), H_e4m3[r, c] = E4M3(h / s), H_scale[r, c/128] = s.
  *
- * A, A_scale, a_row_index, B_scale, group_offsets: as grouped_fp8_gemm with
+ * A, A_scale, a_row_index, A_rows, B_scale, group_offsets: as grouped_fp8_gemm with
  * N = 2I.  H_e4m3 (out) [M_total, I] e4m3; H_scale (out) [M_total, I/128].
  * Requirements: I % 128 == 0, K % 128 == 0, 1 <= G <= 1024.
  */
 int grouped_fp8_gemm_swiglu(const uint8_t* A, const float* A_scale,
-                            const int32_t* a_row_index, const uint8_t* B,
+                            const int32_t* a_row_index, int64_t A_rows, const uint8_t* B,
                             const float* B_scale, const int32_t* group_offsets,
                             int32_t G, int64_t M_total, int64_t I, int64_t K,
                             uint8_t* H_e4m3, float* H_scale, void* stream);

@@ -52,7 +52,9 @@ def test_quant_validation():
 
 
 def test_gemm_validation():
-    f = lambda G, M, N, K, A=FAKE: rc("grouped_fp8_gemm", A, FAKE, None, FAKE, FAKE, FAKE, G, M, N, K, FAKE, None)
+    def f(G, M, N, K, A=FAKE, idx=None, A_rows=None):
+        A_rows = M if A_rows is None else A_rows
+        return rc("grouped_fp8_gemm", A, FAKE, idx, A_rows, FAKE, FAKE, FAKE, G, M, N, K, FAKE, None)
     assert f(0, 10, 128, 128) == L.MOE_ERR_INVALID
     assert f(5000, 10, 128, 128) == L.MOE_ERR_UNSUPPORTED   # more groups than the LDS tables hold
     assert f(4, 10, 100, 128) == L.MOE_ERR_INVALID and "N=100" in L.last_error()
@@ -60,6 +62,10 @@ def test_gemm_validation():
     assert f(4, -1, 128, 128) == L.MOE_ERR_INVALID
     assert f(4, 10, 128, 128, A=None) == L.MOE_ERR_INVALID
     assert f(4, 0, 128, 128, A=None) == L.MOE_OK          # empty problem is a no-op
+    # A_rows: at least M_total rows without a row index, at least one with it
+    assert f(4, 10, 128, 128, A_rows=9) == L.MOE_ERR_INVALID and "A_rows" in L.last_error()
+    assert f(4, 10, 128, 128, idx=FAKE, A_rows=0) == L.MOE_ERR_INVALID
+    assert f(4, 10, 128, 128, idx=FAKE, A_rows=1 << 31) == L.MOE_ERR_INVALID
 
 
 def test_route_validation():

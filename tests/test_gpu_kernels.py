@@ -354,9 +354,9 @@ def test_gemm_integer_exact_many_tiles(mean_rows, G, N, K, with_index):
 
 # Large groups (256x256 tiles, taken for an even number of >= 4 K blocks):
 # every remainder class of the last M tile (1..64, 65..128, 129..192,
-# 193..256 rows), empty groups, 4 to 12 K blocks (tiles shorter and longer
-# than the copy pipeline's reach), with and without row gather.
-@pytest.mark.parametrize("K", [512, 1024, 1536])
+# 193..256 rows), empty groups, 6 to 12 K blocks (6: no interior steps
+# between a tile's first 4 and last 8), with and without row gather.
+@pytest.mark.parametrize("K", [768, 1024, 1536])
 @pytest.mark.parametrize("with_index", [False, True])
 def test_gemm_integer_exact_wide(K, with_index):
     sizes = [1000, 0, 170, 400, 256, 513, 65, 129, 200, 0, 700]
@@ -369,6 +369,21 @@ def test_gemm_integer_exact_wide(K, with_index):
     qAr = qA[rowidx] if with_index else qA
     sAr = sA[rowidx] if with_index else sA
     ref = OG.to_bf16(OG.grouped_gemm(qAr, sAr, qB, sB, offsets))
+    assert np.array_equal(got, ref), int((got != ref).sum())
+
+
+# Gathered row indices outside [0, A_rows) read row A_rows - 1 (documented
+# clamp; the copies never leave A).  Small-group and 256-row-tile kernels.
+@pytest.mark.parametrize("sizes", [[40, 7, 90], [300, 200, 0, 260]])
+def test_gemm_gather_index_clamped(sizes):
+    N, K, rows_src = 256, 1024, 50
+    offsets, Mt, qA, sA, qB, sB = _int_gemm_case(sizes, N, K, rows_src, 7)
+    rng = np.random.default_rng(3)
+    rowidx = rng.integers(-5, rows_src + 20, Mt).astype(np.int32)
+    rowidx[:3] = [-2**31, 2**31 - 1, rows_src]
+    got = _gemm_gpu(qA, sA, rowidx, qB, sB, offsets, N, K)
+    clamped = np.where((rowidx < 0) | (rowidx >= rows_src), rows_src - 1, rowidx)
+    ref = OG.to_bf16(OG.grouped_gemm(qA[clamped], sA[clamped], qB, sB, offsets))
     assert np.array_equal(got, ref), int((got != ref).sum())
 
 
@@ -453,7 +468,7 @@ def check_fused_swiglu(q, s, exact, bound, I, what):
                                                   ([1000], 128, 7168, False),
                                                   ([2500] * 12, 256, 384, True),
                                                   ([6] * 200, 256, 256, True),
-                                                  ([300, 0, 77, 513], 256, 512, True),
+                                                  ([300, 0, 77, 513], 256, 768, True),
                                                   ([600, 190], 384, 1024, False)])
 def test_gemm_swiglu_fused(sizes, I, K, with_index):
     G = len(sizes)

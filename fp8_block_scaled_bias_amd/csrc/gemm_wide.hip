@@ -26,18 +26,21 @@
 // rescaled accumulator.
 //
 // Pipeline: a step is 64 K (one v_mfma_f32_32x32x64_f8f6f4 per 32x32
-// block); a ring of 4 LDS stages (A 256 x 64 B, B 256 x 64 B) is filled
-// 3 steps ahead by buffer_load ... lds copies that each wave spreads over its
-// MFMAs; K-block scales come 4 steps ahead, the gathered row-index table of
-// a tile 7 steps ahead.  Copies address memory as a per-tile buffer resource
-// (SGPRs) + a per-tile lane offset (one VGPR) + the K position as the SGPR
-// soffset, which moves only the global address, never the LDS one; so a step
-// spends no vector instructions on addressing.  Every wave issues the same
-// number of copies per step, and each step waits (vmcnt) only for the copies
-// of the step it is about to use.
-//   step s: wait, barrier; per wave 8 MFMAs with the copies of step s+3
-//   interleaved; after the second step of a K block, the ratios of the next
-//   block; after the last step of a tile, the epilogue.
+// block), two steps a K block.  LDS holds two K-block stages (A 256 x 128 B,
+// B 256 x 128 B): while block kb is used, block kb+1 is copied into the
+// other stage by buffer_load ... lds copies that each wave spreads over the
+// MFMAs of kb's first step.  A copy moves 8 rows x 128 B, so every row is
+// one whole cache line (half the memory requests of 64 B row pieces).
+// K-block scales come 4 steps ahead, the gathered row-index table of a tile 7
+// steps ahead.  Copies address memory as a per-tile buffer resource (SGPRs)
+// + a per-tile lane offset (VGPR) + the K position as the SGPR soffset,
+// which moves only the global address, never the LDS one; so a step spends
+// no vector instructions on addressing.  Every wave issues the same copies,
+// and each step waits (vmcnt) only for what it is about to use.
+//   step s: wait, barrier; per wave 8 MFMAs (the first step of a K block
+//   with the next block's copies interleaved); after the first step of a K
+//   block, the ratios of the next block; after the last step of a tile, the
+//   epilogue.
 // The steps away from a tile's first 4 and last 8 carry no run-time tests.
 // Waves whose 64 rows lie past the group's end skip their MFMAs (a ragged
 // last tile costs about half a tile when at most 128 rows remain).
@@ -54,12 +57,10 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 
 constexpr int WT = 512;                  // 8 waves, 2 per SIMD
 constexpr int WBM = 256;                 // tile rows
-constexpr int A_BYTES = 256 * 64;        // A stage: 256 rows x 64 B (swizzled)
-constexpr int B_BYTES = 256 * 64;        // B stage: 256 rows x 64 B
-constexpr int STAGE = A_BYTES + B_BYTES;
-constexpr int NSTAGE = 4;
+constexpr int ST_BYTES = 256 * 128;      // one operand's K-block stage: 256 rows x 128 B
+constexpr int OFF_B = 2 * ST_BYTES;      // A stages 0, 1, then B stages 0, 1
 constexpr int SSLOT = 320 * 4;           // sA[256], then sB[2] (64-float landing area)
-constexpr int OFF_SC = NSTAGE * STAGE;               // 4 scale slots
+constexpr int OFF_SC = 4 * ST_BYTES;                 // 4 scale slots
 constexpr int OFF_R = OFF_SC + 4 * SSLOT;            // float [2][2 halves][256 rows]
 constexpr int OFF_PREF = OFF_R + 2 * 2 * 256 * 4;    // int [MAXG + 1]
 constexpr int OFF_OFFS = OFF_PREF + (MAXG + 1) * 4;  // int [MAXG + 1]
@@ -68,12 +69,6 @@ constexpr int OFF_AMAX = OFF_RIDX + 4 * 256 * 4;     // float [256][2]
 constexpr int LDS = OFF_AMAX + 256 * 2 * 4;
 static_assert(LDS <= 160 * 1024 - 256, "LDS budget");
 static_assert(OFF_R % 16 == 0 && OFF_SC % 16 == 0 && SSLOT % 16 == 0, "float4 reads");
-
-// 64 B rows: 16 B chunk c of row r sits in slot c ^ swz64(r).  For any 16
-// consecutive rows read at one chunk (a 16-lane phase of ds_read_b128 on a
-// 64-bank LDS) and any 8 consecutive rows (an 8-lane phase on 32 banks) the
-// slots spread the rows over distinct banks.
-__device__ __forceinline__ int swz64(int row) { return ((row >> 1) & 3) ^ ((row >> 3) & 1); }
 
 // 32x32 block over 64 K: lane l feeds row l%32 of x and of y (K bytes
 // 32*(l/32)..+31); result element r of lane l is x row 8*(r/4) + 4*(l/32) +
@@ -151,8 +146,9 @@ __global__ __launch_bounds__(WT, 1) void wide_gemm_kernel(GemmArgs args) {
   const int nkb = (int)(K >> 7);  // even, >= 6 (host)
   const int spt = 2 * nkb;        // steps per tile, a multiple of 4, >= 12
   const int nblk = (int)(N >> 7);
-  // copies per wave per step: 4 tile rows + 1 scale (+ 1 row-index table)
-  constexpr int NC = GATHER ? 6 : 5;
+  // small copies per wave per step: 1 scale (+ 1 row-index table); the first
+  // step of a K block also issues the 8 tile copies of the next block
+  constexpr int NS = GATHER ? 2 : 1;
 
   build_group_tables<WT, WBM>(args.offs, G, s_offs, s_pref, s_red, &s_carry);
   const int64_t total = (int64_t)s_pref[G] * ntiles;
@@ -190,16 +186,22 @@ __global__ __launch_bounds__(WT, 1) void wide_gemm_kernel(GemmArgs args) {
 
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
 
-  // ---- copy sources of one tile.  Tile copy p (0..15) of a stage half
-  // covers rows 16p..16p+15: lane -> row 16p + lane/4, LDS slot lane%4,
-  // global chunk (lane%4) ^ swz64(row); wave wv issues p = 2wv, 2wv+1 for A
-  // and for B.  Scales: waves 0-3 copy sA of 64 rows each, waves 4-7 the two
-  // sB of the tile (the same bytes to the same place).  Gathered A rows come
-  // from the tile's row-index table in LDS (buffer ord & 3), clamped to A.
+  // ---- copy sources of one tile.  Stage rows are 128 B with 16 B chunk c
+  // of row r in slot c ^ swz(r) (conflict-free operand reads).  Wave wv
+  // copies rows 32wv..32wv+31 of A and of B in 4 copies of 8 rows: copy p
+  // covers rows 32wv + rb(p) + lane/8 (rb = 0, 16, 8, 24: copies 0, 1 and
+  // 2, 3 share swz), lane -> LDS slot lane%8 <- global chunk
+  // (lane%8) ^ swz(row).  Scales: waves 0-3 copy sA of 64 rows each, waves
+  // 4-7 the two sB of the tile (the same bytes to the same place).  Gathered
+  // A rows come from the tile's row-index table in LDS (buffer ord & 3),
+  // clamped to A.
   struct Srcs {
-    v4i rb;                            // the group's B
-    uint32_t va0, va1, vb0, vb1, vs;  // lane offsets
+    v4i rb;             // the group's B
+    uint32_t va[4];     // A lane offsets of copies 0..3
+    uint32_t vb[2];     // B lane offsets of copies 0 and 2 (1, 3: 16 rows further)
+    uint32_t vs;        // scale lane offset
   };
+  auto crow = [&](int p) -> int { return 32 * wv + 16 * (p & 1) + 8 * (p >> 1) + (lane >> 3); };
   // A and the scales are addressed whole (32-bit offsets: the host checks
   // the sizes); only B's base moves with the tile's group
   const uint32_t a_last = (uint32_t)(args.A_rows - 1);
@@ -213,24 +215,19 @@ __global__ __launch_bounds__(WT, 1) void wide_gemm_kernel(GemmArgs args) {
   };
   auto make_srcs = [&](const Tile& t, int ord) {
     Srcs r;
-    uint32_t va[2];
 #pragma unroll
-    for (int pi = 0; pi < 2; ++pi) {
-      const int row = 32 * wv + 16 * pi + (lane >> 2);
-      const uint32_t gch = (uint32_t)((lane & 3) ^ swz64(row));
-      va[pi] = a_row(t, ord, row) * K + gch * 16;
+    for (int p = 0; p < 4; ++p) {
+      const int row = crow(p);
+      r.va[p] = a_row(t, ord, row) * K + (uint32_t)((lane & 7) ^ swz(row)) * 16;
     }
-    r.va0 = va[0];
-    r.va1 = va[1];
     r.rb = load_rsrc(args.B + ((int64_t)t.g * N) * K, (uint32_t)N * K);
-    {
-      const int row = 32 * wv + (lane >> 2);
-      const uint32_t gch = (uint32_t)((lane & 3) ^ swz64(row));
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int row = crow(2 * h);
       uint32_t n;
       if (SWIGLU) n = (uint32_t)((row < 128 ? 0 : (int)args.I - 128) + 128 * (int)t.nt + row);
       else n = (uint32_t)(256 * (int)t.nt + row);
-      r.vb0 = n * K + gch * 16;
-      r.vb1 = r.vb0 + 16 * K;
+      r.vb[h] = n * K + (uint32_t)((lane & 7) ^ swz(row)) * 16;
     }
     if (wv < 4) r.vs = a_row(t, ord, 64 * wv + lane) * (uint32_t)nkb * 4;
     else r.vs = (uint32_t)((t.g * nblk + nblk_of(t, lane == 1)) * nkb * 4);
@@ -248,24 +245,33 @@ __global__ __launch_bounds__(WT, 1) void wide_gemm_kernel(GemmArgs args) {
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(m0)
                  : "memory", "m0");
   };
-  // LDS destinations: this wave's first tile-copy slot, its scale slice
+  // LDS destinations: this wave's first tile-copy row, its scale slice
   const uint32_t m0_w =
-      (uint32_t)__builtin_amdgcn_readfirstlane((int)(lds0 + (uint32_t)(2 * wv) * 1024));
+      (uint32_t)__builtin_amdgcn_readfirstlane((int)(lds0 + (uint32_t)(32 * wv) * 128));
   const uint32_t sc_w = (uint32_t)__builtin_amdgcn_readfirstlane(
       (int)(lds0 + OFF_SC + (wv < 4 ? (uint32_t)wv * 256 : 1024u)));
-  // tile copy op (0, 1: A rows p = 2wv, 2wv+1; 2, 3: B rows) into stage TST
+  const uint32_t k16 = (uint32_t)__builtin_amdgcn_readfirstlane((int)(16 * K));
+  // tile copy op of K block at global offset so into stage TST: 0..3 A
+  // copies, 4..7 B copies
   auto tile_op = [&](auto TST_, const Srcs& r, int op, uint32_t so) __attribute__((always_inline)) {
     constexpr int TST = decltype(TST_)::value;
-    if (op == 0) copy16<TST * STAGE>(ra, r.va0, so, m0_w);
-    else if (op == 1) copy16<TST * STAGE + 1024>(ra, r.va1, so, m0_w);
-    else if (op == 2) copy16<TST * STAGE + A_BYTES>(r.rb, r.vb0, so, m0_w);
-    else copy16<TST * STAGE + A_BYTES + 1024>(r.rb, r.vb1, so, m0_w);
+    constexpr int A0 = TST * ST_BYTES, B0 = OFF_B + TST * ST_BYTES;
+    switch (op) {
+      case 0: copy16<A0>(ra, r.va[0], so, m0_w); break;
+      case 1: copy16<A0 + 16 * 128>(ra, r.va[1], so, m0_w); break;
+      case 2: copy16<A0 + 8 * 128>(ra, r.va[2], so, m0_w); break;
+      case 3: copy16<A0 + 24 * 128>(ra, r.va[3], so, m0_w); break;
+      case 4: copy16<B0>(r.rb, r.vb[0], so, m0_w); break;
+      case 5: copy16<B0 + 16 * 128>(r.rb, r.vb[0], so + k16, m0_w); break;
+      case 6: copy16<B0 + 8 * 128>(r.rb, r.vb[1], so, m0_w); break;
+      default: copy16<B0 + 24 * 128>(r.rb, r.vb[1], so + k16, m0_w); break;
+    }
   };
   auto scale_copy = [&](const Srcs& r, int kb, int gslot) __attribute__((always_inline)) {
     copy4(rs, r.vs, (uint32_t)kb * 4, sc_w + (uint32_t)gslot * SSLOT);
   };
 
-  // ---- prologue: table of tile 0, then its first 3 steps and the scales
+  // ---- prologue: table of tile 0, then its first K block and the scales
   // of its first 3 K blocks; all waited for.
   Tile tc = tile_at(gh, 0);
   const int32_t* tb_c = nullptr;
@@ -281,11 +287,7 @@ __global__ __launch_bounds__(WT, 1) void wide_gemm_kernel(GemmArgs args) {
   Srcs cur = make_srcs(tc, 0);
   Srcs nxt = cur;
 #pragma unroll
-  for (int op = 0; op < 4; ++op) {
-    tile_op(ic<0>(), cur, op, 0);
-    tile_op(ic<1>(), cur, op, 64);
-    tile_op(ic<2>(), cur, op, 128);
-  }
+  for (int op = 0; op < 8; ++op) tile_op(ic<0>(), cur, op, 0);
   scale_copy(cur, 0, 0);
   scale_copy(cur, 1, 1);
   scale_copy(cur, 2, 2);
@@ -301,16 +303,18 @@ __global__ __launch_bounds__(WT, 1) void wide_gemm_kernel(GemmArgs args) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   // LDS operand reads: lane-constant offsets of the two 16 B chunks of its
-  // 32 B K slice (rows are multiples of 32 plus l32, so swz64 depends on l32
-  // only); everything else is a compile-time offset.  Stages 2, 3 use a
-  // second base so that immediate offsets stay below 64 KiB.
-  const int sw = swz64(l32);
-  const uint32_t o_lo = (uint32_t)(l32 * 64 + (((2 * q) ^ sw) << 4));
-  const uint32_t o_hi = (uint32_t)(l32 * 64 + (((2 * q + 1) ^ sw) << 4));
-  const uint8_t* pa_lo = smem + wm * 64 * 64 + o_lo;
-  const uint8_t* pa_hi = smem + wm * 64 * 64 + o_hi;
-  const uint8_t* pb_lo = smem + A_BYTES + (SWIGLU ? wn * 64 : wn * 128) * 64 + o_lo;
-  const uint8_t* pb_hi = smem + A_BYTES + (SWIGLU ? wn * 64 : wn * 128) * 64 + o_hi;
+  // 32 B K slice in step half h of a K block (chunks 4h + 2q, 4h + 2q + 1;
+  // rows are multiples of 32 plus l32, so swz depends on l32 only);
+  // everything else (stage, row block) is a compile-time offset.
+  const int sw = swz(l32);
+  uint32_t o_lo[2], o_hi[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    o_lo[h] = (uint32_t)(l32 * 128 + (((4 * h + 2 * q) ^ sw) << 4));
+    o_hi[h] = (uint32_t)(l32 * 128 + (((4 * h + 2 * q + 1) ^ sw) << 4));
+  }
+  const uint8_t* pa = smem + wm * 64 * 128;
+  const uint8_t* pb = smem + OFF_B + (SWIGLU ? wn * 64 : wn * 128) * 128;
   auto read_frag = [&](const uint8_t* lo, const uint8_t* hi, int off) -> v8i {
     const uint4 a = *reinterpret_cast<const uint4*>(lo + off);
     const uint4 b = *reinterpret_cast<const uint4*>(hi + off);
@@ -337,16 +341,18 @@ __global__ __launch_bounds__(WT, 1) void wide_gemm_kernel(GemmArgs args) {
     // 8, spt - 4; spt >= 12).  Every test below is decided by U and PH
     // except the first step's wait for the previous epilogue's stores.
     // After the last tile the copies still run (onto the last tile's own
-    // sources): every step then issues NC copies and one vmcnt suffices.
+    // sources), so every K block issues the same copies.
     auto step = [&](auto U_, auto PH_, int k4) __attribute__((always_inline)) {
       constexpr int U = decltype(U_)::value;
       constexpr int PH = decltype(PH_)::value;
       const int k = k4 + U;
-      // copies of step k are done (those of the next two steps may still
-      // fly; after the epilogue's stores, everything); then everyone is
-      // past the previous step
+      // first step of a K block: its copies (issued in the block before) are
+      // done, only the last step's small copies may still fly (after the
+      // epilogue's stores: everything); then everyone is past the previous
+      // step (and its stage is free)
       if (PH == 0 && U == 0) wait_vm_lgkm0();
-      else wait_vmcnt_lgkm0<2 * NC>();
+      else if ((U & 1) == 0) wait_vmcnt_lgkm0<NS>();
+      else wait_lgkm0();
       barrier();
 
       // ---- next tile: decode (its table is copied from step spt-8 on) and
@@ -373,14 +379,16 @@ __global__ __launch_bounds__(WT, 1) void wide_gemm_kernel(GemmArgs args) {
         if (PH >= 2) table_copy(tb_n, tbm_n);
         else table_copy(tb_c, tbm_c);
       }
-      // ---- tile copies of step k+3 ride between the MFMAs below (the
-      // last 3 steps copy the next tile's first steps)
-      constexpr bool T_NEXT = PH == 3 && U >= 1;
-      const uint32_t so = (uint32_t)((T_NEXT ? k + 3 - spt : k + 3) * 64);
-      constexpr int ST = U;                   // stage of step k
-      constexpr int SOFF = (ST & 1) * STAGE;  // offset within the stage pair
-      constexpr int TST = (U + 3) & 3;        // stage of step k+3
+      // ---- the first step of K block kb copies block kb+1 into the other
+      // stage, between its MFMAs (the last block: the next tile's block 0)
+      constexpr bool T_COPY = (U & 1) == 0;
+      constexpr bool T_NEXT = PH == 3 && U == 2;
+      constexpr int ST = U >> 1;              // stage of step k (k4 / 2 is even)
+      constexpr int H = U & 1;                // half of the K block
+      constexpr int TST = ST ^ 1;             // stage of block kb+1
+      const uint32_t so = (uint32_t)((T_NEXT ? 0 : (k >> 1) + 1) * 128);
       auto copies = [&](int op) __attribute__((always_inline)) {
+        if (!T_COPY) return;
         if (T_NEXT) tile_op(ic<TST>(), nxt, op, so);
         else tile_op(ic<TST>(), cur, op, so);
       };
@@ -396,15 +404,13 @@ __global__ __launch_bounds__(WT, 1) void wide_gemm_kernel(GemmArgs args) {
       // ratios S_kb / S_kb+1 after a K block's first step, but the last
       constexpr bool RATIO = (U & 1) == 0 && !(PH == 3 && U == 2);
       if (wvalid) {
-        const uint8_t* alo = pa_lo + (ST >= 2 ? 2 * STAGE : 0);
-        const uint8_t* ahi = pa_hi + (ST >= 2 ? 2 * STAGE : 0);
-        const uint8_t* blo = pb_lo + (ST >= 2 ? 2 * STAGE : 0);
-        const uint8_t* bhi = pb_hi + (ST >= 2 ? 2 * STAGE : 0);
         v8i a[2], b[4];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) a[i] = read_frag(alo, ahi, SOFF + i * 32 * 64);
+        for (int i = 0; i < 2; ++i)
+          a[i] = read_frag(pa + o_lo[H], pa + o_hi[H], ST * ST_BYTES + i * 32 * 128);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) b[j] = read_frag(blo, bhi, SOFF + b_roff(j) * 64);
+        for (int j = 0; j < 4; ++j)
+          b[j] = read_frag(pb + o_lo[H], pb + o_hi[H], ST * ST_BYTES + b_roff(j) * 128);
         // the ratio of a (token row, column half) pair: one value per lane
         // and row block
         float rr[2];
@@ -424,8 +430,10 @@ __global__ __launch_bounds__(WT, 1) void wide_gemm_kernel(GemmArgs args) {
         for (int j = 0; j < 4; ++j) {
           if (RESC_NOW && j >= 2) rescale_block(j);
 #pragma unroll
-          for (int i = 0; i < 2; ++i) acc[i][j] = mfma32(b[j], a[i], acc[i][j]);
-          copies(j);
+          for (int i = 0; i < 2; ++i) {
+            acc[i][j] = mfma32(b[j], a[i], acc[i][j]);
+            copies(2 * j + i);
+          }
         }
         if (RESC_NEXT) {
           load_ratios(kb + 1, SWIGLU ? 0 : wn);
@@ -434,7 +442,7 @@ __global__ __launch_bounds__(WT, 1) void wide_gemm_kernel(GemmArgs args) {
         }
       } else {
 #pragma unroll
-        for (int op = 0; op < 4; ++op) copies(op);
+        for (int op = 0; op < 8; ++op) copies(op);
       }
 
       if (RATIO) {

@@ -1,14 +1,18 @@
 """Benchmark of the DeepSeekMoE layer forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                    [--decode-steps D] [--skewed-steps S]
 
 One step is one pass of the whole hot path over one batch of T=16384 tokens
 at V3 shapes (hidden 7168, 256 routed experts in 8 groups keeping 4, top-8,
 one shared expert, intermediate 2048): route -> quantise x -> permute ->
 gate+up GEMM with fused SwiGLU requantisation -> down GEMM -> combine ->
 bias update.  Inputs are seeded synthetic tensors already resident in HBM.
-Prints one JSON line (rank 0).  The decode batch (T=128) is timed on the same
-weights and reported under "decode".
+Prints one JSON line (rank 0).  On the same weights it also reports: the
+decode batch (T=128, under "decode"), the standalone grouped GEMM over 256
+groups with Multinomial(65536) rows ("grouped_gemm") and the skewed-load
+layer (T=8192, Zipf(1.1) expert popularity, 100 steps of the bias update,
+"skewed").
 """
 from __future__ import annotations
 
@@ -95,10 +99,68 @@ def copy_probe(gib=1, reps=5):
 
 
 def gemm_source_digest():
+    """Digest of the grouped-GEMM kernel sources (both tile shapes)."""
     import hashlib
-    p = os.path.join(ROOT, "fp8_block_scaled_bias_amd", "csrc", "gemm.hip")
-    with open(p, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for name in ("gemm_common.h", "gemm.hip", "gemm_wide.hip"):
+        with open(os.path.join(ROOT, "fp8_block_scaled_bias_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def bench_grouped_gemm(layer, reps=20, warmup=5):
+    """Standalone block-scaled FP8 grouped GEMM: 256 groups (the layer's routed
+    experts' weights), rows per group Multinomial(65536, uniform) at seed 0,
+    A = N(0,1) activations quantised 1x128 on the GPU, bf16 output, no row
+    gather.  Fused gate+up (K=7168, N=4096) and down (K=2048, N=7168), each
+    timed alone (median of `reps` after `warmup`).  Roofline: the larger of
+    the FP8 MFMA time and the HBM time of the algorithmic bytes (A + scales
+    + all 256 groups' B + scales + C)."""
+    import numpy as np
+    import torch
+    import synth
+    import fp8_block_scaled_bias_amd as M
+    s = layer.shape
+    G, rows = s.E, s.E * 256
+    counts = synth.gen_group_counts(rows, G, seed=0)
+    offs = torch.from_numpy(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)).cuda()
+    out = {"workload": "standalone grouped GEMM, 256 groups, Multinomial(65536) rows",
+           "groups": G, "rows": rows, "rows_min": int(counts.min()), "rows_max": int(counts.max())}
+    st = torch.cuda.current_stream()
+    for name, K, N, B, Bs, seed in (("gate_up", s.H, 2 * s.I, layer.w_gu, layer.w_gu_s, 1),
+                                    ("down", s.I, s.H, layer.w_dn, layer.w_dn_s, 2)):
+        a = torch.from_numpy(synth.gen_gemm_activations(rows, K, seed).view(np.int16)).cuda()
+        a = a.view(torch.bfloat16)
+        aq = torch.empty((rows, K), dtype=torch.uint8, device="cuda")
+        asc = torch.empty((rows, K // 128), dtype=torch.float32, device="cuda")
+        M.fp8_quant_1x128(a, rows, K, K, 0, aq, asc)
+        del a
+        c = torch.empty((rows, N), dtype=torch.bfloat16, device="cuda")
+        run = lambda: M.grouped_fp8_gemm(aq, asc, None, B, Bs, offs, G, rows, N, K, c)
+        for _ in range(warmup):
+            run()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            run()
+            e1.record(st)
+            ts.append((e0, e1))
+        torch.cuda.synchronize()
+        ms = float(np.median([e0.elapsed_time(e1) for e0, e1 in ts]))
+        flop = 2.0 * rows * N * K
+        nbytes = (rows * K + rows * (K // 128) * 4 + G * N * K + G * (N // 128) * (K // 128) * 4
+                  + rows * N * 2)
+        t_mfma, t_hbm = flop / (FP8_PEAK_TFLOPS * 1e12), nbytes / (HBM_PEAK_GBS * 1e9)
+        out[name] = {"K": K, "N": N, "ms": ms, "TFLOPS": flop / (ms * 1e-3) / 1e12,
+                     "GB_s": nbytes / (ms * 1e-3) / 1e9, "algorithmic_bytes": nbytes,
+                     "bound": "hbm" if t_hbm > t_mfma else "mfma",
+                     "frac_of_bound": max(t_mfma, t_hbm) / (ms * 1e-3)}
+        log(f"[bench] grouped GEMM {name}: {ms:.3f} ms, {out[name]['TFLOPS']:.0f} TFLOP/s, "
+            f"{out[name]['GB_s']:.0f} GB/s, {out[name]['frac_of_bound']:.2f} of the "
+            f"{out[name]['bound']} roof")
+        del aq, asc, c
+    return out
 
 
 # HBM traffic of the gate+up kernel at T=16384, from two rocprofv3 --pmc runs
@@ -107,6 +169,47 @@ def gemm_source_digest():
 GATE_UP_TRAFFIC = {"gemm_src": "3a3544bd06e733ce",
                    # FETCH_SIZE 6,871,815 KiB x 2.000 + WRITE_SIZE 322,852 KiB x 1.000
                    "bytes": 6871815 * 1024 * 2 + 322852 * 1024}
+
+
+def bench_skewed(layer, steps=100):
+    """Skewed-load layer: T=8192 at V3 shapes, router centroids with
+    Zipf(1.1)-scaled expert rows (stored fit), bias starting at 0, `steps`
+    forward steps each on a fresh batch (seed 1000 + step) followed by the
+    bias update (gamma = 0.001).  Per step: max/mean expert load of that
+    step's routing and the forward time (HIP events on the launch stream).
+    Batches are drawn on host threads ahead of use (not timed)."""
+    from concurrent.futures import ThreadPoolExecutor
+    import numpy as np
+    import torch
+    import synth
+    import fp8_block_scaled_bias_amd as M
+    cfg = synth.SKEWED
+    C = torch.from_numpy(synth.gen_zipf_centroids(cfg)).cuda()
+    b = torch.zeros(cfg.E, dtype=torch.float32, device="cuda")
+    sk = M.MoELayer(layer.shape, C, b, layer.w_gu, layer.w_gu_s, layer.w_dn, layer.w_dn_s)
+    st = torch.cuda.current_stream()
+    loads, times = [], []
+    mean = cfg.T * cfg.k / cfg.E
+    with ThreadPoolExecutor(8) as ex:
+        futs = [ex.submit(synth.gen_x, cfg, synth.ZIPF_STEP_SEED0 + i) for i in range(steps)]
+        for i in range(steps):
+            xb = torch.from_numpy(futs[i].result().view(np.int16)).cuda().view(torch.bfloat16)
+            futs[i] = None
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            sk.forward(xb, update_bias=True)
+            e1.record(st)
+            cnt = sk.buffers(cfg.T).counts.cpu().numpy()
+            times.append(e0.elapsed_time(e1))
+            loads.append(float(cnt.max()) / mean)
+    ms = float(np.median(times))
+    flop = 2.0 * cfg.R * 3 * cfg.I * cfg.H
+    log(f"[bench] skewed T={cfg.T}: max/mean load step 0 {loads[0]:.2f} -> step {steps - 1} "
+        f"{loads[-1]:.2f}; median {ms:.3f} ms/step")
+    return {"workload": "skewed-load layer, Zipf(1.1) centroids, bias update each step",
+            "T": cfg.T, "steps": steps, "gamma": 0.001, "max_over_mean_load": loads,
+            "ms_per_step": times, "median_ms": ms, "tokens_per_s": cfg.T / (ms * 1e-3),
+            "TFLOPS": flop / (ms * 1e-3) / 1e12}
 
 
 def cpu_baseline(cfg, n_tokens=32):
@@ -145,6 +248,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=50)
+    ap.add_argument("--skewed-steps", type=int, default=100)
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -186,6 +290,9 @@ def main():
     dgbs = dbytes / (dms * 1e-3) / 1e9
     log(f"[bench] decode per-kernel ms: " + ", ".join(f"{k} {v:.3f}" for k, v in dper.items()))
 
+    gg = bench_grouped_gemm(layer)
+    skew = bench_skewed(layer, args.skewed_steps) if args.skewed_steps > 0 else None
+
     traffic = None
     if GATE_UP_TRAFFIC and GATE_UP_TRAFFIC["gemm_src"] == gemm_source_digest():
         traffic = GATE_UP_TRAFFIC["bytes"]
@@ -217,6 +324,8 @@ def main():
         "decode": {"T": dcfg.T, "ms_per_step": dms, "touched_experts": touched,
                    "algorithmic_bytes": dbytes, "GB_s": dgbs, "frac_hbm_peak": dgbs / HBM_PEAK_GBS,
                    "per_kernel_ms": dper},
+        "grouped_gemm": gg,
+        "skewed": skew,
         "copy_probe": cp,
     }
     if not args.no_cpu_baseline:

@@ -180,3 +180,33 @@ def pow2_scales(shape, seed: int, lo: int = -3, hi: int = 3) -> np.ndarray:
     """Power-of-two fp32 scales 2^[lo, hi] (exact-arithmetic GEMM cases)."""
     r = np.random.default_rng([seed, 98])
     return np.ldexp(np.float32(1.0), r.integers(lo, hi + 1, size=shape)).astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# Skewed-load workload: router centroids N(0, c_std) whose expert rows are
+# scaled by per-expert factors, so that expert popularity follows a Zipf(1.1)
+# curve over a random ranking of the experts.  The factors are fitted once, on
+# a calibration batch, by tests/golden/make_zipf_scale.py and stored in
+# tests/golden/zipf_scale.txt; this module only reads them.
+ZIPF_S = 1.1
+ZIPF_CAL_SEED = 7          # calibration batch of the fit
+ZIPF_STEP_SEED0 = 1000     # batch of run step i: seed 1000 + i
+ZIPF_SCALE_FILE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                               "tests", "golden", "zipf_scale.txt")
+
+
+def zipf_ranks(E: int, seed: int = 0) -> np.ndarray:
+    """Popularity rank (1 = most popular) of each expert: a random permutation."""
+    return _rng(seed, TID_ZIPF_SCALE).permutation(E).astype(np.int64) + 1
+
+
+def load_zipf_scale(path: str = ZIPF_SCALE_FILE) -> np.ndarray:
+    """Per-expert centroid scale factors [E] (fp32) from the stored fit."""
+    rows = [l.split() for l in open(path) if l.strip() and not l.startswith("#")]
+    return np.array([float(r[1]) for r in rows], dtype=np.float32)
+
+
+def gen_zipf_centroids(cfg: MoEConfig, scale: np.ndarray | None = None) -> np.ndarray:
+    """Skewed-load centroids: gen_centroids(cfg) with row e multiplied by scale[e]."""
+    scale = load_zipf_scale() if scale is None else np.asarray(scale, np.float32)
+    return (gen_centroids(cfg) * scale[:, None]).astype(np.float32)

@@ -7,7 +7,10 @@
   configuration the benchmark times: routing of every token against the
   FP64 oracle (near-ties logged), the GPU weight quantiser against the
   oracle's on the touched experts, and the layer output of sampled tokens
-  against the direct per-token oracle (rel L2 <= 2e-3).
+  against the direct per-token oracle (rel L2 <= 2e-3);
+* the skewed-load workload (T=8192, Zipf-scaled centroids, bias from 0):
+  three steps on fresh batches with the bias update after each, against the
+  oracle's own bias trajectory.
 """
 import numpy as np
 import pytest
@@ -17,6 +20,7 @@ import synth
 import fp8_block_scaled_bias_amd as M
 from gpu_common import bf16_dev, bf16_values_host, host, log, rel_l2, compare_routes
 from test_gpu_kernels import check_fused_swiglu, gemm_accumulation_bound
+from oracle import balance as OB
 from oracle import gemm as OG
 from oracle import layer as OL
 from oracle import route as OR
@@ -129,3 +133,44 @@ def test_layer_v3_decode(v3_layer):
 
 def test_layer_v3_prefill(v3_layer):
     _v3_check(v3_layer, synth.PREFILL, _sample(16384, 16, 2))
+
+
+def test_layer_skewed_bias_steps(v3_layer):
+    """Skewed-load workload: 3 steps, each on a fresh batch (seed 1000 + step)
+    and followed by the bias update (news.qq.com article, section 无额外损耗的
+    负载均衡: bias -/+ gamma for over/under-loaded experts).  Per step: routing
+    of all 8192 tokens against the oracle run with the oracle's own bias
+    trajectory (near-ties logged), counts exact, the updated bias bit-exact;
+    at step 0 also the layer output of sampled tokens (rel L2 <= 2e-3)."""
+    base = v3_layer[0]
+    cfg = synth.SKEWED
+    C = synth.gen_zipf_centroids(cfg)
+    layer = M.MoELayer(base.shape, torch.from_numpy(C).cuda(),
+                       torch.zeros(cfg.E, dtype=torch.float32, device="cuda"),
+                       base.w_gu, base.w_gu_s, base.w_dn, base.w_dn_s)
+    b_ora = np.zeros(cfg.E, np.float32)
+    mean = cfg.T * cfg.k / cfg.E
+    for step in range(3):
+        log(f"[skewed] step {step}: forward")
+        x = synth.gen_x(cfg, seed=synth.ZIPF_STEP_SEED0 + step)
+        b_used = b_ora.copy()
+        y = layer.forward(bf16_dev(x), update_bias=True)
+        got = bf16_values_host(y)
+        bufs = layer.buffers(cfg.T)
+        ora = OR.route(x, C, b_used, cfg.n_group, cfg.topk_group, cfg.k)
+        mism = compare_routes(host(bufs.topk_idx), ora, f"skewed step {step}")
+        cnt = host(bufs.counts)
+        log(f"[skewed] step {step}: max/mean load {cnt.max() / mean:.2f}")
+        if len(mism) == 0:
+            assert np.array_equal(cnt, ora["counts"])
+        # the update follows the counts the GPU routed (equal unless a near-tie moved one)
+        b_ora = OB.bias_update(cnt, b_ora)
+        assert np.array_equal(host(layer.bias), b_ora)
+        if step == 0:
+            sample = [t for t in _sample(cfg.T, 8, 3) if t not in set(mism.tolist())]
+            wts = oracle_weights(cfg)
+            ref = OL.layer_tokens(x, C, b_used, wts, cfg.n_group, cfg.topk_group, cfg.k, cfg.I,
+                                  sample)
+            rel = rel_l2(got[sample], ref["y"])
+            log(f"[skewed] step 0: rel L2 of sampled y ({len(sample)} tokens) = {rel:.3e}")
+            assert rel <= REL_L2_BAR

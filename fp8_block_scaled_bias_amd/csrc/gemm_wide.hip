@@ -329,6 +329,7 @@ __global__ __launch_bounds__(WT, 1) void wide_gemm_kernel(GemmArgs args) {
 
   int gh_n = gh;  // hint for decoding the next tile
   Tile tn = tc;
+  v8i a[2], b[4];  // MFMA operands of the current step (A rows, B rows)
 
   for (int ord = 0; ord < my_n; ++ord) {
     const bool has_next = ord + 1 < my_n;
@@ -394,9 +395,8 @@ __global__ __launch_bounds__(WT, 1) void wide_gemm_kernel(GemmArgs args) {
       };
 
       const int kb = (k4 >> 1) + (U >> 1);
-      // rescale by S_kb-1 / S_kb in two halves: column blocks 2, 3 on the
-      // first step of K block kb (between the MFMAs of blocks 0, 1 and
-      // their own), blocks 0, 1 at the end of the step before; each step then
+      // rescale by S_kb-1 / S_kb in two halves: column blocks 2, 3 in the
+      // first step of K block kb, blocks 0, 1 in the step before; each step
       // carries half of the multiplies.  None before K block 1; none after
       // the last block.
       constexpr bool RESC_NOW = (U & 1) == 0 && !(PH == 0 && U == 0);
@@ -404,42 +404,48 @@ __global__ __launch_bounds__(WT, 1) void wide_gemm_kernel(GemmArgs args) {
       // ratios S_kb / S_kb+1 after a K block's first step, but the last
       constexpr bool RATIO = (U & 1) == 0 && !(PH == 3 && U == 2);
       if (wvalid) {
-        v8i a[2], b[4];
+        // operands of this step: the first step of a K block reads them; the
+        // second step's were read at the end of the first (same stage, no
+        // wait needed), so that their LDS latency hides behind MFMAs
+        auto read_ops = [&](auto H_) __attribute__((always_inline)) {
+          constexpr int HH = decltype(H_)::value;
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-          a[i] = read_frag(pa + o_lo[H], pa + o_hi[H], ST * ST_BYTES + i * 32 * 128);
+          for (int i = 0; i < 2; ++i)
+            a[i] = read_frag(pa + o_lo[HH], pa + o_hi[HH], ST * ST_BYTES + i * 32 * 128);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          b[j] = read_frag(pb + o_lo[H], pb + o_hi[H], ST * ST_BYTES + b_roff(j) * 128);
+          for (int j = 0; j < 4; ++j)
+            b[j] = read_frag(pb + o_lo[HH], pb + o_hi[HH], ST * ST_BYTES + b_roff(j) * 128);
+        };
+        if (H == 0) read_ops(ic<0>());
         // the ratio of a (token row, column half) pair: one value per lane
         // and row block
-        float rr[2];
-        auto load_ratios = [&](int kbr, int hb) __attribute__((always_inline)) {
+        auto load_ratios = [&](float* rr, int kbr, int hb) __attribute__((always_inline)) {
           const float* rsh = s_r + (kbr & 1) * 512 + hb * 256 + wm * 64 + l32;
           rr[0] = rsh[0];
           rr[1] = rsh[32];
         };
-        auto rescale_block = [&](int j) __attribute__((always_inline)) {
+        auto rescale = [&](int i, int j, float r_) __attribute__((always_inline)) {
 #pragma unroll
-          for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] *= rr[i];
+          for (int r = 0; r < 16; ++r) acc[i][j][r] *= r_;
         };
-        if (RESC_NOW) load_ratios(kb, SWIGLU ? 1 : wn);
+        float r_now[2], r_next[2];
+        if (RESC_NOW) load_ratios(r_now, kb, SWIGLU ? 1 : wn);
+        if (RESC_NEXT) load_ratios(r_next, kb + 1, SWIGLU ? 0 : wn);
+        // MFMA s = (block j = s/2, row block i = s%2); after each of the
+        // first four, a quarter of blocks 2, 3's rescale (before their own
+        // MFMAs), after each of the last four, a quarter of blocks 0, 1's
+        // rescale for the next K block (after theirs): 16 multiplies between
+        // consecutive MFMAs, which the other wave's MFMAs cover
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (RESC_NOW && j >= 2) rescale_block(j);
-#pragma unroll
-          for (int i = 0; i < 2; ++i) {
-            acc[i][j] = mfma32(b[j], a[i], acc[i][j]);
-            copies(2 * j + i);
-          }
+        for (int s = 0; s < 8; ++s) {
+          const int j = s >> 1, i = s & 1;
+          acc[i][j] = mfma32(b[j], a[i], acc[i][j]);
+          copies(s);
+          if (RESC_NOW && s < 4) rescale(s & 1, 2 + (s >> 1), r_now[s & 1]);
+          if (RESC_NEXT && s >= 4) rescale(s & 1, (s - 4) >> 1, r_next[s & 1]);
+          __builtin_amdgcn_sched_barrier(0);  // keep this order (the scheduler would group)
         }
-        if (RESC_NEXT) {
-          load_ratios(kb + 1, SWIGLU ? 0 : wn);
-          rescale_block(0);
-          rescale_block(1);
-        }
+        if (H == 0) read_ops(ic<1>());
       } else {
 #pragma unroll
         for (int op = 0; op < 8; ++op) copies(op);

@@ -403,6 +403,21 @@ __global__ __launch_bounds__(WT, 1) void wide_gemm_kernel(GemmArgs args) {
       constexpr bool RESC_NEXT = (U & 1) == 1 && !(PH == 3 && U == 3);
       // ratios S_kb / S_kb+1 after a K block's first step, but the last
       constexpr bool RATIO = (U & 1) == 0 && !(PH == 3 && U == 2);
+      // ratios S_kb / S_kb+1 for the next K block of this tile, one (row,
+      // column half) per thread: scales read at the start of a K block's
+      // first step, the quotient stored between its MFMAs (read from the
+      // next step on, after its barrier)
+      float rsc[4];
+      const int rrow = tid & 255, rb = tid >> 8;
+      auto ratio_load = [&]() __attribute__((always_inline)) {
+        const float* sc0 = s_sc + ((gbase + kb) & 3) * (SSLOT / 4);
+        const float* sc1 = s_sc + ((gbase + kb + 1) & 3) * (SSLOT / 4);
+        rsc[0] = sc0[rrow]; rsc[1] = sc0[256 + rb];
+        rsc[2] = sc1[rrow]; rsc[3] = sc1[256 + rb];
+      };
+      auto ratio_store = [&]() __attribute__((always_inline)) {
+        s_r[((kb + 1) & 1) * 512 + rb * 256 + rrow] = (rsc[0] * rsc[1]) / (rsc[2] * rsc[3]);
+      };
       if (wvalid) {
         // operands of this step: the first step of a K block reads them; the
         // second step's were read at the end of the first (same stage, no
@@ -417,6 +432,7 @@ __global__ __launch_bounds__(WT, 1) void wide_gemm_kernel(GemmArgs args) {
             b[j] = read_frag(pb + o_lo[HH], pb + o_hi[HH], ST * ST_BYTES + b_roff(j) * 128);
         };
         if (H == 0) read_ops(ic<0>());
+        if (RATIO) ratio_load();
         // the ratio of a (token row, column half) pair: one value per lane
         // and row block
         auto load_ratios = [&](float* rr, int kbr, int hb) __attribute__((always_inline)) {
@@ -443,21 +459,17 @@ __global__ __launch_bounds__(WT, 1) void wide_gemm_kernel(GemmArgs args) {
           copies(s);
           if (RESC_NOW && s < 4) rescale(s & 1, 2 + (s >> 1), r_now[s & 1]);
           if (RESC_NEXT && s >= 4) rescale(s & 1, (s - 4) >> 1, r_next[s & 1]);
+          if (RATIO && s == 5) ratio_store();
           __builtin_amdgcn_sched_barrier(0);  // keep this order (the scheduler would group)
         }
         if (H == 0) read_ops(ic<1>());
       } else {
 #pragma unroll
         for (int op = 0; op < 8; ++op) copies(op);
-      }
-
-      if (RATIO) {
-        const float* sc0 = s_sc + ((gbase + kb) & 3) * (SSLOT / 4);
-        const float* sc1 = s_sc + ((gbase + kb + 1) & 3) * (SSLOT / 4);
-        const int row = tid & 255, b = tid >> 8;
-        const float S0 = sc0[row] * sc0[256 + b];
-        const float S1 = sc1[row] * sc1[256 + b];
-        s_r[((kb + 1) & 1) * 512 + b * 256 + row] = S0 / S1;
+        if (RATIO) {
+          ratio_load();
+          ratio_store();
+        }
       }
     };
     step(ic<0>(), ic<0>(), 0);

@@ -330,6 +330,17 @@ __global__ __launch_bounds__(WT, 1) void wide_gemm_kernel(GemmArgs args) {
   int gh_n = gh;  // hint for decoding the next tile
   Tile tn = tc;
   v8i a[2], b[4];  // MFMA operands of the current step (A rows, B rows)
+  // operands of step half HH of the K block in stage STG
+  auto read_ops = [&](auto STG_, auto HH_) __attribute__((always_inline)) {
+    constexpr int STG = decltype(STG_)::value, HH = decltype(HH_)::value;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      a[i] = read_frag(pa + o_lo[HH], pa + o_hi[HH], STG * ST_BYTES + i * 32 * 128);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      b[j] = read_frag(pb + o_lo[HH], pb + o_hi[HH], STG * ST_BYTES + b_roff(j) * 128);
+  };
+  read_ops(ic<0>(), ic<0>());
 
   for (int ord = 0; ord < my_n; ++ord) {
     const bool has_next = ord + 1 < my_n;
@@ -347,14 +358,13 @@ __global__ __launch_bounds__(WT, 1) void wide_gemm_kernel(GemmArgs args) {
       constexpr int U = decltype(U_)::value;
       constexpr int PH = decltype(PH_)::value;
       const int k = k4 + U;
-      // first step of a K block: its copies (issued in the block before) are
-      // done, only the last step's small copies may still fly (after the
-      // epilogue's stores: everything); then everyone is past the previous
-      // step (and its stage is free)
-      if (PH == 0 && U == 0) wait_vm_lgkm0();
-      else if ((U & 1) == 0) wait_vmcnt_lgkm0<NS>();
-      else wait_lgkm0();
-      barrier();
+      // second step of a K block: everyone is past the first (whose ratios
+      // it uses); the first step of a K block synchronises at the end of the
+      // block before
+      if ((U & 1) == 1) {
+        wait_lgkm0();
+        barrier();
+      }
 
       // ---- next tile: decode (its table is copied from step spt-8 on) and
       // copy sources (at step spt-5, when that table has landed)
@@ -419,19 +429,10 @@ __global__ __launch_bounds__(WT, 1) void wide_gemm_kernel(GemmArgs args) {
         s_r[((kb + 1) & 1) * 512 + rb * 256 + rrow] = (rsc[0] * rsc[1]) / (rsc[2] * rsc[3]);
       };
       if (wvalid) {
-        // operands of this step: the first step of a K block reads them; the
-        // second step's were read at the end of the first (same stage, no
-        // wait needed), so that their LDS latency hides behind MFMAs
-        auto read_ops = [&](auto H_) __attribute__((always_inline)) {
-          constexpr int HH = decltype(H_)::value;
-#pragma unroll
-          for (int i = 0; i < 2; ++i)
-            a[i] = read_frag(pa + o_lo[HH], pa + o_hi[HH], ST * ST_BYTES + i * 32 * 128);
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            b[j] = read_frag(pb + o_lo[HH], pb + o_hi[HH], ST * ST_BYTES + b_roff(j) * 128);
-        };
-        if (H == 0) read_ops(ic<0>());
+        // this step's operands are in registers: a K block's first-step
+        // operands were read at the end of the block before (after its
+        // wait and barrier), its second step's at the end of its first step
+        // (same stage), so their LDS latency hides behind MFMAs
         if (RATIO) ratio_load();
         // the ratio of a (token row, column half) pair: one value per lane
         // and row block
@@ -462,7 +463,7 @@ __global__ __launch_bounds__(WT, 1) void wide_gemm_kernel(GemmArgs args) {
           if (RATIO && s == 5) ratio_store();
           __builtin_amdgcn_sched_barrier(0);  // keep this order (the scheduler would group)
         }
-        if (H == 0) read_ops(ic<1>());
+        if (H == 0) read_ops(ic<ST>(), ic<1>());
       } else {
 #pragma unroll
         for (int op = 0; op < 8; ++op) copies(op);
@@ -470,6 +471,19 @@ __global__ __launch_bounds__(WT, 1) void wide_gemm_kernel(GemmArgs args) {
           ratio_load();
           ratio_store();
         }
+      }
+      // end of a K block: the next block's copies (issued in this block's
+      // first step) are done, only this step's small copies may still fly
+      // (in a tile's first block: everything, as the last epilogue's stores
+      // count too); then everyone is past this block (its stage is free) and
+      // the next block's first-step operands are read (the next tile's block
+      // 0 after a tile's last block; every wave, valid in the next tile or
+      // not)
+      if ((U & 1) == 1) {
+        if (PH == 0 && U == 1) wait_vm_lgkm0();
+        else wait_vmcnt_lgkm0<NS>();
+        barrier();
+        read_ops(ic<(U == 1 ? 1 : 0)>(), ic<0>());
       }
     };
     step(ic<0>(), ic<0>(), 0);

@@ -166,9 +166,9 @@ def bench_grouped_gemm(layer, reps=20, warmup=5):
 # HBM traffic of the gate+up kernel at T=16384, from two rocprofv3 --pmc runs
 # (FETCH_SIZE, WRITE_SIZE) of this script, each scaled by the same counter on
 # the 1 GiB copy probe.  Valid only for the kernel source with this digest.
-GATE_UP_TRAFFIC = {"gemm_src": "3a3544bd06e733ce",
-                   # FETCH_SIZE 6,871,815 KiB x 2.000 + WRITE_SIZE 322,852 KiB x 1.000
-                   "bytes": 6871815 * 1024 * 2 + 322852 * 1024}
+GATE_UP_TRAFFIC = {"gemm_src": "420375aa73a129af",
+                   # FETCH_SIZE 9,409,011 KiB x 2.000 + WRITE_SIZE 328,820 KiB x 1.000
+                   "bytes": 9409011 * 1024 * 2 + 328820 * 1024}
 
 
 def bench_skewed(layer, steps=100):

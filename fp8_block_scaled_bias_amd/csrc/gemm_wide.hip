@@ -524,25 +524,51 @@ __global__ __launch_bounds__(WT, 1) void wide_gemm_kernel(GemmArgs args) {
       }
     }
     if (!SWIGLU) {
-      // bf16 (round to nearest even): 4 consecutive columns per 8-byte store
+      // bf16 (round to nearest even), staged through LDS so that each store
+      // writes whole 128 B rows: per half of its columns (j = 2c, 2c+1) a
+      // wave writes its 64 rows x 64 columns into its own 8 KB of the
+      // tile's free K-block stage (stage 1: the last K block's, all of whose
+      // reads ended at the last step's barrier; 16 B chunks XOR-swizzled by
+      // row), reads them back 8 rows x 128 B per instruction and stores them.
+      // Only the wave itself touches its region; the barrier after the
+      // epilogue keeps the next tile's copies into stage 1 behind it.
       if (wvalid) {
         const uint32_t rowb = (uint32_t)N * 2;
         const __amdgpu_buffer_rsrc_t rs =
             out_rsrc(args.C + (int64_t)t.m0 * N, (uint32_t)min(t.m1 - t.m0, WBM) * rowb);
+        uint8_t* reg = smem + (wv < 4 ? ST_BYTES + wv * 8192 : OFF_B + ST_BYTES + (wv - 4) * 8192);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int vb = (wm * 64 + 32 * i + l32) * (int)rowb + (int)(256 * t.nt + wn * 128 + 4 * q) * 2;
+        for (int c = 0; c < 2; ++c) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
+          for (int i = 0; i < 2; ++i) {
+            const int row = 32 * i + l32;  // in the wave's 64
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              typedef uint32_t v2u __attribute__((ext_vector_type(2)));
-              const v2u w = {f32x2_to_bf16x2(acc[i][j][4 * g], acc[i][j][4 * g + 1]),
-                             f32x2_to_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3])};
-              __builtin_amdgcn_raw_buffer_store_b64(w, rs, vb, (32 * j + 8 * g) * 2, 0);
-            }
+            for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+              for (int g = 0; g < 4; ++g) {
+                const v16f& v = acc[i][2 * c + jj];
+                typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+                const v2u w = {f32x2_to_bf16x2(v[4 * g], v[4 * g + 1]),
+                               f32x2_to_bf16x2(v[4 * g + 2], v[4 * g + 3])};
+                const int chunk = (4 * jj + g) ^ (row & 7);
+                *reinterpret_cast<v2u*>(reg + row * 128 + chunk * 16 + q * 8) = w;
+              }
+          }
+          wait_lgkm0();
+          const int vb = (wm * 64 + (lane >> 3)) * (int)rowb +
+                         (int)(256 * t.nt + wn * 128 + 64 * c + 8 * (lane & 7)) * 2;
+#pragma unroll
+          for (int r8 = 0; r8 < 8; ++r8) {
+            const int row = 8 * r8 + (lane >> 3);
+            const uint4 d = *reinterpret_cast<const uint4*>(reg + row * 128 + (((lane & 7) ^ (row & 7)) << 4));
+            typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+            const v4u w = {d.x, d.y, d.z, d.w};
+            __builtin_amdgcn_raw_buffer_store_b128(w, rs, vb, 8 * r8 * (int)rowb, 0);
+          }
+          wait_lgkm0();
         }
       }
+      barrier();
     } else {
       // h = silu(g) * u: gate block j pairs with up block j + 2.  A row's 128
       // h columns of this N tile: 32 in each lane of the pair (q = 0, 1) of

@@ -568,8 +568,10 @@ __global__ __launch_bounds__(WT, 1) void wide_gemm_kernel(GemmArgs args) {
           wait_lgkm0();
         }
       }
-      barrier();
     } else {
+      // the row pair's (wm) 64 rows x 128 B of codes, staged in the tile's
+      // free K-block stage (A part of stage 1) for whole-row stores
+      uint8_t* hreg = smem + ST_BYTES + wm * 8192;
       // h = silu(g) * u: gate block j pairs with up block j + 2.  A row's 128
       // h columns of this N tile: 32 in each lane of the pair (q = 0, 1) of
       // both column waves; the row maximum meets over the pair by a lane
@@ -598,7 +600,6 @@ __global__ __launch_bounds__(WT, 1) void wide_gemm_kernel(GemmArgs args) {
       if (wvalid) {
         const int I = (int)args.I, hb = I >> 7;
         const uint32_t rows = (uint32_t)min(t.m1 - t.m0, WBM);
-        const __amdgpu_buffer_rsrc_t rq = out_rsrc(args.Hq + (int64_t)t.m0 * I, rows * I);
         const __amdgpu_buffer_rsrc_t rsc = out_rsrc(args.Hs + (int64_t)t.m0 * hb, rows * hb * 4);
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
@@ -608,20 +609,41 @@ __global__ __launch_bounds__(WT, 1) void wide_gemm_kernel(GemmArgs args) {
           inv[i] = 1.0f / sc;
           if (wn == 0 && q == 0)
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), rsc, (trow * hb + (int)t.nt) * 4, 0, 0);
-          const int vq = trow * I + (int)(128 * t.nt) + wn * 64 + 4 * q;
+          // codes into the pair's 64 rows x 128 B of LDS (16 B chunks
+          // swizzled by row): columns wn*64 + 32j + 8g + 4q, 4 per dword
+          const int row = 32 * i + l32;
 #pragma unroll
           for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
               const v16f& h = acc[i][j];
-              __builtin_amdgcn_raw_buffer_store_b32(
+              const int chunk = (4 * wn + 2 * j + (g >> 1)) ^ (row & 7);
+              *reinterpret_cast<uint32_t*>(hreg + row * 128 + chunk * 16 + 8 * (g & 1) + 4 * q) =
                   f32x4_to_e4m3x4(h[4 * g] * inv[i], h[4 * g + 1] * inv[i], h[4 * g + 2] * inv[i],
-                                  h[4 * g + 3] * inv[i]),
-                  rq, vq, 32 * j + 8 * g, 0);
+                                  h[4 * g + 3] * inv[i]);
             }
         }
       }
+      wait_lgkm0();
+      barrier();
+      // whole 128 B rows: wave wn stores rows 32wn..32wn+31 of its pair's 64
+      if (wvalid) {
+        const int I = (int)args.I;
+        const uint32_t rows = (uint32_t)min(t.m1 - t.m0, WBM);
+        const __amdgpu_buffer_rsrc_t rq = out_rsrc(args.Hq + (int64_t)t.m0 * I, rows * I);
+        const int vq = (wm * 64 + 32 * wn + (lane >> 3)) * I + (int)(128 * t.nt) + 16 * (lane & 7);
+#pragma unroll
+        for (int r8 = 0; r8 < 4; ++r8) {
+          const int row = 32 * wn + 8 * r8 + (lane >> 3);
+          const uint4 d = *reinterpret_cast<const uint4*>(hreg + row * 128 + (((lane & 7) ^ (row & 7)) << 4));
+          typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+          const v4u w = {d.x, d.y, d.z, d.w};
+          __builtin_amdgcn_raw_buffer_store_b128(w, rq, vq, 8 * r8 * I, 0);
+        }
+      }
     }
+    // the next tile's copies into stage 1 wait for every wave's epilogue
+    barrier();
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll

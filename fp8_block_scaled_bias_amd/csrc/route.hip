@@ -135,6 +135,174 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
   }
 }
 
+// ---- large batches: the centroids are split once per call into three bf16
+// planes (hi, mid, lo; C = hi + mid + lo exactly) in the workspace, and a
+// workgroup computes 256 tokens x 256 experts over a K range (split-K
+// partials, added in fixed order by router_select) on
+// v_mfma_f32_32x32x16_bf16: x is the row operand, each plane the column
+// operand, all three into one accumulator.  Operands move global -> LDS by
+// buffer_load ... lds copies into two 64 KB stages (x 256 rows x 64 B,
+// planes 3 x 256 rows x 64 B); rows' 16 B chunks are XOR-swizzled so the
+// operand reads are conflict-free.
+
+constexpr int RW_TOK = 256;
+constexpr int RW_XB = 256 * 64;            // x stage: 256 rows x 32 bf16
+constexpr int RW_PB = 256 * 64;            // one plane's stage
+constexpr int RW_STAGE = RW_XB + 3 * RW_PB;
+
+typedef float v16f_r __attribute__((ext_vector_type(16)));
+typedef int v4i_r __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int rw_swz(int row) { return ((row >> 1) & 3) ^ ((row >> 3) & 1); }
+
+__device__ __forceinline__ v4i_r rw_rsrc(const void* p, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  v4i_r r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+  r[3] = 0x00020000;
+  return r;
+}
+
+// Lane i's 16 bytes from buffer offset voff + soff land at m0 + IMM + i*16
+// (soff moves the global address only; loads past the buffer return 0).
+template <int IMM>
+__device__ __forceinline__ void rw_copy(const v4i_r& r, uint32_t voff, uint32_t soff, uint32_t m0b) {
+  asm volatile("s_add_u32 m0, %3, %4\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               ::"v"(voff), "s"(r), "s"(soff), "s"(m0b), "n"(IMM)
+               : "memory", "m0", "scc");
+}
+
+__global__ void split_planes_kernel(const float* __restrict__ C, int64_t n,
+                                    uint16_t* __restrict__ planes) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    uint32_t h, m, l;
+    split3(C[i], h, m, l);
+    planes[i] = (uint16_t)h;
+    planes[n + i] = (uint16_t)m;
+    planes[2 * n + i] = (uint16_t)l;
+  }
+}
+
+__global__ __launch_bounds__(512, 1) void router_logits_wide_kernel(
+    const uint16_t* __restrict__ x, int64_t T, int64_t H, const uint16_t* __restrict__ planes,
+    int E, int64_t kper, float* __restrict__ part) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * RW_STAGE];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wv >> 1, wn = wv & 1;  // tokens 64wm.., experts 128wn..
+  const int q = lane >> 5, l32 = lane & 31;
+  const int64_t tok0 = (int64_t)blockIdx.x * RW_TOK;
+  const int64_t k0 = (int64_t)blockIdx.y * kper;
+  const int nst = (int)((min<int64_t>(H, k0 + kper) - k0) >> 5);  // 32-K steps
+  const uint32_t rowb = (uint32_t)H * 2;
+
+  // copies: waves 0, 1 move x rows 128(wv&1).., waves 2..7 plane (wv-2)/2's
+  // expert rows 128(wv&1)..; copy c (0..7) covers 16 rows: lane -> row
+  // +lane/4, LDS slot lane%4 <- global chunk (lane%4) ^ rw_swz(row)
+  const int rl = 128 * (wv & 1) + (lane >> 2);
+  const uint32_t gch = (uint32_t)((lane & 3) ^ rw_swz(rl));
+  v4i_r rs;
+  uint32_t voff;
+  uint32_t region;
+  if (wv < 2) {
+    rs = rw_rsrc(x, (uint32_t)T * rowb);
+    voff = (uint32_t)(tok0 + rl) * rowb + gch * 16;
+    region = 0;
+  } else {
+    const int pl = (wv - 2) >> 1;
+    rs = rw_rsrc(planes, 3u * (uint32_t)E * rowb);
+    voff = (uint32_t)(pl * E + rl) * rowb + gch * 16;
+    region = RW_XB + pl * RW_PB;
+  }
+  const uint32_t m0b = (uint32_t)__builtin_amdgcn_readfirstlane(
+      (int)((uint32_t)(uintptr_t)smem + region + (uint32_t)(128 * (wv & 1)) * 64));
+  const uint32_t s16 = (uint32_t)__builtin_amdgcn_readfirstlane((int)(16 * rowb));
+  auto copy_step = [&](auto ST_, int st) __attribute__((always_inline)) {
+    constexpr int ST = decltype(ST_)::value;
+    const uint32_t so = (uint32_t)(k0 + 32 * st) * 2;
+    rw_copy<ST * RW_STAGE + 0 * 1024>(rs, voff, so, m0b);
+    rw_copy<ST * RW_STAGE + 1 * 1024>(rs, voff, so + s16, m0b);
+    rw_copy<ST * RW_STAGE + 2 * 1024>(rs, voff, so + 2 * s16, m0b);
+    rw_copy<ST * RW_STAGE + 3 * 1024>(rs, voff, so + 3 * s16, m0b);
+    rw_copy<ST * RW_STAGE + 4 * 1024>(rs, voff, so + 4 * s16, m0b);
+    rw_copy<ST * RW_STAGE + 5 * 1024>(rs, voff, so + 5 * s16, m0b);
+    rw_copy<ST * RW_STAGE + 6 * 1024>(rs, voff, so + 6 * s16, m0b);
+    rw_copy<ST * RW_STAGE + 7 * 1024>(rs, voff, so + 7 * s16, m0b);
+  };
+
+  v16f_r acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // operand reads: lane's 16 B (K 8q..8q+7 of half kh) of row l32 + 32i
+  const int sw = rw_swz(l32);
+  const uint8_t* pa[2];
+  const uint8_t* pb[2];
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh) {
+    const int o = l32 * 64 + (((2 * kh + q) ^ sw) << 4);
+    pa[kh] = smem + wm * 64 * 64 + o;
+    pb[kh] = smem + RW_XB + wn * 128 * 64 + o;
+  }
+  auto compute = [&](auto ST_) __attribute__((always_inline)) {
+    constexpr int ST = decltype(ST_)::value;
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      v8bf a[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        a[i] = *reinterpret_cast<const v8bf*>(pa[kh] + ST * RW_STAGE + i * 32 * 64);
+#pragma unroll
+      for (int pl = 0; pl < 3; ++pl)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const v8bf b = *reinterpret_cast<const v8bf*>(pb[kh] + ST * RW_STAGE + pl * RW_PB + j * 32 * 64);
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b, acc[i][j], 0, 0, 0);
+        }
+    }
+  };
+
+  copy_step(std::integral_constant<int, 0>(), 0);
+  __builtin_amdgcn_s_waitcnt(7 << 4);  // vmcnt(0) lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  for (int st = 0; st < nst; st += 2) {
+    if (st + 1 < nst) copy_step(std::integral_constant<int, 1>(), st + 1);
+    compute(std::integral_constant<int, 0>());
+    __builtin_amdgcn_s_waitcnt(7 << 4);
+    __builtin_amdgcn_s_barrier();
+    if (st + 1 < nst) {
+      if (st + 2 < nst) copy_step(std::integral_constant<int, 0>(), st + 2);
+      compute(std::integral_constant<int, 1>());
+      __builtin_amdgcn_s_waitcnt(7 << 4);
+      __builtin_amdgcn_s_barrier();
+    }
+  }
+
+  // result element r of lane l: token 8(r/4) + 4q + r%4 of row block i,
+  // expert l32 of block j
+  float* out = part + (int64_t)blockIdx.y * T * E;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = 128 * wn + 32 * j + l32;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t t = tok0 + 64 * wm + 32 * i + 8 * (r >> 2) + 4 * q + (r & 3);
+        if (t < T && e < E) out[t * E + e] = acc[i][j][r];
+      }
+  }
+}
+
 __global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
        i += (int64_t)gridDim.x * blockDim.x)
@@ -307,15 +475,34 @@ __global__ __launch_bounds__(256) void bias_update_kernel(const int32_t* __restr
 
 struct RouteSplit {
   int64_t ks, kper;
+  bool wide;  // the 256-token kernel with pre-split planes
 };
 
+// the 256-token kernel: large batches whose x and planes fit 32-bit offsets
+bool route_wide(int64_t T, int64_t H, int32_t E) {
+  return T >= 2048 && E <= 256 && H % 256 == 0 && T * H * 2 < ((int64_t)1 << 32) &&
+         3 * (int64_t)E * H * 2 < ((int64_t)1 << 32);
+}
+
 RouteSplit route_split(int64_t T, int64_t H, int32_t E) {
+  if (route_wide(T, H, E)) {
+    const int64_t tiles = ceil_div(T, RW_TOK);
+    int64_t ks = std::max<int64_t>(1, std::min<int64_t>(ceil_div(256, tiles), H / 256));
+    const int64_t kper = ceil_div(ceil_div(H, ks), 32) * 32;
+    ks = ceil_div(H, kper);
+    return {ks, kper, true};
+  }
   const int64_t tiles = ceil_div(T, RT_TOK) * ceil_div(E, RT_EXP);
   int64_t ks = std::max<int64_t>(1, ceil_div(1024, std::max<int64_t>(tiles, 1)));
   ks = std::min<int64_t>(std::min<int64_t>(ks, 1024), std::max<int64_t>(1, H / 256));
   int64_t kper = ceil_div(ceil_div(H, ks), RT_KC) * RT_KC;
   ks = ceil_div(H, kper);
-  return {ks, kper};
+  return {ks, kper, false};
+}
+
+// workspace: the split-K partials [ks, T, E] fp32, then (wide) the planes
+size_t route_ws_partials(const RouteSplit& sp, int64_t T, int32_t E) {
+  return ((size_t)(sp.ks * T * E) * sizeof(float) + 255) / 256 * 256;
 }
 
 }  // namespace
@@ -326,7 +513,7 @@ using namespace moe;
 extern "C" size_t moe_route_workspace_bytes(int64_t T, int64_t H, int32_t E) {
   if (T <= 0 || H <= 0 || E <= 0) return 0;
   const RouteSplit sp = route_split(T, H, E);
-  return (size_t)(sp.ks * T * E) * sizeof(float);
+  return route_ws_partials(sp, T, E) + (sp.wide ? (size_t)3 * E * H * sizeof(uint16_t) : 0);
 }
 
 extern "C" int moe_route(const void* x_bf16, int64_t T, int64_t H, const float* centroids,
@@ -369,10 +556,19 @@ extern "C" int moe_route(const void* x_bf16, int64_t T, int64_t H, const float* 
   float* part = static_cast<float*>(workspace);
 
   fill_i32_kernel<<<1, 256, 0, st>>>(expert_counts, E, 0);
-  router_logits_kernel<<<dim3((unsigned)ceil_div(T, RT_TOK), (unsigned)ceil_div(E, RT_EXP),
-                              (unsigned)sp.ks),
-                         dim3(256), 0, st>>>(static_cast<const uint16_t*>(x_bf16), T, H,
-                                             centroids, E, sp.kper, part);
+  if (sp.wide) {
+    uint16_t* planes = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(workspace) +
+                                                   route_ws_partials(sp, T, E));
+    split_planes_kernel<<<dim3(1024), dim3(256), 0, st>>>(centroids, (int64_t)E * H, planes);
+    router_logits_wide_kernel<<<dim3((unsigned)ceil_div(T, RW_TOK), (unsigned)sp.ks), dim3(512), 0,
+                                st>>>(static_cast<const uint16_t*>(x_bf16), T, H, planes, E,
+                                      sp.kper, part);
+  } else {
+    router_logits_kernel<<<dim3((unsigned)ceil_div(T, RT_TOK), (unsigned)ceil_div(E, RT_EXP),
+                                (unsigned)sp.ks),
+                           dim3(256), 0, st>>>(static_cast<const uint16_t*>(x_bf16), T, H,
+                                               centroids, E, sp.kper, part);
+  }
   const int64_t sel_blocks = std::min<int64_t>(ceil_div(T, 4), 2048);
   router_select_kernel<<<dim3((unsigned)sel_blocks), dim3(256), 0, st>>>(
       part, (int)sp.ks, T, bias, E, n_group, topk_group, k, lpg, topk_idx, topk_w,

@@ -108,7 +108,8 @@ def test_permute_and_combine_and_bias_validation():
 def test_workspace_sizes():
     assert L.moe_permute_workspace_bytes(16384, 8, 256) == 256 * 256 * 4
     assert L.moe_permute_workspace_bytes(0, 8, 256) == 0
-    # router: partial logits [splits, T, E] fp32; at least one split
-    assert L.moe_route_workspace_bytes(16384, 7168, 256) == 16384 * 256 * 4
+    # router: partial logits [splits, T, E] fp32 (256-byte aligned); large
+    # batches (4 splits here) also hold the three bf16 planes of the centroids
+    assert L.moe_route_workspace_bytes(16384, 7168, 256) == 4 * 16384 * 256 * 4 + 3 * 256 * 7168 * 2
     b = L.moe_route_workspace_bytes(128, 7168, 256)
     assert b % (128 * 256 * 4) == 0 and b >= 128 * 256 * 4

@@ -199,6 +199,14 @@ def test_route_v3_shapes():
     _check_route(synth.DECODE, 1000, 5, "v3-T1000")
 
 
+# Large batches take the 256-token kernel with pre-split centroid planes:
+# a ragged last token tile, fewer experts than the tile (E=64) and 4 or more
+# K splits.
+def test_route_large_batches():
+    _check_route(synth.DECODE, 2100, 6, "v3-T2100")
+    _check_route(synth.MID, 2500, 7, "mid-T2500")
+
+
 def test_route_hand_traced_ties():
     from test_oracle_route import _ties_rows
     for E, ng, tg, k, b, ids, ws in _ties_rows():

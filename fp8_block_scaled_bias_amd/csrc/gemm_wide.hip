@@ -124,6 +124,48 @@ __device__ __forceinline__ void wait_vmcnt_lgkm0() {
 template <int V>
 using ic = std::integral_constant<int, V>;
 
+// Estimated cost of a tile in 1/20 of a full one (timed per tile): a group's
+// last tile copies all of B but only its own A rows, and the waves past its
+// rows skip their MFMAs.
+constexpr int COST_FULL = 20;
+__device__ __forceinline__ int last_tile_cost(int rem) {
+  return rem == 0 ? 0 : rem <= 64 ? 14 : rem <= 128 ? 15 : rem <= 192 ? 19 : COST_FULL;
+}
+
+// s_cpref[0..G] = exclusive prefix over groups of the cost of one N-tile
+// column of the group's M tiles.  A block-wide scan over WT threads; ends
+// with a barrier.
+__device__ __forceinline__ void build_cost_prefix(const int* s_offs, int G, int* s_cpref,
+                                                  int* s_red, int* s_carry) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  if (tid == 0) {
+    *s_carry = 0;
+    s_cpref[0] = 0;
+  }
+  __syncthreads();
+  for (int g0 = 0; g0 < G; g0 += WT) {
+    const int g = g0 + tid;
+    int v = 0;
+    if (g < G) {
+      const int rows = s_offs[g + 1] - s_offs[g], rem = rows & (WBM - 1);
+      v = (rows / WBM) * COST_FULL + last_tile_cost(rem);
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int n = __shfl_up(v, o, 64);
+      if (lane >= o) v += n;
+    }
+    if (lane == 63) s_red[wv] = v;
+    __syncthreads();
+    int add = *s_carry;
+    for (int w = 0; w < wv; ++w) add += s_red[w];
+    if (g < G) s_cpref[g + 1] = add + v;
+    __syncthreads();
+    if (tid == WT - 1) *s_carry = add + v;
+    __syncthreads();
+  }
+}
+
 template <bool SWIGLU, bool GATHER>
 __global__ __launch_bounds__(WT, 1) void wide_gemm_kernel(GemmArgs args) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[LDS];
@@ -152,9 +194,45 @@ __global__ __launch_bounds__(WT, 1) void wide_gemm_kernel(GemmArgs args) {
 
   build_group_tables<WT, WBM>(args.offs, G, s_offs, s_pref, s_red, &s_carry);
   const int64_t total = (int64_t)s_pref[G] * ntiles;
+  // Tiles are numbered group by group, then in blocks of NBW N tiles (the
+  // last block may be narrower), M tile by M tile, N tile last: tiles close
+  // in number share weight panels (same N tile) or token rows (same M tile).
+  // Blocks of 4 (32 consecutive tiles of a large group read 8 row panels and
+  // 4 weight panels) time faster for the fused gate+up shapes, single N tiles
+  // for the plain ones (K = 2048, N = 7168).  The workgroups of an XCD
+  // (blockIdx % 8) take a contiguous range of tile numbers of equal
+  // estimated cost, so that what they read together shares that XCD's L2;
+  // within it workgroup j takes every (grid/8)-th tile from j on.  The cost
+  // table sits in stage 1, which the first copies write only after the
+  // prologue's barrier.
+  constexpr int NBW = SWIGLU ? 4 : 1;
+  int* s_cpref = reinterpret_cast<int*>(smem + ST_BYTES);
+  build_cost_prefix(s_offs, G, s_cpref, s_red, &s_carry);
+  const int64_t ctot = (int64_t)s_cpref[G] * ntiles;
+  // first tile whose cost before it is at least c (total if c >= ctot)
+  auto tile_at_cost = [&](int64_t c) -> int64_t {
+    if (c >= ctot) return total;
+    int lo = 0, hi = G - 1;  // the first group with cost past c
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if ((int64_t)s_cpref[mid + 1] * ntiles > c) hi = mid;
+      else lo = mid + 1;
+    }
+    // cost d into the group: N-tile block b, then (cnt - 1) rows of w full
+    // tiles and a row of w last tiles (cost cl each)
+    const int64_t d = c - (int64_t)s_cpref[lo] * ntiles;
+    const int cg = s_cpref[lo + 1] - s_cpref[lo], cnt = s_pref[lo + 1] - s_pref[lo];
+    const int cl = cg - (cnt - 1) * COST_FULL;
+    const int64_t b = d / ((int64_t)NBW * cg);
+    const int w = (int)min((int64_t)NBW, ntiles - NBW * b);
+    const int64_t d2 = d - b * NBW * cg, dfull = (int64_t)(cnt - 1) * w * COST_FULL;
+    int64_t idx = d2 <= dfull ? (d2 + COST_FULL - 1) / COST_FULL
+                              : (int64_t)(cnt - 1) * w + (d2 - dfull + cl - 1) / cl;
+    idx = min(idx, (int64_t)cnt * w);
+    return (int64_t)s_pref[lo] * ntiles + b * NBW * cnt + idx;
+  };
   const int xcd = blockIdx.x & 7, jw = blockIdx.x >> 3, nper = gridDim.x >> 3;
-  const int64_t chunk = (total + 7) >> 3;
-  const int64_t tlo = xcd * chunk, thi = min(total, tlo + chunk);
+  const int64_t tlo = tile_at_cost(ctot * xcd / 8), thi = tile_at_cost(ctot * (xcd + 1) / 8);
   const int64_t L0 = tlo + jw;
   if (L0 >= thi) return;
   const int my_n = (int)((thi - L0 + nper - 1) / nper);
@@ -171,10 +249,12 @@ __global__ __launch_bounds__(WT, 1) void wide_gemm_kernel(GemmArgs args) {
     Tile t;
     const uint32_t cnt = (uint32_t)(s_pref[g + 1] - s_pref[g]);
     const uint32_t rem = (uint32_t)(L - (int64_t)s_pref[g] * ntiles);
-    const uint32_t nt = rem / cnt;
+    const uint32_t b = rem / (NBW * cnt), r2 = rem - b * NBW * cnt;
+    const uint32_t w = (uint32_t)min((int64_t)NBW, ntiles - NBW * (int64_t)b);
+    const uint32_t m = r2 / w;
     t.g = g;
-    t.nt = __builtin_amdgcn_readfirstlane((int)nt);
-    t.m0 = __builtin_amdgcn_readfirstlane(s_offs[g] + (int)(rem - nt * cnt) * WBM);
+    t.nt = __builtin_amdgcn_readfirstlane((int)(NBW * b + r2 - m * w));
+    t.m0 = __builtin_amdgcn_readfirstlane(s_offs[g] + (int)m * WBM);
     t.m1 = __builtin_amdgcn_readfirstlane(s_offs[g + 1]);
     return t;
   };
@@ -200,6 +280,7 @@ __global__ __launch_bounds__(WT, 1) void wide_gemm_kernel(GemmArgs args) {
     uint32_t va[4];     // A lane offsets of copies 0..3
     uint32_t vb[2];     // B lane offsets of copies 0 and 2 (1, 3: 16 rows further)
     uint32_t vs;        // scale lane offset
+    bool a_live;        // the wave's 32 A rows reach into the tile
   };
   auto crow = [&](int p) -> int { return 32 * wv + 16 * (p & 1) + 8 * (p >> 1) + (lane >> 3); };
   // A and the scales are addressed whole (32-bit offsets: the host checks
@@ -221,6 +302,7 @@ __global__ __launch_bounds__(WT, 1) void wide_gemm_kernel(GemmArgs args) {
       r.va[p] = a_row(t, ord, row) * K + (uint32_t)((lane & 7) ^ swz(row)) * 16;
     }
     r.rb = load_rsrc(args.B + ((int64_t)t.g * N) * K, (uint32_t)N * K);
+    r.a_live = 32 * wv < t.m1 - t.m0;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int row = crow(2 * h);
@@ -256,6 +338,9 @@ __global__ __launch_bounds__(WT, 1) void wide_gemm_kernel(GemmArgs args) {
   auto tile_op = [&](auto TST_, const Srcs& r, int op, uint32_t so) __attribute__((always_inline)) {
     constexpr int TST = decltype(TST_)::value;
     constexpr int A0 = TST * ST_BYTES, B0 = OFF_B + TST * ST_BYTES;
+    // rows past the tile's end are never stored: their A copies are left out
+    // (the stage keeps older bytes there)
+    if (op < 4 && !r.a_live) return;
     switch (op) {
       case 0: copy16<A0>(ra, r.va[0], so, m0_w); break;
       case 1: copy16<A0 + 16 * 128>(ra, r.va[1], so, m0_w); break;

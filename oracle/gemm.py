@@ -63,3 +63,59 @@ def grouped_gemm(qA, sA, qB_groups, sB_groups, offsets) -> np.ndarray:
 def to_bf16(C: np.ndarray) -> np.ndarray:
     """Storage rounding of GEMM outputs (bf16, ties to even), as float64 values."""
     return bf16_round(C)
+
+
+# ---- input gradient (backward for input) of the expert GEMMs -------------
+#
+# The forward product of a group is C = A W^T (C[i, n] = sum_k A[i, k] W[n, k]),
+# so the gradient with respect to A of a loss with gradient dY = dL/dC is
+# dA = dY W, a contraction over n.  In FP8 (news.qq.com article, section FP8
+# 低精度训练: FP8 compute with 1x128 activation tiles and 128x128 weight
+# blocks; the pipeline figure of the same article names the "backward for
+# input" chunks) dY is quantised in 1x128 tiles along n, its contraction
+# axis, and W keeps its 128x128 blocks.
+
+
+def transpose_blocks(qW, sW):
+    """Weights [..., N, K] with scales [..., N/128, K/128] -> W^T [..., K, N] with
+    scales [..., K/128, N/128].  A 128x128 block's codes move as they are and its
+    one scale moves with it, so the result quantises W^T exactly."""
+    qW = np.asarray(qW)
+    sW = np.asarray(sW)
+    return np.ascontiguousarray(np.swapaxes(qW, -1, -2)), np.ascontiguousarray(np.swapaxes(sW, -1, -2))
+
+
+def block_scaled_dgrad(qdY, sdY, qW, sW) -> np.ndarray:
+    """One group: qdY [m, N] codes with 1x128 scales sdY [m, N/128]; qW [N, K] codes
+    with 128x128 scales sW [N/128, K/128].
+
+    dA[i, k] = sum_nb sdY[i, nb] * sW[nb, k // 128] * sum_{n in nb} dY[i, n] W[n, k]
+    (each 128-term partial exact in float64, blocks added in float64).
+    """
+    qdY = np.asarray(qdY)
+    m, N = qdY.shape
+    K = np.asarray(qW).shape[1]
+    dY = e4m3_decode(qdY)
+    W = e4m3_decode(qW)
+    sY = np.asarray(sdY, dtype=np.float32).astype(np.float64)
+    sWk = np.repeat(np.asarray(sW, dtype=np.float32).astype(np.float64), TILE, axis=1)  # [N/128, K]
+    dA = np.zeros((m, K), dtype=np.float64)
+    for nb in range(N // TILE):
+        ns = slice(nb * TILE, (nb + 1) * TILE)
+        part = dY[:, ns] @ W[ns, :]                        # exact
+        dA += (sY[:, nb][:, None] * sWk[nb][None, :]) * part
+    return dA
+
+
+def grouped_dgrad(qdY, sdY, qW_groups, sW_groups, offsets) -> np.ndarray:
+    """Rows offsets[g]:offsets[g+1] of dY use group g's W.  float64 [M_total, K]."""
+    offsets = np.asarray(offsets, dtype=np.int64)
+    G = len(offsets) - 1
+    M = int(offsets[-1])
+    K = np.asarray(qW_groups[0]).shape[1]
+    dA = np.zeros((M, K), dtype=np.float64)
+    for g in range(G):
+        r0, r1 = int(offsets[g]), int(offsets[g + 1])
+        if r1 > r0:
+            dA[r0:r1] = block_scaled_dgrad(qdY[r0:r1], sdY[r0:r1], qW_groups[g], sW_groups[g])
+    return dA

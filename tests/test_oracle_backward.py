@@ -1,0 +1,121 @@
+"""Pins of the oracle's backward-for-input pieces of the expert GEMMs: the
+128x128 block transpose of FP8 weights and the block-scaled input gradient
+dA = dY W (contraction over the forward's output columns).
+
+The gradient is pinned to the forward it differentiates (a finite difference
+of <dY, A W^T> in A), to a pure-Python loop on an exact integer case, to
+dequantise-then-matmul, to the forward oracle applied to transposed blocks
+(two separately written formulas), and by its scale-block indexing.
+"""
+import numpy as np
+
+import synth
+from oracle import formats as F
+from oracle import gemm as GM
+from oracle import quant as Q
+
+
+def _int_codes(shape, seed):
+    v = synth.int_fp8_operand(shape, seed)
+    return F.e4m3_encode(v), v
+
+
+def test_transpose_blocks_definition_and_involution():
+    rng = np.random.default_rng(0)
+    qW = rng.integers(0, 256, (2, 256, 384), dtype=np.uint8)
+    sW = rng.random((2, 2, 3)).astype(np.float32)
+    qT, sT = GM.transpose_blocks(qW, sW)
+    assert qT.shape == (2, 384, 256) and sT.shape == (2, 3, 2)
+    for g in range(2):
+        for k in range(0, 384, 41):
+            for n in range(0, 256, 29):
+                assert qT[g, k, n] == qW[g, n, k]
+        for kb in range(3):
+            for nb in range(2):
+                assert sT[g, kb, nb] == sW[g, nb, kb]
+                blk = qW[g, nb * 128:(nb + 1) * 128, kb * 128:(kb + 1) * 128]
+                assert np.array_equal(qT[g, kb * 128:(kb + 1) * 128, nb * 128:(nb + 1) * 128], blk.T)
+    q2, s2 = GM.transpose_blocks(qT, sT)
+    assert np.array_equal(q2, qW) and np.array_equal(s2, sW)
+
+
+def test_transposed_blocks_quantise_the_transpose():
+    rng = np.random.default_rng(1)
+    w = (rng.standard_normal((256, 384)) * 0.02).astype(np.float32)
+    qW, sW = Q.quant_128x128(w)
+    qT, sT = GM.transpose_blocks(qW, sW)
+    qT2, sT2 = Q.quant_128x128(np.ascontiguousarray(w.T))
+    assert np.array_equal(qT, qT2) and np.array_equal(sT, sT2)
+
+
+def test_integer_dgrad_matches_python_loop():
+    M, N, K = 4, 256, 384
+    qY, Y = _int_codes((M, N), 11)
+    qW, W = _int_codes((N, K), 12)
+    sY = synth.pow2_scales((M, N // 128), 13)
+    sW = synth.pow2_scales((N // 128, K // 128), 14)
+    dA = GM.block_scaled_dgrad(qY, sY, qW, sW)
+    for i in range(M):
+        for k in range(0, K, 23):
+            acc = 0.0
+            for n in range(N):
+                acc += float(Y[i, n]) * float(W[n, k]) * float(sY[i, n // 128]) * float(sW[n // 128, k // 128])
+            assert dA[i, k] == acc
+
+
+def test_dgrad_equals_dequantised_matmul_and_forward_on_transpose():
+    rng = np.random.default_rng(2)
+    dy = rng.standard_normal((37, 256)).astype(np.float32)
+    w = (rng.standard_normal((256, 384)) * 0.02).astype(np.float32)
+    qY, sY = Q.quant_1x128(dy)
+    qW, sW = Q.quant_128x128(w)
+    dA = GM.block_scaled_dgrad(qY, sY, qW, sW)
+    ref = Q.dequant_1x128(qY, sY) @ Q.dequant_128x128(qW, sW)
+    np.testing.assert_allclose(dA, ref, rtol=1e-12, atol=1e-14)
+    assert np.array_equal(dA, GM.block_scaled_matmul(qY, sY, *GM.transpose_blocks(qW, sW)))
+    # the transposed contraction (dY W^T shapes do not even fit) or a
+    # forgotten weight scale would not match
+    assert not np.allclose(dA, Q.dequant_1x128(qY, sY) @ F.e4m3_decode(qW), rtol=1e-3)
+
+
+def test_dgrad_is_the_derivative_of_the_forward():
+    """<dY, A W^T> is linear in A: a unit step in A[i, k] changes it by dA[i, k]."""
+    rng = np.random.default_rng(3)
+    qY, sY = Q.quant_1x128(rng.standard_normal((6, 256)).astype(np.float32))
+    qW, sW = Q.quant_128x128((rng.standard_normal((256, 128)) * 0.05).astype(np.float32))
+    dYd = Q.dequant_1x128(qY, sY)
+    Wd = Q.dequant_128x128(qW, sW)
+    A = rng.standard_normal((6, 128))
+    loss = lambda a: float(np.sum(dYd * (a @ Wd.T)))
+    dA = GM.block_scaled_dgrad(qY, sY, qW, sW)
+    for (i, k) in [(0, 0), (2, 17), (5, 127), (3, 64)]:
+        a2 = A.copy()
+        a2[i, k] += 1.0
+        assert abs((loss(a2) - loss(A)) - dA[i, k]) <= 1e-9 * max(1.0, abs(dA[i, k]))
+
+
+def test_dgrad_scale_blocks_are_indexed_by_n_and_k():
+    M, N, K = 3, 256, 384           # 2 contraction blocks x 3 output blocks
+    qY, Y = _int_codes((M, N), 15)
+    qW, W = _int_codes((N, K), 16)
+    sY = np.ones((M, 2), np.float32)
+    for nb in range(2):
+        for kb in range(3):
+            sW = np.ones((2, 3), np.float32)
+            sW[nb, kb] = 4.0
+            dA = GM.block_scaled_dgrad(qY, sY, qW, sW)
+            exp = Y @ W
+            exp[:, kb * 128:(kb + 1) * 128] += 3.0 * (Y[:, nb * 128:(nb + 1) * 128] @ W[nb * 128:(nb + 1) * 128, kb * 128:(kb + 1) * 128])
+            assert np.array_equal(dA, exp)
+
+
+def test_grouped_dgrad_uses_each_groups_weights():
+    qY, Y = _int_codes((7, 128), 17)
+    qW0, W0 = _int_codes((128, 256), 18)
+    qW1, W1 = _int_codes((128, 256), 19)
+    sY = np.ones((7, 1), np.float32)
+    sW = np.ones((2, 1, 2), np.float32)
+    dA = GM.grouped_dgrad(qY, sY, [qW0, qW1], sW, [0, 3, 7])
+    assert np.array_equal(dA[:3], Y[:3] @ W0) and np.array_equal(dA[3:], Y[3:] @ W1)
+    empty = GM.grouped_dgrad(qY, sY, [qW0, qW1], sW, [0, 0, 7])
+    assert np.array_equal(empty, Y @ W1)

@@ -35,6 +35,7 @@ SIGNATURES = {
                                    _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
     "fp8_quant_1x128": (ctypes.c_int, [_vp, _i64, _i64, _i64, _i32, _vp, _vp, _vp]),
     "fp8_quant_128x128": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _vp, _vp]),
+    "fp8_transpose_128x128": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp]),
     "grouped_fp8_gemm": (ctypes.c_int, [_vp, _vp, _vp, _i64, _vp, _vp, _vp, _i32, _i64, _i64,
                                         _i64, _vp, _vp]),
     "grouped_fp8_gemm_swiglu": (ctypes.c_int, [_vp, _vp, _vp, _i64, _vp, _vp, _vp, _i32, _i64,
@@ -149,6 +150,11 @@ def fp8_quant_1x128(in_bf16, M, K, ld_in, mode, out_e4m3, scales, stream=None):
 def fp8_quant_128x128(w_f32, G, N, K, out_e4m3, scales, stream=None):
     return _call("fp8_quant_128x128", _dev(w_f32), G, N, K, _dev(out_e4m3), _dev(scales),
                  _stream(stream))
+
+
+def fp8_transpose_128x128(w_e4m3, w_scale, G, N, K, wt_e4m3, wt_scale, stream=None):
+    return _call("fp8_transpose_128x128", _dev(w_e4m3), _dev(w_scale), G, N, K, _dev(wt_e4m3),
+                 _dev(wt_scale), _stream(stream))
 
 
 def grouped_fp8_gemm(A, A_scale, a_row_index, B, B_scale, group_offsets, G, M_total, N, K,

@@ -171,6 +171,27 @@ int fp8_quant_128x128(const float* w_f32, int64_t G, int64_t N, int64_t K,
                       uint8_t* out_e4m3, float* scales, void* stream);
 
 /*
+ * fp8_transpose_128x128 - weights in 128x128 blocks, transposed block by block
+ * (news.qq.com article, section FP8 低精度训练 › 细粒度量化: 128x128 weight
+ * blocks; section 工程 › DualPipe 流水线并行: the pipeline's backward-for-input
+ * chunks).  The expert GEMM C = A W^T has the input gradient dA = dY W, a
+ * contraction over n: grouped_fp8_gemm computes it with dY quantised by
+ * fp8_quant_1x128 and B = W^T from this call (N' = K, K' = N).
+ *
+ *   wt[g, k, n] = w[g, n, k];   wt_scale[g, kb, nb] = w_scale[g, nb, kb]
+ *
+ * Codes and scales move unchanged, so the output is exactly the 128x128
+ * quantisation of W^T.
+ * w_e4m3   [G, N, K] e4m3 (16-byte aligned);  w_scale [G, N/128, K/128] fp32
+ * wt_e4m3  (out) [G, K, N] e4m3;  wt_scale (out) [G, K/128, N/128] fp32
+ * Requirements: N % 128 == 0, K % 128 == 0, 0 <= G <= 65535, outputs not
+ * aliasing inputs.  G == 0 is a no-op.
+ */
+int fp8_transpose_128x128(const uint8_t* w_e4m3, const float* w_scale, int64_t G,
+                          int64_t N, int64_t K, uint8_t* wt_e4m3, float* wt_scale,
+                          void* stream);
+
+/*
  * grouped_fp8_gemm - block-scaled FP8 grouped GEMM with FP32 accumulation
  * (news.qq.com article, section FP8 低精度训练, items 细粒度量化 and
  * 提高累加精度).

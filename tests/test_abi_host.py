@@ -51,6 +51,18 @@ def test_quant_validation():
     assert rc("fp8_quant_128x128", None, 0, 128, 128, None, None, None) == L.MOE_OK
 
 
+def test_transpose_validation():
+    def f(G=2, N=256, K=384, w=FAKE, ws=FAKE, wt=ctypes.c_void_p(8192), wts=ctypes.c_void_p(8192 + 64)):
+        return rc("fp8_transpose_128x128", w, ws, G, N, K, wt, wts, None)
+    assert f(N=100) == L.MOE_ERR_INVALID and "N=100" in L.last_error()
+    assert f(K=0) == L.MOE_ERR_INVALID
+    assert f(G=-1) == L.MOE_ERR_INVALID and f(G=70000) == L.MOE_ERR_INVALID
+    assert f(w=None) == L.MOE_ERR_INVALID and "null" in L.last_error()
+    assert f(w=ctypes.c_void_p(4104)) == L.MOE_ERR_INVALID and "aligned" in L.last_error()
+    assert f(wt=FAKE) == L.MOE_ERR_INVALID and "alias" in L.last_error()
+    assert f(G=0, w=None, ws=None, wt=None, wts=None) == L.MOE_OK
+
+
 def test_gemm_validation():
     def f(G, M, N, K, A=FAKE, idx=None, A_rows=None):
         A_rows = M if A_rows is None else A_rows

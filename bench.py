@@ -1,7 +1,7 @@
 """Benchmark of the DeepSeekMoE layer forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                    [--decode-steps D] [--skewed-steps S]
+                    [--decode-steps D] [--skewed-steps S] [--no-backward]
 
 One step is one pass of the whole hot path over one batch of T=16384 tokens
 at V3 shapes (hidden 7168, 256 routed experts in 8 groups keeping 4, top-8,
@@ -12,7 +12,8 @@ Prints one JSON line (rank 0).  On the same weights it also reports: the
 decode batch (T=128, under "decode"), the standalone grouped GEMM over 256
 groups with Multinomial(65536) rows ("grouped_gemm") and the skewed-load
 layer (T=8192, Zipf(1.1) expert popularity, 100 steps of the bias update,
-"skewed").
+"skewed") and the input gradients of the two expert GEMMs at T=16384 with
+their 128x128 weight-block transposes ("backward_dgrad").
 """
 from __future__ import annotations
 
@@ -163,6 +164,69 @@ def bench_grouped_gemm(layer, reps=20, warmup=5):
     return out
 
 
+def _median_ms(run, reps, warmup):
+    import numpy as np
+    import torch
+    st = torch.cuda.current_stream()
+    for _ in range(warmup):
+        run()
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        run()
+        e1.record(st)
+        ts.append((e0, e1))
+    torch.cuda.synchronize()
+    return float(np.median([e0.elapsed_time(e1) for e0, e1 in ts]))
+
+
+def bench_backward(layer, T, reps=10, warmup=3):
+    """Input gradients of the two expert GEMMs at T=16384 (backward for input):
+    the 257 experts' weights transposed in 128x128 blocks (fp8_transpose_128x128,
+    HBM-bound: read + write of every code and scale), then grouped_fp8_gemm on
+    them.  Rows per group: Multinomial(T*k, uniform over E) at seed 0 plus the
+    T-row shared group (R = 147,456); output gradients N(0,1) from a seeded
+    device generator, quantised 1x128 along their contraction axis (untimed).
+    down: dH [R, I] = dD [R, H] W_dn; gate+up: dX [R, H] = dGU [R, 2I] W_gu."""
+    import numpy as np
+    import torch
+    import synth
+    import fp8_block_scaled_bias_amd as M
+    s = layer.shape
+    G = s.E + s.n_shared
+    counts = np.concatenate([synth.gen_group_counts(T * s.k, s.E, seed=0), [T] * s.n_shared])
+    offs = torch.from_numpy(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)).cuda()
+    R = int(counts.sum())
+    gen = torch.Generator(device="cuda").manual_seed(2024)
+    out = {"workload": "input gradients of the expert GEMMs, T=16384 (257 groups, R=%d rows)" % R}
+    for name, W, Ws, N, K in (("down", layer.w_dn, layer.w_dn_s, s.H, s.I),
+                              ("gate_up", layer.w_gu, layer.w_gu_s, 2 * s.I, s.H)):
+        # forward C = A W^T with W [G, N, K]; dA = dY W contracts over N
+        wt = torch.empty((G, K, N), dtype=torch.uint8, device="cuda")
+        wts = torch.empty((G, K // 128, N // 128), dtype=torch.float32, device="cuda")
+        t_ms = _median_ms(lambda: M.fp8_transpose_128x128(W, Ws, G, N, K, wt, wts), 5, 2)
+        t_bytes = 2 * (G * N * K + G * (N // 128) * (K // 128) * 4)
+        dy = torch.randn((R, N), dtype=torch.float32, device="cuda", generator=gen).to(torch.bfloat16)
+        dyq = torch.empty((R, N), dtype=torch.uint8, device="cuda")
+        dys = torch.empty((R, N // 128), dtype=torch.float32, device="cuda")
+        M.fp8_quant_1x128(dy, R, N, N, 0, dyq, dys)
+        del dy
+        da = torch.empty((R, K), dtype=torch.bfloat16, device="cuda")
+        g_ms = _median_ms(lambda: M.grouped_fp8_gemm(dyq, dys, None, wt, wts, offs, G, R, K, N, da),
+                          reps, warmup)
+        flop = 2.0 * R * N * K
+        tf = flop / (g_ms * 1e-3) / 1e12
+        out[name] = {"transpose_ms": t_ms, "transpose_GB_s": t_bytes / (t_ms * 1e-3) / 1e9,
+                     "transpose_frac_hbm": t_bytes / (t_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                     "dgrad_ms": g_ms, "dgrad_TFLOPS": tf, "dgrad_frac_fp8_peak": tf / FP8_PEAK_TFLOPS,
+                     "contraction": N, "out_cols": K}
+        log(f"[bench] backward {name}: transpose {t_ms:.3f} ms ({out[name]['transpose_GB_s']:.0f} GB/s), "
+            f"dgrad {g_ms:.3f} ms ({tf:.0f} TFLOP/s)")
+        del wt, wts, dyq, dys, da
+    return out
+
+
 # HBM traffic of the gate+up kernel at T=16384, from two rocprofv3 --pmc runs
 # (FETCH_SIZE, WRITE_SIZE) of this script, each scaled by the same counter on
 # the 1 GiB copy probe.  Valid only for the kernel source with this digest.
@@ -249,6 +313,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=50)
     ap.add_argument("--skewed-steps", type=int, default=100)
+    ap.add_argument("--no-backward", action="store_true")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -291,6 +356,7 @@ def main():
     log(f"[bench] decode per-kernel ms: " + ", ".join(f"{k} {v:.3f}" for k, v in dper.items()))
 
     gg = bench_grouped_gemm(layer)
+    bwd = bench_backward(layer, cfg.T) if not args.no_backward else None
     skew = bench_skewed(layer, args.skewed_steps) if args.skewed_steps > 0 else None
 
     traffic = None
@@ -325,6 +391,7 @@ def main():
                    "algorithmic_bytes": dbytes, "GB_s": dgbs, "frac_hbm_peak": dgbs / HBM_PEAK_GBS,
                    "per_kernel_ms": dper},
         "grouped_gemm": gg,
+        "backward_dgrad": bwd,
         "skewed": skew,
         "copy_probe": cp,
     }

@@ -119,3 +119,35 @@ def grouped_dgrad(qdY, sdY, qW_groups, sW_groups, offsets) -> np.ndarray:
         if r1 > r0:
             dA[r0:r1] = block_scaled_dgrad(qdY[r0:r1], sdY[r0:r1], qW_groups[g], sW_groups[g])
     return dA
+
+
+# ---- weight gradient (backward for weights) of the expert GEMMs ----------
+#
+# For group g the forward C_g = A_g W_g^T has dW_g = dY_g^T A_g, a
+# contraction over the group's tokens.  Both operands come quantised in
+# 128x1 tiles along the tokens (quant.quant_128x1_grouped: transposed, each
+# group padded to whole 128-token chunks), so each 128-token chunk is one
+# partial with one scale per (output row, chunk) on either side.
+
+
+def grouped_wgrad(qYT, sYT, qAT, sAT, chunk_pref) -> np.ndarray:
+    """qYT [N, P] codes, sYT [N, P/128]; qAT [K, P], sAT [K, P/128]; group g owns
+    chunks [chunk_pref[g], chunk_pref[g+1]).  Returns float64 [G, N, K]:
+
+    dW[g, n, k] = sum_{c in g} sYT[n, c] * sAT[k, c] * sum_{j<128} Y[n, 128c+j] A[k, 128c+j]
+    (exact 128-term partials, chunks added in float64 in order).
+    """
+    chunk_pref = np.asarray(chunk_pref, dtype=np.int64)
+    G = len(chunk_pref) - 1
+    Y = e4m3_decode(qYT)
+    A = e4m3_decode(qAT)
+    sY = np.asarray(sYT, dtype=np.float32).astype(np.float64)
+    sA = np.asarray(sAT, dtype=np.float32).astype(np.float64)
+    N, K = Y.shape[0], A.shape[0]
+    dW = np.zeros((G, N, K), dtype=np.float64)
+    for g in range(G):
+        for c in range(int(chunk_pref[g]), int(chunk_pref[g + 1])):
+            cs = slice(c * TILE, (c + 1) * TILE)
+            part = Y[:, cs] @ A[:, cs].T                   # exact
+            dW[g] += (sY[:, c][:, None] * sA[:, c][None, :]) * part
+    return dW

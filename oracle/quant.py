@@ -70,3 +70,41 @@ def dequant_128x128(q: np.ndarray, s: np.ndarray) -> np.ndarray:
     N, K = q.shape
     return (e4m3_decode(q).reshape(N // TILE, TILE, K // TILE, TILE)
             * s.astype(np.float64)[:, None, :, None]).reshape(N, K)
+
+
+def chunk_prefix(offsets) -> np.ndarray:
+    """Exclusive prefix over groups of ceil(rows / 128): group g's token chunks
+    are [pref[g], pref[g+1]) in a layout that pads every group to whole
+    128-token chunks."""
+    offsets = np.asarray(offsets, dtype=np.int64)
+    rows = np.diff(offsets)
+    return np.concatenate([[0], np.cumsum((rows + TILE - 1) // TILE)]).astype(np.int64)
+
+
+def quant_128x1_grouped(v: np.ndarray, offsets):
+    """Quantise v [M, C] in 128x1 tiles along the token axis, per group.
+
+    The weight gradient of an expert contracts over that expert's tokens, so
+    its FP8 operands need one scale per 128 tokens of one column (the 1x128
+    tile of the transposed matrix; the pages give 1x128 activation tiles
+    without the backward orientation - this is the reading used).  Group g
+    (rows offsets[g]:offsets[g+1]) is cut into 128-row chunks from its first
+    row; a last partial chunk is padded with zeros.
+
+    Returns codes uint8 [C, P] and scales fp32 [C, P/128], transposed (tokens
+    contiguous), P = 128 * chunk_prefix(offsets)[-1]: column 128*c + j of the
+    output is row j of chunk c.  Padding codes are 0; an all-zero tile has
+    scale 1.
+    """
+    v = np.asarray(v, dtype=np.float32)
+    M, C = v.shape
+    pref = chunk_prefix(offsets)
+    offsets = np.asarray(offsets, dtype=np.int64)
+    P = int(pref[-1]) * TILE
+    padded = np.zeros((P, C), dtype=np.float32)
+    for g in range(len(offsets) - 1):
+        r0, r1 = int(offsets[g]), int(offsets[g + 1])
+        p0 = int(pref[g]) * TILE
+        padded[p0:p0 + (r1 - r0)] = v[r0:r1]
+    q, s = quant_1x128(np.ascontiguousarray(padded.T))
+    return q, s

@@ -119,3 +119,104 @@ def test_grouped_dgrad_uses_each_groups_weights():
     assert np.array_equal(dA[:3], Y[:3] @ W0) and np.array_equal(dA[3:], Y[3:] @ W1)
     empty = GM.grouped_dgrad(qY, sY, [qW0, qW1], sW, [0, 0, 7])
     assert np.array_equal(empty, Y @ W1)
+
+
+# ---- weight gradient ------------------------------------------------------
+
+def test_chunk_prefix():
+    assert np.array_equal(Q.chunk_prefix([0, 300, 300, 377, 890]), [0, 3, 3, 4, 9])
+    assert np.array_equal(Q.chunk_prefix([0, 128, 256]), [0, 1, 2])
+
+
+def test_quant_128x1_grouped_elementwise():
+    rng = np.random.default_rng(4)
+    offs = [0, 130, 130, 200]
+    v = rng.standard_normal((200, 256)).astype(np.float32)
+    v[130:200, 5] = 0.0                                   # an all-zero tile
+    qT, sT = Q.quant_128x1_grouped(v, offs)
+    pref = Q.chunk_prefix(offs)
+    assert qT.shape == (256, 384) and sT.shape == (256, 3)
+    # group 0: chunks 0 (rows 0..127) and 1 (rows 128, 129 + padding); group 2: chunk 2
+    for (c, col0, r0, n) in [(0, 0, 0, 128), (1, 128, 128, 2), (2, 256, 130, 70)]:
+        for col in (0, 5, 77, 255):
+            amax = 0.0
+            for j in range(n):
+                amax = max(amax, abs(float(v[r0 + j, col])))
+            s = np.float32(amax) / np.float32(448.0) if amax > 0 else np.float32(1.0)
+            assert sT[col, c] == s
+            for j in (0, n - 1):
+                assert qT[col, col0 + j] == F.e4m3_encode(np.float32(v[r0 + j, col]) / s)
+            assert (qT[col, col0 + n:col0 + 128] == 0).all()
+    assert sT[5, 2] == 1.0 and (qT[5, 256:384] == 0).all()
+    assert int(pref[-1]) * 128 == qT.shape[1]
+
+
+def _wgrad_case(seed, offs, N, K, integer):
+    if integer:
+        Y = synth.int_fp8_operand((offs[-1], N), seed)
+        A = synth.int_fp8_operand((offs[-1], K), seed + 1)
+    else:
+        rng = np.random.default_rng(seed)
+        Y = rng.standard_normal((offs[-1], N)).astype(np.float32)
+        A = rng.standard_normal((offs[-1], K)).astype(np.float32)
+    qY, sY = Q.quant_128x1_grouped(Y, offs)
+    qA, sA = Q.quant_128x1_grouped(A, offs)
+    return Y, A, qY, sY, qA, sA, Q.chunk_prefix(offs)
+
+
+def test_integer_wgrad_matches_python_loop():
+    offs = [0, 150, 150, 190]
+    Y, A, qY, sY, qA, sA, pref = _wgrad_case(21, offs, 128, 256, True)
+    # integers within [-4, 4] make every tile scale 4/448 or 1/112 etc.: the
+    # dequantised values are the integers themselves only up to rounding, so
+    # the loop runs over the decoded, scaled operands
+    Yd = Q.dequant_1x128(qY, sY)
+    Ad = Q.dequant_1x128(qA, sA)
+    dW = GM.grouped_wgrad(qY, sY, qA, sA, pref)
+    for g, (c0, c1) in enumerate(zip(pref[:-1], pref[1:])):
+        for n in (0, 55, 127):
+            for k in (0, 200, 255):
+                acc = 0.0
+                for c in range(int(c0), int(c1)):
+                    part = 0.0
+                    for j in range(128):
+                        part += float(Yd[n, 128 * c + j]) / float(sY[n, c]) * (float(Ad[k, 128 * c + j]) / float(sA[k, c]))
+                    acc += float(sY[n, c]) * float(sA[k, c]) * part
+                assert dW[g, n, k] == acc
+    assert not dW[1].any()                                # empty group
+
+
+def test_wgrad_equals_dequantised_matmul_per_group():
+    offs = [0, 300, 377, 377, 890]
+    Y, A, qY, sY, qA, sA, pref = _wgrad_case(22, offs, 256, 384, False)
+    dW = GM.grouped_wgrad(qY, sY, qA, sA, pref)
+    Yd = Q.dequant_1x128(qY, sY)
+    Ad = Q.dequant_1x128(qA, sA)
+    for g in range(4):
+        cs = slice(int(pref[g]) * 128, int(pref[g + 1]) * 128)
+        np.testing.assert_allclose(dW[g], Yd[:, cs] @ Ad[:, cs].T, rtol=1e-12, atol=1e-12)
+    # the quantised gradient is close to the unquantised dY^T A of each group
+    for g in range(4):
+        r0, r1 = offs[g], offs[g + 1]
+        ref = Y[r0:r1].astype(np.float64).T @ A[r0:r1].astype(np.float64)
+        if r1 > r0:
+            assert np.linalg.norm(dW[g] - ref) <= 0.1 * np.linalg.norm(ref)
+
+
+def test_wgrad_is_the_derivative_of_the_forward():
+    """<dY_g, A_g W^T> is linear in W: a unit step in W[n, k] changes it by dW_g[n, k]."""
+    offs = [0, 70, 200]
+    Y, A, qY, sY, qA, sA, pref = _wgrad_case(23, offs, 128, 128, False)
+    Yd = Q.dequant_1x128(qY, sY)
+    Ad = Q.dequant_1x128(qA, sA)
+    dW = GM.grouped_wgrad(qY, sY, qA, sA, pref)
+    rng = np.random.default_rng(5)
+    W = rng.standard_normal((128, 128))
+    for g in range(2):
+        cs = slice(int(pref[g]) * 128, int(pref[g + 1]) * 128)
+        Yg, Ag = Yd[:, cs].T, Ad[:, cs].T                   # tokens x features (padding rows are zero)
+        loss = lambda w: float(np.sum(Yg * (Ag @ w.T)))
+        for (n, k) in [(0, 0), (9, 100), (127, 3)]:
+            w2 = W.copy()
+            w2[n, k] += 1.0
+            assert abs((loss(w2) - loss(W)) - dW[g, n, k]) <= 1e-9 * max(1.0, abs(dW[g, n, k]))

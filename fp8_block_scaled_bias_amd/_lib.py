@@ -36,6 +36,10 @@ SIGNATURES = {
     "fp8_quant_1x128": (ctypes.c_int, [_vp, _i64, _i64, _i64, _i32, _vp, _vp, _vp]),
     "fp8_quant_128x128": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _vp, _vp]),
     "fp8_transpose_128x128": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp]),
+    "fp8_quant_128x1_grouped": (ctypes.c_int, [_vp, _i64, _vp, _i32, _i64, _i64, _vp, _vp, _i64,
+                                               _vp]),
+    "grouped_fp8_wgrad": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _vp, _i32, _i64, _i64, _i64,
+                                         _vp, _vp]),
     "grouped_fp8_gemm": (ctypes.c_int, [_vp, _vp, _vp, _i64, _vp, _vp, _vp, _i32, _i64, _i64,
                                         _i64, _vp, _vp]),
     "grouped_fp8_gemm_swiglu": (ctypes.c_int, [_vp, _vp, _vp, _i64, _vp, _vp, _vp, _i32, _i64,
@@ -155,6 +159,23 @@ def fp8_quant_128x128(w_f32, G, N, K, out_e4m3, scales, stream=None):
 def fp8_transpose_128x128(w_e4m3, w_scale, G, N, K, wt_e4m3, wt_scale, stream=None):
     return _call("fp8_transpose_128x128", _dev(w_e4m3), _dev(w_scale), G, N, K, _dev(wt_e4m3),
                  _dev(wt_scale), _stream(stream))
+
+
+def wgrad_pitch(M_total, G):
+    """Smallest row pitch of the token-chunk layout (bytes of codes per row)."""
+    return 128 * (-(-M_total // 128) + G)
+
+
+def fp8_quant_128x1_grouped(in_bf16, ld_in, group_offsets, G, M_total, C, out_t, scales_t, ld_out,
+                            stream=None):
+    return _call("fp8_quant_128x1_grouped", _dev(in_bf16), ld_in, _dev(group_offsets), G, M_total,
+                 C, _dev(out_t), _dev(scales_t), ld_out, _stream(stream))
+
+
+def grouped_fp8_wgrad(dy_t, dy_scale_t, a_t, a_scale_t, ld, group_offsets, G, M_total, N, K, dW,
+                      stream=None):
+    return _call("grouped_fp8_wgrad", _dev(dy_t), _dev(dy_scale_t), _dev(a_t), _dev(a_scale_t), ld,
+                 _dev(group_offsets), G, M_total, N, K, _dev(dW), _stream(stream))
 
 
 def grouped_fp8_gemm(A, A_scale, a_row_index, B, B_scale, group_offsets, G, M_total, N, K,

@@ -1,0 +1,278 @@
+// Weight gradient of the expert GEMMs in FP8: dW_g = dY_g^T A_g over each
+// expert's tokens (the "backward for weights" chunks of the DualPipe overlap
+// figure, news.qq.com/rain/a/20241229A05OQF00, section 工程 › DualPipe
+// 流水线并行; FP8 compute with fine-grained scales and FP32 accumulation,
+// section FP8 低精度训练).
+//
+// The contraction runs over tokens, so both operands are quantised with one
+// scale per 128 tokens of one column: the 1x128 tile of the transposed
+// matrix (the pages give 1x128 activation tiles without the backward
+// orientation; this is the reading used).  fp8_quant_128x1_grouped writes
+// them transposed (tokens contiguous) with every group padded to whole
+// 128-token chunks, and grouped_fp8_wgrad multiplies them group by group:
+// each chunk is one FP8 MFMA partial in FP32, promoted into the FP32 total
+// with its two scales (the pages' accumulation at a fixed K interval).
+#include "gemm_common.h"
+
+namespace moe {
+namespace {
+
+typedef float v16f __attribute__((ext_vector_type(16)));
+using gemm::v8i;
+
+// ---- quantiser ---------------------------------------------------------------
+// One workgroup per (token chunk, 128 columns); thread t owns column t % 128
+// and rows 64 * (t / 128) .. +63 of the chunk.  Reads are 128 B row pieces
+// per wave; each thread writes its 64 codes contiguously.
+constexpr int QT = 256;
+
+__global__ __launch_bounds__(QT) void quant_128x1_grouped_kernel(
+    const uint16_t* __restrict__ in, int64_t ld_in, const int32_t* __restrict__ offs, int G,
+    uint8_t* __restrict__ out, float* __restrict__ scales, int64_t ld_out) {
+  __shared__ int s_offs[gemm::MAXG + 1];
+  __shared__ int s_pref[gemm::MAXG + 1];
+  __shared__ int s_red[QT / 64];
+  __shared__ int s_carry;
+  __shared__ float s_amax[128];
+  gemm::build_group_tables<QT, 128>(offs, G, s_offs, s_pref, s_red, &s_carry);
+  const int64_t L = blockIdx.x;  // chunk
+  if (L >= s_pref[G]) return;
+  const gemm::Tile t = gemm::decode_tile(s_pref, s_offs, G, 1, L, 128);
+  const int tid = threadIdx.x, half = tid >> 7;
+  const int64_t col = (int64_t)blockIdx.y * 128 + (tid & 127);
+  const int r0 = t.m0 + 64 * half;
+  float v[64];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 64; ++i) {
+    const int r = r0 + i;
+    v[i] = r < t.m1 ? bf16_to_f32(in[(int64_t)r * ld_in + col]) : 0.0f;
+    amax = fmaxf(amax, fabsf(v[i]));
+  }
+  if (half) s_amax[tid & 127] = amax;
+  __syncthreads();
+  if (!half) s_amax[tid] = fmaxf(amax, s_amax[tid]);
+  __syncthreads();
+  amax = s_amax[tid & 127];
+  const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+  uint8_t* dst = out + col * ld_out + L * 128 + 64 * half;
+#pragma unroll
+  for (int i = 0; i < 64; i += 16) {
+    uint4 w;
+    w.x = f32x4_to_e4m3x4(v[i] / s, v[i + 1] / s, v[i + 2] / s, v[i + 3] / s);
+    w.y = f32x4_to_e4m3x4(v[i + 4] / s, v[i + 5] / s, v[i + 6] / s, v[i + 7] / s);
+    w.z = f32x4_to_e4m3x4(v[i + 8] / s, v[i + 9] / s, v[i + 10] / s, v[i + 11] / s);
+    w.w = f32x4_to_e4m3x4(v[i + 12] / s, v[i + 13] / s, v[i + 14] / s, v[i + 15] / s);
+    *reinterpret_cast<uint4*>(dst + i) = w;
+  }
+  if (!half) scales[col * (ld_out >> 7) + L] = s;
+}
+
+// ---- weight-gradient GEMM ----------------------------------------------------
+// One workgroup (4 waves) per 128 (n) x 128 (k) tile of one group's dW; wave
+// (wm, wn) owns rows 64wm.. and columns 64wn.. as 2 x 2 blocks of
+// v_mfma_f32_32x32x64_f8f6f4.  The group's 128-token chunks stream through
+// two LDS stages (rows 128 B, 16 B chunks XOR-swizzled by row so the
+// fragment reads are conflict-free); chunk c+1 is loaded into registers while
+// chunk c is multiplied.  Per chunk: P = the two 64-token MFMA steps from
+// zero, then total += (sY[n, c] * sA[k, c]) * P.
+constexpr int WGT = 256;
+constexpr int TILE_B = 128 * 128;
+
+__device__ __forceinline__ v16f mfma32(const v8i& x, const v8i& y, const v16f& c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x, y, c, 0, 0, 0, 0, 0, 0);
+}
+
+__global__ __launch_bounds__(WGT) void wgrad_kernel(
+    const uint8_t* __restrict__ yt, const float* __restrict__ ys, const uint8_t* __restrict__ at,
+    const float* __restrict__ as, int64_t ld, const int32_t* __restrict__ offs, int64_t N,
+    int64_t K, float* __restrict__ dw) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_y[2][TILE_B];
+  __shared__ __attribute__((aligned(16))) uint8_t s_a[2][TILE_B];
+  __shared__ __attribute__((aligned(16))) float s_sy[2][128];
+  __shared__ __attribute__((aligned(16))) float s_sa[2][128];
+  __shared__ int s_red[WGT / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int wm = wv >> 1, wn = wv & 1, q = lane >> 5, l32 = lane & 31;
+  const int g = blockIdx.y;
+  const int64_t ktiles = K >> 7;
+  const int64_t n0 = (int64_t)(blockIdx.x / ktiles) * 128, k0 = (int64_t)(blockIdx.x % ktiles) * 128;
+  const int64_t ldc = ld >> 7;
+
+  // first chunk of group g: sum over the groups before it of ceil(rows / 128)
+  int part = 0;
+  for (int i = tid; i < g; i += WGT) part += (offs[i + 1] - offs[i] + 127) >> 7;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o, 64);
+  if (lane == 0) s_red[wv] = part;
+  __syncthreads();
+  const int c0 = s_red[0] + s_red[1] + s_red[2] + s_red[3];
+  const int c1 = c0 + ((offs[g + 1] - offs[g] + 127) >> 7);
+
+  // chunk loads: thread -> rows (tid >> 3) + 32 i, 16 B piece tid & 7
+  const int lrow = tid >> 3, lpc = tid & 7;
+  uint4 ry[4], ra[4];
+  float rsc = 0.0f;
+  auto load = [&](int c) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t row = lrow + 32 * i;
+      ry[i] = *reinterpret_cast<const uint4*>(yt + (n0 + row) * ld + (int64_t)c * 128 + lpc * 16);
+      ra[i] = *reinterpret_cast<const uint4*>(at + (k0 + row) * ld + (int64_t)c * 128 + lpc * 16);
+    }
+    rsc = tid < 128 ? ys[(n0 + tid) * ldc + c] : as[(k0 + tid - 128) * ldc + c];
+  };
+  auto store = [&](int b) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = lrow + 32 * i;
+      const int off = row * 128 + ((lpc ^ (row & 7)) << 4);
+      *reinterpret_cast<uint4*>(&s_y[b][off]) = ry[i];
+      *reinterpret_cast<uint4*>(&s_a[b][off]) = ra[i];
+    }
+    if (tid < 128) s_sy[b][tid] = rsc;
+    else s_sa[b][tid - 128] = rsc;
+  };
+  // fragment of tile row `row` (l32 + a multiple of 32), step half h: its
+  // 16 B pieces 4h + 2q and 4h + 2q + 1
+  auto frag = [&](const uint8_t* base, int row, int h) -> v8i {
+    const int sw = row & 7;
+    const uint4 lo = *reinterpret_cast<const uint4*>(base + row * 128 + (((4 * h + 2 * q) ^ sw) << 4));
+    const uint4 hi = *reinterpret_cast<const uint4*>(base + row * 128 + (((4 * h + 2 * q + 1) ^ sw) << 4));
+    v8i r;
+    r[0] = lo.x; r[1] = lo.y; r[2] = lo.z; r[3] = lo.w;
+    r[4] = hi.x; r[5] = hi.y; r[6] = hi.z; r[7] = hi.w;
+    return r;
+  };
+
+  v16f tot[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) tot[i][j][r] = 0.0f;
+  v16f zero;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) zero[r] = 0.0f;
+
+  if (c0 < c1) {
+    load(c0);
+    store(0);
+  }
+  __syncthreads();
+  for (int c = c0; c < c1; ++c) {
+    const int b = (c - c0) & 1;
+    const bool more = c + 1 < c1;
+    if (more) load(c + 1);
+    // x = weights-side rows k (a_t), y = rows n (dy_t): lane holds row n =
+    // 64wm + 32j + l32 and, per x block i, columns k = 64wn + 32i + 8e + 4q
+    // + (0..3) for e = 0..3
+    v16f p[2][2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      v8i xa[2], yb[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) xa[i] = frag(s_a[b], 64 * wn + 32 * i + l32, h);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) yb[j] = frag(s_y[b], 64 * wm + 32 * j + l32, h);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          if (h == 0) p[i][j] = mfma32(xa[i], yb[j], zero);
+          else p[i][j] = mfma32(xa[i], yb[j], p[i][j]);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const float sy = s_sy[b][64 * wm + 32 * j + l32];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float4 sa = *reinterpret_cast<const float4*>(&s_sa[b][64 * wn + 32 * i + 8 * e + 4 * q]);
+          tot[i][j][4 * e + 0] = fmaf(sy * sa.x, p[i][j][4 * e + 0], tot[i][j][4 * e + 0]);
+          tot[i][j][4 * e + 1] = fmaf(sy * sa.y, p[i][j][4 * e + 1], tot[i][j][4 * e + 1]);
+          tot[i][j][4 * e + 2] = fmaf(sy * sa.z, p[i][j][4 * e + 2], tot[i][j][4 * e + 2]);
+          tot[i][j][4 * e + 3] = fmaf(sy * sa.w, p[i][j][4 * e + 3], tot[i][j][4 * e + 3]);
+        }
+      }
+    }
+    if (more) store(b ^ 1);
+    __syncthreads();
+  }
+
+  float* out = dw + ((int64_t)g * N + n0) * K + k0;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int64_t n = 64 * wm + 32 * j + l32;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int k = 64 * wn + 32 * i + 8 * e + 4 * q;
+        *reinterpret_cast<float4*>(out + n * K + k) =
+            make_float4(tot[i][j][4 * e], tot[i][j][4 * e + 1], tot[i][j][4 * e + 2], tot[i][j][4 * e + 3]);
+      }
+  }
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+static int64_t chunk_pitch_min(int64_t M_total, int32_t G) {
+  return 128 * (ceil_div(M_total, 128) + G);
+}
+
+extern "C" int fp8_quant_128x1_grouped(const void* in_bf16, int64_t ld_in,
+                                       const int32_t* group_offsets, int32_t G, int64_t M_total,
+                                       int64_t C, uint8_t* out_t, float* scales_t, int64_t ld_out,
+                                       void* stream) {
+  clear_error();
+  MOE_INVALID(G >= 1, "fp8_quant_128x1_grouped: G=%d < 1", (int)G);
+  MOE_UNSUPPORTED(G <= gemm::MAXG, "fp8_quant_128x1_grouped: G=%d > %d", (int)G, gemm::MAXG);
+  MOE_INVALID(M_total >= 0 && M_total < (1ll << 31), "fp8_quant_128x1_grouped: M_total=%lld out of range",
+              (long long)M_total);
+  MOE_INVALID(C > 0 && C % 128 == 0 && C / 128 <= 65535,
+              "fp8_quant_128x1_grouped: C=%lld must be a positive multiple of 128 (at most 65535*128)",
+              (long long)C);
+  MOE_INVALID(ld_in >= C, "fp8_quant_128x1_grouped: ld_in=%lld < C", (long long)ld_in);
+  MOE_INVALID(ld_out % 128 == 0 && ld_out >= chunk_pitch_min(M_total, G),
+              "fp8_quant_128x1_grouped: ld_out=%lld must be a multiple of 128 and >= %lld",
+              (long long)ld_out, (long long)chunk_pitch_min(M_total, G));
+  MOE_INVALID(in_bf16 && group_offsets && out_t && scales_t, "fp8_quant_128x1_grouped: null pointer");
+  MOE_INVALID(((uintptr_t)in_bf16 & 1) == 0 && ((uintptr_t)out_t & 15) == 0 && ((uintptr_t)scales_t & 3) == 0,
+              "fp8_quant_128x1_grouped: in must be 2-byte, out 16-byte, scales 4-byte aligned");
+  const int64_t chunks = ceil_div(M_total, 128) + G;
+  quant_128x1_grouped_kernel<<<dim3((unsigned)chunks, (unsigned)(C / 128)), dim3(QT), 0, as_stream(stream)>>>(
+      static_cast<const uint16_t*>(in_bf16), ld_in, group_offsets, G, out_t, scales_t, ld_out);
+  return check_launch("fp8_quant_128x1_grouped");
+}
+
+extern "C" int grouped_fp8_wgrad(const uint8_t* dy_t, const float* dy_scale_t, const uint8_t* a_t,
+                                 const float* a_scale_t, int64_t ld, const int32_t* group_offsets,
+                                 int32_t G, int64_t M_total, int64_t N, int64_t K, float* dW,
+                                 void* stream) {
+  clear_error();
+  MOE_INVALID(G >= 1 && G <= 65535, "grouped_fp8_wgrad: G=%d out of [1, 65535]", (int)G);
+  MOE_INVALID(M_total >= 0 && M_total < (1ll << 31), "grouped_fp8_wgrad: M_total=%lld out of range",
+              (long long)M_total);
+  MOE_INVALID(N > 0 && N % 128 == 0 && K > 0 && K % 128 == 0,
+              "grouped_fp8_wgrad: N=%lld and K=%lld must be positive multiples of 128", (long long)N,
+              (long long)K);
+  MOE_INVALID((N / 128) * (K / 128) <= (1ll << 31) - 1, "grouped_fp8_wgrad: too many tiles");
+  MOE_INVALID(ld % 128 == 0 && ld >= chunk_pitch_min(M_total, G),
+              "grouped_fp8_wgrad: ld=%lld must be a multiple of 128 and >= %lld", (long long)ld,
+              (long long)chunk_pitch_min(M_total, G));
+  MOE_INVALID(dy_t && dy_scale_t && a_t && a_scale_t && group_offsets && dW,
+              "grouped_fp8_wgrad: null pointer");
+  MOE_INVALID(((uintptr_t)dy_t & 15) == 0 && ((uintptr_t)a_t & 15) == 0 && ((uintptr_t)dW & 15) == 0 &&
+                  ((uintptr_t)dy_scale_t & 3) == 0 && ((uintptr_t)a_scale_t & 3) == 0,
+              "grouped_fp8_wgrad: operands and dW must be 16-byte, scales 4-byte aligned");
+  wgrad_kernel<<<dim3((unsigned)((N / 128) * (K / 128)), (unsigned)G), dim3(WGT), 0, as_stream(stream)>>>(
+      dy_t, dy_scale_t, a_t, a_scale_t, ld, group_offsets, N, K, dW);
+  return check_launch("grouped_fp8_wgrad");
+}

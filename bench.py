@@ -13,7 +13,8 @@ decode batch (T=128, under "decode"), the standalone grouped GEMM over 256
 groups with Multinomial(65536) rows ("grouped_gemm") and the skewed-load
 layer (T=8192, Zipf(1.1) expert popularity, 100 steps of the bias update,
 "skewed") and the input gradients of the two expert GEMMs at T=16384 with
-their 128x128 weight-block transposes ("backward_dgrad").
+their 128x128 weight-block transposes, and the two weight gradients
+("backward").
 """
 from __future__ import annotations
 
@@ -182,13 +183,17 @@ def _median_ms(run, reps, warmup):
 
 
 def bench_backward(layer, T, reps=10, warmup=3):
-    """Input gradients of the two expert GEMMs at T=16384 (backward for input):
+    """Backward of the two expert GEMMs at T=16384.  Input gradients (backward for input):
     the 257 experts' weights transposed in 128x128 blocks (fp8_transpose_128x128,
     HBM-bound: read + write of every code and scale), then grouped_fp8_gemm on
     them.  Rows per group: Multinomial(T*k, uniform over E) at seed 0 plus the
     T-row shared group (R = 147,456); output gradients N(0,1) from a seeded
     device generator, quantised 1x128 along their contraction axis (untimed).
-    down: dH [R, I] = dD [R, H] W_dn; gate+up: dX [R, H] = dGU [R, 2I] W_gu."""
+    down: dH [R, I] = dD [R, H] W_dn; gate+up: dX [R, H] = dGU [R, 2I] W_gu.
+    Weight gradients (backward for weights): dW_g = dY_g^T A_g per expert with
+    dY and A (N(0,1) bf16 from the same generator) quantised 128x1 along the
+    tokens by fp8_quant_128x1_grouped (timed: both operands), then
+    grouped_fp8_wgrad (fp32 dW, 15 / 30 GB: HBM-bound on its output)."""
     import numpy as np
     import torch
     import synth
@@ -199,7 +204,7 @@ def bench_backward(layer, T, reps=10, warmup=3):
     offs = torch.from_numpy(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)).cuda()
     R = int(counts.sum())
     gen = torch.Generator(device="cuda").manual_seed(2024)
-    out = {"workload": "input gradients of the expert GEMMs, T=16384 (257 groups, R=%d rows)" % R}
+    out = {"workload": "backward of the expert GEMMs, T=16384 (257 groups, R=%d rows)" % R}
     for name, W, Ws, N, K in (("down", layer.w_dn, layer.w_dn_s, s.H, s.I),
                               ("gate_up", layer.w_gu, layer.w_gu_s, 2 * s.I, s.H)):
         # forward C = A W^T with W [G, N, K]; dA = dY W contracts over N
@@ -224,6 +229,34 @@ def bench_backward(layer, T, reps=10, warmup=3):
         log(f"[bench] backward {name}: transpose {t_ms:.3f} ms ({out[name]['transpose_GB_s']:.0f} GB/s), "
             f"dgrad {g_ms:.3f} ms ({tf:.0f} TFLOP/s)")
         del wt, wts, dyq, dys, da
+        # weight gradient dW_g = dY_g^T A_g: both operands quantised 128x1 along the
+        # tokens (transposed, chunk-padded), fp32 output [G, N, K]
+        cap = M.wgrad_chunks(R, G)
+        dy = torch.randn((R, N), dtype=torch.float32, device="cuda", generator=gen).to(torch.bfloat16)
+        a = torch.randn((R, K), dtype=torch.float32, device="cuda", generator=gen).to(torch.bfloat16)
+        yq = torch.empty((cap, N, 128), dtype=torch.uint8, device="cuda")
+        ys = torch.empty((cap, N), dtype=torch.float32, device="cuda")
+        aq = torch.empty((cap, K, 128), dtype=torch.uint8, device="cuda")
+        asc = torch.empty((cap, K), dtype=torch.float32, device="cuda")
+        q_ms = _median_ms(lambda: (M.fp8_quant_128x1_grouped(dy, N, offs, G, R, N, yq, ys, cap),
+                                   M.fp8_quant_128x1_grouped(a, K, offs, G, R, K, aq, asc, cap)), 5, 2)
+        q_bytes = 3 * R * (N + K) + 4 * (N + K) * (R // 128)
+        del dy, a
+        dw = torch.empty((G, N, K), dtype=torch.float32, device="cuda")
+        w_ms = _median_ms(lambda: M.grouped_fp8_wgrad(yq, ys, aq, asc, cap, offs, G, R, N, K, dw), 5, 2)
+        nch = int(((counts + 127) // 128).sum())          # chunks the groups use
+        w_bytes = (N + K) * 128 * nch + 4 * (N + K) * nch + 4 * G * N * K
+        t_mfma, t_hbm = flop / (FP8_PEAK_TFLOPS * 1e12), w_bytes / (HBM_PEAK_GBS * 1e9)
+        out[name].update({
+            "quant_128x1_ms": q_ms, "quant_128x1_GB_s": q_bytes / (q_ms * 1e-3) / 1e9,
+            "wgrad_ms": w_ms, "wgrad_TFLOPS": flop / (w_ms * 1e-3) / 1e12,
+            "wgrad_GB_s": w_bytes / (w_ms * 1e-3) / 1e9, "wgrad_algorithmic_bytes": w_bytes,
+            "wgrad_bound": "hbm" if t_hbm > t_mfma else "mfma",
+            "wgrad_frac_of_bound": max(t_mfma, t_hbm) / (w_ms * 1e-3)})
+        log(f"[bench] backward {name}: quant 128x1 {q_ms:.3f} ms, wgrad {w_ms:.3f} ms "
+            f"({out[name]['wgrad_TFLOPS']:.0f} TFLOP/s, {out[name]['wgrad_GB_s']:.0f} GB/s, "
+            f"{out[name]['wgrad_frac_of_bound']:.2f} of the {out[name]['wgrad_bound']} roof)")
+        del yq, ys, aq, asc, dw
     return out
 
 
@@ -391,7 +424,7 @@ def main():
                    "algorithmic_bytes": dbytes, "GB_s": dgbs, "frac_hbm_peak": dgbs / HBM_PEAK_GBS,
                    "per_kernel_ms": dper},
         "grouped_gemm": gg,
-        "backward_dgrad": bwd,
+        "backward": bwd,
         "skewed": skew,
         "copy_probe": cp,
     }

@@ -161,21 +161,21 @@ def fp8_transpose_128x128(w_e4m3, w_scale, G, N, K, wt_e4m3, wt_scale, stream=No
                  _dev(wt_scale), _stream(stream))
 
 
-def wgrad_pitch(M_total, G):
-    """Smallest row pitch of the token-chunk layout (bytes of codes per row)."""
-    return 128 * (-(-M_total // 128) + G)
+def wgrad_chunks(M_total, G):
+    """Chunks of 128 tokens that the weight-gradient layout needs at most."""
+    return -(-M_total // 128) + G
 
 
-def fp8_quant_128x1_grouped(in_bf16, ld_in, group_offsets, G, M_total, C, out_t, scales_t, ld_out,
-                            stream=None):
+def fp8_quant_128x1_grouped(in_bf16, ld_in, group_offsets, G, M_total, C, out_c, scales_c,
+                            chunks_cap, stream=None):
     return _call("fp8_quant_128x1_grouped", _dev(in_bf16), ld_in, _dev(group_offsets), G, M_total,
-                 C, _dev(out_t), _dev(scales_t), ld_out, _stream(stream))
+                 C, _dev(out_c), _dev(scales_c), chunks_cap, _stream(stream))
 
 
-def grouped_fp8_wgrad(dy_t, dy_scale_t, a_t, a_scale_t, ld, group_offsets, G, M_total, N, K, dW,
-                      stream=None):
-    return _call("grouped_fp8_wgrad", _dev(dy_t), _dev(dy_scale_t), _dev(a_t), _dev(a_scale_t), ld,
-                 _dev(group_offsets), G, M_total, N, K, _dev(dW), _stream(stream))
+def grouped_fp8_wgrad(dy_c, dy_scale_c, a_c, a_scale_c, chunks_cap, group_offsets, G, M_total, N,
+                      K, dW, stream=None):
+    return _call("grouped_fp8_wgrad", _dev(dy_c), _dev(dy_scale_c), _dev(a_c), _dev(a_scale_c),
+                 chunks_cap, _dev(group_offsets), G, M_total, N, K, _dev(dW), _stream(stream))
 
 
 def grouped_fp8_gemm(A, A_scale, a_row_index, B, B_scale, group_offsets, G, M_total, N, K,

@@ -8,8 +8,10 @@
 // scale per 128 tokens of one column: the 1x128 tile of the transposed
 // matrix (the pages give 1x128 activation tiles without the backward
 // orientation; this is the reading used).  fp8_quant_128x1_grouped writes
-// them transposed (tokens contiguous) with every group padded to whole
-// 128-token chunks, and grouped_fp8_wgrad multiplies them group by group:
+// them chunk-major - [chunk][column][128 tokens], every group padded to
+// whole 128-token chunks, so the 128 columns of one chunk that a tile reads
+// are one contiguous 16 KB block - and grouped_fp8_wgrad multiplies them
+// group by group:
 // each chunk is one FP8 MFMA partial in FP32, promoted into the FP32 total
 // with its two scales (the pages' accumulation at a fixed K interval).
 #include "gemm_common.h"
@@ -23,12 +25,12 @@ using gemm::v8i;
 // ---- quantiser ---------------------------------------------------------------
 // One workgroup per (token chunk, 128 columns); thread t owns column t % 128
 // and rows 64 * (t / 128) .. +63 of the chunk.  Reads are 128 B row pieces
-// per wave; each thread writes its 64 codes contiguously.
+// per wave; the workgroup writes one contiguous 16 KB block of codes.
 constexpr int QT = 256;
 
 __global__ __launch_bounds__(QT) void quant_128x1_grouped_kernel(
     const uint16_t* __restrict__ in, int64_t ld_in, const int32_t* __restrict__ offs, int G,
-    uint8_t* __restrict__ out, float* __restrict__ scales, int64_t ld_out) {
+    int64_t C, uint8_t* __restrict__ out, float* __restrict__ scales) {
   __shared__ int s_offs[gemm::MAXG + 1];
   __shared__ int s_pref[gemm::MAXG + 1];
   __shared__ int s_red[QT / 64];
@@ -55,7 +57,7 @@ __global__ __launch_bounds__(QT) void quant_128x1_grouped_kernel(
   __syncthreads();
   amax = s_amax[tid & 127];
   const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
-  uint8_t* dst = out + col * ld_out + L * 128 + 64 * half;
+  uint8_t* dst = out + (L * C + col) * 128 + 64 * half;
 #pragma unroll
   for (int i = 0; i < 64; i += 16) {
     uint4 w;
@@ -65,7 +67,7 @@ __global__ __launch_bounds__(QT) void quant_128x1_grouped_kernel(
     w.w = f32x4_to_e4m3x4(v[i + 12] / s, v[i + 13] / s, v[i + 14] / s, v[i + 15] / s);
     *reinterpret_cast<uint4*>(dst + i) = w;
   }
-  if (!half) scales[col * (ld_out >> 7) + L] = s;
+  if (!half) scales[L * C + col] = s;
 }
 
 // ---- weight-gradient GEMM ----------------------------------------------------
@@ -85,8 +87,8 @@ __device__ __forceinline__ v16f mfma32(const v8i& x, const v8i& y, const v16f& c
 
 __global__ __launch_bounds__(WGT) void wgrad_kernel(
     const uint8_t* __restrict__ yt, const float* __restrict__ ys, const uint8_t* __restrict__ at,
-    const float* __restrict__ as, int64_t ld, const int32_t* __restrict__ offs, int64_t N,
-    int64_t K, float* __restrict__ dw) {
+    const float* __restrict__ as, const int32_t* __restrict__ offs, int64_t N, int64_t K,
+    float* __restrict__ dw) {
   __shared__ __attribute__((aligned(16))) uint8_t s_y[2][TILE_B];
   __shared__ __attribute__((aligned(16))) uint8_t s_a[2][TILE_B];
   __shared__ __attribute__((aligned(16))) float s_sy[2][128];
@@ -97,7 +99,6 @@ __global__ __launch_bounds__(WGT) void wgrad_kernel(
   const int g = blockIdx.y;
   const int64_t ktiles = K >> 7;
   const int64_t n0 = (int64_t)(blockIdx.x / ktiles) * 128, k0 = (int64_t)(blockIdx.x % ktiles) * 128;
-  const int64_t ldc = ld >> 7;
 
   // first chunk of group g: sum over the groups before it of ceil(rows / 128)
   int part = 0;
@@ -109,27 +110,37 @@ __global__ __launch_bounds__(WGT) void wgrad_kernel(
   const int c0 = s_red[0] + s_red[1] + s_red[2] + s_red[3];
   const int c1 = c0 + ((offs[g + 1] - offs[g] + 127) >> 7);
 
-  // chunk loads: thread -> rows (tid >> 3) + 32 i, 16 B piece tid & 7
+  // chunk loads: thread -> rows (tid >> 3) + 32 i (i = 0..3), 16 B piece
+  // tid & 7; named registers (an indexed array here ends up in scratch)
   const int lrow = tid >> 3, lpc = tid & 7;
-  uint4 ry[4], ra[4];
+  const int soff = lrow * 128 + ((lpc ^ (lrow & 7)) << 4);  // + 32 * 128 * i
+  uint4 y0, y1, y2, y3, a0, a1, a2, a3;
   float rsc = 0.0f;
+  auto ld16 = [](const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); };
   auto load = [&](int c) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t row = lrow + 32 * i;
-      ry[i] = *reinterpret_cast<const uint4*>(yt + (n0 + row) * ld + (int64_t)c * 128 + lpc * 16);
-      ra[i] = *reinterpret_cast<const uint4*>(at + (k0 + row) * ld + (int64_t)c * 128 + lpc * 16);
-    }
-    rsc = tid < 128 ? ys[(n0 + tid) * ldc + c] : as[(k0 + tid - 128) * ldc + c];
+    const uint8_t* py = yt + ((int64_t)c * N + n0 + lrow) * 128 + lpc * 16;
+    const uint8_t* pa = at + ((int64_t)c * K + k0 + lrow) * 128 + lpc * 16;
+    y0 = ld16(py);
+    y1 = ld16(py + 32 * 128);
+    y2 = ld16(py + 64 * 128);
+    y3 = ld16(py + 96 * 128);
+    a0 = ld16(pa);
+    a1 = ld16(pa + 32 * 128);
+    a2 = ld16(pa + 64 * 128);
+    a3 = ld16(pa + 96 * 128);
+    rsc = tid < 128 ? ys[(int64_t)c * N + n0 + tid] : as[(int64_t)c * K + k0 + tid - 128];
   };
   auto store = [&](int b) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = lrow + 32 * i;
-      const int off = row * 128 + ((lpc ^ (row & 7)) << 4);
-      *reinterpret_cast<uint4*>(&s_y[b][off]) = ry[i];
-      *reinterpret_cast<uint4*>(&s_a[b][off]) = ra[i];
-    }
+    uint8_t* dy = s_y[b] + soff;
+    uint8_t* da = s_a[b] + soff;
+    *reinterpret_cast<uint4*>(dy) = y0;
+    *reinterpret_cast<uint4*>(dy + 32 * 128) = y1;
+    *reinterpret_cast<uint4*>(dy + 64 * 128) = y2;
+    *reinterpret_cast<uint4*>(dy + 96 * 128) = y3;
+    *reinterpret_cast<uint4*>(da) = a0;
+    *reinterpret_cast<uint4*>(da + 32 * 128) = a1;
+    *reinterpret_cast<uint4*>(da + 64 * 128) = a2;
+    *reinterpret_cast<uint4*>(da + 96 * 128) = a3;
     if (tid < 128) s_sy[b][tid] = rsc;
     else s_sa[b][tid - 128] = rsc;
   };
@@ -223,14 +234,12 @@ __global__ __launch_bounds__(WGT) void wgrad_kernel(
 
 using namespace moe;
 
-static int64_t chunk_pitch_min(int64_t M_total, int32_t G) {
-  return 128 * (ceil_div(M_total, 128) + G);
-}
+static int64_t chunks_needed(int64_t M_total, int32_t G) { return ceil_div(M_total, 128) + G; }
 
 extern "C" int fp8_quant_128x1_grouped(const void* in_bf16, int64_t ld_in,
                                        const int32_t* group_offsets, int32_t G, int64_t M_total,
-                                       int64_t C, uint8_t* out_t, float* scales_t, int64_t ld_out,
-                                       void* stream) {
+                                       int64_t C, uint8_t* out_c, float* scales_c,
+                                       int64_t chunks_cap, void* stream) {
   clear_error();
   MOE_INVALID(G >= 1, "fp8_quant_128x1_grouped: G=%d < 1", (int)G);
   MOE_UNSUPPORTED(G <= gemm::MAXG, "fp8_quant_128x1_grouped: G=%d > %d", (int)G, gemm::MAXG);
@@ -240,22 +249,22 @@ extern "C" int fp8_quant_128x1_grouped(const void* in_bf16, int64_t ld_in,
               "fp8_quant_128x1_grouped: C=%lld must be a positive multiple of 128 (at most 65535*128)",
               (long long)C);
   MOE_INVALID(ld_in >= C, "fp8_quant_128x1_grouped: ld_in=%lld < C", (long long)ld_in);
-  MOE_INVALID(ld_out % 128 == 0 && ld_out >= chunk_pitch_min(M_total, G),
-              "fp8_quant_128x1_grouped: ld_out=%lld must be a multiple of 128 and >= %lld",
-              (long long)ld_out, (long long)chunk_pitch_min(M_total, G));
-  MOE_INVALID(in_bf16 && group_offsets && out_t && scales_t, "fp8_quant_128x1_grouped: null pointer");
-  MOE_INVALID(((uintptr_t)in_bf16 & 1) == 0 && ((uintptr_t)out_t & 15) == 0 && ((uintptr_t)scales_t & 3) == 0,
+  MOE_INVALID(chunks_cap >= chunks_needed(M_total, G),
+              "fp8_quant_128x1_grouped: chunks_cap=%lld < ceil(M_total/128) + G = %lld",
+              (long long)chunks_cap, (long long)chunks_needed(M_total, G));
+  MOE_INVALID(in_bf16 && group_offsets && out_c && scales_c, "fp8_quant_128x1_grouped: null pointer");
+  MOE_INVALID(((uintptr_t)in_bf16 & 1) == 0 && ((uintptr_t)out_c & 15) == 0 && ((uintptr_t)scales_c & 3) == 0,
               "fp8_quant_128x1_grouped: in must be 2-byte, out 16-byte, scales 4-byte aligned");
-  const int64_t chunks = ceil_div(M_total, 128) + G;
+  const int64_t chunks = chunks_needed(M_total, G);
   quant_128x1_grouped_kernel<<<dim3((unsigned)chunks, (unsigned)(C / 128)), dim3(QT), 0, as_stream(stream)>>>(
-      static_cast<const uint16_t*>(in_bf16), ld_in, group_offsets, G, out_t, scales_t, ld_out);
+      static_cast<const uint16_t*>(in_bf16), ld_in, group_offsets, G, C, out_c, scales_c);
   return check_launch("fp8_quant_128x1_grouped");
 }
 
-extern "C" int grouped_fp8_wgrad(const uint8_t* dy_t, const float* dy_scale_t, const uint8_t* a_t,
-                                 const float* a_scale_t, int64_t ld, const int32_t* group_offsets,
-                                 int32_t G, int64_t M_total, int64_t N, int64_t K, float* dW,
-                                 void* stream) {
+extern "C" int grouped_fp8_wgrad(const uint8_t* dy_c, const float* dy_scale_c, const uint8_t* a_c,
+                                 const float* a_scale_c, int64_t chunks_cap,
+                                 const int32_t* group_offsets, int32_t G, int64_t M_total, int64_t N,
+                                 int64_t K, float* dW, void* stream) {
   clear_error();
   MOE_INVALID(G >= 1 && G <= 65535, "grouped_fp8_wgrad: G=%d out of [1, 65535]", (int)G);
   MOE_INVALID(M_total >= 0 && M_total < (1ll << 31), "grouped_fp8_wgrad: M_total=%lld out of range",
@@ -264,15 +273,15 @@ extern "C" int grouped_fp8_wgrad(const uint8_t* dy_t, const float* dy_scale_t, c
               "grouped_fp8_wgrad: N=%lld and K=%lld must be positive multiples of 128", (long long)N,
               (long long)K);
   MOE_INVALID((N / 128) * (K / 128) <= (1ll << 31) - 1, "grouped_fp8_wgrad: too many tiles");
-  MOE_INVALID(ld % 128 == 0 && ld >= chunk_pitch_min(M_total, G),
-              "grouped_fp8_wgrad: ld=%lld must be a multiple of 128 and >= %lld", (long long)ld,
-              (long long)chunk_pitch_min(M_total, G));
-  MOE_INVALID(dy_t && dy_scale_t && a_t && a_scale_t && group_offsets && dW,
+  MOE_INVALID(chunks_cap >= chunks_needed(M_total, G),
+              "grouped_fp8_wgrad: chunks_cap=%lld < ceil(M_total/128) + G = %lld", (long long)chunks_cap,
+              (long long)chunks_needed(M_total, G));
+  MOE_INVALID(dy_c && dy_scale_c && a_c && a_scale_c && group_offsets && dW,
               "grouped_fp8_wgrad: null pointer");
-  MOE_INVALID(((uintptr_t)dy_t & 15) == 0 && ((uintptr_t)a_t & 15) == 0 && ((uintptr_t)dW & 15) == 0 &&
-                  ((uintptr_t)dy_scale_t & 3) == 0 && ((uintptr_t)a_scale_t & 3) == 0,
+  MOE_INVALID(((uintptr_t)dy_c & 15) == 0 && ((uintptr_t)a_c & 15) == 0 && ((uintptr_t)dW & 15) == 0 &&
+                  ((uintptr_t)dy_scale_c & 3) == 0 && ((uintptr_t)a_scale_c & 3) == 0,
               "grouped_fp8_wgrad: operands and dW must be 16-byte, scales 4-byte aligned");
   wgrad_kernel<<<dim3((unsigned)((N / 128) * (K / 128)), (unsigned)G), dim3(WGT), 0, as_stream(stream)>>>(
-      dy_t, dy_scale_t, a_t, a_scale_t, ld, group_offsets, N, K, dW);
+      dy_c, dy_scale_c, a_c, a_scale_c, group_offsets, N, K, dW);
   return check_launch("grouped_fp8_wgrad");
 }

@@ -193,31 +193,33 @@ int fp8_transpose_128x128(const uint8_t* w_e4m3, const float* w_scale, int64_t G
 
 /*
  * fp8_quant_128x1_grouped - the weight-gradient operands: per-group FP8
- * quantisation in 128x1 tiles along the token axis, stored transposed
- * (news.qq.com article, section FP8 低精度训练 › 细粒度量化 gives 1x128
- * activation tiles; the weight gradient contracts over tokens, so the tile
- * is taken along them - a reading, the pages give no backward orientation;
- * section 工程 › DualPipe 流水线并行 names the backward-for-weights chunks).
+ * quantisation in 128x1 tiles along the token axis (news.qq.com article,
+ * section FP8 低精度训练 › 细粒度量化 gives 1x128 activation tiles; the
+ * weight gradient contracts over tokens, so the tile is taken along them - a
+ * reading, the pages give no backward orientation; section 工程 › DualPipe
+ * 流水线并行 names the backward-for-weights chunks).
  *
  * Group g (rows group_offsets[g] .. group_offsets[g+1]) is cut into 128-row
  * chunks from its first row, the last one padded with zeros; chunk c of the
- * whole layout is the c-th in group order (group g's chunks start at
- * sum over g' < g of ceil(rows_g' / 128)).  For column j and chunk c:
+ * layout is the c-th in group order (group g's chunks start at the sum over
+ * g' < g of ceil(rows_g' / 128)).  Stored chunk-major: for column j and
+ * chunk c,
  *   s = amax over the chunk's rows of |in[r, j]| / 448 (1 if 0)
- *   out_t[j, 128c + i] = E4M3(in[row i of chunk c, j] / s)  (0 for padding)
- *   scales_t[j, c] = s
- * with the rounding of fp8_quant_1x128.
+ *   out_c[c, j, i]  = E4M3(in[row i of chunk c, j] / s)  (0 for padding)
+ *   scales_c[c, j]  = s
+ * with the rounding of fp8_quant_1x128.  (out_c[c] transposed is the 128
+ * tokens of chunk c as rows: a tile's chunk is one contiguous block.)
  *
  * in_bf16   [M_total, ld_in] bf16 (C columns used, 2-byte aligned)
  * group_offsets [G+1] int32 on the device, as in grouped_fp8_gemm
- * out_t     (out) [C, ld_out] e4m3 (16-byte aligned); scales_t (out) [C, ld_out/128]
- * Columns of out_t past the last chunk are not written.
- * Requirements: 1 <= G <= 1024, C % 128 == 0, ld_in >= C, ld_out % 128 == 0 and
- * ld_out >= 128 * (ceil(M_total / 128) + G).
+ * out_c     (out) [chunks_cap, C, 128] e4m3 (16-byte aligned)
+ * scales_c  (out) [chunks_cap, C] fp32
+ * chunks_cap >= ceil(M_total / 128) + G (chunks past the last are not written)
+ * Requirements: 1 <= G <= 1024, C % 128 == 0, ld_in >= C.
  */
 int fp8_quant_128x1_grouped(const void* in_bf16, int64_t ld_in, const int32_t* group_offsets,
-                            int32_t G, int64_t M_total, int64_t C, uint8_t* out_t,
-                            float* scales_t, int64_t ld_out, void* stream);
+                            int32_t G, int64_t M_total, int64_t C, uint8_t* out_c,
+                            float* scales_c, int64_t chunks_cap, void* stream);
 
 /*
  * grouped_fp8_wgrad - weight gradient of the expert GEMMs (news.qq.com article,
@@ -225,20 +227,22 @@ int fp8_quant_128x1_grouped(const void* in_bf16, int64_t ld_in, const int32_t* g
  * 低精度训练: FP8 products accumulated in FP32 at a fixed K interval).
  *
  * For the forward C_g = A_g W_g^T (W_g [N, K]) and the output gradient dY,
- *   dW[g, n, k] = sum_{c in group g's chunks}  dy_scale_t[n, c] * a_scale_t[k, c]
- *                 * sum_{i<128} dy_t[n, 128c + i] * a_t[k, 128c + i]
- * with dy_t / a_t from fp8_quant_128x1_grouped of dY [M_total, N] and
+ *   dW[g, n, k] = sum_{c in group g's chunks}  dy_scale_c[c, n] * a_scale_c[c, k]
+ *                 * sum_{i<128} dy_c[c, n, i] * a_c[c, k, i]
+ * with dy_c / a_c from fp8_quant_128x1_grouped of dY [M_total, N] and
  * A [M_total, K] on the same group_offsets.  Each chunk's 128-term FP8
  * partial is an FP32 MFMA sum that is scaled and added to an FP32 total.
  * A group without rows gets dW[g] = 0.
  *
- * dy_t [N, ld], dy_scale_t [N, ld/128];  a_t [K, ld], a_scale_t [K, ld/128]
+ * dy_c [chunks_cap, N, 128], dy_scale_c [chunks_cap, N];
+ * a_c  [chunks_cap, K, 128], a_scale_c  [chunks_cap, K]
  * dW   (out) [G, N, K] fp32 (overwritten)
- * Requirements: N % 128 == 0, K % 128 == 0, 1 <= G <= 65535, ld as in
- * fp8_quant_128x1_grouped; operands and dW 16-byte, scales 4-byte aligned.
+ * Requirements: N % 128 == 0, K % 128 == 0, 1 <= G <= 65535,
+ * chunks_cap >= ceil(M_total / 128) + G; operands and dW 16-byte, scales
+ * 4-byte aligned.
  */
-int grouped_fp8_wgrad(const uint8_t* dy_t, const float* dy_scale_t, const uint8_t* a_t,
-                      const float* a_scale_t, int64_t ld, const int32_t* group_offsets,
+int grouped_fp8_wgrad(const uint8_t* dy_c, const float* dy_scale_c, const uint8_t* a_c,
+                      const float* a_scale_c, int64_t chunks_cap, const int32_t* group_offsets,
                       int32_t G, int64_t M_total, int64_t N, int64_t K, float* dW,
                       void* stream);
 

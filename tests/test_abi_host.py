@@ -64,23 +64,23 @@ def test_transpose_validation():
 
 
 def test_wgrad_validation():
-    pitch = 128 * (1 + 4)                    # M_total = 100, G = 4
-    def q(G=4, M=100, C=256, ld_in=256, ld_out=pitch, out=FAKE):
-        return rc("fp8_quant_128x1_grouped", FAKE, ld_in, FAKE, G, M, C, out, FAKE, ld_out, None)
+    cap = 1 + 4                              # M_total = 100, G = 4
+    def q(G=4, M=100, C=256, ld_in=256, cap=cap, out=FAKE):
+        return rc("fp8_quant_128x1_grouped", FAKE, ld_in, FAKE, G, M, C, out, FAKE, cap, None)
     assert q(C=100) == L.MOE_ERR_INVALID and "C=100" in L.last_error()
     assert q(G=0) == L.MOE_ERR_INVALID
     assert q(G=2000) == L.MOE_ERR_UNSUPPORTED
     assert q(ld_in=128) == L.MOE_ERR_INVALID and "ld_in" in L.last_error()
-    assert q(ld_out=pitch - 128) == L.MOE_ERR_INVALID and "ld_out" in L.last_error()
+    assert q(cap=cap - 1) == L.MOE_ERR_INVALID and "chunks_cap" in L.last_error()
     assert q(out=None) == L.MOE_ERR_INVALID
     assert q(out=ctypes.c_void_p(4104)) == L.MOE_ERR_INVALID and "aligned" in L.last_error()
-    def w(G=4, M=100, N=256, K=384, ld=pitch, dW=FAKE):
-        return rc("grouped_fp8_wgrad", FAKE, FAKE, FAKE, FAKE, ld, FAKE, G, M, N, K, dW, None)
+    def w(G=4, M=100, N=256, K=384, cap=cap, dW=FAKE):
+        return rc("grouped_fp8_wgrad", FAKE, FAKE, FAKE, FAKE, cap, FAKE, G, M, N, K, dW, None)
     assert w(N=200) == L.MOE_ERR_INVALID and "N=200" in L.last_error()
     assert w(G=0) == L.MOE_ERR_INVALID
-    assert w(ld=pitch + 64) == L.MOE_ERR_INVALID and "ld=" in L.last_error()
+    assert w(cap=4) == L.MOE_ERR_INVALID and "chunks_cap" in L.last_error()
     assert w(dW=None) == L.MOE_ERR_INVALID
-    assert L.wgrad_pitch(100, 4) == pitch and L.wgrad_pitch(256, 3) == 128 * 5
+    assert L.wgrad_chunks(100, 4) == cap and L.wgrad_chunks(256, 3) == 5
 
 
 def test_gemm_validation():

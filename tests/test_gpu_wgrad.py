@@ -1,5 +1,9 @@
 """Weight gradient of the expert GEMMs on the GPU, through the C ABI.
 
+The library keeps the 128x1-quantised operands chunk-major ([chunk, column,
+128 tokens]); the oracle's are the logical transposed matrices [column,
+tokens]: the tests convert between the two (_to_logical, _to_chunks).
+
 fp8_quant_128x1_grouped must equal the oracle's grouped 128x1 quantiser
 byte for byte (codes and scales: every decision is taken in fp32 on both
 sides).  grouped_fp8_wgrad on integer-valued E4M3 codes in [-2, 2] with
@@ -35,14 +39,28 @@ def _offsets(rows):
     return np.concatenate([[0], np.cumsum(rows)]).astype(np.int64)
 
 
+def _to_logical(q_c, s_c, nch):
+    """chunk-major [cap, C, 128] codes, [cap, C] scales -> [C, 128 nch], [C, nch]"""
+    C = q_c.shape[1]
+    return (np.ascontiguousarray(q_c[:nch].transpose(1, 0, 2)).reshape(C, nch * 128),
+            np.ascontiguousarray(s_c[:nch].T))
+
+
+def _to_chunks(q, s):
+    """logical [C, 128 cap], [C, cap] -> chunk-major [cap, C, 128], [cap, C]"""
+    C, P = q.shape
+    return (np.ascontiguousarray(q.reshape(C, P // 128, 128).transpose(1, 0, 2)),
+            np.ascontiguousarray(s.T))
+
+
 def _quant_dev(x_bits, offs, G, C):
     Mt = x_bits.shape[0]
-    ld = M.wgrad_pitch(Mt, G)
-    q = torch.zeros((C, ld), dtype=torch.uint8, device="cuda")
-    s = torch.zeros((C, ld // 128), dtype=torch.float32, device="cuda")
+    cap = M.wgrad_chunks(Mt, G)
+    q = torch.zeros((cap, C, 128), dtype=torch.uint8, device="cuda")
+    s = torch.zeros((cap, C), dtype=torch.float32, device="cuda")
     xb = torch.from_numpy(np.ascontiguousarray(x_bits).view(np.int16)).cuda().view(torch.bfloat16)
-    M.fp8_quant_128x1_grouped(xb, C, dev(offs.astype(np.int32)), G, Mt, C, q, s, ld)
-    return q, s, ld
+    M.fp8_quant_128x1_grouped(xb, C, dev(offs.astype(np.int32)), G, Mt, C, q, s, cap)
+    return q, s, cap
 
 
 @pytest.mark.parametrize("rows,C", [([300, 0, 77, 513, 129], 256), ([1], 128), ([128, 256, 5, 0], 384)])
@@ -52,11 +70,11 @@ def test_quant_128x1_grouped_exact(rows, C):
     bits = synth.gen_gemm_activations(Mt, C, seed=len(rows) + C)
     bits[:: 7, 3] = 0                                      # zeros inside tiles
     log(f"[quant128x1] rows {rows} C={C}")
-    q, s, ld = _quant_dev(bits, offs, G, C)
+    q, s, cap = _quant_dev(bits, offs, G, C)
     qo, so = OQ.quant_128x1_grouped(OF.bf16_value_from_bits(bits).astype(np.float32), offs)
-    P = qo.shape[1]
-    assert np.array_equal(host(q)[:, :P], qo)
-    assert np.array_equal(host(s)[:, :P // 128], so)
+    ql, sl = _to_logical(host(q), host(s), qo.shape[1] // 128)
+    assert np.array_equal(ql, qo)
+    assert np.array_equal(sl, so)
 
 
 @pytest.mark.parametrize("rows,N,K", [([300, 0, 77, 513, 129], 256, 384), ([2000, 1100], 128, 256)],
@@ -64,15 +82,17 @@ def test_quant_128x1_grouped_exact(rows, C):
 def test_wgrad_exact(rows, N, K):
     offs = _offsets(rows)
     G, Mt = len(rows), int(offs[-1])
-    ld = M.wgrad_pitch(Mt, G)
+    cap = M.wgrad_chunks(Mt, G)
     pref = OQ.chunk_prefix(offs)
-    qY = _codes((N, ld), 51 + N)
-    qA = _codes((K, ld), 52 + K)
-    sY = synth.pow2_scales((N, ld // 128), 53, -2, 2)
-    sA = synth.pow2_scales((K, ld // 128), 54, -2, 2)
-    log(f"[wgrad] rows {rows} N={N} K={K} ld={ld}")
+    qY = _codes((N, 128 * cap), 51 + N)
+    qA = _codes((K, 128 * cap), 52 + K)
+    sY = synth.pow2_scales((N, cap), 53, -2, 2)
+    sA = synth.pow2_scales((K, cap), 54, -2, 2)
+    log(f"[wgrad] rows {rows} N={N} K={K} chunks {cap}")
     dW = torch.full((G, N, K), float("nan"), dtype=torch.float32, device="cuda")
-    M.grouped_fp8_wgrad(dev(qY), dev(sY), dev(qA), dev(sA), ld, dev(offs.astype(np.int32)), G, Mt, N, K, dW)
+    (qYc, sYc), (qAc, sAc) = _to_chunks(qY, sY), _to_chunks(qA, sA)
+    M.grouped_fp8_wgrad(dev(qYc), dev(sYc), dev(qAc), dev(sAc), cap, dev(offs.astype(np.int32)), G, Mt,
+                        N, K, dW)
     ref = OG.grouped_wgrad(qY, sY, qA, sA, pref).astype(np.float32)
     got = host(dW)
     assert np.array_equal(got, ref), int((got != ref).sum())
@@ -93,10 +113,10 @@ def test_wgrad_random_end_to_end():
     G, Mt, N, K = len(rows), int(offs[-1]), 256, 384
     yb = synth.gen_gemm_activations(Mt, N, seed=61)
     ab = synth.gen_gemm_activations(Mt, K, seed=62)
-    qY, sY, ld = _quant_dev(yb, offs, G, N)
+    qY, sY, cap = _quant_dev(yb, offs, G, N)
     qA, sA, _ = _quant_dev(ab, offs, G, K)
     dW = torch.empty((G, N, K), dtype=torch.float32, device="cuda")
-    M.grouped_fp8_wgrad(qY, sY, qA, sA, ld, dev(offs.astype(np.int32)), G, Mt, N, K, dW)
+    M.grouped_fp8_wgrad(qY, sY, qA, sA, cap, dev(offs.astype(np.int32)), G, Mt, N, K, dW)
     qYo, sYo = OQ.quant_128x1_grouped(OF.bf16_value_from_bits(yb).astype(np.float32), offs)
     qAo, sAo = OQ.quant_128x1_grouped(OF.bf16_value_from_bits(ab).astype(np.float32), offs)
     pref = OQ.chunk_prefix(offs)
@@ -127,17 +147,21 @@ def test_wgrad_full_shape_sampled(N, K):
     counts = np.concatenate([synth.gen_group_counts(131072, G - 1, seed=0), [16384]])
     offs = _offsets(counts)
     Mt = int(offs[-1])
-    ld = M.wgrad_pitch(Mt, G)
+    cap = M.wgrad_chunks(Mt, G)
     pref = OQ.chunk_prefix(offs)
-    log(f"[wgrad full] N={N} K={K}: M={Mt} ld={ld}")
-    yb, ab = _codes((61, ld), 71), _codes((59, ld), 72)
-    sY = synth.pow2_scales((N, ld // 128), 73, -2, 2)
-    sA = synth.pow2_scales((K, ld // 128), 74, -2, 2)
-    qY_d = torch.from_numpy(yb).cuda()[torch.arange(N, device="cuda") % 61]
-    qA_d = torch.from_numpy(ab).cuda()[torch.arange(K, device="cuda") % 59]
+    log(f"[wgrad full] N={N} K={K}: M={Mt} chunks {cap}")
+    yb, ab = _codes((61, 128 * cap), 71), _codes((59, 128 * cap), 72)
+    sY = synth.pow2_scales((N, cap), 73, -2, 2)
+    sA = synth.pow2_scales((K, cap), 74, -2, 2)
+    # chunk-major operands: [c, n, i] = yb[n % 61, 128 c + i]
+    qY_d = torch.from_numpy(yb).cuda().view(61, cap, 128)[torch.arange(N, device="cuda") % 61]
+    qY_d = qY_d.permute(1, 0, 2).contiguous()
+    qA_d = torch.from_numpy(ab).cuda().view(59, cap, 128)[torch.arange(K, device="cuda") % 59]
+    qA_d = qA_d.permute(1, 0, 2).contiguous()
     dW = torch.empty((G, N, K), dtype=torch.float32, device="cuda")
     log(f"[wgrad full] N={N} K={K}: launch")
-    M.grouped_fp8_wgrad(qY_d, dev(sY), qA_d, dev(sA), ld, dev(offs.astype(np.int32)), G, Mt, N, K, dW)
+    M.grouped_fp8_wgrad(qY_d, dev(np.ascontiguousarray(sY.T)), qA_d, dev(np.ascontiguousarray(sA.T)), cap,
+                        dev(offs.astype(np.int32)), G, Mt, N, K, dW)
     torch.cuda.synchronize()
     rng = np.random.default_rng(9)
     for g in list(range(0, G, 32)) + [G - 1]:

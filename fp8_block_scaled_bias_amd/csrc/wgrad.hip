@@ -23,10 +23,13 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 using gemm::v8i;
 
 // ---- quantiser ---------------------------------------------------------------
-// One workgroup per (token chunk, 128 columns); thread t owns column t % 128
-// and rows 64 * (t / 128) .. +63 of the chunk.  Reads are 128 B row pieces
-// per wave; the workgroup writes one contiguous 16 KB block of codes.
+// One workgroup per (token chunk, 128 columns).  The chunk's rows come into
+// LDS by 16 B loads (16 lanes per 256 B row piece; rows past the group's end
+// read as zero); then thread t owns column t % 128 and rows 64 (t / 128) ..
+// +63, read from LDS (consecutive lanes, consecutive columns), and the
+// workgroup writes one contiguous 16 KB block of codes.
 constexpr int QT = 256;
+constexpr int QP = 136;  // LDS row pitch in bf16 (272 B: 16 B aligned rows)
 
 __global__ __launch_bounds__(QT) void quant_128x1_grouped_kernel(
     const uint16_t* __restrict__ in, int64_t ld_in, const int32_t* __restrict__ offs, int G,
@@ -36,28 +39,40 @@ __global__ __launch_bounds__(QT) void quant_128x1_grouped_kernel(
   __shared__ int s_red[QT / 64];
   __shared__ int s_carry;
   __shared__ float s_amax[128];
+  __shared__ __attribute__((aligned(16))) uint16_t s_x[128 * QP];
   gemm::build_group_tables<QT, 128>(offs, G, s_offs, s_pref, s_red, &s_carry);
   const int64_t L = blockIdx.x;  // chunk
   if (L >= s_pref[G]) return;
   const gemm::Tile t = gemm::decode_tile(s_pref, s_offs, G, 1, L, 128);
-  const int tid = threadIdx.x, half = tid >> 7;
-  const int64_t col = (int64_t)blockIdx.y * 128 + (tid & 127);
-  const int r0 = t.m0 + 64 * half;
+  const int tid = threadIdx.x;
+  const int64_t c0 = (int64_t)blockIdx.y * 128;
+  {
+    const int piece = tid & 15;
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int row = (tid >> 4) + 16 * it;
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (t.m0 + row < t.m1)
+        v = *reinterpret_cast<const uint4*>(in + (int64_t)(t.m0 + row) * ld_in + c0 + piece * 8);
+      *reinterpret_cast<uint4*>(&s_x[row * QP + piece * 8]) = v;
+    }
+  }
+  __syncthreads();
+  const int col = tid & 127, half = tid >> 7;
   float v[64];
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 64; ++i) {
-    const int r = r0 + i;
-    v[i] = r < t.m1 ? bf16_to_f32(in[(int64_t)r * ld_in + col]) : 0.0f;
+    v[i] = bf16_to_f32(s_x[(64 * half + i) * QP + col]);
     amax = fmaxf(amax, fabsf(v[i]));
   }
-  if (half) s_amax[tid & 127] = amax;
+  if (half) s_amax[col] = amax;
   __syncthreads();
-  if (!half) s_amax[tid] = fmaxf(amax, s_amax[tid]);
+  if (!half) s_amax[col] = fmaxf(amax, s_amax[col]);
   __syncthreads();
-  amax = s_amax[tid & 127];
+  amax = s_amax[col];
   const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
-  uint8_t* dst = out + (L * C + col) * 128 + 64 * half;
+  uint8_t* dst = out + (L * C + c0 + col) * 128 + 64 * half;
 #pragma unroll
   for (int i = 0; i < 64; i += 16) {
     uint4 w;
@@ -67,7 +82,7 @@ __global__ __launch_bounds__(QT) void quant_128x1_grouped_kernel(
     w.w = f32x4_to_e4m3x4(v[i + 12] / s, v[i + 13] / s, v[i + 14] / s, v[i + 15] / s);
     *reinterpret_cast<uint4*>(dst + i) = w;
   }
-  if (!half) scales[L * C + col] = s;
+  if (!half) scales[L * C + c0 + col] = s;
 }
 
 // ---- weight-gradient GEMM ----------------------------------------------------
@@ -253,8 +268,10 @@ extern "C" int fp8_quant_128x1_grouped(const void* in_bf16, int64_t ld_in,
               "fp8_quant_128x1_grouped: chunks_cap=%lld < ceil(M_total/128) + G = %lld",
               (long long)chunks_cap, (long long)chunks_needed(M_total, G));
   MOE_INVALID(in_bf16 && group_offsets && out_c && scales_c, "fp8_quant_128x1_grouped: null pointer");
-  MOE_INVALID(((uintptr_t)in_bf16 & 1) == 0 && ((uintptr_t)out_c & 15) == 0 && ((uintptr_t)scales_c & 3) == 0,
-              "fp8_quant_128x1_grouped: in must be 2-byte, out 16-byte, scales 4-byte aligned");
+  MOE_INVALID(((uintptr_t)in_bf16 & 15) == 0 && ld_in % 8 == 0 && ((uintptr_t)out_c & 15) == 0 &&
+                  ((uintptr_t)scales_c & 3) == 0,
+              "fp8_quant_128x1_grouped: in must be 16-byte aligned with ld_in %% 8 == 0, out 16-byte, "
+              "scales 4-byte aligned");
   const int64_t chunks = chunks_needed(M_total, G);
   quant_128x1_grouped_kernel<<<dim3((unsigned)chunks, (unsigned)(C / 128)), dim3(QT), 0, as_stream(stream)>>>(
       static_cast<const uint16_t*>(in_bf16), ld_in, group_offsets, G, C, out_c, scales_c);

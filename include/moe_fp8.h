@@ -210,7 +210,7 @@ int fp8_transpose_128x128(const uint8_t* w_e4m3, const float* w_scale, int64_t G
  * with the rounding of fp8_quant_1x128.  (out_c[c] transposed is the 128
  * tokens of chunk c as rows: a tile's chunk is one contiguous block.)
  *
- * in_bf16   [M_total, ld_in] bf16 (C columns used, 2-byte aligned)
+ * in_bf16   [M_total, ld_in] bf16 (C columns used; 16-byte aligned, ld_in % 8 == 0)
  * group_offsets [G+1] int32 on the device, as in grouped_fp8_gemm
  * out_c     (out) [chunks_cap, C, 128] e4m3 (16-byte aligned)
  * scales_c  (out) [chunks_cap, C] fp32

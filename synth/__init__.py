@@ -31,6 +31,7 @@ TID_W_DN = 5
 TID_GEMM_A = 6
 TID_GEMM_COUNTS = 7
 TID_ZIPF_SCALE = 8
+TID_DY = 9
 
 
 @dataclasses.dataclass(frozen=True)
@@ -108,6 +109,13 @@ def gen_x(cfg: MoEConfig, seed: int | None = None, T: int | None = None) -> np.n
     if cfg.x_std != 1.0:
         x *= np.float32(cfg.x_std)
     return f32_to_bf16_bits(x)
+
+
+def gen_dy(cfg: MoEConfig, seed: int | None = None, T: int | None = None) -> np.ndarray:
+    """Gradient of the layer output dy [T, H] as bf16 bit patterns, N(0, 1) then RNE."""
+    seed = cfg.seed if seed is None else seed
+    T = cfg.T if T is None else T
+    return f32_to_bf16_bits(_rng(seed, TID_DY).standard_normal((T, cfg.H), dtype=np.float32))
 
 
 def gen_centroids(cfg: MoEConfig, seed: int | None = None) -> np.ndarray:

@@ -220,3 +220,97 @@ def test_wgrad_is_the_derivative_of_the_forward():
             w2 = W.copy()
             w2[n, k] += 1.0
             assert abs((loss(w2) - loss(W)) - dW[g, n, k]) <= 1e-9 * max(1.0, abs(dW[g, n, k]))
+
+
+# ---- layer backward (expert path) -----------------------------------------
+
+from oracle import backward as OB          # noqa: E402
+from oracle import combine as OC           # noqa: E402
+from oracle import layer as LY             # noqa: E402
+
+
+def test_combine_backward_is_the_derivative_of_combine():
+    rng = np.random.default_rng(31)
+    T, k, H = 5, 3, 16
+    R = T * k + T
+    D = rng.standard_normal((R, H))
+    inv_perm = rng.permutation(T * k).astype(np.int32)
+    w = rng.random((T, k)).astype(np.float32)
+    dy = rng.standard_normal((T, H))
+    shared = lambda Dm: Dm[T * k:]
+    loss = lambda Dm, wm: float(np.sum(dy * OC.combine(Dm, inv_perm, wm, T, k, shared(Dm))[1]))
+    cb = OB.combine_backward(dy, D, inv_perm, w, T, k, 1)
+    for (r, h) in [(0, 0), (inv_perm[7], 5), (T * k + 2, 15), (R - 1, 3)]:
+        D2 = D.copy()
+        D2[r, h] += 1.0
+        assert abs((loss(D2, w) - loss(D, w)) - cb["dD64"][r, h]) < 1e-12
+    for (t, j) in [(0, 0), (4, 2), (2, 1)]:
+        w2 = w.copy()
+        w2[t, j] += np.float32(2.0 ** -10)
+        assert abs((loss(D, w2) - loss(D, w)) / 2.0 ** -10 - cb["dw"][t, j]) < 1e-9
+    # stored form: bf16 of the fp32 product
+    t, j = 3, 1
+    r = inv_perm[t * k + j]
+    assert np.array_equal(cb["dD"][r], F.bf16_round((w[t, j] * dy[t].astype(np.float32)).astype(np.float64)))
+
+
+def test_swiglu_backward_is_the_derivative_of_swiglu():
+    rng = np.random.default_rng(32)
+    I = 8
+    gu = rng.standard_normal((6, 2 * I)) * 4.0
+    gu[0, :I] = 0.0
+    dh = rng.standard_normal((6, I))
+    dgu, h = OB.swiglu_backward(gu, dh, I)
+    hf = lambda g, u: g / (1.0 + np.exp(-g)) * u
+    np.testing.assert_allclose(h, hf(gu[:, :I], gu[:, I:]), rtol=1e-14)
+    eps = 1e-6
+    g, u = gu[:, :I], gu[:, I:]
+    dg_fd = dh * (hf(g + eps, u) - hf(g - eps, u)) / (2 * eps)
+    du_fd = dh * (hf(g, u + eps) - hf(g, u - eps)) / (2 * eps)
+    np.testing.assert_allclose(dgu[:, :I], dg_fd, rtol=1e-6, atol=1e-8)
+    np.testing.assert_allclose(dgu[:, I:], du_fd, rtol=1e-6, atol=1e-8)
+    # g = 0: silu(0) = 0, silu'(0) = 1/2
+    np.testing.assert_allclose(dgu[0, :I], 0.5 * dh[0] * u[0], rtol=1e-15)
+    assert not dgu[0, I:].any()
+
+
+def test_expert_backward_close_to_float64_autograd_tiny():
+    """The FP8 composition against torch float64 autograd through the same forward
+    with every quantisation taken as identity (the dequantised x and weights, h
+    unquantised): they differ by E4M3 rounding only; a transposed product, a
+    wrong permutation or a missing scale would be off by O(1)."""
+    import torch
+    cfg = synth.TINY
+    x = synth.gen_x(cfg)
+    c, b = synth.gen_centroids(cfg), synth.gen_bias(cfg)
+    wts = LY.ExpertWeights(lambda e: synth.gen_expert_weight(cfg, "gu", e),
+                           lambda e: synth.gen_expert_weight(cfg, "dn", e))
+    fwd = LY.layer(x, c, b, wts, cfg.n_group, cfg.topk_group, cfg.k, cfg.I)
+    dy = synth.gen_dy(cfg)
+    bw = OB.expert_backward(dy, fwd, wts, x, cfg.T, cfg.k, cfg.I)
+    T, k, I, G = cfg.T, cfg.k, cfg.I, cfg.E + 1
+    offs = np.asarray(fwd["offsets"], dtype=np.int64)
+    t64 = lambda a: torch.tensor(np.asarray(a, dtype=np.float64))
+    A = t64(Q.dequant_1x128(fwd["xq"], fwd["xs"])[fwd["perm_src"]]).requires_grad_()
+    Wg = [t64(Q.dequant_128x128(*wts.gu(g))).requires_grad_() for g in range(G)]
+    Wd = [t64(Q.dequant_128x128(*wts.dn(g))).requires_grad_() for g in range(G)]
+    w = t64(fwd["route"]["w32"]).requires_grad_()
+    Ds = []
+    for g in range(G):
+        a = A[offs[g]:offs[g + 1]]
+        gu = a @ Wg[g].T
+        h = torch.nn.functional.silu(gu[:, :I]) * gu[:, I:]
+        Ds.append(h @ Wd[g].T)
+    D = torch.cat(Ds)
+    rows = torch.tensor(np.asarray(fwd["inv_perm"], dtype=np.int64).reshape(T, k))
+    y = (w[:, :, None] * D[rows]).sum(1) + D[T * k:]
+    dyv = t64(F.bf16_value_from_bits(dy))
+    (y * dyv).sum().backward()
+    dx_ref = torch.zeros((T, cfg.H), dtype=torch.float64).index_add_(
+        0, torch.tensor(np.asarray(fwd["perm_src"], dtype=np.int64)), A.grad).numpy()
+    rel = lambda a, r: float(np.linalg.norm(a - r) / np.linalg.norm(r))
+    errs = dict(dx=rel(bw["dx"], dx_ref), dw=rel(bw["dw"], w.grad.numpy()),
+                dW_gu=rel(bw["dW_gu"], np.stack([W.grad.numpy() for W in Wg])),
+                dW_dn=rel(bw["dW_dn"], np.stack([W.grad.numpy() for W in Wd])))
+    print(errs)
+    assert max(errs.values()) < 0.08, errs

@@ -238,8 +238,9 @@ def bench_backward(layer, T, reps=10, warmup=3):
         ys = torch.empty((cap, N), dtype=torch.float32, device="cuda")
         aq = torch.empty((cap, K, 128), dtype=torch.uint8, device="cuda")
         asc = torch.empty((cap, K), dtype=torch.float32, device="cuda")
-        q_ms = _median_ms(lambda: (M.fp8_quant_128x1_grouped(dy, N, offs, G, R, N, yq, ys, cap),
-                                   M.fp8_quant_128x1_grouped(a, K, offs, G, R, K, aq, asc, cap)), 5, 2)
+        q_ms = _median_ms(lambda: (M.fp8_quant_128x1_grouped(dy, N, None, offs, G, R, N, yq, ys, cap),
+                                   M.fp8_quant_128x1_grouped(a, K, None, offs, G, R, K, aq, asc, cap)),
+                          5, 2)
         q_bytes = 3 * R * (N + K) + 4 * (N + K) * (R // 128)
         del dy, a
         dw = torch.empty((G, N, K), dtype=torch.float32, device="cuda")

@@ -36,8 +36,11 @@ SIGNATURES = {
     "fp8_quant_1x128": (ctypes.c_int, [_vp, _i64, _i64, _i64, _i32, _vp, _vp, _vp]),
     "fp8_quant_128x128": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _vp, _vp]),
     "fp8_transpose_128x128": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp]),
-    "fp8_quant_128x1_grouped": (ctypes.c_int, [_vp, _i64, _vp, _i32, _i64, _i64, _vp, _vp, _i64,
-                                               _vp]),
+    "fp8_quant_128x1_grouped": (ctypes.c_int, [_vp, _i64, _vp, _i64, _vp, _i32, _i64, _i64, _vp,
+                                               _vp, _i64, _vp]),
+    "moe_combine_backward": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i32, _i64, _i32, _vp, _vp,
+                                            _vp]),
+    "swiglu_backward": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp, _vp, _vp]),
     "grouped_fp8_wgrad": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _vp, _i32, _i64, _i64, _i64,
                                          _vp, _vp]),
     "grouped_fp8_gemm": (ctypes.c_int, [_vp, _vp, _vp, _i64, _vp, _vp, _vp, _i32, _i64, _i64,
@@ -166,10 +169,23 @@ def wgrad_chunks(M_total, G):
     return -(-M_total // 128) + G
 
 
-def fp8_quant_128x1_grouped(in_bf16, ld_in, group_offsets, G, M_total, C, out_c, scales_c,
-                            chunks_cap, stream=None):
-    return _call("fp8_quant_128x1_grouped", _dev(in_bf16), ld_in, _dev(group_offsets), G, M_total,
-                 C, _dev(out_c), _dev(scales_c), chunks_cap, _stream(stream))
+def fp8_quant_128x1_grouped(in_bf16, ld_in, row_index, group_offsets, G, M_total, C, out_c,
+                            scales_c, chunks_cap, stream=None):
+    return _call("fp8_quant_128x1_grouped", _dev(in_bf16), ld_in, _dev(row_index), _rows(in_bf16),
+                 _dev(group_offsets), G, M_total, C, _dev(out_c), _dev(scales_c), chunks_cap,
+                 _stream(stream))
+
+
+def moe_combine_backward(dy_bf16, inv_perm, topk_w, expert_out_bf16, T, k, H, n_shared,
+                         d_expert_out_bf16, d_topk_w, stream=None):
+    return _call("moe_combine_backward", _dev(dy_bf16), _dev(inv_perm), _dev(topk_w),
+                 _dev(expert_out_bf16), T, k, H, n_shared, _dev(d_expert_out_bf16), _dev(d_topk_w),
+                 _stream(stream))
+
+
+def swiglu_backward(gu_bf16, dh_bf16, M, I, dgu_bf16, h_bf16, stream=None):
+    return _call("swiglu_backward", _dev(gu_bf16), _dev(dh_bf16), M, I, _dev(dgu_bf16),
+                 _dev(h_bf16), _stream(stream))
 
 
 def grouped_fp8_wgrad(dy_c, dy_scale_c, a_c, a_scale_c, chunks_cap, group_offsets, G, M_total, N,

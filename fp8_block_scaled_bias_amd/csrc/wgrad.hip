@@ -25,15 +25,17 @@ using gemm::v8i;
 // ---- quantiser ---------------------------------------------------------------
 // One workgroup per (token chunk, 128 columns).  The chunk's rows come into
 // LDS by 16 B loads (16 lanes per 256 B row piece; rows past the group's end
-// read as zero); then thread t owns column t % 128 and rows 64 (t / 128) ..
+// read as zero; with a row index, layout row r reads input row
+// row_index[r], clamped to the input); then thread t owns column t % 128 and rows 64 (t / 128) ..
 // +63, read from LDS (consecutive lanes, consecutive columns), and the
 // workgroup writes one contiguous 16 KB block of codes.
 constexpr int QT = 256;
 constexpr int QP = 136;  // LDS row pitch in bf16 (272 B: 16 B aligned rows)
 
 __global__ __launch_bounds__(QT) void quant_128x1_grouped_kernel(
-    const uint16_t* __restrict__ in, int64_t ld_in, const int32_t* __restrict__ offs, int G,
-    int64_t C, uint8_t* __restrict__ out, float* __restrict__ scales) {
+    const uint16_t* __restrict__ in, int64_t ld_in, const int32_t* __restrict__ row_index,
+    int64_t in_rows, const int32_t* __restrict__ offs, int G, int64_t C, uint8_t* __restrict__ out,
+    float* __restrict__ scales) {
   __shared__ int s_offs[gemm::MAXG + 1];
   __shared__ int s_pref[gemm::MAXG + 1];
   __shared__ int s_red[QT / 64];
@@ -52,8 +54,11 @@ __global__ __launch_bounds__(QT) void quant_128x1_grouped_kernel(
     for (int it = 0; it < 8; ++it) {
       const int row = (tid >> 4) + 16 * it;
       uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (t.m0 + row < t.m1)
-        v = *reinterpret_cast<const uint4*>(in + (int64_t)(t.m0 + row) * ld_in + c0 + piece * 8);
+      if (t.m0 + row < t.m1) {
+        const int64_t src = row_index ? (int64_t)min((uint32_t)row_index[t.m0 + row], (uint32_t)(in_rows - 1))
+                                      : (int64_t)(t.m0 + row);
+        v = *reinterpret_cast<const uint4*>(in + src * ld_in + c0 + piece * 8);
+      }
       *reinterpret_cast<uint4*>(&s_x[row * QP + piece * 8]) = v;
     }
   }
@@ -252,6 +257,7 @@ using namespace moe;
 static int64_t chunks_needed(int64_t M_total, int32_t G) { return ceil_div(M_total, 128) + G; }
 
 extern "C" int fp8_quant_128x1_grouped(const void* in_bf16, int64_t ld_in,
+                                       const int32_t* row_index, int64_t in_rows,
                                        const int32_t* group_offsets, int32_t G, int64_t M_total,
                                        int64_t C, uint8_t* out_c, float* scales_c,
                                        int64_t chunks_cap, void* stream) {
@@ -264,6 +270,9 @@ extern "C" int fp8_quant_128x1_grouped(const void* in_bf16, int64_t ld_in,
               "fp8_quant_128x1_grouped: C=%lld must be a positive multiple of 128 (at most 65535*128)",
               (long long)C);
   MOE_INVALID(ld_in >= C, "fp8_quant_128x1_grouped: ld_in=%lld < C", (long long)ld_in);
+  MOE_INVALID(row_index ? (in_rows >= 1 && in_rows < (1ll << 31)) : in_rows >= M_total,
+              "fp8_quant_128x1_grouped: in_rows=%lld must be >= %s and < 2^31", (long long)in_rows,
+              row_index ? "1" : "M_total");
   MOE_INVALID(chunks_cap >= chunks_needed(M_total, G),
               "fp8_quant_128x1_grouped: chunks_cap=%lld < ceil(M_total/128) + G = %lld",
               (long long)chunks_cap, (long long)chunks_needed(M_total, G));
@@ -274,7 +283,8 @@ extern "C" int fp8_quant_128x1_grouped(const void* in_bf16, int64_t ld_in,
               "scales 4-byte aligned");
   const int64_t chunks = chunks_needed(M_total, G);
   quant_128x1_grouped_kernel<<<dim3((unsigned)chunks, (unsigned)(C / 128)), dim3(QT), 0, as_stream(stream)>>>(
-      static_cast<const uint16_t*>(in_bf16), ld_in, group_offsets, G, C, out_c, scales_c);
+      static_cast<const uint16_t*>(in_bf16), ld_in, row_index, in_rows, group_offsets, G, C, out_c,
+      scales_c);
   return check_launch("fp8_quant_128x1_grouped");
 }
 

@@ -17,6 +17,25 @@ FP8 低精度训练):
   6. moe_combine       gate-weighted sum of routed outputs + shared output
   7. moe_bias_update   (optional) aux-loss-free bias step for the next batch
 
+MoELayer.backward runs the backward of the expert path in FP8 (the pages'
+backward-for-input and backward-for-weights chunks, section 工程 › DualPipe
+流水线并行, with the FP8 formats of section FP8 低精度训练):
+
+  1. moe_combine_backward   dD = w * dy per routed row, dy for the shared rows;
+                            dw = <dy, D> (the gate weights' gradient)
+  2. fp8_quant_1x128 + grouped_fp8_gemm on W_dn^T      dh = dD W_dn
+  3. grouped_fp8_gemm       the gate+up outputs again (bf16; the fused
+                            forward keeps none)
+  4. swiglu_backward        dGU = [dg | du], h
+  5. fp8_quant_1x128 + grouped_fp8_gemm on W_gu^T      dX = dGU W_gu
+  6. moe_combine            dx = the sum of a token's rows of dX (unit weights)
+  7. fp8_quant_128x1_grouped + grouped_fp8_wgrad       dW_dn = dD^T h,
+                            dW_gu = dGU^T x (x gathered through the permutation)
+
+The weight transposes (fp8_transpose_128x128) are cached on the layer and
+redone by transpose_weights() when the weights change.  The router's
+backward (from dw on) is not part of this path.
+
 torch is only used to hold device memory and to name the stream; every step
 runs in the library's HIP kernels.
 """
@@ -82,6 +101,43 @@ class Buffers:
         return self._hgu
 
 
+class BackwardBuffers:
+    """Device buffers of one expert-path backward at T tokens (reused across calls)."""
+
+    def __init__(self, shape: LayerShape, T: int, device="cuda"):
+        s = shape
+        R = T * s.k + s.n_shared * T
+        dev = torch.device(device)
+        u8, f32, bf = torch.uint8, torch.float32, torch.bfloat16
+        H, I = s.H, s.I
+        self.T, self.R = T, R
+        self.dD = torch.empty((R, H), dtype=bf, device=dev)
+        self.dw = torch.empty((T, s.k), dtype=f32, device=dev)
+        self.dDq = torch.empty((R, H), dtype=u8, device=dev)
+        self.dDs = torch.empty((R, H // 128), dtype=f32, device=dev)
+        self.dh = torch.empty((R, I), dtype=bf, device=dev)
+        self.gu = torch.empty((R, 2 * I), dtype=bf, device=dev)
+        self.dgu = torch.empty((R, 2 * I), dtype=bf, device=dev)
+        self.h = torch.empty((R, I), dtype=bf, device=dev)
+        self.dguq = torch.empty((R, 2 * I), dtype=u8, device=dev)
+        self.dgus = torch.empty((R, 2 * I // 128), dtype=f32, device=dev)
+        self.dxp = torch.empty((R, H), dtype=bf, device=dev)
+        self.dx = torch.empty((T, H), dtype=bf, device=dev)
+        self.ones = torch.ones((T, s.k), dtype=f32, device=dev)
+        self.cap = L.wgrad_chunks(R, s.G)
+        c = self.cap
+        self.c_dD = torch.empty((c, H, 128), dtype=u8, device=dev)
+        self.s_dD = torch.empty((c, H), dtype=f32, device=dev)
+        self.c_h = torch.empty((c, I, 128), dtype=u8, device=dev)
+        self.s_h = torch.empty((c, I), dtype=f32, device=dev)
+        self.c_dgu = torch.empty((c, 2 * I, 128), dtype=u8, device=dev)
+        self.s_dgu = torch.empty((c, 2 * I), dtype=f32, device=dev)
+        self.c_x = torch.empty((c, H, 128), dtype=u8, device=dev)
+        self.s_x = torch.empty((c, H), dtype=f32, device=dev)
+        self.dW_gu = torch.empty((s.G, 2 * I, H), dtype=f32, device=dev)
+        self.dW_dn = torch.empty((s.G, H, I), dtype=f32, device=dev)
+
+
 class MoELayer:
     """One MoE layer on one GPU: router state and FP8 expert weights.
 
@@ -96,6 +152,8 @@ class MoELayer:
         self.centroids = centroids
         self.bias = bias
         self.w_gu, self.w_gu_s, self.w_dn, self.w_dn_s = w_gu, w_gu_s, w_dn, w_dn_s
+        self._wt = None          # transposed weight blocks, made on first backward
+        self._bwd = {}
         self._bufs = {}
 
     @staticmethod
@@ -170,6 +228,87 @@ class MoELayer:
         if update_bias:
             L.moe_bias_update(b.counts, self.bias, s.E, gamma, stream)
         return b.y
+
+    def transpose_weights(self, stream=None):
+        """W^T of both weight sets in 128x128 blocks (the dgrad operands); call
+        again after the weights change."""
+        s = self.shape
+        if self._wt is None:
+            dev = self.w_gu.device
+            self._wt = dict(
+                gu=torch.empty((s.G, s.H, 2 * s.I), dtype=torch.uint8, device=dev),
+                gu_s=torch.empty((s.G, s.H // 128, 2 * s.I // 128), dtype=torch.float32, device=dev),
+                dn=torch.empty((s.G, s.I, s.H), dtype=torch.uint8, device=dev),
+                dn_s=torch.empty((s.G, s.I // 128, s.H // 128), dtype=torch.float32, device=dev))
+        w = self._wt
+        L.fp8_transpose_128x128(self.w_gu, self.w_gu_s, s.G, 2 * s.I, s.H, w["gu"], w["gu_s"], stream)
+        L.fp8_transpose_128x128(self.w_dn, self.w_dn_s, s.G, s.H, s.I, w["dn"], w["dn_s"], stream)
+        return w
+
+    def backward_buffers(self, T: int) -> BackwardBuffers:
+        bb = self._bwd.get(T)
+        if bb is None:
+            bb = self._bwd[T] = BackwardBuffers(self.shape, T, self.centroids.device)
+        return bb
+
+    def backward(self, dy_bf16: torch.Tensor, x_bf16: torch.Tensor, bufs: Buffers | None = None,
+                 bwd: BackwardBuffers | None = None, stream=None, events: dict | None = None):
+        """Backward of the expert path for the output gradient dy, after a
+        forward of x on `bufs` (its routing, permutation, quantised x and D).
+        Returns the BackwardBuffers: dx (expert path), dw (gate weights),
+        dW_gu, dW_dn.  `events` as in forward, keys "combine_bwd", "dgrad_down",
+        "recompute_gate_up", "swiglu_bwd", "dgrad_gate_up", "unpermute",
+        "wgrad_down", "wgrad_gate_up"."""
+        s = self.shape
+        T = dy_bf16.shape[0]
+        b = bufs or self.buffers(T)
+        bb = bwd or self.backward_buffers(T)
+        if self._wt is None:
+            self.transpose_weights(stream)
+        w = self._wt
+        R, G, H, I, k, cap = b.R, s.G, s.H, s.I, s.k, bb.cap
+        st = stream if stream is not None else torch.cuda.current_stream()
+
+        def step(name, fn):
+            if events is None:
+                fn()
+                return
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            fn()
+            e1.record(st)
+            events.setdefault(name, []).append((e0, e1))
+
+        step("combine_bwd", lambda: L.moe_combine_backward(
+            dy_bf16, b.inv_perm, b.topk_w, b.d, T, k, H, s.n_shared, bb.dD, bb.dw, st))
+        step("dgrad_down", lambda: (
+            L.fp8_quant_1x128(bb.dD, R, H, H, 0, bb.dDq, bb.dDs, st),
+            L.grouped_fp8_gemm(bb.dDq, bb.dDs, None, w["dn"], w["dn_s"], b.offsets, G, R, I, H,
+                               bb.dh, st)))
+        step("recompute_gate_up", lambda: L.grouped_fp8_gemm(
+            b.xq, b.xs, b.perm_src, self.w_gu, self.w_gu_s, b.offsets, G, R, 2 * I, H, bb.gu, st))
+        step("swiglu_bwd", lambda: L.swiglu_backward(bb.gu, bb.dh, R, I, bb.dgu, bb.h, st))
+        step("dgrad_gate_up", lambda: (
+            L.fp8_quant_1x128(bb.dgu, R, 2 * I, 2 * I, 0, bb.dguq, bb.dgus, st),
+            L.grouped_fp8_gemm(bb.dguq, bb.dgus, None, w["gu"], w["gu_s"], b.offsets, G, R, H,
+                               2 * I, bb.dxp, st)))
+        shared = bb.dxp[T * k:T * k + T] if s.n_shared else None
+        step("unpermute", lambda: L.moe_combine(bb.dxp, b.inv_perm, bb.ones, shared, T, k, H,
+                                                bb.dx, st))
+        step("wgrad_down", lambda: (
+            L.fp8_quant_128x1_grouped(bb.dD, H, None, b.offsets, G, R, H, bb.c_dD, bb.s_dD, cap, st),
+            L.fp8_quant_128x1_grouped(bb.h, I, None, b.offsets, G, R, I, bb.c_h, bb.s_h, cap, st),
+            L.grouped_fp8_wgrad(bb.c_dD, bb.s_dD, bb.c_h, bb.s_h, cap, b.offsets, G, R, H, I,
+                                bb.dW_dn, st)))
+        step("wgrad_gate_up", lambda: (
+            L.fp8_quant_128x1_grouped(bb.dgu, 2 * I, None, b.offsets, G, R, 2 * I, bb.c_dgu,
+                                      bb.s_dgu, cap, st),
+            L.fp8_quant_128x1_grouped(x_bf16, H, b.perm_src, b.offsets, G, R, H, bb.c_x, bb.s_x,
+                                      cap, st),
+            L.grouped_fp8_wgrad(bb.c_dgu, bb.s_dgu, bb.c_x, bb.s_x, cap, b.offsets, G, R, 2 * I, H,
+                                bb.dW_gu, st)))
+        return bb
 
     def _forward_timed(self, x_bf16, b, stream, update_bias, gamma, fused, events):
         s = self.shape

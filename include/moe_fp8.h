@@ -210,16 +210,20 @@ int fp8_transpose_128x128(const uint8_t* w_e4m3, const float* w_scale, int64_t G
  * with the rounding of fp8_quant_1x128.  (out_c[c] transposed is the 128
  * tokens of chunk c as rows: a tile's chunk is one contiguous block.)
  *
- * in_bf16   [M_total, ld_in] bf16 (C columns used; 16-byte aligned, ld_in % 8 == 0)
+ * in_bf16   [in_rows, ld_in] bf16 (C columns used; 16-byte aligned, ld_in % 8 == 0)
+ * row_index [M_total] int32 or NULL: layout row r reads input row row_index[r]
+ *           (an entry outside [0, in_rows) reads row in_rows - 1), else row r
+ * in_rows   rows of in_bf16: >= M_total without a row index, >= 1 with one
  * group_offsets [G+1] int32 on the device, as in grouped_fp8_gemm
  * out_c     (out) [chunks_cap, C, 128] e4m3 (16-byte aligned)
  * scales_c  (out) [chunks_cap, C] fp32
  * chunks_cap >= ceil(M_total / 128) + G (chunks past the last are not written)
  * Requirements: 1 <= G <= 1024, C % 128 == 0, ld_in >= C.
  */
-int fp8_quant_128x1_grouped(const void* in_bf16, int64_t ld_in, const int32_t* group_offsets,
-                            int32_t G, int64_t M_total, int64_t C, uint8_t* out_c,
-                            float* scales_c, int64_t chunks_cap, void* stream);
+int fp8_quant_128x1_grouped(const void* in_bf16, int64_t ld_in, const int32_t* row_index,
+                            int64_t in_rows, const int32_t* group_offsets, int32_t G,
+                            int64_t M_total, int64_t C, uint8_t* out_c, float* scales_c,
+                            int64_t chunks_cap, void* stream);
 
 /*
  * grouped_fp8_wgrad - weight gradient of the expert GEMMs (news.qq.com article,
@@ -245,6 +249,38 @@ int grouped_fp8_wgrad(const uint8_t* dy_c, const float* dy_scale_c, const uint8_
                       const float* a_scale_c, int64_t chunks_cap, const int32_t* group_offsets,
                       int32_t G, int64_t M_total, int64_t N, int64_t K, float* dW,
                       void* stream);
+
+/*
+ * moe_combine_backward - backward of moe_combine (news.qq.com article, section
+ * DeepSeekMoE 架构: gate-weighted routed experts plus the always-on shared
+ * one; section 工程 › DualPipe 流水线并行: the backward-for-input chunks).
+ *
+ * For the forward y[t] = sum_j w[t,j] D[inv_perm[t*k+j]] + D[T*k + t]:
+ *   dD[inv_perm[t*k+j], :] = bf16( w[t,j] * dy[t, :] )   (fp32 product)
+ *   dD[T*k + t, :]         = dy[t, :]                      (n_shared == 1)
+ *   dw[t*k + j]            = sum_h dy[t, h] * D[inv_perm[t*k+j], h]  (fp32,
+ *                            summed in a fixed order)
+ * dy_bf16 [T, H]; inv_perm [T*k] (a permutation of [0, T*k)); topk_w [T*k];
+ * expert_out_bf16 D [T*k + n_shared*T, H]; d_expert_out_bf16 (out) like D;
+ * d_topk_w (out) [T*k] fp32.  Requirements: 1 <= k <= 8, H % 8 == 0,
+ * n_shared in {0, 1}; dy, D, dD 16-byte aligned, dD not aliasing D.
+ */
+int moe_combine_backward(const void* dy_bf16, const int32_t* inv_perm, const float* topk_w,
+                         const void* expert_out_bf16, int64_t T, int32_t k, int64_t H,
+                         int32_t n_shared, void* d_expert_out_bf16, float* d_topk_w,
+                         void* stream);
+
+/*
+ * swiglu_backward - backward of h = silu(g) * u (the experts' SwiGLU, see
+ * grouped_fp8_gemm_swiglu) from the bf16 gate/up outputs, in fp32:
+ *   s = 1 / (1 + exp(-g));  dg = dh * u * s * (1 + g * (1 - s));  du = dh * g * s;
+ *   h = g * s * u
+ * gu_bf16 [M, 2I] = [g | u]; dh_bf16 [M, I]; dgu_bf16 (out) [M, 2I] = [dg | du];
+ * h_bf16 (out) [M, I] (the down projection's weight-gradient operand); all
+ * stored as bf16 (round to nearest even), 16-byte aligned.  I % 8 == 0.
+ */
+int swiglu_backward(const void* gu_bf16, const void* dh_bf16, int64_t M, int64_t I,
+                    void* dgu_bf16, void* h_bf16, void* stream);
 
 /*
  * grouped_fp8_gemm - block-scaled FP8 grouped GEMM with FP32 accumulation

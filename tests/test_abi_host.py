@@ -65,8 +65,9 @@ def test_transpose_validation():
 
 def test_wgrad_validation():
     cap = 1 + 4                              # M_total = 100, G = 4
-    def q(G=4, M=100, C=256, ld_in=256, cap=cap, out=FAKE):
-        return rc("fp8_quant_128x1_grouped", FAKE, ld_in, FAKE, G, M, C, out, FAKE, cap, None)
+    def q(G=4, M=100, C=256, ld_in=256, cap=cap, out=FAKE, idx=None, in_rows=100):
+        return rc("fp8_quant_128x1_grouped", FAKE, ld_in, idx, in_rows, FAKE, G, M, C, out, FAKE, cap,
+                  None)
     assert q(C=100) == L.MOE_ERR_INVALID and "C=100" in L.last_error()
     assert q(G=0) == L.MOE_ERR_INVALID
     assert q(G=2000) == L.MOE_ERR_UNSUPPORTED
@@ -74,6 +75,8 @@ def test_wgrad_validation():
     assert q(cap=cap - 1) == L.MOE_ERR_INVALID and "chunks_cap" in L.last_error()
     assert q(out=None) == L.MOE_ERR_INVALID
     assert q(out=ctypes.c_void_p(4104)) == L.MOE_ERR_INVALID and "aligned" in L.last_error()
+    assert q(in_rows=99) == L.MOE_ERR_INVALID and "in_rows" in L.last_error()
+    assert q(idx=FAKE, in_rows=0) == L.MOE_ERR_INVALID
     def w(G=4, M=100, N=256, K=384, cap=cap, dW=FAKE):
         return rc("grouped_fp8_wgrad", FAKE, FAKE, FAKE, FAKE, cap, FAKE, G, M, N, K, dW, None)
     assert w(N=200) == L.MOE_ERR_INVALID and "N=200" in L.last_error()
@@ -81,6 +84,23 @@ def test_wgrad_validation():
     assert w(cap=4) == L.MOE_ERR_INVALID and "chunks_cap" in L.last_error()
     assert w(dW=None) == L.MOE_ERR_INVALID
     assert L.wgrad_chunks(100, 4) == cap and L.wgrad_chunks(256, 3) == 5
+
+
+def test_backward_elementwise_validation():
+    def c(T=4, k=2, H=256, ns=1, dD=ctypes.c_void_p(8192)):
+        return rc("moe_combine_backward", FAKE, FAKE, FAKE, FAKE, T, k, H, ns, dD, FAKE, None)
+    assert c(k=9) == L.MOE_ERR_INVALID and "k=9" in L.last_error()
+    assert c(H=100) == L.MOE_ERR_INVALID
+    assert c(ns=2) == L.MOE_ERR_INVALID
+    assert c(dD=FAKE) == L.MOE_ERR_INVALID and "alias" in L.last_error()
+    assert c(dD=None) == L.MOE_ERR_INVALID
+    assert c(T=0, dD=None) == L.MOE_OK
+    def g(M=4, I=128, out=FAKE):
+        return rc("swiglu_backward", FAKE, FAKE, M, I, out, FAKE, None)
+    assert g(I=100) == L.MOE_ERR_INVALID and "I=100" in L.last_error()
+    assert g(out=None) == L.MOE_ERR_INVALID
+    assert g(out=ctypes.c_void_p(4104)) == L.MOE_ERR_INVALID and "aligned" in L.last_error()
+    assert g(M=0, out=None) == L.MOE_OK
 
 
 def test_gemm_validation():

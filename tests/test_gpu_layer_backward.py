@@ -1,0 +1,188 @@
+"""Backward of the layer's expert path on the GPU, through the C ABI.
+
+* moe_combine_backward: dD bit-exact (bf16 of the fp32 product w * dy on both
+  sides; the shared rows are dy itself), dw within the fp32 accumulation
+  bound H * 2^-23 * sum |dy D|;
+* swiglu_backward: dg, du and h within one bf16 ulp of the FP64 values (the
+  GPU evaluates in fp32, then rounds once to bf16);
+* MoELayer.backward on the tiny and mid configs: every stage against the
+  oracle applied to the GPU's own inputs to that stage (dD, every E4M3 code
+  and scale, both operand layouts bit-exact; GEMM outputs within the grouped
+  GEMM's derived bound plus one bf16 rounding; SwiGLU backward within one
+  bf16 ulp; weight gradients within the wgrad bound), then dx, dw, dW_gu and
+  dW_dn against the oracle's independent chain (oracle.backward after
+  oracle.layer) within relative L2 5e-3.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+import fp8_block_scaled_bias_amd as M
+from gpu_common import (assert_within_one_bf16_ulp, bf16_dev, bf16_ulp, bf16_values_host,
+                        compare_routes, dev, host, log, rel_l2)
+from test_gpu_kernels import gemm_accumulation_bound
+from test_gpu_layer import build_layer, oracle_weights
+from oracle import backward as OBK
+from oracle import combine as OC
+from oracle import formats as OF
+from oracle import gemm as OG
+from oracle import layer as OL
+from oracle import quant as OQ
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("T,k,H,ns", [(37, 8, 1024, 1), (5, 3, 256, 0), (64, 4, 7168, 1)])
+def test_combine_backward_kernel(T, k, H, ns):
+    rng = np.random.default_rng([T, k, H])
+    R = T * k + ns * T
+    dy = synth.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    D = synth.f32_to_bf16_bits(rng.standard_normal((R, H)).astype(np.float32))
+    inv_perm = rng.permutation(T * k).astype(np.int32)
+    w = rng.random((T, k)).astype(np.float32)
+    log(f"[combine bwd] T={T} k={k} H={H} shared={ns}")
+    dD = torch.full((R, H), float("nan"), dtype=torch.bfloat16, device="cuda")
+    dw = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    M.moe_combine_backward(bf16_dev(dy), dev(inv_perm), dev(w), bf16_dev(D), T, k, H, ns, dD, dw)
+    dyv, Dv = OF.bf16_value_from_bits(dy), OF.bf16_value_from_bits(D)
+    ref = OBK.combine_backward(dyv, Dv, inv_perm, w, T, k, ns)
+    assert np.array_equal(bf16_values_host(dD), ref["dD"])
+    rows = inv_perm.reshape(T, k).astype(np.int64)
+    bound = H * 2.0 ** -23 * np.stack([np.sum(np.abs(dyv * Dv[rows[:, j]]), axis=1) for j in range(k)], 1)
+    assert (np.abs(host(dw) - ref["dw"]) <= bound).all()
+
+
+@pytest.mark.parametrize("M_,I", [(300, 128), (7, 2048)])
+def test_swiglu_backward_kernel(M_, I):
+    rng = np.random.default_rng([M_, I])
+    gu = rng.standard_normal((M_, 2 * I)).astype(np.float32) * 3.0
+    gu[0, :8] = [0.0, -0.0, 20.0, -20.0, 80.0, -80.0, 1e-3, -1e-3]
+    gub = synth.f32_to_bf16_bits(gu)
+    dh = synth.f32_to_bf16_bits(rng.standard_normal((M_, I)).astype(np.float32))
+    log(f"[swiglu bwd] M={M_} I={I}")
+    dgu = torch.empty((M_, 2 * I), dtype=torch.bfloat16, device="cuda")
+    h = torch.empty((M_, I), dtype=torch.bfloat16, device="cuda")
+    M.swiglu_backward(bf16_dev(gub), bf16_dev(dh), M_, I, dgu, h)
+    r_dgu, r_h = OBK.swiglu_backward(OF.bf16_value_from_bits(gub), OF.bf16_value_from_bits(dh), I)
+    for got, ref, what in ((bf16_values_host(dgu), r_dgu, "dgu"), (bf16_values_host(h), r_h, "h")):
+        d = np.abs(got - ref)
+        assert (d <= bf16_ulp(np.maximum(np.abs(got), np.abs(ref))) + 1e-30).all(), what
+
+
+def _logical(c, sc, nch):
+    """chunk-major [cap, C, 128], [cap, C] -> [C, 128 nch], [C, nch]"""
+    C = c.shape[1]
+    return (np.ascontiguousarray(c[:nch].transpose(1, 0, 2)).reshape(C, nch * 128),
+            np.ascontiguousarray(sc[:nch].T))
+
+
+# The FP8 MFMA's error on one 128-term dot product, relative to the sum of
+# |products|: at most 2^-15.6 over 10^6 random-code dot products, but up to
+# 2^-13.3 on these weight-gradient operands (128x1 tiles of w * dy and of h:
+# a wide dynamic range within one tile), so the wgrad stage allows 2^-12.
+MFMA_REL_WGRAD = 2.0 ** -12
+
+
+def _wgrad_bound(qY, sY, qA, sA, pref):
+    S = OG.grouped_wgrad(np.asarray(qY) & 0x7F, sY, np.asarray(qA) & 0x7F, sA, pref)
+    nch = np.diff(pref).astype(np.float64)[:, None, None]
+    return (MFMA_REL_WGRAD + 2 * (nch + 1) * 2.0 ** -24) * S
+
+
+@pytest.mark.parametrize("name", ["tiny", "mid"])
+def test_layer_backward_small(name):
+    """Every stage against the oracle applied to the GPU's own inputs to that
+    stage (bit-exact codes and copies, GEMM outputs within their derived
+    bounds, elementwise steps within one bf16 ulp), then the end result
+    against the oracle's independent chain."""
+    cfg = synth.CONFIGS[name]
+    T, k, H, I, G = cfg.T, cfg.k, cfg.H, cfg.I, cfg.G
+    log(f"[layer bwd] {name}: T={T} H={H} E={cfg.E} I={I}")
+    layer, C, b = build_layer(cfg)
+    x = synth.gen_x(cfg)
+    dy = synth.gen_dy(cfg)
+    x_d = bf16_dev(x)
+    layer.forward(x_d)
+    bufs = layer.buffers(T)
+    bb = layer.backward(bf16_dev(dy), x_d)
+    torch.cuda.synchronize()
+    wts = oracle_weights(cfg)
+    fwd = OL.layer(x, C, b, wts, cfg.n_group, cfg.topk_group, k, I)
+    mism = compare_routes(host(bufs.topk_idx), fwd["route"], name)
+    assert len(mism) == 0, "routing differs (near-tie): the backward comparison needs equal routing"
+    offs = host(bufs.offsets).astype(np.int64)
+    perm_src, inv_perm = host(bufs.perm_src)[:cfg.R], host(bufs.inv_perm)[:T * k]
+    qgu = [wts.gu(g) for g in range(G)]
+    qdn = [wts.dn(g) for g in range(G)]
+    dyv, xv = OF.bf16_value_from_bits(dy), OF.bf16_value_from_bits(x)
+    # combine backward on the GPU's D
+    cb = OBK.combine_backward(dyv, bf16_values_host(bufs.d), inv_perm, host(bufs.topk_w), T, k, 1)
+    dD = bf16_values_host(bb.dD)
+    assert np.array_equal(dD, cb["dD"])
+    Dv = bf16_values_host(bufs.d)
+    rows = inv_perm.reshape(T, k).astype(np.int64)
+    wb = H * 2.0 ** -23 * np.stack([np.sum(np.abs(dyv * Dv[rows[:, j]]), axis=1) for j in range(k)], 1)
+    assert (np.abs(host(bb.dw) - cb["dw"]) <= wb).all()
+    # dgrad down on the GPU's quantised dD
+    qd, sd = OQ.quant_1x128(dD)
+    assert np.array_equal(host(bb.dDq), qd) and np.array_equal(host(bb.dDs), sd)
+    dnT = [OG.transpose_blocks(q, s_) for q, s_ in qdn]
+    ref = OG.to_bf16(OG.grouped_dgrad(qd, sd, [q for q, _ in qdn], [s_ for _, s_ in qdn], offs))
+    bound = gemm_accumulation_bound(qd, sd, [q for q, _ in dnT], [s_ for _, s_ in dnT], offs, H)
+    assert_within_one_bf16_ulp(bf16_values_host(bb.dh), ref, f"{name} dh", bound)
+    # recomputed gate+up
+    ref = OG.to_bf16(OG.grouped_gemm(fwd["xq"][perm_src], fwd["xs"][perm_src], [q for q, _ in qgu],
+                                     [s_ for _, s_ in qgu], offs))
+    bound = gemm_accumulation_bound(fwd["xq"][perm_src], fwd["xs"][perm_src], [q for q, _ in qgu],
+                                    [s_ for _, s_ in qgu], offs, H)
+    gu = bf16_values_host(bb.gu)
+    assert_within_one_bf16_ulp(gu, ref, f"{name} gate+up recomputed", bound)
+    # SwiGLU backward on the GPU's GU and dh
+    r_dgu, r_h = OBK.swiglu_backward(gu, bf16_values_host(bb.dh), I)
+    dgu, h = bf16_values_host(bb.dgu), bf16_values_host(bb.h)
+    for got, r, what in ((dgu, r_dgu, "dGU"), (h, r_h, "h")):
+        assert (np.abs(got - r) <= bf16_ulp(np.maximum(np.abs(got), np.abs(r))) + 1e-30).all(), what
+    # dgrad gate+up on the GPU's quantised dGU, then the unpermute
+    qg, sg = OQ.quant_1x128(dgu)
+    assert np.array_equal(host(bb.dguq), qg) and np.array_equal(host(bb.dgus), sg)
+    guT = [OG.transpose_blocks(q, s_) for q, s_ in qgu]
+    ref = OG.to_bf16(OG.grouped_dgrad(qg, sg, [q for q, _ in qgu], [s_ for _, s_ in qgu], offs))
+    bound = gemm_accumulation_bound(qg, sg, [q for q, _ in guT], [s_ for _, s_ in guT], offs, 2 * I)
+    dxp = bf16_values_host(bb.dxp)
+    assert_within_one_bf16_ulp(dxp, ref, f"{name} dX", bound)
+    ref_dx, dx64 = OC.combine(dxp, inv_perm, np.ones((T, k), np.float32), T, k, dxp[T * k:T * k + T])
+    acc = (k + 1) * 2.0 ** -23 * (np.abs(dxp[rows]).sum(1) + np.abs(dxp[T * k:T * k + T]))
+    assert_within_one_bf16_ulp(bf16_values_host(bb.dx), ref_dx, f"{name} dx", acc)
+    # weight gradients on the GPU's 128x1 operands (themselves bit-exact)
+    pref = OQ.chunk_prefix(offs)
+    nch = int(pref[-1])
+    for (c_, s_, src, what) in ((bb.c_dD, bb.s_dD, dD, "dD"), (bb.c_h, bb.s_h, h, "h"),
+                                (bb.c_dgu, bb.s_dgu, dgu, "dGU"), (bb.c_x, bb.s_x, xv[perm_src], "x")):
+        qo, so = OQ.quant_128x1_grouped(src.astype(np.float32), offs)
+        ql, sl = _logical(host(c_), host(s_), nch)
+        assert np.array_equal(ql, qo) and np.array_equal(sl, so), what
+    for (cy, sy, ca, sa, dW, what) in ((bb.c_dD, bb.s_dD, bb.c_h, bb.s_h, bb.dW_dn, "dW_dn"),
+                                       (bb.c_dgu, bb.s_dgu, bb.c_x, bb.s_x, bb.dW_gu, "dW_gu")):
+        qy, sy_ = _logical(host(cy), host(sy), nch)
+        qa, sa_ = _logical(host(ca), host(sa), nch)
+        ref = OG.grouped_wgrad(qy, sy_, qa, sa_, pref)
+        got = host(dW).astype(np.float64)
+        bnd = _wgrad_bound(qy, sy_, qa, sa_, pref) + 1e-30
+        ratio = np.abs(got - ref) / bnd
+        if not (ratio <= 1).all():
+            g_, n_, k_ = np.unravel_index(int(np.argmax(ratio)), ratio.shape)
+            log(f"[layer bwd] {what}: {int((ratio > 1).sum())} elements over the bound; worst "
+                f"ratio {ratio.max():.3e} at group {g_} ({int(pref[g_ + 1] - pref[g_])} chunks) "
+                f"n {n_} k {k_}: got {got[g_, n_, k_]!r} ref {ref[g_, n_, k_]!r} bound {bnd[g_, n_, k_]!r}; "
+                f"nonfinite got {int((~np.isfinite(got)).sum())}")
+        assert (ratio <= 1).all(), what
+    # end to end against the oracle's own chain: the two chains requantise
+    # slightly different bf16 intermediates (GEMM accumulation order) to E4M3,
+    # so codes next to a rounding midpoint differ (one code step is 1/16 of an
+    # element); relative L2 within 5e-3
+    ref = OBK.expert_backward(dy, fwd, wts, x, T, k, I)
+    errs = dict(dx=rel_l2(bf16_values_host(bb.dx), ref["dx"]), dw=rel_l2(host(bb.dw), ref["dw"]),
+                dW_gu=rel_l2(host(bb.dW_gu), ref["dW_gu"]), dW_dn=rel_l2(host(bb.dW_dn), ref["dW_dn"]))
+    log(f"[layer bwd] {name}: end to end " + ", ".join(f"{k_} {v:.2e}" for k_, v in errs.items()))
+    assert max(errs.values()) <= 5e-3, errs

@@ -59,7 +59,7 @@ def _quant_dev(x_bits, offs, G, C):
     q = torch.zeros((cap, C, 128), dtype=torch.uint8, device="cuda")
     s = torch.zeros((cap, C), dtype=torch.float32, device="cuda")
     xb = torch.from_numpy(np.ascontiguousarray(x_bits).view(np.int16)).cuda().view(torch.bfloat16)
-    M.fp8_quant_128x1_grouped(xb, C, dev(offs.astype(np.int32)), G, Mt, C, q, s, cap)
+    M.fp8_quant_128x1_grouped(xb, C, None, dev(offs.astype(np.int32)), G, Mt, C, q, s, cap)
     return q, s, cap
 
 

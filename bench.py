@@ -12,9 +12,9 @@ Prints one JSON line (rank 0).  On the same weights it also reports: the
 decode batch (T=128, under "decode"), the standalone grouped GEMM over 256
 groups with Multinomial(65536) rows ("grouped_gemm") and the skewed-load
 layer (T=8192, Zipf(1.1) expert popularity, 100 steps of the bias update,
-"skewed") and the input gradients of the two expert GEMMs at T=16384 with
-their 128x128 weight-block transposes, and the two weight gradients
-("backward").
+"skewed"), the backward pieces of the two expert GEMMs at T=16384 (weight
+transposes, input and weight gradients: "backward") and the whole
+expert-path backward step ("backward_step").
 """
 from __future__ import annotations
 
@@ -261,6 +261,42 @@ def bench_backward(layer, T, reps=10, warmup=3):
     return out
 
 
+def bench_backward_step(layer, x, cfg, steps=3, warmup=1):
+    """The expert path's backward (MoELayer.backward) at T=16384 after a forward
+    of the same batch: combine backward, dgrad of down, the recomputed
+    gate+up, SwiGLU backward, dgrad of gate+up, unpermute and both weight
+    gradients; dy N(0,1) bf16 (synth.gen_dy).  The weight transposes are made
+    once per weight update (cached on the layer, timed under "backward").
+    Flops: 2RHI for each of dgrad-down and wgrad-down, 4RHI for each of the
+    recomputed gate+up, dgrad-gate+up and wgrad-gate+up (34.6 TFLOP)."""
+    import time
+    import numpy as np
+    import torch
+    import synth
+    dy = torch.from_numpy(synth.gen_dy(cfg).view(np.int16)).cuda().view(torch.bfloat16)
+    layer.forward(x)
+    layer.transpose_weights()
+    for _ in range(warmup):
+        layer.backward(dy, x)
+    torch.cuda.synchronize()
+    events = {}
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        layer.backward(dy, x, events=events)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / steps * 1e3
+    per = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in events.items()}
+    R = cfg.R
+    flop = 2.0 * R * cfg.H * cfg.I * (1 + 1 + 2 + 2 + 2)
+    out = {"workload": "expert-path backward, T=16384, V3 shapes", "ms_per_step": ms,
+           "tokens_per_s": cfg.T / (ms * 1e-3), "TFLOPS": flop / (ms * 1e-3) / 1e12,
+           "flop_per_step": flop, "per_stage_ms": per}
+    log(f"[bench] backward step: {ms:.3f} ms ({out['TFLOPS']:.0f} TFLOP/s); " +
+        ", ".join(f"{k} {v:.3f}" for k, v in per.items()))
+    del dy
+    return out
+
+
 # HBM traffic of the gate+up kernel at T=16384, from two rocprofv3 --pmc runs
 # (FETCH_SIZE, WRITE_SIZE) of this script, each scaled by the same counter on
 # the 1 GiB copy probe.  Valid only for the kernel source with this digest.
@@ -391,6 +427,7 @@ def main():
 
     gg = bench_grouped_gemm(layer)
     bwd = bench_backward(layer, cfg.T) if not args.no_backward else None
+    bstep = bench_backward_step(layer, x, cfg) if not args.no_backward else None
     skew = bench_skewed(layer, args.skewed_steps) if args.skewed_steps > 0 else None
 
     traffic = None
@@ -426,6 +463,7 @@ def main():
                    "per_kernel_ms": dper},
         "grouped_gemm": gg,
         "backward": bwd,
+        "backward_step": bstep,
         "skewed": skew,
         "copy_probe": cp,
     }

@@ -683,7 +683,12 @@ __global__ __launch_bounds__(WT, 1) void wide_gemm_kernel(GemmArgs args) {
       wait_lgkm0();
       barrier();
       if (wvalid) {
-        const int I = (int)args.I, hb = I >> 7;
+        // hb passes through an empty asm so that the per-row scale offsets
+        // below are computed here, not kept live across the K loop (they
+        // had cost a spilled VGPR whose reload waited for every copy)
+        const int I = (int)args.I;
+        int hb = I >> 7;
+        asm volatile("" : "+s"(hb));
         const uint32_t rows = (uint32_t)min(t.m1 - t.m0, WBM);
         const __amdgpu_buffer_rsrc_t rsc = out_rsrc(args.Hs + (int64_t)t.m0 * hb, rows * hb * 4);
 #pragma unroll

@@ -12,7 +12,7 @@ study note "DeepSeek-V3：671B 巨兽" (developer.aliyun.com/article/1776647),
 section 一 (规模), and the news.qq.com article on how V3 was built
 (news.qq.com/rain/a/20241229A05OQF00), section 架构 › DeepSeekMoE 架构.
 The expert intermediate width (2048), the 8-group / keep-4 group rule and the
-distributions are the definitions of the measured workloads (no page gives them).
+distributions define the measured workloads (the pages give them only in part).
 """
 from __future__ import annotations
 

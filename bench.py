@@ -300,9 +300,9 @@ def bench_backward_step(layer, x, cfg, steps=3, warmup=1):
 # HBM traffic of the gate+up kernel at T=16384, from two rocprofv3 --pmc runs
 # (FETCH_SIZE, WRITE_SIZE) of this script, each scaled by the same counter on
 # the 1 GiB copy probe.  Valid only for the kernel source with this digest.
-GATE_UP_TRAFFIC = {"gemm_src": "ed2ff2e925032502",
-                   # FETCH_SIZE 9,293,284 KiB x 2.000 + WRITE_SIZE 312,429 KiB x 1.000
-                   "bytes": 9293284 * 1024 * 2 + 312429 * 1024}
+GATE_UP_TRAFFIC = {"gemm_src": "38f0b00aa90fd45b",
+                   # FETCH_SIZE 9,393,070 KiB x 2.000 + WRITE_SIZE 311,488 KiB x 1.000
+                   "bytes": 9393070 * 1024 * 2 + 311488 * 1024}
 
 
 def bench_skewed(layer, steps=100):

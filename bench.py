@@ -262,12 +262,13 @@ def bench_backward(layer, T, reps=10, warmup=3):
 
 
 def bench_backward_step(layer, x, cfg, steps=3, warmup=1):
-    """The expert path's backward (MoELayer.backward) at T=16384 after a forward
-    of the same batch: combine backward, dgrad of down, the recomputed
-    gate+up, SwiGLU backward, dgrad of gate+up, unpermute and both weight
-    gradients; dy N(0,1) bf16 (synth.gen_dy).  The weight transposes are made
-    once per weight update (cached on the layer, timed under "backward").
-    Flops: 2RHI for each of dgrad-down and wgrad-down, 4RHI for each of the
+    """The layer's backward (MoELayer.backward) at T=16384 after a forward of
+    the same batch: combine backward, dgrad of down, the recomputed gate+up,
+    SwiGLU backward, dgrad of gate+up, unpermute, both weight gradients and
+    the router's backward (dx and the centroids' gradient); dy N(0,1) bf16
+    (synth.gen_dy).  The weight transposes are made once per weight update
+    (cached on the layer, timed under "backward").  Flops counted: the GEMMs
+    only, 2RHI for each of dgrad-down and wgrad-down, 4RHI for each of the
     recomputed gate+up, dgrad-gate+up and wgrad-gate+up (34.6 TFLOP)."""
     import time
     import numpy as np
@@ -288,7 +289,7 @@ def bench_backward_step(layer, x, cfg, steps=3, warmup=1):
     per = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in events.items()}
     R = cfg.R
     flop = 2.0 * R * cfg.H * cfg.I * (1 + 1 + 2 + 2 + 2)
-    out = {"workload": "expert-path backward, T=16384, V3 shapes", "ms_per_step": ms,
+    out = {"workload": "layer backward (experts + router), T=16384, V3 shapes", "ms_per_step": ms,
            "tokens_per_s": cfg.T / (ms * 1e-3), "TFLOPS": flop / (ms * 1e-3) / 1e12,
            "flop_per_step": flop, "per_stage_ms": per}
     log(f"[bench] backward step: {ms:.3f} ms ({out['TFLOPS']:.0f} TFLOP/s); " +

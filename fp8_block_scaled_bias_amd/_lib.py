@@ -41,6 +41,9 @@ SIGNATURES = {
     "moe_combine_backward": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i32, _i64, _i32, _vp, _vp,
                                             _vp]),
     "swiglu_backward": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp, _vp, _vp]),
+    "moe_router_backward": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i32, _i32,
+                                           _vp, _vp, _vp]),
+    "moe_router_dcentroids": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp]),
     "grouped_fp8_wgrad": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _vp, _i32, _i64, _i64, _i64,
                                          _vp, _vp]),
     "grouped_fp8_gemm": (ctypes.c_int, [_vp, _vp, _vp, _i64, _vp, _vp, _vp, _i32, _i64, _i64,
@@ -181,6 +184,19 @@ def moe_combine_backward(dy_bf16, inv_perm, topk_w, expert_out_bf16, T, k, H, n_
     return _call("moe_combine_backward", _dev(dy_bf16), _dev(inv_perm), _dev(topk_w),
                  _dev(expert_out_bf16), T, k, H, n_shared, _dev(d_expert_out_bf16), _dev(d_topk_w),
                  _stream(stream))
+
+
+def moe_router_backward(x_bf16, centroids, topk_idx, d_topk_w, inv_perm, dx_in_bf16, T, H, E, k,
+                        dx_out_bf16, dlogit_rows, stream=None):
+    return _call("moe_router_backward", _dev(x_bf16), _dev(centroids), _dev(topk_idx),
+                 _dev(d_topk_w), _dev(inv_perm), _dev(dx_in_bf16), T, H, E, k, _dev(dx_out_bf16),
+                 _dev(dlogit_rows), _stream(stream))
+
+
+def moe_router_dcentroids(x_bf16, perm_src, group_offsets, dlogit_rows, T, H, E, d_centroids,
+                          stream=None):
+    return _call("moe_router_dcentroids", _dev(x_bf16), _dev(perm_src), _dev(group_offsets),
+                 _dev(dlogit_rows), T, H, E, _dev(d_centroids), _stream(stream))
 
 
 def swiglu_backward(gu_bf16, dh_bf16, M, I, dgu_bf16, h_bf16, stream=None):

@@ -153,3 +153,174 @@ extern "C" int swiglu_backward(const void* gu_bf16, const void* dh_bf16, int64_t
       static_cast<uint16_t*>(dgu_bf16), static_cast<uint16_t*>(h_bf16));
   return check_launch("swiglu_backward");
 }
+
+// ---- router backward -----------------------------------------------------------
+// The gate weights are w_j = s_j / S over a token's k selected experts,
+// s_j = sigmoid(x . C[e_j]) (unbiased scores; the selection and the bias
+// carry no gradient: the bias only selects, news.qq.com article section
+// 无额外损耗的负载均衡; gating stays in FP32, section FP8 低精度训练), S = sum s_j:
+//   dlogit_j = (dw_j - sum_i dw_i w_i) / S * s_j (1 - s_j)
+//   dx[t]    = dx_in[t] + sum_j dlogit_j C[e_j]
+//   dC[e]    = sum over the rows r of expert e of dlogit(r) x[token(r)]
+// The logits are recomputed here in fp32 (one workgroup per token, fixed
+// summation order); dlogit is written in expert-row order (through
+// inv_perm) for the centroid gradient, which sums each expert's rows in
+// row order (one workgroup per expert and 2048 columns).
+namespace moe {
+namespace {
+
+constexpr int RB = 256;
+
+template <int KMAX>
+__global__ __launch_bounds__(RB) void router_backward_kernel(
+    const uint16_t* __restrict__ x, const float* __restrict__ C, const int32_t* __restrict__ idx,
+    const float* __restrict__ dw, const int32_t* __restrict__ inv_perm,
+    const uint16_t* __restrict__ dx_in, int64_t H, int k, uint16_t* __restrict__ dx_out,
+    float* __restrict__ dlogit_rows) {
+  __shared__ float s_part[RB / 64][KMAX];
+  __shared__ float s_dl[KMAX];
+  const int64_t t = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  int64_t e[KMAX];
+  float dot[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    e[j] = j < k ? idx[t * k + j] : 0;
+    dot[j] = 0.0f;
+  }
+  const uint16_t* xr = x + t * H;
+  for (int64_t c = (int64_t)tid * 8; c < H; c += RB * 8) {
+    float xv[8];
+    bf16x8_to_f32(*reinterpret_cast<const uint4*>(xr + c), xv);
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      if (j >= k) break;
+      const float4 c0 = *reinterpret_cast<const float4*>(C + e[j] * H + c);
+      const float4 c1 = *reinterpret_cast<const float4*>(C + e[j] * H + c + 4);
+      const float cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dot[j] = fmaf(xv[i], cv[i], dot[j]);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    float v = dot[j];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    if (lane == 0) s_part[wv][j] = v;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float s[KMAX], S = 0.0f;
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      if (j >= k) break;
+      const float l = (s_part[0][j] + s_part[1][j]) + (s_part[2][j] + s_part[3][j]);
+      s[j] = 1.0f / (1.0f + expf(-l));
+      S += s[j];
+    }
+    float m = 0.0f;
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      if (j >= k) break;
+      m = fmaf(dw[t * k + j], s[j] / S, m);
+    }
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      if (j >= k) break;
+      const float dl = (dw[t * k + j] - m) / S * s[j] * (1.0f - s[j]);
+      s_dl[j] = dl;
+      dlogit_rows[inv_perm[t * k + j]] = dl;
+    }
+  }
+  __syncthreads();
+  float dl[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) dl[j] = j < k ? s_dl[j] : 0.0f;
+  for (int64_t c = (int64_t)tid * 8; c < H; c += RB * 8) {
+    float o[8];
+    if (dx_in) bf16x8_to_f32(*reinterpret_cast<const uint4*>(dx_in + t * H + c), o);
+    else
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o[i] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      if (j >= k) break;
+      const float4 c0 = *reinterpret_cast<const float4*>(C + e[j] * H + c);
+      const float4 c1 = *reinterpret_cast<const float4*>(C + e[j] * H + c + 4);
+      const float cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o[i] = fmaf(dl[j], cv[i], o[i]);
+    }
+    *reinterpret_cast<uint4*>(dx_out + t * H + c) = f32_to_bf16x8(o);
+  }
+}
+
+constexpr int DC_COLS = RB * 8;
+
+__global__ __launch_bounds__(RB) void router_dcentroids_kernel(
+    const uint16_t* __restrict__ x, const int32_t* __restrict__ perm_src,
+    const int32_t* __restrict__ offs, const float* __restrict__ dlogit_rows, int64_t H,
+    float* __restrict__ dC) {
+  const int e = blockIdx.y;
+  const int64_t c = (int64_t)blockIdx.x * DC_COLS + threadIdx.x * 8;
+  if (c >= H) return;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const int r0 = offs[e], r1 = offs[e + 1];
+  for (int r = r0; r < r1; ++r) {
+    const float d = dlogit_rows[r];
+    float xv[8];
+    bf16x8_to_f32(*reinterpret_cast<const uint4*>(x + (int64_t)perm_src[r] * H + c), xv);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = fmaf(d, xv[i], acc[i]);
+  }
+  float* o = dC + (int64_t)e * H + c;
+  *reinterpret_cast<float4*>(o) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  *reinterpret_cast<float4*>(o + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+}
+
+}  // namespace
+}  // namespace moe
+
+extern "C" int moe_router_backward(const void* x_bf16, const float* centroids,
+                                   const int32_t* topk_idx, const float* d_topk_w,
+                                   const int32_t* inv_perm, const void* dx_in_bf16, int64_t T,
+                                   int64_t H, int32_t E, int32_t k, void* dx_out_bf16,
+                                   float* dlogit_rows, void* stream) {
+  clear_error();
+  MOE_INVALID(T >= 0 && T < (1ll << 31), "moe_router_backward: T=%lld out of range", (long long)T);
+  MOE_INVALID(k >= 1 && k <= 8, "moe_router_backward: k=%d must be in [1, 8]", (int)k);
+  MOE_INVALID(E >= k, "moe_router_backward: E=%d < k", (int)E);
+  MOE_INVALID(H > 0 && H % 8 == 0, "moe_router_backward: H=%lld must be a positive multiple of 8",
+              (long long)H);
+  if (T == 0) return MOE_OK;
+  MOE_INVALID(x_bf16 && centroids && topk_idx && d_topk_w && inv_perm && dx_out_bf16 && dlogit_rows,
+              "moe_router_backward: null pointer");
+  MOE_INVALID(((uintptr_t)x_bf16 & 15) == 0 && ((uintptr_t)centroids & 15) == 0 &&
+                  ((uintptr_t)dx_out_bf16 & 15) == 0 && ((uintptr_t)dx_in_bf16 & 15) == 0,
+              "moe_router_backward: x, centroids, dx_in and dx_out must be 16-byte aligned");
+  router_backward_kernel<8><<<dim3((unsigned)T), dim3(RB), 0, as_stream(stream)>>>(
+      static_cast<const uint16_t*>(x_bf16), centroids, topk_idx, d_topk_w, inv_perm,
+      static_cast<const uint16_t*>(dx_in_bf16), H, k, static_cast<uint16_t*>(dx_out_bf16),
+      dlogit_rows);
+  return check_launch("moe_router_backward");
+}
+
+extern "C" int moe_router_dcentroids(const void* x_bf16, const int32_t* perm_src,
+                                     const int32_t* group_offsets, const float* dlogit_rows,
+                                     int64_t T, int64_t H, int32_t E, float* d_centroids,
+                                     void* stream) {
+  clear_error();
+  MOE_INVALID(T >= 0 && T < (1ll << 31), "moe_router_dcentroids: T=%lld out of range", (long long)T);
+  MOE_INVALID(E >= 1 && E <= 65535, "moe_router_dcentroids: E=%d out of [1, 65535]", (int)E);
+  MOE_INVALID(H > 0 && H % 8 == 0, "moe_router_dcentroids: H=%lld must be a positive multiple of 8",
+              (long long)H);
+  MOE_INVALID(x_bf16 && perm_src && group_offsets && dlogit_rows && d_centroids,
+              "moe_router_dcentroids: null pointer");
+  MOE_INVALID(((uintptr_t)x_bf16 & 15) == 0 && ((uintptr_t)d_centroids & 15) == 0,
+              "moe_router_dcentroids: x and d_centroids must be 16-byte aligned");
+  router_dcentroids_kernel<<<dim3((unsigned)ceil_div(H, DC_COLS), (unsigned)E), dim3(RB), 0,
+                             as_stream(stream)>>>(static_cast<const uint16_t*>(x_bf16), perm_src,
+                                                  group_offsets, dlogit_rows, H, d_centroids);
+  return check_launch("moe_router_dcentroids");
+}

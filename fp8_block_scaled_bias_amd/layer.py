@@ -31,10 +31,11 @@ backward-for-input and backward-for-weights chunks, section 工程 › DualPipe
   6. moe_combine            dx = the sum of a token's rows of dX (unit weights)
   7. fp8_quant_128x1_grouped + grouped_fp8_wgrad       dW_dn = dD^T h,
                             dW_gu = dGU^T x (x gathered through the permutation)
+  8. moe_router_backward    dw -> the gate logits' gradient, dx += its part
+     moe_router_dcentroids  the centroids' gradient (the bias has none)
 
 The weight transposes (fp8_transpose_128x128) are cached on the layer and
-redone by transpose_weights() when the weights change.  The router's
-backward (from dw on) is not part of this path.
+redone by transpose_weights() when the weights change.
 
 torch is only used to hold device memory and to name the stream; every step
 runs in the library's HIP kernels.
@@ -136,6 +137,9 @@ class BackwardBuffers:
         self.s_x = torch.empty((c, H), dtype=f32, device=dev)
         self.dW_gu = torch.empty((s.G, 2 * I, H), dtype=f32, device=dev)
         self.dW_dn = torch.empty((s.G, H, I), dtype=f32, device=dev)
+        self.dx_total = torch.empty((T, H), dtype=bf, device=dev)
+        self.dlogit_rows = torch.empty((max(T * s.k, 1),), dtype=f32, device=dev)
+        self.dC = torch.empty((s.E, H), dtype=f32, device=dev)
 
 
 class MoELayer:
@@ -253,12 +257,13 @@ class MoELayer:
 
     def backward(self, dy_bf16: torch.Tensor, x_bf16: torch.Tensor, bufs: Buffers | None = None,
                  bwd: BackwardBuffers | None = None, stream=None, events: dict | None = None):
-        """Backward of the expert path for the output gradient dy, after a
-        forward of x on `bufs` (its routing, permutation, quantised x and D).
-        Returns the BackwardBuffers: dx (expert path), dw (gate weights),
-        dW_gu, dW_dn.  `events` as in forward, keys "combine_bwd", "dgrad_down",
-        "recompute_gate_up", "swiglu_bwd", "dgrad_gate_up", "unpermute",
-        "wgrad_down", "wgrad_gate_up"."""
+        """Backward of the layer for the output gradient dy, after a forward of
+        x on `bufs` (its routing, permutation, quantised x and D).  Returns the
+        BackwardBuffers: dx_total (the input gradient), dx (its expert-path
+        part), dw (gate weights), dC (centroids), dW_gu, dW_dn.  `events` as in
+        forward, keys "combine_bwd", "dgrad_down", "recompute_gate_up",
+        "swiglu_bwd", "dgrad_gate_up", "unpermute", "wgrad_down",
+        "wgrad_gate_up", "router_bwd"."""
         s = self.shape
         T = dy_bf16.shape[0]
         b = bufs or self.buffers(T)
@@ -308,6 +313,11 @@ class MoELayer:
                                       cap, st),
             L.grouped_fp8_wgrad(bb.c_dgu, bb.s_dgu, bb.c_x, bb.s_x, cap, b.offsets, G, R, 2 * I, H,
                                 bb.dW_gu, st)))
+        step("router_bwd", lambda: (
+            L.moe_router_backward(x_bf16, self.centroids, b.topk_idx, bb.dw, b.inv_perm, bb.dx, T,
+                                  H, s.E, k, bb.dx_total, bb.dlogit_rows, st),
+            L.moe_router_dcentroids(x_bf16, b.perm_src, b.offsets, bb.dlogit_rows, T, H, s.E,
+                                    bb.dC, st)))
         return bb
 
     def _forward_timed(self, x_bf16, b, stream, update_bias, gamma, fused, events):

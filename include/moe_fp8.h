@@ -283,6 +283,44 @@ int swiglu_backward(const void* gu_bf16, const void* dh_bf16, int64_t M, int64_t
                     void* dgu_bf16, void* h_bf16, void* stream);
 
 /*
+ * moe_router_backward - backward of the gate weights to the router's input and
+ * the per-expert logits (news.qq.com article: section 无额外损耗的负载均衡 - the
+ * bias only selects, so neither it nor the choice of experts has a gradient;
+ * section FP8 低精度训练 - the gating stays in FP32).
+ *
+ * For token t with selected experts e_j = topk_idx[t, j] and the unbiased
+ * scores s_j = sigmoid(x[t] . C[e_j]) recomputed here in fp32 (S = sum_j s_j,
+ * w_j = s_j / S, the forward's gate weights):
+ *   dlogit_j = (dw_j - sum_i dw_i w_i) / S * s_j * (1 - s_j)
+ *   dx_out[t, :] = bf16( dx_in[t, :] + sum_j dlogit_j * C[e_j, :] )   (fp32 sums)
+ *   dlogit_rows[inv_perm[t*k + j]] = dlogit_j   (expert-row order, for the
+ *                                                centroid gradient)
+ * x_bf16 [T, H]; centroids [E, H] fp32; topk_idx, d_topk_w, inv_perm [T*k];
+ * dx_in_bf16 [T, H] or NULL (then 0); dx_out_bf16 (out) [T, H] (may equal
+ * dx_in); dlogit_rows (out) [T*k] fp32.  Requirements: 1 <= k <= 8, k <= E,
+ * H % 8 == 0; x, centroids, dx_in, dx_out 16-byte aligned.
+ */
+int moe_router_backward(const void* x_bf16, const float* centroids, const int32_t* topk_idx,
+                        const float* d_topk_w, const int32_t* inv_perm, const void* dx_in_bf16,
+                        int64_t T, int64_t H, int32_t E, int32_t k, void* dx_out_bf16,
+                        float* dlogit_rows, void* stream);
+
+/*
+ * moe_router_dcentroids - gradient of the router centroids (same sections):
+ *   dC[e, :] = sum over rows r in [group_offsets[e], group_offsets[e+1]) of
+ *              dlogit_rows[r] * x[perm_src[r], :]
+ * summed in fp32 in row order (the rows of expert e are its tokens in
+ * ascending order, as moe_permute lays them out).
+ * x_bf16 [T, H]; perm_src, dlogit_rows: moe_permute's / moe_router_backward's;
+ * group_offsets [E+1] (the routed part of moe_permute's offsets, on the device);
+ * d_centroids (out) [E, H] fp32.  Requirements: H % 8 == 0, 1 <= E <= 65535;
+ * x and d_centroids 16-byte aligned.
+ */
+int moe_router_dcentroids(const void* x_bf16, const int32_t* perm_src,
+                          const int32_t* group_offsets, const float* dlogit_rows, int64_t T,
+                          int64_t H, int32_t E, float* d_centroids, void* stream);
+
+/*
  * grouped_fp8_gemm - block-scaled FP8 grouped GEMM with FP32 accumulation
  * (news.qq.com article, section FP8 低精度训练, items 细粒度量化 and
  * 提高累加精度).

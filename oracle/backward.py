@@ -20,7 +20,9 @@ kernel-level recipe; the reading used here (the GPU path's):
 
 Storage points mirror the GPU: bf16 after every elementwise step and GEMM,
 E4M3 with fp32 scales for GEMM operands, FP32 weight gradients.  The router's
-backward (dw onward) is not part of this path.
+backward (router_backward, below) takes the gate weights' gradient dw to the
+router's part of dx and to the centroids' gradient; layer_backward adds the
+two parts of dx (one bf16 rounding of their sum, as the GPU stores it).
 """
 from __future__ import annotations
 
@@ -104,3 +106,49 @@ def expert_backward(dy_bits, fwd: dict, wts, x_bits, T: int, k: int, I: int, n_s
     dW_gu = grouped_wgrad(qg, sg, qx, sx, pref).astype(np.float32).astype(np.float64)
     return dict(dx=dx, dw=cb["dw"], dW_gu=dW_gu, dW_dn=dW_dn, dD=dD, dh=dh, GU=GU, dGU=dGU,
                 h=h, dXp=dXp)
+
+
+# ---- router -----------------------------------------------------------------
+#
+# The gate weights are w_j = s_(e_j) / sum_i s_(e_i) over a token's selected
+# experts, s = sigmoid(x . C_e) (the unbiased scores; the bias and the choice of
+# experts carry no gradient - the bias only selects, section 无额外损耗的负载均衡
+# of the news.qq.com article; the gating stays in FP32, section FP8 低精度训练).
+# With S = sum_i s_(e_i):
+#   ds_(e_i)     = (dw_i - sum_j dw_j w_j) / S
+#   dlogit_(e_i) = ds_(e_i) s_(e_i) (1 - s_(e_i))
+#   dx[t]        = sum_i dlogit_i C[e_i]           (the router's part of dx)
+#   dC[e]        = sum over the (t, i) that chose e of dlogit_i x[t]
+
+
+def router_backward(x_bits, centroids, idx, dw):
+    """x bf16 bits [T, H]; centroids fp32 [E, H]; idx [T, k]; dw [T, k].
+    float64 throughout (logits recomputed exactly).  Returns dict(dlogit [T, k],
+    dx [T, H], dC [E, H])."""
+    x = bf16_value_from_bits(x_bits)
+    C = np.asarray(centroids, dtype=np.float32).astype(np.float64)
+    idx = np.asarray(idx, dtype=np.int64)
+    dw = np.asarray(dw, dtype=np.float64)
+    T, k = idx.shape
+    logit = np.einsum("th,tkh->tk", x, C[idx])
+    s = 1.0 / (1.0 + np.exp(-logit))
+    S = s.sum(axis=1, keepdims=True)
+    w = s / S
+    ds = (dw - np.sum(dw * w, axis=1, keepdims=True)) / S
+    dlogit = ds * s * (1.0 - s)
+    dx = np.einsum("tk,tkh->th", dlogit, C[idx])
+    dC = np.zeros_like(C)
+    np.add.at(dC, idx.reshape(-1), dlogit.reshape(-1, 1) * np.repeat(x, k, axis=0))
+    return dict(dlogit=dlogit, dx=dx, dC=dC)
+
+
+def layer_backward(dy_bits, fwd: dict, wts, x_bits, centroids, T: int, k: int, I: int,
+                   n_shared: int = 1):
+    """Whole-layer backward: expert_backward's results plus dlogit and dC from
+    router_backward on its dw, and dx_total = bf16(dx_expert + dx_router)."""
+    eb = expert_backward(dy_bits, fwd, wts, x_bits, T, k, I, n_shared)
+    rb = router_backward(x_bits, centroids, fwd["route"]["idx"], eb["dw"])
+    out = dict(eb)
+    out.update(dx_expert=eb["dx"], dx=bf16_round(eb["dx"] + rb["dx"]), dlogit=rb["dlogit"],
+               dC=rb["dC"])
+    return out

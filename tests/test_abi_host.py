@@ -101,6 +101,15 @@ def test_backward_elementwise_validation():
     assert g(out=None) == L.MOE_ERR_INVALID
     assert g(out=ctypes.c_void_p(4104)) == L.MOE_ERR_INVALID and "aligned" in L.last_error()
     assert g(M=0, out=None) == L.MOE_OK
+    def r(T=4, H=256, E=16, k=4, dx=FAKE):
+        return rc("moe_router_backward", FAKE, FAKE, FAKE, FAKE, FAKE, None, T, H, E, k, dx, FAKE, None)
+    assert r(k=9) == L.MOE_ERR_INVALID and r(E=2) == L.MOE_ERR_INVALID
+    assert r(H=100) == L.MOE_ERR_INVALID and r(dx=None) == L.MOE_ERR_INVALID
+    assert r(dx=ctypes.c_void_p(4104)) == L.MOE_ERR_INVALID and "aligned" in L.last_error()
+    assert r(T=0, dx=None) == L.MOE_OK
+    def d(E=16, H=256, out=FAKE):
+        return rc("moe_router_dcentroids", FAKE, FAKE, FAKE, FAKE, 4, H, E, out, None)
+    assert d(E=0) == L.MOE_ERR_INVALID and d(H=12) == L.MOE_ERR_INVALID and d(out=None) == L.MOE_ERR_INVALID
 
 
 def test_gemm_validation():

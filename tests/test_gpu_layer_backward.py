@@ -5,13 +5,19 @@
   bound H * 2^-23 * sum |dy D|;
 * swiglu_backward: dg, du and h within one bf16 ulp of the FP64 values (the
   GPU evaluates in fp32, then rounds once to bf16);
+* moe_router_backward / moe_router_dcentroids: dlogit against the oracle's
+  float64 router backward within 2^-14 of the token's gradient scale (the
+  GPU recomputes the logits in fp32); dx and dC against the exact sums of
+  the GPU's own dlogit, within one bf16 ulp plus the fp32 accumulation bound
+  (dx) and within the fp32 accumulation bound (dC);
 * MoELayer.backward on the tiny and mid configs: every stage against the
   oracle applied to the GPU's own inputs to that stage (dD, every E4M3 code
   and scale, both operand layouts bit-exact; GEMM outputs within the grouped
   GEMM's derived bound plus one bf16 rounding; SwiGLU backward within one
-  bf16 ulp; weight gradients within the wgrad bound), then dx, dw, dW_gu and
-  dW_dn against the oracle's independent chain (oracle.backward after
-  oracle.layer) within relative L2 5e-3.
+  bf16 ulp; weight gradients within the wgrad bound; the router stage as
+  above), then dx, dw, dC, dW_gu and dW_dn against the oracle's independent
+  chain (oracle.backward.layer_backward after oracle.layer) within relative
+  L2 5e-3.
 """
 import numpy as np
 import pytest
@@ -68,6 +74,87 @@ def test_swiglu_backward_kernel(M_, I):
     for got, ref, what in ((bf16_values_host(dgu), r_dgu, "dgu"), (bf16_values_host(h), r_h, "h")):
         d = np.abs(got - ref)
         assert (d <= bf16_ulp(np.maximum(np.abs(got), np.abs(ref))) + 1e-30).all(), what
+
+
+def _expert_rows(idx, E):
+    """perm_src, inv_perm [T*k] and offsets [E+1] in moe_permute's layout: rows
+    grouped by expert, each expert's tokens in ascending order."""
+    T, k = idx.shape
+    perm_src, inv_perm, offs = [], np.zeros(T * k, np.int32), [0]
+    for e in range(E):
+        for t in range(T):
+            for j in range(k):
+                if idx[t, j] == e:
+                    inv_perm[t * k + j] = len(perm_src)
+                    perm_src.append(t)
+        offs.append(len(perm_src))
+    return np.array(perm_src, np.int32), inv_perm, np.array(offs, np.int32)
+
+
+def check_router_stage(xbits, C, idx, dw32, inv_perm, perm_src, offs, dx_in, dl_rows, dx_out,
+                       dC, label):
+    """dl_rows (fp32 [T*k], expert-row order), dx_out (bf16 values), dC (fp32)
+    from the GPU; dx_in (bf16 values or None) and the rest its inputs."""
+    T, k = idx.shape
+    E = len(offs) - 1
+    xv = OF.bf16_value_from_bits(xbits)
+    C64 = np.asarray(C, np.float32).astype(np.float64)
+    ref = OBK.router_backward(xbits, C, idx, dw32)
+    dl = np.asarray(dl_rows, np.float64)[inv_perm.astype(np.int64)].reshape(T, k)
+    # dlogit: the GPU's fp32 logits are within ~1e-6 relative of the exact
+    # ones; dlogit moves by at most the token's gradient scale times that
+    s = 1.0 / (1.0 + np.exp(-np.einsum("th,tkh->tk", xv, C64[idx])))
+    S = s.sum(1, keepdims=True)
+    dw64 = np.asarray(dw32, np.float64)
+    scale = (np.abs(dw64).max(1, keepdims=True) + np.sum(np.abs(dw64) * s / S, 1, keepdims=True)) / S
+    err = np.abs(dl - ref["dlogit"])
+    log(f"[{label}] dlogit: max |err| / scale {float((err / scale).max()):.2e}")
+    assert (err <= 2.0 ** -14 * scale).all(), label
+    # dx from the GPU's own dlogit: exact sum, one bf16 rounding, fp32 fmas
+    base = np.zeros((T, C64.shape[1])) if dx_in is None else np.asarray(dx_in, np.float64)
+    terms = dl[:, :, None] * C64[idx]
+    exact = base + terms.sum(1)
+    acc = (k + 1) * 2.0 ** -23 * (np.abs(base) + np.abs(terms).sum(1))
+    assert_within_one_bf16_ulp(dx_out, exact, f"{label} dx", acc)
+    # dC: each expert's rows in row order, fp32 fmas
+    dC = np.asarray(dC, np.float64)
+    dlr = np.asarray(dl_rows, np.float64)
+    for e in range(E):
+        r0, r1 = int(offs[e]), int(offs[e + 1])
+        t_ = perm_src[r0:r1].astype(np.int64)
+        prod = dlr[r0:r1, None] * xv[t_]
+        ex = prod.sum(0)
+        bnd = (r1 - r0 + 1) * 2.0 ** -24 * np.abs(prod).sum(0)
+        assert (np.abs(dC[e] - ex) <= bnd).all(), f"{label} dC expert {e}"
+    assert rel_l2(dC, ref["dC"]) <= 1e-4, (label, rel_l2(dC, ref["dC"]))
+
+
+@pytest.mark.parametrize("T,H,E,k,mode", [(37, 1024, 64, 8, "dx_in"), (5, 256, 16, 3, "none"),
+                                          (64, 7168, 256, 8, "in_place")])
+def test_router_backward_kernel(T, H, E, k, mode):
+    rng = np.random.default_rng([T, H, E, k])
+    xbits = synth.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    C = (rng.standard_normal((E, H)) * 0.02).astype(np.float32)
+    idx = np.sort(np.stack([rng.choice(E, k, replace=False) for _ in range(T)]), 1).astype(np.int32)
+    dw = rng.standard_normal((T, k)).astype(np.float32)
+    perm_src, inv_perm, offs = _expert_rows(idx, E)
+    log(f"[router bwd] T={T} H={H} E={E} k={k} {mode}; experts with no rows: "
+        f"{int((np.diff(offs) == 0).sum())}")
+    dx_in = None if mode == "none" else synth.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    x_d, C_d = bf16_dev(xbits), dev(C)
+    dx_in_d = None if dx_in is None else bf16_dev(dx_in)
+    dx_out = dx_in_d if mode == "in_place" else torch.full((T, H), float("nan"), dtype=torch.bfloat16,
+                                                          device="cuda")
+    dl_rows = torch.full((T * k,), float("nan"), dtype=torch.float32, device="cuda")
+    dC = torch.full((E, H), float("nan"), dtype=torch.float32, device="cuda")
+    M.moe_router_backward(x_d, C_d, dev(idx), dev(dw), dev(inv_perm), dx_in_d, T, H, E, k, dx_out,
+                          dl_rows)
+    M.moe_router_dcentroids(x_d, dev(perm_src), dev(offs), dl_rows, T, H, E, dC)
+    torch.cuda.synchronize()
+    check_router_stage(xbits, C, idx, dw, inv_perm, perm_src, offs,
+                       None if dx_in is None else OF.bf16_value_from_bits(dx_in), host(dl_rows),
+                       bf16_values_host(dx_out), host(dC), f"router bwd T={T}")
+    assert not host(dC)[np.diff(offs) == 0].any()
 
 
 def _logical(c, sc, nch):
@@ -177,12 +264,19 @@ def test_layer_backward_small(name):
                 f"n {n_} k {k_}: got {got[g_, n_, k_]!r} ref {ref[g_, n_, k_]!r} bound {bnd[g_, n_, k_]!r}; "
                 f"nonfinite got {int((~np.isfinite(got)).sum())}")
         assert (ratio <= 1).all(), what
+    # the router: on the GPU's own dw, routing and expert-path dx
+    offs_r = offs[:cfg.E + 1]
+    check_router_stage(x, C, host(bufs.topk_idx).reshape(T, k), host(bb.dw), inv_perm,
+                       perm_src, offs_r, bf16_values_host(bb.dx), host(bb.dlogit_rows)[:T * k],
+                       bf16_values_host(bb.dx_total), host(bb.dC), f"{name} router")
     # end to end against the oracle's own chain: the two chains requantise
     # slightly different bf16 intermediates (GEMM accumulation order) to E4M3,
     # so codes next to a rounding midpoint differ (one code step is 1/16 of an
     # element); relative L2 within 5e-3
-    ref = OBK.expert_backward(dy, fwd, wts, x, T, k, I)
-    errs = dict(dx=rel_l2(bf16_values_host(bb.dx), ref["dx"]), dw=rel_l2(host(bb.dw), ref["dw"]),
+    ref = OBK.layer_backward(dy, fwd, wts, x, C, T, k, I)
+    errs = dict(dx=rel_l2(bf16_values_host(bb.dx_total), ref["dx"]),
+                dx_expert=rel_l2(bf16_values_host(bb.dx), ref["dx_expert"]),
+                dw=rel_l2(host(bb.dw), ref["dw"]), dC=rel_l2(host(bb.dC), ref["dC"]),
                 dW_gu=rel_l2(host(bb.dW_gu), ref["dW_gu"]), dW_dn=rel_l2(host(bb.dW_dn), ref["dW_dn"]))
     log(f"[layer bwd] {name}: end to end " + ", ".join(f"{k_} {v:.2e}" for k_, v in errs.items()))
     assert max(errs.values()) <= 5e-3, errs

@@ -274,11 +274,13 @@ def test_swiglu_backward_is_the_derivative_of_swiglu():
     assert not dgu[0, I:].any()
 
 
-def test_expert_backward_close_to_float64_autograd_tiny():
+def test_layer_backward_close_to_float64_autograd_tiny():
     """The FP8 composition against torch float64 autograd through the same forward
     with every quantisation taken as identity (the dequantised x and weights, h
-    unquantised): they differ by E4M3 rounding only; a transposed product, a
-    wrong permutation or a missing scale would be off by O(1)."""
+    unquantised) and the router's gate weights computed from x and C with the
+    selection held fixed: they differ by E4M3 rounding only; a transposed
+    product, a wrong permutation, a missing scale or a dropped router term
+    would be off by O(1)."""
     import torch
     cfg = synth.TINY
     x = synth.gen_x(cfg)
@@ -287,14 +289,18 @@ def test_expert_backward_close_to_float64_autograd_tiny():
                            lambda e: synth.gen_expert_weight(cfg, "dn", e))
     fwd = LY.layer(x, c, b, wts, cfg.n_group, cfg.topk_group, cfg.k, cfg.I)
     dy = synth.gen_dy(cfg)
-    bw = OB.expert_backward(dy, fwd, wts, x, cfg.T, cfg.k, cfg.I)
+    bw = OB.layer_backward(dy, fwd, wts, x, c, cfg.T, cfg.k, cfg.I)
     T, k, I, G = cfg.T, cfg.k, cfg.I, cfg.E + 1
     offs = np.asarray(fwd["offsets"], dtype=np.int64)
     t64 = lambda a: torch.tensor(np.asarray(a, dtype=np.float64))
     A = t64(Q.dequant_1x128(fwd["xq"], fwd["xs"])[fwd["perm_src"]]).requires_grad_()
     Wg = [t64(Q.dequant_128x128(*wts.gu(g))).requires_grad_() for g in range(G)]
     Wd = [t64(Q.dequant_128x128(*wts.dn(g))).requires_grad_() for g in range(G)]
-    w = t64(fwd["route"]["w32"]).requires_grad_()
+    xr = t64(F.bf16_value_from_bits(x)).requires_grad_()
+    Cr = t64(c).requires_grad_()
+    idx = torch.tensor(np.asarray(fwd["route"]["idx"], dtype=np.int64))
+    sc = torch.sigmoid((xr[:, None, :] * Cr[idx]).sum(-1))
+    w = sc / sc.sum(1, keepdim=True)
     Ds = []
     for g in range(G):
         a = A[offs[g]:offs[g + 1]]
@@ -305,12 +311,57 @@ def test_expert_backward_close_to_float64_autograd_tiny():
     rows = torch.tensor(np.asarray(fwd["inv_perm"], dtype=np.int64).reshape(T, k))
     y = (w[:, :, None] * D[rows]).sum(1) + D[T * k:]
     dyv = t64(F.bf16_value_from_bits(dy))
+    w.retain_grad()
     (y * dyv).sum().backward()
-    dx_ref = torch.zeros((T, cfg.H), dtype=torch.float64).index_add_(
+    dx_exp = torch.zeros((T, cfg.H), dtype=torch.float64).index_add_(
         0, torch.tensor(np.asarray(fwd["perm_src"], dtype=np.int64)), A.grad).numpy()
     rel = lambda a, r: float(np.linalg.norm(a - r) / np.linalg.norm(r))
-    errs = dict(dx=rel(bw["dx"], dx_ref), dw=rel(bw["dw"], w.grad.numpy()),
+    errs = dict(dx_expert=rel(bw["dx_expert"], dx_exp), dx=rel(bw["dx"], dx_exp + xr.grad.numpy()),
+                dw=rel(bw["dw"], w.grad.numpy()), dC=rel(bw["dC"], Cr.grad.numpy()),
                 dW_gu=rel(bw["dW_gu"], np.stack([W.grad.numpy() for W in Wg])),
                 dW_dn=rel(bw["dW_dn"], np.stack([W.grad.numpy() for W in Wd])))
     print(errs)
     assert max(errs.values()) < 0.08, errs
+    # the router's part of dx is a few per cent of dx here: check it on its own
+    # (a dropped term reads 1, a flipped sign 2; the rest is the bf16 rounding
+    # of the sum and the E4M3 error in dw)
+    err_r = rel(bw["dx"] - bw["dx_expert"], xr.grad.numpy())
+    print("router part of dx", err_r)
+    assert err_r < 0.25, err_r
+
+
+def test_router_backward_is_the_derivative_of_the_gate_weights():
+    """With the selection held fixed, L = <dw, w(x, C)> for the normalised sigmoid
+    weights of oracle.route; finite differences in x and in C."""
+    from oracle import route as OR
+    rng = np.random.default_rng(41)
+    T, H, E, k = 6, 32, 16, 4
+    xv = (rng.standard_normal((T, H)) * 0.5).astype(np.float32)
+    xb = synth.f32_to_bf16_bits(xv)
+    C = (rng.standard_normal((E, H)) * 0.3).astype(np.float32)
+    idx = np.stack([rng.choice(E, k, replace=False) for _ in range(T)])
+    dw = rng.standard_normal((T, k))
+    rb = OB.router_backward(xb, C, idx, dw)
+
+    def loss(xm, Cm):
+        s = 1.0 / (1.0 + np.exp(-np.einsum("th,tkh->tk", xm, Cm[idx])))
+        return float(np.sum(dw * s / s.sum(1, keepdims=True)))
+    x64, C64 = F.bf16_value_from_bits(xb), C.astype(np.float64)
+    eps = 1e-6
+    for (t, h) in [(0, 0), (3, 17), (5, 31)]:
+        xp, xm = x64.copy(), x64.copy()
+        xp[t, h] += eps
+        xm[t, h] -= eps
+        assert abs((loss(xp, C64) - loss(xm, C64)) / (2 * eps) - rb["dx"][t, h]) < 1e-7
+    for (e, h) in [(int(idx[0, 0]), 3), (int(idx[4, 2]), 30)]:
+        Cp, Cm = C64.copy(), C64.copy()
+        Cp[e, h] += eps
+        Cm[e, h] -= eps
+        assert abs((loss(x64, Cp) - loss(x64, Cm)) / (2 * eps) - rb["dC"][e, h]) < 1e-7
+    unused = np.setdiff1d(np.arange(E), idx)
+    assert not rb["dC"][unused].any()
+    # the recomputed scores are the oracle router's
+    s, _ = OR.router_scores(xb, C, np.zeros(E, np.float32))
+    np.testing.assert_allclose(
+        rb["dlogit"], (dw - np.sum(dw * (s[np.arange(T)[:, None], idx] / s[np.arange(T)[:, None], idx].sum(1, keepdims=True)), 1, keepdims=True))
+        / s[np.arange(T)[:, None], idx].sum(1, keepdims=True) * s[np.arange(T)[:, None], idx] * (1 - s[np.arange(T)[:, None], idx]), rtol=1e-12)

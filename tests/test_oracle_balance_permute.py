@@ -73,3 +73,87 @@ def test_permute_empty_experts_and_no_shared():
     off, ps, inv = PM.permute(idx, 6, 0)
     assert off.tolist() == [0, 0, 0, 0, 4, 4, 4]
     assert ps.tolist() == [0, 0, 1, 1] and inv.tolist() == [0, 1, 2, 3]
+
+
+# ---- sequence-wise balance statistic ----------------------------------------
+
+def _scores_and_choice(T, E, k, seed):
+    rng = np.random.default_rng(seed)
+    s = 1.0 / (1.0 + np.exp(-rng.standard_normal((T, E))))
+    idx = np.sort(np.stack([rng.choice(E, k, replace=False) for _ in range(T)]), 1)
+    return s, idx
+
+
+def test_seq_balance_python_loop():
+    """Per sequence, expert by expert, in plain loops."""
+    T, E, k, L, alpha = 11, 8, 3, 4, 0.25
+    s, idx = _scores_and_choice(T, E, k, 3)
+    st = BL.seq_balance(s, idx, L, alpha)
+    starts = list(range(0, T, L))
+    assert st["loss"].shape == (len(starts),)
+    for b, t0 in enumerate(starts):
+        toks = range(t0, min(T, t0 + L))
+        n = len(toks)
+        tot = 0.0
+        for e in range(E):
+            cnt = sum(1 for t in toks for j in range(k) if idx[t, j] == e)
+            pe = sum(s[t, e] / sum(s[t, i] for i in range(E)) for t in toks) / n
+            fe = E * cnt / (k * n)
+            assert st["f"][b, e] == pytest.approx(fe, rel=1e-15)
+            assert st["P"][b, e] == pytest.approx(pe, rel=1e-13)
+            tot += fe * pe
+        assert st["loss"][b] == pytest.approx(alpha * tot, rel=1e-13)
+
+
+def test_seq_balance_closed_forms():
+    T, E, k, L = 24, 16, 4, 8
+    _, idx = _scores_and_choice(T, E, k, 5)
+    # equal scores: P = 1/E and sum f = E, so the loss is alpha whatever the choice
+    st = BL.seq_balance(np.full((T, E), 0.37), idx, L, 1e-4)
+    np.testing.assert_allclose(st["loss"], 1e-4, rtol=1e-14)
+    np.testing.assert_allclose(st["f"].sum(1), E, rtol=1e-14)
+    # every token picks the same k experts with score a, the others score c:
+    # loss = alpha E a / (k a + (E - k) c)
+    a, c = 0.9, 0.2
+    chosen = np.array([1, 5, 6, 11])
+    s = np.full((T, E), c)
+    s[:, chosen] = a
+    st = BL.seq_balance(s, np.tile(chosen, (T, 1)), L, 1.0)
+    np.testing.assert_allclose(st["loss"], E * a / (k * a + (E - k) * c), rtol=1e-14)
+    assert not st["f"][:, np.setdiff1d(np.arange(E), chosen)].any()
+
+
+def test_seq_balance_invariances():
+    T, E, k, L = 30, 16, 4, 8
+    s, idx = _scores_and_choice(T, E, k, 9)
+    st = BL.seq_balance(s, idx, L)
+    # tokens reordered inside each sequence: same statistic
+    perm = np.concatenate([np.random.default_rng(1).permutation(np.arange(t0, min(T, t0 + L)))
+                           for t0 in range(0, T, L)])
+    st2 = BL.seq_balance(s[perm], idx[perm], L)
+    for key in ("f", "P", "loss"):
+        np.testing.assert_allclose(st2[key], st[key], rtol=1e-13)
+    # the ragged last sequence (6 tokens) equals that sequence on its own
+    last = BL.seq_balance(s[24:], idx[24:], 6)
+    np.testing.assert_allclose(st["loss"][-1], last["loss"][0], rtol=1e-14)
+    # scores scaled per token: s' and so the statistic are unchanged
+    st3 = BL.seq_balance(s * np.linspace(0.5, 2.0, T)[:, None], idx, L)
+    np.testing.assert_allclose(st3["loss"], st["loss"], rtol=1e-13)
+
+
+def test_seq_balance_grad_is_the_derivative():
+    """Central differences of the summed loss in each logit, selection fixed."""
+    T, E, k, L = 10, 8, 2, 4
+    rng = np.random.default_rng(17)
+    logit = rng.standard_normal((T, E))
+    idx = np.sort(np.stack([rng.choice(E, k, replace=False) for _ in range(T)]), 1)
+    sig = lambda z: 1.0 / (1.0 + np.exp(-z))
+    g = BL.seq_balance_grad_logits(sig(logit), idx, L, 0.5)
+    eps = 1e-6
+    for (t, e) in [(0, 0), (3, 5), (9, 7), (8, 2)]:
+        lp, lm = logit.copy(), logit.copy()
+        lp[t, e] += eps
+        lm[t, e] -= eps
+        fd = (BL.seq_balance(sig(lp), idx, L, 0.5)["loss"].sum()
+              - BL.seq_balance(sig(lm), idx, L, 0.5)["loss"].sum()) / (2 * eps)
+        assert abs(fd - g[t, e]) < 1e-9, (t, e, fd, g[t, e])

@@ -306,6 +306,36 @@ GATE_UP_TRAFFIC = {"gemm_src": "38f0b00aa90fd45b",
                    "bytes": 9393070 * 1024 * 2 + 311488 * 1024}
 
 
+def bench_seq_balance(layer, x, cfg, seq_len=4096, steps=10, warmup=2):
+    """The layer forward with the sequence-wise balance statistic (sequences
+    of seq_len tokens): per-step time, the router with its score output and
+    the statistic itself (HIP events on the launch stream, mean over steps).
+    The statistic reads T*E fp32 scores, T sums and T*k choices."""
+    import time
+    import numpy as np
+    import torch
+    for _ in range(warmup):
+        layer.forward(x, seq_len=seq_len, update_bias=True)
+    torch.cuda.synchronize()
+    events = {}
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        layer.forward(x, seq_len=seq_len, update_bias=True, events=events)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / steps * 1e3
+    per = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in events.items()}
+    nbytes = cfg.T * cfg.E * 4 + cfg.T * 4 + cfg.T * cfg.k * 4
+    out = {"workload": f"layer forward with the sequence-wise balance statistic, T={cfg.T}, "
+                       f"sequences of {seq_len}", "ms_per_step": ms,
+           "route_with_scores_ms": per["route"], "seq_balance_ms": per["seq_balance"],
+           "seq_balance_bytes": nbytes,
+           "seq_balance_GB_s": nbytes / (per["seq_balance"] * 1e-3) / 1e9,
+           "loss": layer.buffers(cfg.T).seq_loss.cpu().tolist()}
+    log(f"[bench] seq balance: step {ms:.3f} ms, route+scores {per['route']:.3f} ms, "
+        f"statistic {per['seq_balance']:.4f} ms, loss {out['loss']}")
+    return out
+
+
 def bench_skewed(layer, steps=100):
     """Skewed-load layer: T=8192 at V3 shapes, router centroids with
     Zipf(1.1)-scaled expert rows (stored fit), bias starting at 0, `steps`
@@ -430,6 +460,7 @@ def main():
     bwd = bench_backward(layer, cfg.T) if not args.no_backward else None
     bstep = bench_backward_step(layer, x, cfg) if not args.no_backward else None
     skew = bench_skewed(layer, args.skewed_steps) if args.skewed_steps > 0 else None
+    seqb = bench_seq_balance(layer, x, cfg)
 
     traffic = None
     if GATE_UP_TRAFFIC and GATE_UP_TRAFFIC["gemm_src"] == gemm_source_digest():
@@ -466,6 +497,7 @@ def main():
         "backward": bwd,
         "backward_step": bstep,
         "skewed": skew,
+        "seq_balance": seqb,
         "copy_probe": cp,
     }
     if not args.no_cpu_baseline:

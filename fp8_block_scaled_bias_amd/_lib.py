@@ -29,6 +29,11 @@ SIGNATURES = {
     "moe_route_workspace_bytes": (_sz, [_i64, _i64, _i32]),
     "moe_route": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _i32, _i32, _i32, _i32,
                                  _vp, _vp, _vp, _vp, _sz, _vp]),
+    "moe_route_scores": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _i32, _i32, _i32, _i32,
+                                        _vp, _vp, _vp, _vp, _sz, _vp, _vp, _vp]),
+    "moe_seq_balance_workspace_bytes": (_sz, [_i64, _i32, _i64]),
+    "moe_seq_balance": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i32, _i32, _i64, _f32, _vp, _vp, _vp,
+                                       _vp, _sz, _vp]),
     "moe_bias_update": (ctypes.c_int, [_vp, _vp, _i32, _f32, _vp]),
     "moe_permute_workspace_bytes": (_sz, [_i64, _i32, _i32]),
     "moe_permute": (ctypes.c_int, [_vp, _vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp,
@@ -138,6 +143,24 @@ def moe_route(x_bf16, T, H, centroids, bias, E, n_group, topk_group, k,
     return _call("moe_route", _dev(x_bf16), T, H, _dev(centroids), _dev(bias), E, n_group,
                  topk_group, k, _dev(topk_idx), _dev(topk_w), _dev(expert_counts),
                  _dev(workspace), workspace_bytes, _stream(stream))
+
+
+def moe_route_scores(x_bf16, T, H, centroids, bias, E, n_group, topk_group, k, topk_idx, topk_w,
+                     expert_counts, workspace, workspace_bytes, scores, score_sums, stream=None):
+    return _call("moe_route_scores", _dev(x_bf16), T, H, _dev(centroids), _dev(bias), E, n_group,
+                 topk_group, k, _dev(topk_idx), _dev(topk_w), _dev(expert_counts),
+                 _dev(workspace), workspace_bytes, _dev(scores), _dev(score_sums), _stream(stream))
+
+
+def moe_seq_balance_workspace_bytes(T, E, seq_len) -> int:
+    return int(lib().moe_seq_balance_workspace_bytes(T, E, seq_len))
+
+
+def moe_seq_balance(scores, score_sums, topk_idx, T, E, k, seq_len, alpha, f_out, p_out, loss_out,
+                    workspace, workspace_bytes, stream=None):
+    return _call("moe_seq_balance", _dev(scores), _dev(score_sums), _dev(topk_idx), T, E, k,
+                 seq_len, alpha, _dev(f_out), _dev(p_out), _dev(loss_out), _dev(workspace),
+                 workspace_bytes, _stream(stream))
 
 
 def moe_bias_update(expert_counts, bias, E, gamma, stream=None):

@@ -316,7 +316,8 @@ __device__ __forceinline__ bool beats(float v, int e, float ov, int oe) {
 __global__ __launch_bounds__(256) void router_select_kernel(
     const float* __restrict__ part, int KS, int64_t T, const float* __restrict__ bias, int E,
     int n_group, int topk_group, int k, int lpg, int32_t* __restrict__ topk_idx,
-    float* __restrict__ topk_w, int32_t* __restrict__ counts) {
+    float* __restrict__ topk_w, int32_t* __restrict__ counts, float* __restrict__ scores,
+    float* __restrict__ score_sums) {
   __shared__ int hist[256];
   for (int i = threadIdx.x; i < 256; i += 256) hist[i] = 0;
   __syncthreads();
@@ -346,6 +347,16 @@ __global__ __launch_bounds__(256) void router_select_kernel(
     for (int i = 0; i < 4; ++i) {
       s[i] = 1.0f / (1.0f + expf(-lg[i]));
       sb[i] = active ? s[i] + b[i] : -INFINITY;
+    }
+    if (scores) {  // every routed expert's unbiased score, and their sum
+      float ls = 0.f;
+      if (active) {
+        *reinterpret_cast<float4*>(scores + t * E + ebase) = make_float4(s[0], s[1], s[2], s[3]);
+        ls = (s[0] + s[1]) + (s[2] + s[3]);
+      }
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) ls += __shfl_xor(ls, o, 64);
+      if (lane == 0) score_sums[t] = ls;
     }
     // top-2 of this lane's 4 biased scores, then of the group's lanes
     float t1 = fmaxf(sb[0], sb[1]), t2 = fminf(sb[0], sb[1]);
@@ -516,11 +527,12 @@ extern "C" size_t moe_route_workspace_bytes(int64_t T, int64_t H, int32_t E) {
   return route_ws_partials(sp, T, E) + (sp.wide ? (size_t)3 * E * H * sizeof(uint16_t) : 0);
 }
 
-extern "C" int moe_route(const void* x_bf16, int64_t T, int64_t H, const float* centroids,
-                         const float* bias, int32_t E, int32_t n_group, int32_t topk_group,
-                         int32_t k, int32_t* topk_idx, float* topk_w, int32_t* expert_counts,
-                         void* workspace, size_t workspace_bytes, void* stream) {
-  clear_error();
+namespace {
+
+int route_impl(const void* x_bf16, int64_t T, int64_t H, const float* centroids,
+               const float* bias, int32_t E, int32_t n_group, int32_t topk_group, int32_t k,
+               int32_t* topk_idx, float* topk_w, int32_t* expert_counts, void* workspace,
+               size_t workspace_bytes, float* scores, float* score_sums, void* stream) {
   MOE_INVALID(T >= 0, "moe_route: T=%lld < 0", (long long)T);
   MOE_INVALID(H > 0 && H % 128 == 0, "moe_route: H=%lld must be a positive multiple of 128",
               (long long)H);
@@ -572,8 +584,32 @@ extern "C" int moe_route(const void* x_bf16, int64_t T, int64_t H, const float* 
   const int64_t sel_blocks = std::min<int64_t>(ceil_div(T, 4), 2048);
   router_select_kernel<<<dim3((unsigned)sel_blocks), dim3(256), 0, st>>>(
       part, (int)sp.ks, T, bias, E, n_group, topk_group, k, lpg, topk_idx, topk_w,
-      expert_counts);
+      expert_counts, scores, score_sums);
   return check_launch("moe_route");
+}
+
+}  // namespace
+
+extern "C" int moe_route(const void* x_bf16, int64_t T, int64_t H, const float* centroids,
+                         const float* bias, int32_t E, int32_t n_group, int32_t topk_group,
+                         int32_t k, int32_t* topk_idx, float* topk_w, int32_t* expert_counts,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  clear_error();
+  return route_impl(x_bf16, T, H, centroids, bias, E, n_group, topk_group, k, topk_idx, topk_w,
+                    expert_counts, workspace, workspace_bytes, nullptr, nullptr, stream);
+}
+
+extern "C" int moe_route_scores(const void* x_bf16, int64_t T, int64_t H,
+                                const float* centroids, const float* bias, int32_t E,
+                                int32_t n_group, int32_t topk_group, int32_t k,
+                                int32_t* topk_idx, float* topk_w, int32_t* expert_counts,
+                                void* workspace, size_t workspace_bytes, float* scores,
+                                float* score_sums, void* stream) {
+  clear_error();
+  MOE_INVALID(T == 0 || (scores && score_sums), "moe_route_scores: scores or score_sums is null");
+  MOE_INVALID(((uintptr_t)scores & 15) == 0, "moe_route_scores: scores must be 16-byte aligned");
+  return route_impl(x_bf16, T, H, centroids, bias, E, n_group, topk_group, k, topk_idx, topk_w,
+                    expert_counts, workspace, workspace_bytes, scores, score_sums, stream);
 }
 
 extern "C" int moe_bias_update(const int32_t* expert_counts, float* bias, int32_t E, float gamma,

@@ -6,6 +6,8 @@ developer.aliyun.com/article/1776647 section 2.2; news.qq.com/rain/a/
 FP8 低精度训练):
 
   1. moe_route         sigmoid scores + selection bias, 4-of-8-group top-8
+     (moe_route_scores + moe_seq_balance with seq_len: also the
+     sequence-wise balance statistic, factor alpha = 0.0001)
   2. fp8_quant_1x128   x -> E4M3 with 1x128 scales
   3. moe_permute       expert-major dispatch order (no copy: GEMM 1 gathers)
   4. grouped_fp8_gemm_swiglu
@@ -92,6 +94,24 @@ class Buffers:
         self.hs = torch.empty((R, s.I // 128), dtype=f32, device=dev)
         self.d = torch.empty((R, s.H), dtype=bf, device=dev)
         self.y = torch.empty((T, s.H), dtype=bf, device=dev)
+
+    def balance(self, seq_len: int):
+        """Buffers of the sequence-wise balance statistic (allocated on first
+        use, again when seq_len changes): scores [T, E], score_sums [T],
+        seq_f, seq_p [B, E], seq_loss [B], B = ceil(T / seq_len)."""
+        s = self._shape
+        if getattr(self, "_seq_len", None) != seq_len:
+            T, dev, f32 = self.T, self._dev, torch.float32
+            B = -(-T // seq_len)
+            self.scores = torch.empty((max(T, 1), s.E), dtype=f32, device=dev)
+            self.score_sums = torch.empty((max(T, 1),), dtype=f32, device=dev)
+            self.seq_f = torch.empty((max(B, 1), s.E), dtype=f32, device=dev)
+            self.seq_p = torch.empty((max(B, 1), s.E), dtype=f32, device=dev)
+            self.seq_loss = torch.empty((max(B, 1),), dtype=f32, device=dev)
+            self.seq_ws_bytes = max(16, L.moe_seq_balance_workspace_bytes(T, s.E, seq_len))
+            self.seq_ws = torch.empty((self.seq_ws_bytes,), dtype=torch.uint8, device=dev)
+            self._seq_len = seq_len
+        return self
 
     @property
     def hgu(self):
@@ -201,19 +221,25 @@ class MoELayer:
 
     def forward(self, x_bf16: torch.Tensor, bufs: Buffers | None = None, stream=None,
                 update_bias: bool = False, gamma: float = 0.001,
-                fused: bool = True, events: dict | None = None) -> torch.Tensor:
-        """One layer forward.  `events`, if given, maps a step name ("route",
-        "quant", "permute", "gate_up", "down", "combine", "bias") to a list
-        that receives a (start, end) pair of torch.cuda.Event recorded on the
-        launch stream around that step."""
+                fused: bool = True, events: dict | None = None,
+                seq_len: int | None = None, alpha: float = 0.0001) -> torch.Tensor:
+        """One layer forward.  With seq_len, also the sequence-wise balance
+        statistic of the routing (factor alpha) over consecutive runs of
+        seq_len tokens, into bufs.seq_f, seq_p and seq_loss.  `events`, if
+        given, maps a step name ("route", "seq_balance", "quant", "permute",
+        "gate_up", "down", "combine", "bias") to a list that receives a
+        (start, end) pair of torch.cuda.Event recorded on the launch stream
+        around that step."""
         s = self.shape
         T = x_bf16.shape[0]
         b = bufs or self.buffers(T)
         R = b.R
         if events is not None:
-            return self._forward_timed(x_bf16, b, stream, update_bias, gamma, fused, events)
-        L.moe_route(x_bf16, T, s.H, self.centroids, self.bias, s.E, s.n_group, s.topk_group,
-                    s.k, b.topk_idx, b.topk_w, b.counts, b.route_ws, b.route_ws_bytes, stream)
+            return self._forward_timed(x_bf16, b, stream, update_bias, gamma, fused, events,
+                                       seq_len, alpha)
+        self._route(x_bf16, b, seq_len, stream)
+        if seq_len is not None:
+            self._seq_balance(b, seq_len, alpha, stream)
         L.fp8_quant_1x128(x_bf16, T, s.H, s.H, 0, b.xq, b.xs, stream)
         L.moe_permute(b.topk_idx, b.counts, T, s.k, s.E, s.n_shared, b.offsets, b.perm_src,
                       b.inv_perm, None, None, s.H, None, None, b.perm_ws, b.perm_ws_bytes,
@@ -320,7 +346,25 @@ class MoELayer:
                                     bb.dC, st)))
         return bb
 
-    def _forward_timed(self, x_bf16, b, stream, update_bias, gamma, fused, events):
+    def _route(self, x_bf16, b, seq_len, stream):
+        s = self.shape
+        T = x_bf16.shape[0]
+        if seq_len is None:
+            L.moe_route(x_bf16, T, s.H, self.centroids, self.bias, s.E, s.n_group, s.topk_group,
+                        s.k, b.topk_idx, b.topk_w, b.counts, b.route_ws, b.route_ws_bytes, stream)
+        else:
+            b.balance(seq_len)
+            L.moe_route_scores(x_bf16, T, s.H, self.centroids, self.bias, s.E, s.n_group,
+                               s.topk_group, s.k, b.topk_idx, b.topk_w, b.counts, b.route_ws,
+                               b.route_ws_bytes, b.scores, b.score_sums, stream)
+
+    def _seq_balance(self, b, seq_len, alpha, stream):
+        s = self.shape
+        L.moe_seq_balance(b.scores, b.score_sums, b.topk_idx, b.T, s.E, s.k, seq_len, alpha,
+                          b.seq_f, b.seq_p, b.seq_loss, b.seq_ws, b.seq_ws_bytes, stream)
+
+    def _forward_timed(self, x_bf16, b, stream, update_bias, gamma, fused, events, seq_len,
+                       alpha):
         s = self.shape
         T, R = x_bf16.shape[0], b.R
         st = stream if stream is not None else torch.cuda.current_stream()
@@ -333,9 +377,9 @@ class MoELayer:
             e1.record(st)
             events.setdefault(name, []).append((e0, e1))
 
-        timed("route", lambda: L.moe_route(
-            x_bf16, T, s.H, self.centroids, self.bias, s.E, s.n_group, s.topk_group, s.k,
-            b.topk_idx, b.topk_w, b.counts, b.route_ws, b.route_ws_bytes, st))
+        timed("route", lambda: self._route(x_bf16, b, seq_len, st))
+        if seq_len is not None:
+            timed("seq_balance", lambda: self._seq_balance(b, seq_len, alpha, st))
         timed("quant", lambda: L.fp8_quant_1x128(x_bf16, T, s.H, s.H, 0, b.xq, b.xs, st))
         timed("permute", lambda: L.moe_permute(
             b.topk_idx, b.counts, T, s.k, s.E, s.n_shared, b.offsets, b.perm_src, b.inv_perm,

@@ -95,6 +95,42 @@ int moe_route(const void* x_bf16, int64_t T, int64_t H,
               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * moe_route_scores - moe_route that also writes what the sequence-wise
+ * balance statistic reads: scores [T, E] fp32, the unbiased sigmoid score of
+ * every routed expert for every token (16-byte aligned), and score_sums [T]
+ * fp32, their sum per token.  Same arguments, requirements, workspace and
+ * results as moe_route otherwise.
+ */
+int moe_route_scores(const void* x_bf16, int64_t T, int64_t H,
+                     const float* centroids, const float* bias,
+                     int32_t E, int32_t n_group, int32_t topk_group, int32_t k,
+                     int32_t* topk_idx, float* topk_w, int32_t* expert_counts,
+                     void* workspace, size_t workspace_bytes, float* scores,
+                     float* score_sums, void* stream);
+
+/*
+ * moe_seq_balance - sequence-wise balance statistic (news.qq.com article,
+ * section 无额外损耗的负载均衡: factor alpha = 0.0001; the V3 summary at
+ * m.jxzklqfsx.com/aigc/3586.html, section （二）無輔助損失負載均衡策略革新: a
+ * sequence-level term against imbalance inside one sequence).  The pages
+ * give no formula; computed here, for each sequence b of L_b consecutive
+ * tokens (runs of seq_len, the last may be shorter):
+ *   P[b, e] = (1/L_b) sum_t scores[t, e] / score_sums[t]
+ *   f[b, e] = E * (tokens of b that chose e) / (k * L_b)
+ *   loss[b] = alpha * sum_e f[b, e] * P[b, e]
+ * in fp32 with fixed summation order (f is exact up to one rounding).
+ * scores, score_sums: moe_route_scores' outputs; topk_idx [T, k];
+ * f_out, p_out (out) [B, E]; loss_out (out) [B], B = ceil(T / seq_len).
+ * workspace: moe_seq_balance_workspace_bytes(T, E, seq_len) bytes.
+ * Requirements: 1 <= E <= 256, 1 <= k <= E, 1 <= seq_len <= 65536.
+ */
+size_t moe_seq_balance_workspace_bytes(int64_t T, int32_t E, int64_t seq_len);
+int moe_seq_balance(const float* scores, const float* score_sums, const int32_t* topk_idx,
+                    int64_t T, int32_t E, int32_t k, int64_t seq_len, float alpha,
+                    float* f_out, float* p_out, float* loss_out, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/*
  * moe_bias_update - aux-loss-free balancing step, in place.
  *
  * aliyun study note section 2.2 (overloaded experts' bias goes down,

@@ -144,6 +144,29 @@ def test_route_validation():
     assert f(ws=None) == L.MOE_ERR_WORKSPACE
 
 
+def test_route_scores_and_seq_balance_validation():
+    def r(T=64, sc=FAKE, ss=FAKE, k=4):
+        return rc("moe_route_scores", FAKE, T, 256, FAKE, FAKE, 16, 4, 2, k, FAKE, FAKE, FAKE, FAKE,
+                  1 << 30, sc, ss, None)
+    assert r(sc=None) == L.MOE_ERR_INVALID and "scores" in L.last_error()
+    assert r(ss=None) == L.MOE_ERR_INVALID
+    assert r(sc=ctypes.c_void_p(4100)) == L.MOE_ERR_INVALID and "aligned" in L.last_error()
+    assert r(k=9) == L.MOE_ERR_INVALID                       # moe_route's own checks still apply
+    # workspace: two [B, chunks of 64 tokens, E] planes, 256-byte rounded
+    assert L.moe_seq_balance_workspace_bytes(0, 256, 4096) == 0
+    assert L.moe_seq_balance_workspace_bytes(16384, 256, 4096) == 2 * 4 * 64 * 256 * 4
+    assert L.moe_seq_balance_workspace_bytes(100, 16, 64) == 2 * 256 * ((2 * 1 * 16 * 4 + 255) // 256)
+    def b(T=100, E=16, k=4, L_=64, ws=FAKE, wsb=1 << 20, out=FAKE):
+        return rc("moe_seq_balance", FAKE, FAKE, FAKE, T, E, k, L_, 1e-4, out, FAKE, FAKE, ws, wsb,
+                  None)
+    assert b(E=0) == L.MOE_ERR_INVALID and b(E=257) == L.MOE_ERR_INVALID
+    assert b(k=17) == L.MOE_ERR_INVALID and b(k=0) == L.MOE_ERR_INVALID
+    assert b(L_=0) == L.MOE_ERR_INVALID and b(L_=65537) == L.MOE_ERR_INVALID
+    assert b(out=None) == L.MOE_ERR_INVALID
+    assert b(wsb=64) == L.MOE_ERR_WORKSPACE and b(ws=None) == L.MOE_ERR_WORKSPACE
+    assert b(T=0, out=None, ws=None) == L.MOE_OK
+
+
 def test_route_group_size_two_is_valid_shape():
     # E=16 in 8 groups has group size 2: valid, but 2 is not 4 * 2^n
     assert rc("moe_route", FAKE, 8, 256, FAKE, FAKE, 16, 8, 2, 4, FAKE, FAKE, FAKE, FAKE, 1 << 30,

@@ -1,0 +1,191 @@
+"""Sequence-wise balance statistic on the GPU, through the C ABI.
+
+* moe_route_scores: the routing outputs bit-identical to moe_route's on the
+  same inputs; every expert's score within 4e-6 of the oracle's float64
+  sigmoid (the bound the router's weights are held to: fp32-accumulated
+  logits within a few 1e-6); score_sums within the fp32 sum bound of the
+  GPU's own scores;
+* moe_seq_balance on given scores: f bit-exact (fp32 of the exact rational
+  E*count/(k*L)), P within its fp32 evaluation bound, the loss within the
+  bound that P and the last reduction imply; ragged last sequence, a single
+  sequence, seq_len 1, unchosen experts;
+* MoELayer.forward(seq_len=...) on the mid config, and the same two calls at
+  V3 shapes (T=16384, sequences of 4096), against the oracle's statistic on
+  the GPU's own choice.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+import fp8_block_scaled_bias_amd as M
+from gpu_common import bf16_dev, compare_routes, dev, host, log
+from test_gpu_layer import build_layer
+from oracle import balance as OB
+from oracle import route as OR
+
+pytestmark = pytest.mark.gpu
+
+U = 2.0 ** -24
+
+
+def _f32(shape):
+    return torch.full(shape, float("nan"), dtype=torch.float32, device="cuda")
+
+
+def _i32(shape):
+    return torch.full(shape, -7, dtype=torch.int32, device="cuda")
+
+
+def _seq_gpu(scores, ssum, idx, seq_len, alpha):
+    T, E = scores.shape
+    k = idx.shape[1]
+    B = -(-T // seq_len)
+    f, p, loss = _f32((B, E)), _f32((B, E)), _f32((B,))
+    wsb = max(16, M.moe_seq_balance_workspace_bytes(T, E, seq_len))
+    ws = torch.empty((wsb,), dtype=torch.uint8, device="cuda")
+    M.moe_seq_balance(dev(np.ascontiguousarray(scores, np.float32)), dev(ssum), dev(idx), T, E, k,
+                      seq_len, alpha, f, p, loss, ws, wsb)
+    return host(f), host(p), host(loss)
+
+
+def check_statistic(f, p, loss, scores, ssum, idx, seq_len, alpha, label):
+    """GPU f, P, loss against the oracle on the scores the GPU read (float64
+    sum per token) and the sums it divided by (within one fp32 rounding of
+    theirs)."""
+    T, E = scores.shape
+    s64 = np.asarray(scores, np.float64)
+    ref = OB.seq_balance(s64, idx, seq_len, alpha)
+    assert np.array_equal(f, ref["f"].astype(np.float32)), label
+    # P: each term s/S rounded once (plus S itself one rounding away from the
+    # exact sum), then <= 64 + chunks additions and the division by L
+    nch = -(-min(seq_len, T) // 64)
+    relP = (64 + nch + 4) * U
+    S_rel = np.abs(np.asarray(ssum, np.float64) - s64.sum(1)) / s64.sum(1)
+    assert S_rel.max() <= (E + 2) * U, (label, S_rel.max())
+    tolP = (relP + (E + 2) * U) * ref["P"] + 1e-30
+    errP = np.abs(p - ref["P"])
+    log(f"[seq balance] {label}: max |P err| / bound {float((errP / tolP).max()):.2e}")
+    assert (errP <= tolP).all(), label
+    # loss: sum_e f P with P as above, then E products and E additions
+    tolL = alpha * np.sum(ref["f"] * tolP, 1) + (E + 4) * U * ref["loss"]
+    errL = np.abs(loss - ref["loss"])
+    log(f"[seq balance] {label}: loss {loss[:4]} max |err| / bound {float((errL / tolL).max()):.2e}")
+    assert (errL <= tolL).all(), label
+
+
+@pytest.mark.parametrize("T,E,k,seq_len", [(300, 16, 4, 128), (64, 256, 8, 64), (5, 8, 3, 1),
+                                           (1000, 64, 6, 4096), (4100, 256, 8, 1024)])
+def test_seq_balance_kernel(T, E, k, seq_len):
+    rng = np.random.default_rng([T, E, k])
+    scores = (1.0 / (1.0 + np.exp(-rng.standard_normal((T, E)) * 2))).astype(np.float32)
+    idx = np.sort(np.stack([rng.choice(E // 2, k, replace=False) for _ in range(T)]), 1)
+    idx = idx.astype(np.int32)      # the upper half of the experts is never chosen
+    ssum = scores.astype(np.float64).sum(1).astype(np.float32)
+    log(f"[seq balance] T={T} E={E} k={k} seq_len={seq_len}")
+    f, p, loss = _seq_gpu(scores, ssum, idx, seq_len, 1e-4)
+    check_statistic(f, p, loss, scores, ssum, idx, seq_len, 1e-4, f"T={T} L={seq_len}")
+    assert not f[:, E // 2:].any()
+
+
+def test_seq_balance_uniform_scores_give_alpha():
+    T, E, k = 256, 32, 4
+    rng = np.random.default_rng(2)
+    scores = np.full((T, E), 0.5, np.float32)
+    idx = np.sort(np.stack([rng.choice(E, k, replace=False) for _ in range(T)]), 1).astype(np.int32)
+    f, p, loss = _seq_gpu(scores, np.full(T, 16.0, np.float32), idx, 100, 1e-4)
+    np.testing.assert_allclose(loss, 1e-4, rtol=8 * E * U)
+    assert np.all(p == np.float32(1.0 / E))
+
+
+@pytest.mark.parametrize("name,T", [("tiny", 64), ("mid", 200), ("decode", 128)])
+def test_route_scores(name, T):
+    cfg = synth.CONFIGS[name]
+    bits = synth.gen_x(cfg, seed=3, T=T)
+    C = synth.gen_centroids(cfg, seed=3)
+    b = synth.gen_bias(cfg, seed=3)
+    E, k = cfg.E, cfg.k
+    wsb = max(16, M.moe_route_workspace_bytes(T, cfg.H, E))
+    ws = torch.empty((wsb,), dtype=torch.uint8, device="cuda")
+    outs = []
+    for with_scores in (False, True):
+        idx, w, cnt = _i32((T, k)), _f32((T, k)), _i32((E,))
+        sc, ss = _f32((T, E)), _f32((T,))
+        args = (bf16_dev(bits), T, cfg.H, dev(C), dev(b), E, cfg.n_group, cfg.topk_group, k, idx,
+                w, cnt, ws, wsb)
+        if with_scores:
+            M.moe_route_scores(*args, sc, ss)
+        else:
+            M.moe_route(*args)
+        outs.append((host(idx), host(w), host(cnt), host(sc), host(ss)))
+    for a, b_ in zip(outs[0][:3], outs[1][:3]):
+        assert np.array_equal(a.view(np.uint32), b_.view(np.uint32))
+    sc, ss = outs[1][3], outs[1][4]
+    s_ref, _ = OR.router_scores(bits, C, b)
+    err = np.abs(sc - s_ref)
+    log(f"[route scores] {name}: max |s_gpu - s_oracle| = {err.max():.3e}")
+    assert err.max() <= 4e-6
+    own = sc.astype(np.float64).sum(1)
+    assert (np.abs(ss - own) <= (E + 2) * U * own).all()
+
+
+def test_layer_seq_balance_mid():
+    cfg = synth.MID
+    layer, C, b = build_layer(cfg)
+    x = synth.gen_x(cfg)
+    log(f"[layer seq balance] mid: T={cfg.T}, seq_len 64")
+    layer.forward(bf16_dev(x), seq_len=64)
+    bufs = layer.buffers(cfg.T)
+    torch.cuda.synchronize()
+    ora = OR.route(x, C, b, cfg.n_group, cfg.topk_group, cfg.k)
+    assert len(compare_routes(host(bufs.topk_idx), ora, "mid")) == 0
+    s_ref, _ = OR.router_scores(x, C, b)
+    _check_layer(bufs, s_ref, host(bufs.topk_idx), 64, cfg, "mid")
+
+
+def _check_layer(bufs, s_ref, idx, seq_len, cfg, label):
+    """The layer's statistic against the oracle on the GPU's own choice, with
+    the score error (<= 4e-6 per score) carried into P and the loss."""
+    ref = OB.seq_balance(s_ref, idx, seq_len, 1e-4)
+    f, p, loss = host(bufs.seq_f), host(bufs.seq_p), host(bufs.seq_loss)
+    assert np.array_equal(f, ref["f"].astype(np.float32)), label
+    # s' = s/S moves by at most (4e-6 + s' * E * 4e-6) / S per token
+    S = s_ref.sum(1, keepdims=True)
+    ds = (4e-6 + (s_ref / S) * cfg.E * 4e-6) / S
+    B = len(loss)
+    tolP = np.stack([ds[i * seq_len:(i + 1) * seq_len].mean(0) for i in range(B)])
+    tolP = tolP + 1e-5 * ref["P"]
+    errP = np.abs(p - ref["P"])
+    log(f"[layer seq balance] {label}: loss {loss[:4]}, max |P err| / bound "
+        f"{float((errP / tolP).max()):.2e}")
+    assert (errP <= tolP).all(), label
+    tolL = 1e-4 * np.sum(ref["f"] * tolP, 1) + 1e-5 * ref["loss"]
+    assert (np.abs(loss - ref["loss"]) <= tolL).all(), label
+
+
+def test_seq_balance_v3_prefill():
+    """V3 shapes, T=16384 in sequences of 4096, the calls the layer makes."""
+    cfg = synth.PREFILL
+    T, E, k = cfg.T, cfg.E, cfg.k
+    x = synth.gen_x(cfg)
+    C, b = synth.gen_centroids(cfg), synth.gen_bias(cfg)
+    log(f"[seq balance] V3 prefill: T={T}, seq_len 4096")
+    wsb = max(16, M.moe_route_workspace_bytes(T, cfg.H, E))
+    ws = torch.empty((wsb,), dtype=torch.uint8, device="cuda")
+    idx, w, cnt, sc, ss = _i32((T, k)), _f32((T, k)), _i32((E,)), _f32((T, E)), _f32((T,))
+    M.moe_route_scores(bf16_dev(x), T, cfg.H, dev(C), dev(b), E, cfg.n_group, cfg.topk_group, k,
+                       idx, w, cnt, ws, wsb, sc, ss)
+
+    class Bufs:
+        pass
+    bufs = Bufs()
+    B = T // 4096
+    bufs.seq_f, bufs.seq_p, bufs.seq_loss = _f32((B, E)), _f32((B, E)), _f32((B,))
+    swb = M.moe_seq_balance_workspace_bytes(T, E, 4096)
+    sw = torch.empty((swb,), dtype=torch.uint8, device="cuda")
+    M.moe_seq_balance(sc, ss, idx, T, E, k, 4096, 1e-4, bufs.seq_f, bufs.seq_p, bufs.seq_loss, sw,
+                      swb)
+    torch.cuda.synchronize()
+    s_ref, _ = OR.router_scores(x, C, b)
+    assert np.abs(host(sc) - s_ref).max() <= 4e-6
+    _check_layer(bufs, s_ref, host(idx), 4096, cfg, "V3 prefill")

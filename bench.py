@@ -380,7 +380,9 @@ def bench_skewed(layer, steps=100):
 def cpu_baseline(cfg, n_tokens=32):
     """The FP64 oracle on a bounded sample: the layer output of the first
     n_tokens tokens of the same batch (their routes, the weights of every
-    expert they touch, and the shared expert), one BLAS thread."""
+    expert they touch, and the shared expert), with the BLAS threads set to
+    the host cores this process may use (its CPU affinity, at most the
+    OMP_NUM_THREADS share when that is set)."""
     import numpy as np
     import synth
     from threadpoolctl import threadpool_limits
@@ -397,11 +399,14 @@ def cpu_baseline(cfg, n_tokens=32):
     t0 = time.time()
     wts.prefetch(experts)   # weight quantisation is setup, not timed
     log(f"[bench] cpu baseline setup: {len(experts)} experts quantised in {time.time() - t0:.1f}s")
-    with threadpool_limits(limits=1):
+    cores = len(os.sched_getaffinity(0))
+    if os.environ.get("OMP_NUM_THREADS", "").isdigit():
+        cores = max(1, min(cores, int(os.environ["OMP_NUM_THREADS"])))
+    with threadpool_limits(limits=cores):
         t0 = time.perf_counter()
         OL.layer_tokens(x, C, b, wts, cfg.n_group, cfg.topk_group, cfg.k, cfg.I, toks)
         dt = time.perf_counter() - t0
-    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"FP64 oracle layer output for {n_tokens} of the {cfg.T} tokens "
                       f"({len(experts)} experts incl. shared), {dt:.1f}s"}
 

@@ -93,10 +93,10 @@ def _expert_rows(idx, E):
 
 def check_router_stage(xbits, C, idx, dw32, inv_perm, perm_src, offs, dx_in, dl_rows, dx_out,
                        dC, label):
-    """dl_rows (fp32 [T*k], expert-row order), dx_out (bf16 values), dC (fp32)
-    from the GPU; dx_in (bf16 values or None) and the rest its inputs."""
+    """dl_rows (fp32 [T*k], expert-row order), dx_out (bf16 values), dC (fp32,
+    or None to skip it) from the GPU; dx_in (bf16 values or None) and the
+    rest its inputs."""
     T, k = idx.shape
-    E = len(offs) - 1
     xv = OF.bf16_value_from_bits(xbits)
     C64 = np.asarray(C, np.float32).astype(np.float64)
     ref = OBK.router_backward(xbits, C, idx, dw32)
@@ -116,7 +116,10 @@ def check_router_stage(xbits, C, idx, dw32, inv_perm, perm_src, offs, dx_in, dl_
     exact = base + terms.sum(1)
     acc = (k + 1) * 2.0 ** -23 * (np.abs(base) + np.abs(terms).sum(1))
     assert_within_one_bf16_ulp(dx_out, exact, f"{label} dx", acc)
+    if dC is None:
+        return
     # dC: each expert's rows in row order, fp32 fmas
+    E = len(offs) - 1
     dC = np.asarray(dC, np.float64)
     dlr = np.asarray(dl_rows, np.float64)
     for e in range(E):
@@ -155,6 +158,59 @@ def test_router_backward_kernel(T, H, E, k, mode):
                        None if dx_in is None else OF.bf16_value_from_bits(dx_in), host(dl_rows),
                        bf16_values_host(dx_out), host(dC), f"router bwd T={T}")
     assert not host(dC)[np.diff(offs) == 0].any()
+
+
+def test_router_backward_v3_prefill_sampled():
+    """V3 shapes at T=16384 (the benchmark's batch): the GPU's own routing and
+    permutation, dw N(0,1); dlogit and dx on 64 sampled tokens, dC on 8
+    sampled experts, each against the oracle / the exact sums of the GPU's
+    dlogit as in check_router_stage."""
+    from test_gpu_kernels import _permute_gpu
+    cfg = synth.PREFILL
+    T, H, E, k = cfg.T, cfg.H, cfg.E, cfg.k
+    x = synth.gen_x(cfg)
+    C, b = synth.gen_centroids(cfg), synth.gen_bias(cfg)
+    log(f"[router bwd] V3 prefill T={T}: route, permute, backward")
+    wsb = max(16, M.moe_route_workspace_bytes(T, H, E))
+    ws = torch.empty((wsb,), dtype=torch.uint8, device="cuda")
+    idx_d = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w_d = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    cnt_d = torch.empty((E,), dtype=torch.int32, device="cuda")
+    x_d, C_d = bf16_dev(x), dev(C)
+    M.moe_route(x_d, T, H, C_d, dev(b), E, cfg.n_group, cfg.topk_group, k, idx_d, w_d, cnt_d, ws, wsb)
+    idx = host(idx_d)
+    offs, perm_src, inv_perm = _permute_gpu(idx, E, 0)
+    dw = np.random.default_rng(8).standard_normal((T, k)).astype(np.float32)
+    dx_in = synth.gen_dy(cfg)
+    dx_out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    dl_rows = torch.empty((T * k,), dtype=torch.float32, device="cuda")
+    dC = torch.empty((E, H), dtype=torch.float32, device="cuda")
+    M.moe_router_backward(x_d, C_d, idx_d, dev(dw), dev(inv_perm), bf16_dev(dx_in), T, H, E, k,
+                          dx_out, dl_rows)
+    M.moe_router_dcentroids(x_d, dev(perm_src), dev(offs), dl_rows, T, H, E, dC)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(9)
+    toks = np.concatenate([[0, T - 1], rng.choice(T, 62, replace=False)])
+    dlr = host(dl_rows)
+    xs = x[toks]
+    # dlogit and dx on the sampled tokens (their rows through inv_perm)
+    sub_inv = inv_perm.reshape(T, k)[toks].reshape(-1)
+    sub_rows = dlr[sub_inv]
+    ident = np.arange(len(toks) * k, dtype=np.int32)
+    check_router_stage(xs, C, idx[toks], dw[toks], ident, None, None,
+                       OF.bf16_value_from_bits(dx_in[toks]), sub_rows,
+                       bf16_values_host(dx_out)[toks], None, "router bwd V3 sampled tokens")
+    # dC on sampled experts: each expert's rows in row order
+    xv = OF.bf16_value_from_bits(x)
+    dCh = host(dC).astype(np.float64)
+    for e in list(rng.choice(E, 6, replace=False)) + [int(np.argmax(np.diff(offs))),
+                                                       int(np.argmin(np.diff(offs)))]:
+        r0, r1 = int(offs[e]), int(offs[e + 1])
+        prod = dlr[r0:r1, None].astype(np.float64) * xv[perm_src[r0:r1].astype(np.int64)]
+        bnd = (r1 - r0 + 1) * 2.0 ** -24 * np.abs(prod).sum(0)
+        assert (np.abs(dCh[e] - prod.sum(0)) <= bnd).all(), e
+    # every expert's rows are that expert's tokens in ascending order
+    assert np.all(np.diff(offs) >= 0) and offs[-1] == T * k
 
 
 def _logical(c, sc, nch):

@@ -380,6 +380,26 @@ def test_gemm_integer_exact_wide(K, with_index):
     assert np.array_equal(got, ref), int((got != ref).sum())
 
 
+# Collapsed routing: a few groups hold every row, the rest are empty (the
+# 256x256-tile kernel's cost-balanced ranges over very uneven groups).
+@pytest.mark.parametrize("with_index", [False, True])
+def test_gemm_integer_exact_collapsed(with_index):
+    G, N, K = 65, 512, 1024
+    sizes = [0] * G
+    for g in (3, 17, 18, 40, 41, 42, 60, 63):
+        sizes[g] = 2048
+    sizes[G - 1] = 2048
+    rng = np.random.default_rng(11)
+    rows_src = 2048 if with_index else int(sum(sizes))
+    offsets, Mt, qA, sA, qB, sB = _int_gemm_case(sizes, N, K, rows_src, 57)
+    rowidx = np.tile(np.arange(2048, dtype=np.int32), 9) if with_index else None
+    got = _gemm_gpu(qA, sA, rowidx, qB, sB, offsets, N, K)
+    qAr = qA[rowidx] if with_index else qA
+    sAr = sA[rowidx] if with_index else sA
+    ref = OG.to_bf16(OG.grouped_gemm(qAr, sAr, qB, sB, offsets))
+    assert np.array_equal(got, ref), int((got != ref).sum())
+
+
 # Gathered row indices outside [0, A_rows) read row A_rows - 1 (documented
 # clamp; the copies never leave A).  Small-group and 256-row-tile kernels.
 @pytest.mark.parametrize("sizes", [[40, 7, 90], [300, 200, 0, 260]])

@@ -81,6 +81,29 @@ def test_layer_full_small(name):
     assert np.array_equal(y2, got)
 
 
+def test_layer_collapsed_routing():
+    """Degenerate routing: every token identical, so all T tokens choose the
+    same 8 experts (8 groups of T rows next to the shared group of T rows,
+    56 empty groups), at T=2048 on the mid layer: the 256x256-tile kernel
+    takes gate+up.  Output against the oracle, counts exact."""
+    cfg = synth.MID.with_(T=2048)
+    T = cfg.T
+    layer, C, b = build_layer(cfg)
+    x = np.repeat(synth.gen_x(cfg, T=1), T, axis=0)
+    log(f"[layer] collapsed routing: T={T}, every token the same")
+    got = bf16_values_host(layer.forward(bf16_dev(x)))
+    bufs = layer.buffers(T)
+    ref = OL.layer(x, C, b, oracle_weights(cfg), cfg.n_group, cfg.topk_group, cfg.k, cfg.I)
+    assert len(compare_routes(host(bufs.topk_idx), ref["route"], "collapsed")) == 0
+    cnt = host(bufs.counts)
+    assert sorted(cnt.tolist())[-cfg.k:] == [T] * cfg.k and (cnt > 0).sum() == cfg.k
+    assert np.array_equal(host(bufs.offsets), ref["offsets"])
+    rel = rel_l2(got, ref["y"])
+    log(f"[layer] collapsed: rel L2 of y vs oracle = {rel:.3e}")
+    assert rel <= REL_L2_BAR
+    assert np.array_equal(got, np.repeat(got[:1], T, axis=0))   # identical tokens, identical rows
+
+
 @pytest.fixture(scope="module")
 def v3_layer():
     cfg = synth.DECODE

@@ -152,3 +152,28 @@ def layer_backward(dy_bits, fwd: dict, wts, x_bits, centroids, T: int, k: int, I
     out.update(dx_expert=eb["dx"], dx=bf16_round(eb["dx"] + rb["dx"]), dlogit=rb["dlogit"],
                dC=rb["dC"])
     return out
+
+
+def router_backward_with_balance(x_bits, centroids, idx, dw, seq_len: int, alpha: float,
+                                 dx_in=None):
+    """The router's backward when the loss also holds the sequence-wise balance
+    term alpha * sum_b L_bal,b (oracle.balance.seq_balance; f held fixed with
+    the selection): the logits' gradient is the gate part of router_backward
+    on the chosen experts plus seq_balance_grad_logits on every expert, and
+    dx = dx_in + dlogit C, dC = dlogit^T x.  float64.  Returns dict(dlogit
+    [T, E], dx [T, H], dC [E, H])."""
+    from .balance import seq_balance_grad_logits
+    from .route import router_scores
+    x = bf16_value_from_bits(x_bits)
+    C = np.asarray(centroids, dtype=np.float32).astype(np.float64)
+    idx = np.asarray(idx, dtype=np.int64)
+    T, k = idx.shape
+    s, _ = router_scores(x_bits, centroids, np.zeros(C.shape[0], np.float32))
+    g = seq_balance_grad_logits(s, idx, seq_len, alpha)
+    gate = router_backward(x_bits, centroids, idx, dw)["dlogit"]
+    rows = np.repeat(np.arange(T), k)
+    np.add.at(g, (rows, idx.reshape(-1)), gate.reshape(-1))
+    dx = g @ C
+    if dx_in is not None:
+        dx = dx + np.asarray(dx_in, dtype=np.float64)
+    return dict(dlogit=g, dx=dx, dC=g.T @ x)

@@ -365,3 +365,39 @@ def test_router_backward_is_the_derivative_of_the_gate_weights():
     np.testing.assert_allclose(
         rb["dlogit"], (dw - np.sum(dw * (s[np.arange(T)[:, None], idx] / s[np.arange(T)[:, None], idx].sum(1, keepdims=True)), 1, keepdims=True))
         / s[np.arange(T)[:, None], idx].sum(1, keepdims=True) * s[np.arange(T)[:, None], idx] * (1 - s[np.arange(T)[:, None], idx]), rtol=1e-12)
+
+
+def test_router_backward_with_balance_is_the_derivative():
+    """L = <dw, w(x, C)> + sum_b L_bal,b(x, C) with the selection (and so f)
+    held fixed: central differences in x and in C."""
+    from oracle import balance as BL
+    rng = np.random.default_rng(43)
+    T, H, E, k, L, alpha = 10, 32, 16, 4, 4, 0.3
+    xb = synth.f32_to_bf16_bits((rng.standard_normal((T, H)) * 0.5).astype(np.float32))
+    C = (rng.standard_normal((E, H)) * 0.3).astype(np.float32)
+    idx = np.sort(np.stack([rng.choice(E, k, replace=False) for _ in range(T)]), 1)
+    dw = rng.standard_normal((T, k))
+    rb = OB.router_backward_with_balance(xb, C, idx, dw, L, alpha)
+
+    def loss(xm, Cm):
+        s = 1.0 / (1.0 + np.exp(-(xm @ Cm.T)))
+        sel = np.take_along_axis(s, idx, 1)
+        gate = float(np.sum(dw * sel / sel.sum(1, keepdims=True)))
+        return gate + float(BL.seq_balance(s, idx, L, alpha)["loss"].sum())
+    x64, C64 = F.bf16_value_from_bits(xb), C.astype(np.float64)
+    eps = 1e-6
+    for (t, h) in [(0, 0), (5, 17), (9, 31)]:
+        xp, xm = x64.copy(), x64.copy()
+        xp[t, h] += eps
+        xm[t, h] -= eps
+        assert abs((loss(xp, C64) - loss(xm, C64)) / (2 * eps) - rb["dx"][t, h]) < 1e-7
+    for (e, h) in [(0, 3), (int(idx[4, 2]), 30), (15, 0)]:
+        Cp, Cm = C64.copy(), C64.copy()
+        Cp[e, h] += eps
+        Cm[e, h] -= eps
+        assert abs((loss(x64, Cp) - loss(x64, Cm)) / (2 * eps) - rb["dC"][e, h]) < 1e-7
+    # without the balance term it is the gate part alone
+    r0 = OB.router_backward_with_balance(xb, C, idx, dw, L, 0.0)
+    ref = OB.router_backward(xb, C, idx, dw)
+    np.testing.assert_allclose(r0["dx"], ref["dx"], rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(r0["dC"], ref["dC"], rtol=1e-12, atol=1e-15)

@@ -333,6 +333,23 @@ def bench_seq_balance(layer, x, cfg, seq_len=4096, steps=10, warmup=2):
            "loss": layer.buffers(cfg.T).seq_loss.cpu().tolist()}
     log(f"[bench] seq balance: step {ms:.3f} ms, route+scores {per['route']:.3f} ms, "
         f"statistic {per['seq_balance']:.4f} ms, loss {out['loss']}")
+    # the layer's backward with the balance term: the router's dense backward
+    # (fp32 GEMMs dlogit C and dlogit^T x: 2 * 2 T E H flop)
+    import synth
+    dy = torch.from_numpy(synth.gen_dy(cfg).view(np.int16)).cuda().view(torch.bfloat16)
+    layer.forward(x, seq_len=seq_len)
+    layer.backward(dy, x, seq_len=seq_len)
+    torch.cuda.synchronize()
+    bev = {}
+    for _ in range(3):
+        layer.backward(dy, x, seq_len=seq_len, events=bev)
+    torch.cuda.synchronize()
+    rb = float(np.mean([a.elapsed_time(b) for a, b in bev["router_bwd"]]))
+    flop = 4.0 * cfg.T * cfg.E * cfg.H
+    out.update({"router_bwd_dense_ms": rb, "router_bwd_dense_flop": flop,
+                "router_bwd_dense_TFLOPS": flop / (rb * 1e-3) / 1e12})
+    log(f"[bench] dense router backward: {rb:.3f} ms ({out['router_bwd_dense_TFLOPS']:.0f} TFLOP/s fp32)")
+    del dy
     return out
 
 

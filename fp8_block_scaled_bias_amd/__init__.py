@@ -6,6 +6,7 @@ from ._lib import (MoEError, fp8_quant_1x128, fp8_quant_128x128,  # noqa: F401
                    grouped_fp8_gemm_swiglu, grouped_fp8_wgrad, moe_bias_update, moe_combine,
                    moe_combine_backward, moe_permute, moe_permute_workspace_bytes, moe_route,
                    moe_route_scores, moe_route_workspace_bytes, moe_router_backward,
+                   moe_router_backward_dense, moe_router_backward_dense_workspace_bytes,
                    moe_router_dcentroids, moe_seq_balance, moe_seq_balance_workspace_bytes,
                    swiglu_backward, wgrad_chunks)
 from .layer import BackwardBuffers, Buffers, LayerShape, MoELayer  # noqa: F401

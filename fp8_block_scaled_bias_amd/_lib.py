@@ -49,6 +49,10 @@ SIGNATURES = {
     "moe_router_backward": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i32, _i32,
                                            _vp, _vp, _vp]),
     "moe_router_dcentroids": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp]),
+    "moe_router_backward_dense_workspace_bytes": (_sz, [_i64, _i64, _i32]),
+    "moe_router_backward_dense": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i32,
+                                                 _i32, _i64, _f32, _vp, _vp, _vp, _vp, _vp, _sz,
+                                                 _vp]),
     "grouped_fp8_wgrad": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _vp, _i32, _i64, _i64, _i64,
                                          _vp, _vp]),
     "grouped_fp8_gemm": (ctypes.c_int, [_vp, _vp, _vp, _i64, _vp, _vp, _vp, _i32, _i64, _i64,
@@ -220,6 +224,19 @@ def moe_router_dcentroids(x_bf16, perm_src, group_offsets, dlogit_rows, T, H, E,
                           stream=None):
     return _call("moe_router_dcentroids", _dev(x_bf16), _dev(perm_src), _dev(group_offsets),
                  _dev(dlogit_rows), T, H, E, _dev(d_centroids), _stream(stream))
+
+
+def moe_router_backward_dense_workspace_bytes(T, H, E) -> int:
+    return int(lib().moe_router_backward_dense_workspace_bytes(T, H, E))
+
+
+def moe_router_backward_dense(x_bf16, centroids, topk_idx, d_topk_w, scores, score_sums, seq_f, T,
+                              H, E, k, seq_len, alpha, dx_in_bf16, dx_out_bf16, d_centroids,
+                              dlogit, workspace, workspace_bytes, stream=None):
+    return _call("moe_router_backward_dense", _dev(x_bf16), _dev(centroids), _dev(topk_idx),
+                 _dev(d_topk_w), _dev(scores), _dev(score_sums), _dev(seq_f), T, H, E, k, seq_len,
+                 alpha, _dev(dx_in_bf16), _dev(dx_out_bf16), _dev(d_centroids), _dev(dlogit),
+                 _dev(workspace), workspace_bytes, _stream(stream))
 
 
 def swiglu_backward(gu_bf16, dh_bf16, M, I, dgu_bf16, h_bf16, stream=None):

@@ -35,6 +35,8 @@ backward-for-input and backward-for-weights chunks, section 工程 › DualPipe
                             dW_gu = dGU^T x (x gathered through the permutation)
   8. moe_router_backward    dw -> the gate logits' gradient, dx += its part
      moe_router_dcentroids  the centroids' gradient (the bias has none)
+     (with seq_len: moe_router_backward_dense - the balance term's gradient
+     on every expert's logit joins the gate's, dx and dC as fp32 GEMMs)
 
 The weight transposes (fp8_transpose_128x128) are cached on the layer and
 redone by transpose_weights() when the weights change.
@@ -123,7 +125,17 @@ class Buffers:
 
 
 class BackwardBuffers:
-    """Device buffers of one expert-path backward at T tokens (reused across calls)."""
+    """Device buffers of one layer backward at T tokens (reused across calls)."""
+
+    def dense(self):
+        """Buffers of the dense router backward (allocated on first use):
+        dlogit [T, E] fp32 and its workspace."""
+        if self.dlogit is None:
+            s, T = self._shape, self.T
+            self.dlogit = torch.empty((max(T, 1), s.E), dtype=torch.float32, device=self._dev)
+            self.dense_ws_bytes = max(16, L.moe_router_backward_dense_workspace_bytes(T, s.H, s.E))
+            self.dense_ws = torch.empty((self.dense_ws_bytes,), dtype=torch.uint8, device=self._dev)
+        return self
 
     def __init__(self, shape: LayerShape, T: int, device="cuda"):
         s = shape
@@ -158,6 +170,7 @@ class BackwardBuffers:
         self.dW_gu = torch.empty((s.G, 2 * I, H), dtype=f32, device=dev)
         self.dW_dn = torch.empty((s.G, H, I), dtype=f32, device=dev)
         self.dx_total = torch.empty((T, H), dtype=bf, device=dev)
+        self._shape, self._dev, self.dlogit = s, dev, None
         self.dlogit_rows = torch.empty((max(T * s.k, 1),), dtype=f32, device=dev)
         self.dC = torch.empty((s.E, H), dtype=f32, device=dev)
 
@@ -282,14 +295,18 @@ class MoELayer:
         return bb
 
     def backward(self, dy_bf16: torch.Tensor, x_bf16: torch.Tensor, bufs: Buffers | None = None,
-                 bwd: BackwardBuffers | None = None, stream=None, events: dict | None = None):
+                 bwd: BackwardBuffers | None = None, stream=None, events: dict | None = None,
+                 seq_len: int | None = None, alpha: float = 0.0001):
         """Backward of the layer for the output gradient dy, after a forward of
-        x on `bufs` (its routing, permutation, quantised x and D).  Returns the
-        BackwardBuffers: dx_total (the input gradient), dx (its expert-path
-        part), dw (gate weights), dC (centroids), dW_gu, dW_dn.  `events` as in
-        forward, keys "combine_bwd", "dgrad_down", "recompute_gate_up",
-        "swiglu_bwd", "dgrad_gate_up", "unpermute", "wgrad_down",
-        "wgrad_gate_up", "router_bwd"."""
+        x on `bufs` (its routing, permutation, quantised x and D).  With
+        seq_len (the forward's, which left the scores and f in `bufs`), the
+        loss also holds the sequence-wise balance term alpha * sum_b L_bal,b
+        and the router's backward is the dense one (bwd.dlogit [T, E]).
+        Returns the BackwardBuffers: dx_total (the input gradient), dx (its
+        expert-path part), dw (gate weights), dC (centroids), dW_gu, dW_dn.
+        `events` as in forward, keys "combine_bwd", "dgrad_down",
+        "recompute_gate_up", "swiglu_bwd", "dgrad_gate_up", "unpermute",
+        "wgrad_down", "wgrad_gate_up", "router_bwd"."""
         s = self.shape
         T = dy_bf16.shape[0]
         b = bufs or self.buffers(T)
@@ -339,11 +356,20 @@ class MoELayer:
                                       cap, st),
             L.grouped_fp8_wgrad(bb.c_dgu, bb.s_dgu, bb.c_x, bb.s_x, cap, b.offsets, G, R, 2 * I, H,
                                 bb.dW_gu, st)))
-        step("router_bwd", lambda: (
-            L.moe_router_backward(x_bf16, self.centroids, b.topk_idx, bb.dw, b.inv_perm, bb.dx, T,
-                                  H, s.E, k, bb.dx_total, bb.dlogit_rows, st),
-            L.moe_router_dcentroids(x_bf16, b.perm_src, b.offsets, bb.dlogit_rows, T, H, s.E,
-                                    bb.dC, st)))
+        if seq_len is None:
+            step("router_bwd", lambda: (
+                L.moe_router_backward(x_bf16, self.centroids, b.topk_idx, bb.dw, b.inv_perm, bb.dx,
+                                      T, H, s.E, k, bb.dx_total, bb.dlogit_rows, st),
+                L.moe_router_dcentroids(x_bf16, b.perm_src, b.offsets, bb.dlogit_rows, T, H, s.E,
+                                        bb.dC, st)))
+        else:
+            if getattr(b, "_seq_len", None) != seq_len:
+                raise ValueError("backward with seq_len needs the forward run with the same seq_len")
+            bb.dense()
+            step("router_bwd", lambda: L.moe_router_backward_dense(
+                x_bf16, self.centroids, b.topk_idx, bb.dw, b.scores, b.score_sums, b.seq_f, T, H,
+                s.E, k, seq_len, alpha, bb.dx, bb.dx_total, bb.dC, bb.dlogit, bb.dense_ws,
+                bb.dense_ws_bytes, st))
         return bb
 
     def _route(self, x_bf16, b, seq_len, stream):

@@ -357,6 +357,40 @@ int moe_router_dcentroids(const void* x_bf16, const int32_t* perm_src,
                           int64_t H, int32_t E, float* d_centroids, void* stream);
 
 /*
+ * moe_router_backward_dense - the router's backward when the loss also holds
+ * the sequence-wise balance term alpha * sum_b L_bal,b of moe_seq_balance
+ * (news.qq.com article, section 无额外损耗的负载均衡: the bias only selects,
+ * alpha = 0.0001; section FP8 低精度训练: gating in FP32; the V3 summary at
+ * m.jxzklqfsx.com/aigc/3586.html, section （二）無輔助損失負載均衡策略革新).
+ * With the selection (and so f) held fixed, for token t of sequence b
+ * (L_b tokens), s = scores[t, :], S = score_sums[t]:
+ *   dlogit[t, e] = alpha / L_b * (f[b, e] - sum_i f[b, i] s_i / S) / S
+ *                  * s_e (1 - s_e)
+ *                + on each chosen expert e_j: (dw_j - sum_i dw_i w_i) / S_sel
+ *                  * s_j (1 - s_j), S_sel = sum_j s_{e_j}, w_j = s_{e_j} / S_sel
+ *   dx_out[t, :]  = bf16(dx_in[t, :] + sum_e dlogit[t, e] C[e, :])  (fp32 sums)
+ *   d_centroids[e, :] = sum_t dlogit[t, e] x[t, :]  (fp32, tokens in slices of
+ *                       ~1024 summed in order, then the slices in order)
+ * x_bf16 [T, H]; centroids [E, H] fp32; topk_idx, d_topk_w [T, k]; scores,
+ * score_sums: moe_route_scores' outputs of the forward; seq_f [B, E]:
+ * moe_seq_balance's f for the same seq_len; dx_in_bf16 [T, H] or NULL (0),
+ * must not alias dx_out; dx_out_bf16 (out) [T, H]; d_centroids (out) [E, H];
+ * dlogit (out) [T, E] fp32.  workspace:
+ * moe_router_backward_dense_workspace_bytes(T, H, E) bytes (0: none needed).
+ * Requirements: E % 16 == 0, 16 <= E <= 256, 1 <= k <= 8, H % 128 == 0,
+ * 1 <= seq_len <= 65536; x, centroids, scores, seq_f, dx_in, dx_out,
+ * d_centroids, dlogit 16-byte aligned.  T = 0 writes d_centroids = 0.
+ */
+size_t moe_router_backward_dense_workspace_bytes(int64_t T, int64_t H, int32_t E);
+int moe_router_backward_dense(const void* x_bf16, const float* centroids,
+                              const int32_t* topk_idx, const float* d_topk_w,
+                              const float* scores, const float* score_sums, const float* seq_f,
+                              int64_t T, int64_t H, int32_t E, int32_t k, int64_t seq_len,
+                              float alpha, const void* dx_in_bf16, void* dx_out_bf16,
+                              float* d_centroids, float* dlogit, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/*
  * grouped_fp8_gemm - block-scaled FP8 grouped GEMM with FP32 accumulation
  * (news.qq.com article, section FP8 低精度训练, items 细粒度量化 and
  * 提高累加精度).

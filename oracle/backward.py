@@ -143,11 +143,17 @@ def router_backward(x_bits, centroids, idx, dw):
 
 
 def layer_backward(dy_bits, fwd: dict, wts, x_bits, centroids, T: int, k: int, I: int,
-                   n_shared: int = 1):
+                   n_shared: int = 1, seq_len: int | None = None, alpha: float = 0.0001):
     """Whole-layer backward: expert_backward's results plus dlogit and dC from
-    router_backward on its dw, and dx_total = bf16(dx_expert + dx_router)."""
+    router_backward on its dw (router_backward_with_balance when the loss
+    holds the sequence-wise balance term over runs of seq_len tokens), and
+    dx_total = bf16(dx_expert + dx_router)."""
     eb = expert_backward(dy_bits, fwd, wts, x_bits, T, k, I, n_shared)
-    rb = router_backward(x_bits, centroids, fwd["route"]["idx"], eb["dw"])
+    if seq_len is None:
+        rb = router_backward(x_bits, centroids, fwd["route"]["idx"], eb["dw"])
+    else:
+        rb = router_backward_with_balance(x_bits, centroids, fwd["route"]["idx"], eb["dw"],
+                                          seq_len, alpha)
     out = dict(eb)
     out.update(dx_expert=eb["dx"], dx=bf16_round(eb["dx"] + rb["dx"]), dlogit=rb["dlogit"],
                dC=rb["dC"])

@@ -167,6 +167,23 @@ def test_route_scores_and_seq_balance_validation():
     assert b(T=0, out=None, ws=None) == L.MOE_OK
 
 
+def test_router_backward_dense_validation():
+    def d(T=64, H=256, E=16, k=4, L_=32, dxo=FAKE, dC=FAKE, ws=FAKE, wsb=1 << 30, dxi=None):
+        return rc("moe_router_backward_dense", FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, T, H, E, k,
+                  L_, 1e-4, dxi, dxo, dC, FAKE, ws, wsb, None)
+    assert d(E=24) == L.MOE_ERR_INVALID and d(E=272) == L.MOE_ERR_INVALID
+    assert d(k=9) == L.MOE_ERR_INVALID and d(H=192) == L.MOE_ERR_INVALID
+    assert d(L_=0) == L.MOE_ERR_INVALID and d(dC=None) == L.MOE_ERR_INVALID
+    assert d(dxo=None) == L.MOE_ERR_INVALID
+    assert d(dxi=FAKE) == L.MOE_ERR_INVALID and "alias" in L.last_error()
+    assert d(dxo=ctypes.c_void_p(4104)) == L.MOE_ERR_INVALID and "aligned" in L.last_error()
+    # slices of ~1024 tokens, at most 16; one slice needs no workspace
+    assert L.moe_router_backward_dense_workspace_bytes(1000, 256, 16) == 0
+    assert L.moe_router_backward_dense_workspace_bytes(16384, 7168, 256) == 16 * 256 * 7168 * 4
+    assert L.moe_router_backward_dense_workspace_bytes(2000, 256, 16) == 2 * 16 * 256 * 4
+    assert d(T=2000, wsb=16) == L.MOE_ERR_WORKSPACE
+
+
 def test_route_group_size_two_is_valid_shape():
     # E=16 in 8 groups has group size 2: valid, but 2 is not 4 * 2^n
     assert rc("moe_route", FAKE, 8, 256, FAKE, FAKE, 16, 8, 2, 4, FAKE, FAKE, FAKE, FAKE, 1 << 30,

@@ -11,7 +11,13 @@
   sequence, seq_len 1, unchosen experts;
 * MoELayer.forward(seq_len=...) on the mid config, and the same two calls at
   V3 shapes (T=16384, sequences of 4096), against the oracle's statistic on
-  the GPU's own choice.
+  the GPU's own choice;
+* moe_router_backward_dense (the router's backward with the balance term):
+  dlogit against the oracle within 2^-14 of the token's gradient scale; dx
+  and dC against the exact sums of the GPU's own dlogit within their fp32
+  accumulation bounds (dx plus one bf16 rounding); ragged tiles, one and
+  several token slices, with and without an incoming dx; and the layer's
+  backward with seq_len end to end against the oracle's chain.
 """
 import numpy as np
 import pytest
@@ -21,8 +27,12 @@ import synth
 import fp8_block_scaled_bias_amd as M
 from gpu_common import bf16_dev, compare_routes, dev, host, log
 from test_gpu_layer import build_layer
+from oracle import backward as OBK
 from oracle import balance as OB
+from oracle import formats as OF
+from oracle import layer as OL
 from oracle import route as OR
+from gpu_common import assert_within_one_bf16_ulp, bf16_values_host, rel_l2
 
 pytestmark = pytest.mark.gpu
 
@@ -189,3 +199,101 @@ def test_seq_balance_v3_prefill():
     s_ref, _ = OR.router_scores(x, C, b)
     assert np.abs(host(sc) - s_ref).max() <= 4e-6
     _check_layer(bufs, s_ref, host(idx), 4096, cfg, "V3 prefill")
+
+
+def check_dense_router(xbits, C, idx, dw, scores, ssum, seq_len, alpha, dx_in, dl, dx, dC, label,
+                       extra_rel=0.0):
+    """GPU dlogit [T, E], dx (bf16 values) and dC against the oracle (dlogit)
+    and the exact sums of the GPU's own dlogit (dx, dC).  extra_rel widens
+    the dlogit bound when the scores themselves carry the router's error."""
+    T, k = idx.shape
+    E = C.shape[0]
+    ref = OBK.router_backward_with_balance(xbits, C, idx, dw, seq_len, alpha)
+    s64 = np.asarray(scores, np.float64)
+    sel = np.take_along_axis(s64, idx.astype(np.int64), 1)
+    Ssel = sel.sum(1)
+    dw64 = np.abs(np.asarray(dw, np.float64))
+    st = OB.seq_balance(s64, idx, seq_len, alpha)
+    Lb = np.array([min(seq_len, T - (t // seq_len) * seq_len) for t in range(T)], np.float64)
+    fmax = st["f"].max(1)[np.arange(T) // seq_len]
+    scale = (dw64.max(1) + np.sum(dw64 * sel, 1) / Ssel) / Ssel + abs(alpha) / Lb * fmax / s64.sum(1)
+    err = np.abs(dl - ref["dlogit"])
+    tol = (2.0 ** -14 + extra_rel) * scale[:, None]
+    log(f"[dense router] {label}: max |dlogit err| / bound {float((err / tol).max()):.2e}")
+    assert (err <= tol).all(), label
+    Cd = np.asarray(C, np.float32).astype(np.float64)
+    dl64 = np.asarray(dl, np.float64)
+    base = np.zeros((T, Cd.shape[1])) if dx_in is None else np.asarray(dx_in, np.float64)
+    exact = base + dl64 @ Cd
+    acc = (E + 2) * 2.0 ** -24 * (np.abs(base) + np.abs(dl64) @ np.abs(Cd))
+    assert_within_one_bf16_ulp(dx, exact, f"{label} dx", acc)
+    xv = OF.bf16_value_from_bits(xbits)
+    exC = dl64.T @ xv
+    bndC = (1024 + 16 + 2) * 2.0 ** -24 * (np.abs(dl64).T @ np.abs(xv)) + 1e-30
+    ratio = np.abs(np.asarray(dC, np.float64) - exC) / bndC
+    log(f"[dense router] {label}: max |dC err| / bound {float(ratio.max()):.2e}")
+    assert (ratio <= 1).all(), label
+
+
+@pytest.mark.parametrize("T,H,E,k,seq_len,mode", [(300, 256, 16, 4, 128, "dx_in"),
+                                                  (2100, 1024, 64, 8, 1000, "none"),
+                                                  (130, 7168, 256, 8, 4096, "dx_in")])
+def test_router_backward_dense_kernel(T, H, E, k, seq_len, mode):
+    rng = np.random.default_rng([T, H, E])
+    xbits = synth.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    C = (rng.standard_normal((E, H)) * 0.02).astype(np.float32)
+    idx = np.sort(np.stack([rng.choice(E, k, replace=False) for _ in range(T)]), 1).astype(np.int32)
+    dw = rng.standard_normal((T, k)).astype(np.float32)
+    s_ref, _ = OR.router_scores(xbits, C, np.zeros(E, np.float32))
+    scores = s_ref.astype(np.float32)
+    ssum = scores.astype(np.float64).sum(1).astype(np.float32)
+    alpha = 0.05
+    f = OB.seq_balance(scores.astype(np.float64), idx, seq_len, alpha)["f"].astype(np.float32)
+    dx_in = synth.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32)) if mode == "dx_in" else None
+    log(f"[dense router] T={T} H={H} E={E} k={k} seq_len={seq_len} {mode}")
+    wsb = max(16, M.moe_router_backward_dense_workspace_bytes(T, H, E))
+    ws = torch.empty((wsb,), dtype=torch.uint8, device="cuda")
+    dx = torch.full((T, H), float("nan"), dtype=torch.bfloat16, device="cuda")
+    dC, dl = _f32((E, H)), _f32((T, E))
+    M.moe_router_backward_dense(bf16_dev(xbits), dev(C), dev(idx), dev(dw), dev(scores), dev(ssum),
+                                dev(f), T, H, E, k, seq_len, alpha,
+                                None if dx_in is None else bf16_dev(dx_in), dx, dC, dl, ws, wsb)
+    torch.cuda.synchronize()
+    check_dense_router(xbits, C, idx, dw, scores, ssum, seq_len, alpha,
+                       None if dx_in is None else OF.bf16_value_from_bits(dx_in), host(dl),
+                       bf16_values_host(dx), host(dC), f"T={T} E={E}")
+
+
+def test_layer_backward_with_balance_mid():
+    """MoELayer.forward and backward with seq_len on the mid config: the
+    router stage against the oracle on the GPU's own dw, scores and dx, then
+    dx_total and dC end to end against the oracle's chain."""
+    cfg = synth.MID
+    T, k, I, L_ = cfg.T, cfg.k, cfg.I, 64
+    alpha = 0.5
+    layer, C, b = build_layer(cfg)
+    x = synth.gen_x(cfg)
+    dy = synth.gen_dy(cfg)
+    log(f"[layer bwd balance] mid: T={T}, seq_len {L_}, alpha {alpha}")
+    x_d = bf16_dev(x)
+    layer.forward(x_d, seq_len=L_, alpha=alpha)
+    bufs = layer.buffers(T)
+    bb = layer.backward(bf16_dev(dy), x_d, seq_len=L_, alpha=alpha)
+    torch.cuda.synchronize()
+    idx = host(bufs.topk_idx)
+    fwd = OL.layer(x, C, b, _oracle_weights(cfg), cfg.n_group, cfg.topk_group, k, I)
+    assert len(compare_routes(idx, fwd["route"], "mid")) == 0
+    # the scores carry the router's error (<= 4e-6 each): widen the bound
+    check_dense_router(x, C, idx, host(bb.dw), host(bufs.scores), host(bufs.score_sums), L_, alpha,
+                       bf16_values_host(bb.dx), host(bb.dlogit), bf16_values_host(bb.dx_total),
+                       host(bb.dC), "mid layer", extra_rel=1e-4)
+    ref = OBK.layer_backward(dy, fwd, _oracle_weights(cfg), x, C, T, k, I, seq_len=L_, alpha=alpha)
+    errs = dict(dx=rel_l2(bf16_values_host(bb.dx_total), ref["dx"]),
+                dC=rel_l2(host(bb.dC), ref["dC"]))
+    log(f"[layer bwd balance] mid: end to end " + ", ".join(f"{k_} {v:.2e}" for k_, v in errs.items()))
+    assert max(errs.values()) <= 5e-3, errs
+
+
+def _oracle_weights(cfg):
+    from test_gpu_layer import oracle_weights
+    return oracle_weights(cfg)

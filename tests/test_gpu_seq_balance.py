@@ -297,3 +297,69 @@ def test_layer_backward_with_balance_mid():
 def _oracle_weights(cfg):
     from test_gpu_layer import oracle_weights
     return oracle_weights(cfg)
+
+
+def test_router_backward_dense_v3_prefill_sampled():
+    """V3 shapes at T=16384 in sequences of 4096 (the benchmark's batch): the
+    GPU's routing, scores and statistic, dw N(0,1), alpha = 1e-4; dlogit and
+    dx on 48 sampled tokens, dC on 4 sampled experts (over every token)."""
+    cfg = synth.PREFILL
+    T, H, E, k, L_ = cfg.T, cfg.H, cfg.E, cfg.k, 4096
+    alpha = 1e-4
+    x = synth.gen_x(cfg)
+    C, b = synth.gen_centroids(cfg), synth.gen_bias(cfg)
+    log(f"[dense router] V3 prefill T={T}: route with scores, statistic, backward")
+    wsb = max(16, M.moe_route_workspace_bytes(T, H, E))
+    ws = torch.empty((wsb,), dtype=torch.uint8, device="cuda")
+    idx, w, cnt, sc, ss = _i32((T, k)), _f32((T, k)), _i32((E,)), _f32((T, E)), _f32((T,))
+    x_d, C_d = bf16_dev(x), dev(C)
+    M.moe_route_scores(x_d, T, H, C_d, dev(b), E, cfg.n_group, cfg.topk_group, k, idx, w, cnt, ws,
+                       wsb, sc, ss)
+    B = T // L_
+    f, p, loss = _f32((B, E)), _f32((B, E)), _f32((B,))
+    swb = M.moe_seq_balance_workspace_bytes(T, E, L_)
+    sw = torch.empty((swb,), dtype=torch.uint8, device="cuda")
+    M.moe_seq_balance(sc, ss, idx, T, E, k, L_, alpha, f, p, loss, sw, swb)
+    dw = np.random.default_rng(12).standard_normal((T, k)).astype(np.float32)
+    dx_in = synth.gen_dy(cfg)
+    dwb = max(16, M.moe_router_backward_dense_workspace_bytes(T, H, E))
+    dws = torch.empty((dwb,), dtype=torch.uint8, device="cuda")
+    dx = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    dC, dl = _f32((E, H)), _f32((T, E))
+    M.moe_router_backward_dense(x_d, C_d, idx, dev(dw), sc, ss, f, T, H, E, k, L_, alpha,
+                                bf16_dev(dx_in), dx, dC, dl, dws, dwb)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(13)
+    toks = np.sort(np.concatenate([[0, L_ - 1, L_, T - 1], rng.choice(T, 44, replace=False)]))
+    idx_h, dl_h, sc_h, f_h = host(idx), host(dl), host(sc), host(f)
+    s_ref, _ = OR.router_scores(x[toks], C, b)
+    # dlogit on the sampled tokens: the oracle's formulas on exact scores with
+    # the GPU's f (the statistic is checked on its own elsewhere)
+    sel = np.take_along_axis(s_ref, idx_h[toks].astype(np.int64), 1)
+    Ssel = sel.sum(1, keepdims=True)
+    dwt = dw[toks].astype(np.float64)
+    gate = (dwt - np.sum(dwt * sel / Ssel, 1, keepdims=True)) / Ssel * sel * (1 - sel)
+    S = s_ref.sum(1, keepdims=True)
+    fb = f_h[toks // L_].astype(np.float64)
+    ref = alpha / L_ * (fb - np.sum(fb * s_ref / S, 1, keepdims=True)) / S * s_ref * (1 - s_ref)
+    np.add.at(ref, (np.repeat(np.arange(len(toks)), k), idx_h[toks].reshape(-1)), gate.reshape(-1))
+    scale = (np.abs(dwt).max(1) + np.sum(np.abs(dwt) * sel, 1) / Ssel[:, 0]) / Ssel[:, 0] \
+        + alpha / L_ * fb.max(1) / S[:, 0]
+    err = np.abs(dl_h[toks] - ref)
+    log(f"[dense router] V3: max |dlogit err| / scale {float((err / scale[:, None]).max()):.2e}")
+    assert (err <= (2.0 ** -14 + 1e-4) * scale[:, None]).all()
+    # dx on the sampled tokens from the GPU's own dlogit
+    Cd = C.astype(np.float64)
+    dl64 = dl_h[toks].astype(np.float64)
+    base = OF.bf16_value_from_bits(dx_in[toks])
+    exact = base + dl64 @ Cd
+    acc = (E + 2) * 2.0 ** -24 * (np.abs(base) + np.abs(dl64) @ np.abs(Cd))
+    assert_within_one_bf16_ulp(bf16_values_host(dx)[toks], exact, "V3 dense dx", acc)
+    # dC on sampled experts over every token
+    xv = OF.bf16_value_from_bits(x)
+    dCh = host(dC).astype(np.float64)
+    for e in [0, 255] + list(rng.choice(E, 2, replace=False)):
+        col = dl_h[:, e].astype(np.float64)
+        ex = col @ xv
+        bnd = (1024 + 16 + 2) * 2.0 ** -24 * (np.abs(col) @ np.abs(xv)) + 1e-30
+        assert (np.abs(dCh[e] - ex) <= bnd).all(), e

@@ -258,6 +258,11 @@ __global__ __launch_bounds__(RB) void router_backward_kernel(
 
 constexpr int DC_COLS = RB * 8;
 
+__global__ __launch_bounds__(RB) void zero_f32_kernel(float* __restrict__ p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * RB + threadIdx.x; i < n; i += (int64_t)gridDim.x * RB)
+    p[i] = 0.0f;
+}
+
 __global__ __launch_bounds__(RB) void router_dcentroids_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ perm_src,
     const int32_t* __restrict__ offs, const float* __restrict__ dlogit_rows, int64_t H,
@@ -315,7 +320,13 @@ extern "C" int moe_router_dcentroids(const void* x_bf16, const int32_t* perm_src
   MOE_INVALID(E >= 1 && E <= 65535, "moe_router_dcentroids: E=%d out of [1, 65535]", (int)E);
   MOE_INVALID(H > 0 && H % 8 == 0, "moe_router_dcentroids: H=%lld must be a positive multiple of 8",
               (long long)H);
-  MOE_INVALID(x_bf16 && perm_src && group_offsets && dlogit_rows && d_centroids,
+  MOE_INVALID(d_centroids && ((uintptr_t)d_centroids & 15) == 0,
+              "moe_router_dcentroids: d_centroids must be non-null and 16-byte aligned");
+  if (T == 0) {  // no rows: the gradient is zero
+    zero_f32_kernel<<<dim3(256), dim3(RB), 0, as_stream(stream)>>>(d_centroids, (int64_t)E * H);
+    return check_launch("moe_router_dcentroids(zero)");
+  }
+  MOE_INVALID(x_bf16 && perm_src && group_offsets && dlogit_rows,
               "moe_router_dcentroids: null pointer");
   MOE_INVALID(((uintptr_t)x_bf16 & 15) == 0 && ((uintptr_t)d_centroids & 15) == 0,
               "moe_router_dcentroids: x and d_centroids must be 16-byte aligned");

@@ -270,6 +270,7 @@ extern "C" int fp8_quant_128x1_grouped(const void* in_bf16, int64_t ld_in,
               "fp8_quant_128x1_grouped: C=%lld must be a positive multiple of 128 (at most 65535*128)",
               (long long)C);
   MOE_INVALID(ld_in >= C, "fp8_quant_128x1_grouped: ld_in=%lld < C", (long long)ld_in);
+  if (M_total == 0) return MOE_OK;  // every group is empty: no chunk to write
   MOE_INVALID(row_index ? (in_rows >= 1 && in_rows < (1ll << 31)) : in_rows >= M_total,
               "fp8_quant_128x1_grouped: in_rows=%lld must be >= %s and < 2^31", (long long)in_rows,
               row_index ? "1" : "M_total");

@@ -350,7 +350,8 @@ int moe_router_backward(const void* x_bf16, const float* centroids, const int32_
  * x_bf16 [T, H]; perm_src, dlogit_rows: moe_permute's / moe_router_backward's;
  * group_offsets [E+1] (the routed part of moe_permute's offsets, on the device);
  * d_centroids (out) [E, H] fp32.  Requirements: H % 8 == 0, 1 <= E <= 65535;
- * x and d_centroids 16-byte aligned.
+ * x and d_centroids 16-byte aligned.  T = 0 writes d_centroids = 0 (the other
+ * pointers may then be NULL).
  */
 int moe_router_dcentroids(const void* x_bf16, const int32_t* perm_src,
                           const int32_t* group_offsets, const float* dlogit_rows, int64_t T,

@@ -336,3 +336,28 @@ def test_layer_backward_small(name):
                 dW_gu=rel_l2(host(bb.dW_gu), ref["dW_gu"]), dW_dn=rel_l2(host(bb.dW_dn), ref["dW_dn"]))
     log(f"[layer bwd] {name}: end to end " + ", ".join(f"{k_} {v:.2e}" for k_, v in errs.items()))
     assert max(errs.values()) <= 5e-3, errs
+
+
+def test_layer_empty_batch():
+    """T = 0: the forward (with the bias update and the balance statistic)
+    and the backward run as no-ops: counts zero, bias unchanged, weight and
+    centroid gradients zero."""
+    cfg = synth.TINY
+    layer, C, b = build_layer(cfg)
+    log("[layer] empty batch T=0")
+    x = torch.empty((0, cfg.H), dtype=torch.bfloat16, device="cuda")
+    bias0 = host(layer.bias).copy()
+    y = layer.forward(x, update_bias=True)
+    assert tuple(y.shape) == (0, cfg.H)
+    bufs = layer.buffers(0)
+    torch.cuda.synchronize()
+    assert not host(bufs.counts).any() and np.array_equal(host(layer.bias), bias0)
+    assert not host(bufs.offsets).any()
+    for seq_len in (None, 16):
+        if seq_len:
+            layer.forward(x, seq_len=seq_len)
+        bb = layer.backward(torch.empty((0, cfg.H), dtype=torch.bfloat16, device="cuda"), x,
+                            seq_len=seq_len)
+        torch.cuda.synchronize()
+        assert not host(bb.dW_gu).any() and not host(bb.dW_dn).any() and not host(bb.dC).any()
+        assert tuple(bb.dx_total.shape) == (0, cfg.H)

@@ -269,7 +269,9 @@ def bench_backward_step(layer, x, cfg, steps=3, warmup=1):
     (synth.gen_dy).  The weight transposes are made once per weight update
     (cached on the layer, timed under "backward").  Flops counted: the GEMMs
     only, 2RHI for each of dgrad-down and wgrad-down, 4RHI for each of the
-    recomputed gate+up, dgrad-gate+up and wgrad-gate+up (34.6 TFLOP)."""
+    recomputed gate+up, dgrad-gate+up and wgrad-gate+up (34.6 TFLOP).  Then
+    a training step (forward + backward, wall clock) with the gate+up GEMM
+    rerun in the backward and with the forward keeping its outputs."""
     import time
     import numpy as np
     import torch
@@ -294,6 +296,21 @@ def bench_backward_step(layer, x, cfg, steps=3, warmup=1):
            "flop_per_step": flop, "per_stage_ms": per}
     log(f"[bench] backward step: {ms:.3f} ms ({out['TFLOPS']:.0f} TFLOP/s); " +
         ", ".join(f"{k} {v:.3f}" for k, v in per.items()))
+    # a training step (forward + backward) both ways: the fused forward with
+    # the gate+up GEMM run again in the backward, or the unfused forward that
+    # keeps the bf16 gate/up outputs (1.2 GB) for the backward to read
+    for name, keep in (("train_step_recompute", False), ("train_step_keep_gu", True)):
+        layer.forward(x, keep_gu=keep)
+        layer.backward(dy, x)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            layer.forward(x, keep_gu=keep)
+            layer.backward(dy, x)
+        torch.cuda.synchronize()
+        out[name + "_ms"] = (time.perf_counter() - t0) / steps * 1e3
+    log(f"[bench] training step: {out['train_step_recompute_ms']:.3f} ms recomputing gate+up, "
+        f"{out['train_step_keep_gu_ms']:.3f} ms keeping it")
     del dy
     return out
 
@@ -301,12 +318,12 @@ def bench_backward_step(layer, x, cfg, steps=3, warmup=1):
 # HBM traffic of the gate+up kernel at T=16384, from two rocprofv3 --pmc runs
 # (FETCH_SIZE, WRITE_SIZE) of this script, each scaled by the same counter on
 # the 1 GiB copy probe.  Valid only for the kernel source with this digest.
-GATE_UP_TRAFFIC = {"gemm_src": "38f0b00aa90fd45b",
-                   # FETCH_SIZE 9,393,070 KiB x 2.000 + WRITE_SIZE 311,488 KiB x 1.000
-                   "bytes": 9393070 * 1024 * 2 + 311488 * 1024}
+GATE_UP_TRAFFIC = {"gemm_src": "96416b49b44a1449",
+                   # FETCH_SIZE 9,133,671 KiB x 2.000 + WRITE_SIZE 311,311 KiB x 1.000
+                   "bytes": 9133671 * 1024 * 2 + 311311 * 1024}
 
 
-def bench_seq_balance(layer, x, cfg, seq_len=4096, steps=10, warmup=2):
+def bench_seq_balance(layer, x, cfg, seq_len=4096, steps=10, warmup=2, backward=True):
     """The layer forward with the sequence-wise balance statistic (sequences
     of seq_len tokens): per-step time, the router with its score output and
     the statistic itself (HIP events on the launch stream, mean over steps).
@@ -333,6 +350,8 @@ def bench_seq_balance(layer, x, cfg, seq_len=4096, steps=10, warmup=2):
            "loss": layer.buffers(cfg.T).seq_loss.cpu().tolist()}
     log(f"[bench] seq balance: step {ms:.3f} ms, route+scores {per['route']:.3f} ms, "
         f"statistic {per['seq_balance']:.4f} ms, loss {out['loss']}")
+    if not backward:
+        return out
     # the layer's backward with the balance term: the router's dense backward
     # (fp32 GEMMs dlogit C and dlogit^T x: 2 * 2 T E H flop)
     import synth
@@ -482,7 +501,7 @@ def main():
     bwd = bench_backward(layer, cfg.T) if not args.no_backward else None
     bstep = bench_backward_step(layer, x, cfg) if not args.no_backward else None
     skew = bench_skewed(layer, args.skewed_steps) if args.skewed_steps > 0 else None
-    seqb = bench_seq_balance(layer, x, cfg)
+    seqb = bench_seq_balance(layer, x, cfg, backward=not args.no_backward)
 
     traffic = None
     if GATE_UP_TRAFFIC and GATE_UP_TRAFFIC["gemm_src"] == gemm_source_digest():

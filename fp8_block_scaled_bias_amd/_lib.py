@@ -59,6 +59,8 @@ SIGNATURES = {
                                         _i64, _vp, _vp]),
     "grouped_fp8_gemm_swiglu": (ctypes.c_int, [_vp, _vp, _vp, _i64, _vp, _vp, _vp, _i32, _i64,
                                                _i64, _i64, _vp, _vp, _vp]),
+    "grouped_fp8_gemm_swiglu_keep": (ctypes.c_int, [_vp, _vp, _vp, _i64, _vp, _vp, _vp, _i32, _i64,
+                                                    _i64, _i64, _vp, _vp, _vp, _vp]),
     "moe_combine": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i32, _i64, _vp, _vp]),
 }
 
@@ -262,6 +264,13 @@ def grouped_fp8_gemm_swiglu(A, A_scale, a_row_index, B, B_scale, group_offsets, 
     return _call("grouped_fp8_gemm_swiglu", _dev(A), _dev(A_scale), _dev(a_row_index), _rows(A),
                  _dev(B), _dev(B_scale), _dev(group_offsets), G, M_total, I, K, _dev(H_e4m3),
                  _dev(H_scale), _stream(stream))
+
+
+def grouped_fp8_gemm_swiglu_keep(A, A_scale, a_row_index, B, B_scale, group_offsets, G, M_total,
+                                 I, K, H_e4m3, H_scale, GU_bf16, stream=None):
+    return _call("grouped_fp8_gemm_swiglu_keep", _dev(A), _dev(A_scale), _dev(a_row_index),
+                 _rows(A), _dev(B), _dev(B_scale), _dev(group_offsets), G, M_total, I, K,
+                 _dev(H_e4m3), _dev(H_scale), _dev(GU_bf16), _stream(stream))
 
 
 def moe_combine(expert_out_bf16, inv_perm, topk_w, shared_out_bf16, T, k, H, y_bf16,

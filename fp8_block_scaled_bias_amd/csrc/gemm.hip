@@ -433,19 +433,27 @@ int launch(const GemmArgs& a, hipStream_t st) {
   return MOE_OK;
 }
 
+// the 256x256 kernel: groups of at least 160 rows on average; it addresses
+// a tile's output, A and one group's B with 32-bit offsets, and takes an
+// even number of at least 6 K blocks
 template <bool SWIGLU>
-int dispatch(const GemmArgs& a, int64_t M_total, hipStream_t st) {
-  // rows per group decide the M tile: 128 for prefill-sized groups, 32 when
-  // groups hold a handful of rows (decode), 64 in between
+bool takes_wide(const GemmArgs& a, int64_t M_total) {
   const int64_t avg = M_total / a.G;
-  // the 256x256 kernel addresses a tile's output, A and one group's B with
-  // 32-bit offsets, and takes an even number of at least 6 K blocks
   const int64_t nkb = a.K / 128;
   const int64_t lim = (int64_t)1 << 32;
   const bool wide_ok = (SWIGLU ? a.I <= (1 << 22) : (a.N % 256 == 0 && a.N <= (1 << 21))) &&
                        nkb >= 6 && nkb % 2 == 0 && a.K <= (1 << 20) && a.N * a.K < lim &&
                        a.A_rows * a.K < lim;
-  if (avg >= 160 && wide_ok) return launch_wide(a, SWIGLU, st);
+  return avg >= 160 && wide_ok;
+}
+
+template <bool SWIGLU>
+int dispatch(const GemmArgs& a, int64_t M_total, hipStream_t st) {
+  // rows per group decide the M tile: 256 (the wide kernel) or 128 for
+  // prefill-sized groups, 32 when groups hold a handful of rows (decode), 64
+  // in between
+  const int64_t avg = M_total / a.G;
+  if (takes_wide<SWIGLU>(a, M_total)) return launch_wide(a, SWIGLU, st);
   if (avg >= 96) return launch<128, 2, 3, SWIGLU>(a, st);
   if (avg >= 40) return launch<64, 1, 3, SWIGLU>(a, st);
   return launch<32, 1, 4, SWIGLU>(a, st);
@@ -522,4 +530,46 @@ extern "C" int grouped_fp8_gemm_swiglu(const uint8_t* A, const float* A_scale,
   rc = dispatch<true>(a, M_total, as_stream(stream));
   if (rc != MOE_OK) return rc;
   return check_launch("grouped_fp8_gemm_swiglu");
+}
+
+extern "C" int grouped_fp8_gemm_swiglu_keep(const uint8_t* A, const float* A_scale,
+                                            const int32_t* a_row_index, int64_t A_rows,
+                                            const uint8_t* B, const float* B_scale,
+                                            const int32_t* group_offsets, int32_t G,
+                                            int64_t M_total, int64_t I, int64_t K,
+                                            uint8_t* H_e4m3, float* H_scale, void* GU_bf16,
+                                            void* stream) {
+  clear_error();
+  MOE_INVALID(I > 0 && I % 128 == 0, "grouped_fp8_gemm_swiglu_keep: I=%lld must be a positive "
+              "multiple of 128", (long long)I);
+  int rc = validate_common("grouped_fp8_gemm_swiglu_keep", A, A_scale, a_row_index, A_rows, B,
+                           B_scale, group_offsets, G, M_total, 2 * I, K);
+  if (rc != MOE_OK || M_total == 0) return rc;
+  MOE_INVALID(H_e4m3 && H_scale && ((uintptr_t)H_e4m3 & 15) == 0,
+              "grouped_fp8_gemm_swiglu_keep: H must be non-null and 16-byte aligned");
+  MOE_INVALID(GU_bf16 && ((uintptr_t)GU_bf16 & 15) == 0,
+              "grouped_fp8_gemm_swiglu_keep: GU must be non-null and 16-byte aligned");
+  GemmArgs a{};
+  a.A = A; a.A_scale = A_scale; a.a_row_index = a_row_index; a.A_rows = A_rows;
+  a.B = B; a.B_scale = B_scale;
+  a.offs = group_offsets; a.G = G; a.N = 2 * I; a.K = K; a.ntiles = I / 128; a.I = I;
+  a.Hq = H_e4m3; a.Hs = H_scale;
+  hipStream_t st = as_stream(stream);
+  if (takes_wide<true>(a, M_total)) {
+    a.GU = static_cast<uint16_t*>(GU_bf16);  // the fused kernel writes both
+    rc = launch_wide(a, true, st);
+  } else {
+    // smaller groups: the fused kernel, then the plain GEMM for the sums
+    rc = dispatch<true>(a, M_total, st);
+    if (rc == MOE_OK) {
+      GemmArgs p{};
+      p.A = A; p.A_scale = A_scale; p.a_row_index = a_row_index; p.A_rows = A_rows;
+      p.B = B; p.B_scale = B_scale;
+      p.offs = group_offsets; p.G = G; p.N = 2 * I; p.K = K; p.ntiles = ceil_div(2 * I, BN);
+      p.C = static_cast<uint16_t*>(GU_bf16);
+      rc = dispatch<false>(p, M_total, st);
+    }
+  }
+  if (rc != MOE_OK) return rc;
+  return check_launch("grouped_fp8_gemm_swiglu_keep");
 }

@@ -35,6 +35,7 @@ struct GemmArgs {
   uint16_t* C;     // bf16 out [M_total, N]
   uint8_t* Hq;     // SwiGLU out [M_total, I]
   float* Hs;       // SwiGLU scales [M_total, I/128]
+  uint16_t* GU;    // SwiGLU, or null: also the bf16 gate/up sums [M_total, 2I]
 };
 
 // s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt bits [3:0] and

@@ -166,7 +166,7 @@ __device__ __forceinline__ void build_cost_prefix(const int* s_offs, int G, int*
   }
 }
 
-template <bool SWIGLU, bool GATHER>
+template <bool SWIGLU, bool GATHER, bool KEEP = false>
 __global__ __launch_bounds__(WT, 1) void wide_gemm_kernel(GemmArgs args) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[LDS];
   __shared__ int s_red[8];
@@ -654,6 +654,49 @@ __global__ __launch_bounds__(WT, 1) void wide_gemm_kernel(GemmArgs args) {
         }
       }
     } else {
+      // KEEP: the bf16 gate/up sums too, staged like the plain epilogue (a
+      // wave's 64 rows x 64 columns per half, in its own 8 KB of stage 1;
+      // every wave's reads are done before the barrier below, after which
+      // the codes reuse that memory).  Half c = 0 holds gate columns
+      // 128 nt + 64 wn + 32 jj + 8 g + 4 q (+0..3) of blocks j = jj, half
+      // c = 1 the up columns I + the same, of blocks j = 2 + jj.
+      if (KEEP && wvalid) {
+        const int I2 = 2 * (int)args.I;
+        const uint32_t rowb = (uint32_t)I2 * 2;
+        const __amdgpu_buffer_rsrc_t rs =
+            out_rsrc(args.GU + (int64_t)t.m0 * I2, (uint32_t)min(t.m1 - t.m0, WBM) * rowb);
+        uint8_t* reg = smem + (wv < 4 ? ST_BYTES + wv * 8192 : OFF_B + ST_BYTES + (wv - 4) * 8192);
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            const int row = 32 * i + l32;
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+              for (int g = 0; g < 4; ++g) {
+                const v16f& v = acc[i][2 * c + jj];
+                typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+                const v2u w = {f32x2_to_bf16x2(v[4 * g], v[4 * g + 1]),
+                               f32x2_to_bf16x2(v[4 * g + 2], v[4 * g + 3])};
+                const int chunk = (4 * jj + g) ^ (row & 7);
+                *reinterpret_cast<v2u*>(reg + row * 128 + chunk * 16 + q * 8) = w;
+              }
+          }
+          wait_lgkm0();
+          const int vb = (wm * 64 + (lane >> 3)) * (int)rowb +
+                         (c * (int)args.I + (int)(128 * t.nt) + 64 * wn + 8 * (lane & 7)) * 2;
+#pragma unroll
+          for (int r8 = 0; r8 < 8; ++r8) {
+            const int row = 8 * r8 + (lane >> 3);
+            const uint4 d = *reinterpret_cast<const uint4*>(reg + row * 128 + (((lane & 7) ^ (row & 7)) << 4));
+            typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+            const v4u w = {d.x, d.y, d.z, d.w};
+            __builtin_amdgcn_raw_buffer_store_b128(w, rs, vb, 8 * r8 * (int)rowb, 0);
+          }
+          wait_lgkm0();
+        }
+      }
       // the row pair's (wm) 64 rows x 128 B of codes, staged in the tile's
       // free K-block stage (A part of stage 1) for whole-row stores
       uint8_t* hreg = smem + ST_BYTES + wm * 8192;
@@ -754,7 +797,10 @@ __global__ __launch_bounds__(WT, 1) void wide_gemm_kernel(GemmArgs args) {
 
 int launch_wide(const GemmArgs& a, bool swiglu, hipStream_t st) {
   const int grid = std::max(8, (num_cus() / 8) * 8);
-  if (swiglu) {
+  if (swiglu && a.GU) {
+    if (a.a_row_index) wide_gemm_kernel<true, true, true><<<dim3(grid), dim3(WT), 0, st>>>(a);
+    else wide_gemm_kernel<true, false, true><<<dim3(grid), dim3(WT), 0, st>>>(a);
+  } else if (swiglu) {
     if (a.a_row_index) wide_gemm_kernel<true, true><<<dim3(grid), dim3(WT), 0, st>>>(a);
     else wide_gemm_kernel<true, false><<<dim3(grid), dim3(WT), 0, st>>>(a);
   } else {

@@ -235,10 +235,15 @@ class MoELayer:
     def forward(self, x_bf16: torch.Tensor, bufs: Buffers | None = None, stream=None,
                 update_bias: bool = False, gamma: float = 0.001,
                 fused: bool = True, events: dict | None = None,
-                seq_len: int | None = None, alpha: float = 0.0001) -> torch.Tensor:
+                seq_len: int | None = None, alpha: float = 0.0001,
+                keep_gu: bool = False) -> torch.Tensor:
         """One layer forward.  With seq_len, also the sequence-wise balance
         statistic of the routing (factor alpha) over consecutive runs of
-        seq_len tokens, into bufs.seq_f, seq_p and seq_loss.  `events`, if
+        seq_len tokens, into bufs.seq_f, seq_p and seq_loss.  keep_gu (for
+        training): the fused gate+up kernel also writes its bf16 gate/up
+        outputs into bufs.hgu (1.2 GB at T=16384), which the backward then
+        reads instead of running the gate+up GEMM again; the layer's output
+        is unchanged.  `events`, if
         given, maps a step name ("route", "seq_balance", "quant", "permute",
         "gate_up", "down", "combine", "bias") to a list that receives a
         (start, end) pair of torch.cuda.Event recorded on the launch stream
@@ -247,6 +252,7 @@ class MoELayer:
         T = x_bf16.shape[0]
         b = bufs or self.buffers(T)
         R = b.R
+        b.gu_kept = keep_gu
         if events is not None:
             return self._forward_timed(x_bf16, b, stream, update_bias, gamma, fused, events,
                                        seq_len, alpha)
@@ -257,7 +263,10 @@ class MoELayer:
         L.moe_permute(b.topk_idx, b.counts, T, s.k, s.E, s.n_shared, b.offsets, b.perm_src,
                       b.inv_perm, None, None, s.H, None, None, b.perm_ws, b.perm_ws_bytes,
                       stream)
-        if fused:
+        if fused and keep_gu:
+            L.grouped_fp8_gemm_swiglu_keep(b.xq, b.xs, b.perm_src, self.w_gu, self.w_gu_s,
+                                           b.offsets, s.G, R, s.I, s.H, b.hq, b.hs, b.hgu, stream)
+        elif fused:
             L.grouped_fp8_gemm_swiglu(b.xq, b.xs, b.perm_src, self.w_gu, self.w_gu_s, b.offsets,
                                       s.G, R, s.I, s.H, b.hq, b.hs, stream)
         else:
@@ -302,6 +311,8 @@ class MoELayer:
         seq_len (the forward's, which left the scores and f in `bufs`), the
         loss also holds the sequence-wise balance term alpha * sum_b L_bal,b
         and the router's backward is the dense one (bwd.dlogit [T, E]).
+        After a forward with keep_gu the gate+up outputs are read from
+        bufs.hgu; otherwise the gate+up GEMM runs again (into bwd.gu).
         Returns the BackwardBuffers: dx_total (the input gradient), dx (its
         expert-path part), dw (gate weights), dC (centroids), dW_gu, dW_dn.
         `events` as in forward, keys "combine_bwd", "dgrad_down",
@@ -334,9 +345,14 @@ class MoELayer:
             L.fp8_quant_1x128(bb.dD, R, H, H, 0, bb.dDq, bb.dDs, st),
             L.grouped_fp8_gemm(bb.dDq, bb.dDs, None, w["dn"], w["dn_s"], b.offsets, G, R, I, H,
                                bb.dh, st)))
-        step("recompute_gate_up", lambda: L.grouped_fp8_gemm(
-            b.xq, b.xs, b.perm_src, self.w_gu, self.w_gu_s, b.offsets, G, R, 2 * I, H, bb.gu, st))
-        step("swiglu_bwd", lambda: L.swiglu_backward(bb.gu, bb.dh, R, I, bb.dgu, bb.h, st))
+        if getattr(b, "gu_kept", False):
+            gu = b.hgu   # kept by the forward (keep_gu): the same bf16 GEMM output
+        else:
+            gu = bb.gu
+            step("recompute_gate_up", lambda: L.grouped_fp8_gemm(
+                b.xq, b.xs, b.perm_src, self.w_gu, self.w_gu_s, b.offsets, G, R, 2 * I, H, gu,
+                st))
+        step("swiglu_bwd", lambda: L.swiglu_backward(gu, bb.dh, R, I, bb.dgu, bb.h, st))
         step("dgrad_gate_up", lambda: (
             L.fp8_quant_1x128(bb.dgu, R, 2 * I, 2 * I, 0, bb.dguq, bb.dgus, st),
             L.grouped_fp8_gemm(bb.dguq, bb.dgus, None, w["gu"], w["gu_s"], b.offsets, G, R, H,
@@ -410,7 +426,11 @@ class MoELayer:
         timed("permute", lambda: L.moe_permute(
             b.topk_idx, b.counts, T, s.k, s.E, s.n_shared, b.offsets, b.perm_src, b.inv_perm,
             None, None, s.H, None, None, b.perm_ws, b.perm_ws_bytes, st))
-        if fused:
+        if fused and b.gu_kept:
+            timed("gate_up", lambda: L.grouped_fp8_gemm_swiglu_keep(
+                b.xq, b.xs, b.perm_src, self.w_gu, self.w_gu_s, b.offsets, s.G, R, s.I, s.H,
+                b.hq, b.hs, b.hgu, st))
+        elif fused:
             timed("gate_up", lambda: L.grouped_fp8_gemm_swiglu(
                 b.xq, b.xs, b.perm_src, self.w_gu, self.w_gu_s, b.offsets, s.G, R, s.I, s.H,
                 b.hq, b.hs, st))

@@ -448,6 +448,23 @@ int grouped_fp8_gemm_swiglu(const uint8_t* A, const float* A_scale,
                             uint8_t* H_e4m3, float* H_scale, void* stream);
 
 /*
+ * grouped_fp8_gemm_swiglu_keep - grouped_fp8_gemm_swiglu that also writes
+ * the gate/up totals as bf16 (round to nearest even): GU_bf16 [M_total, 2I]
+ * = [gt | ut], the bits grouped_fp8_gemm would write for the same operands.
+ * For training: the backward's SwiGLU step reads them instead of running the
+ * gate+up GEMM again (the pages' FP8 training keeps the FP8 GEMMs; keeping
+ * rather than recomputing these outputs is this library's choice, with the
+ * HBM to hold them).  Same arguments, requirements and H outputs as
+ * grouped_fp8_gemm_swiglu; GU_bf16 16-byte aligned.  Groups below the fused
+ * 256-row kernel's size run the fused kernel and grouped_fp8_gemm in turn.
+ */
+int grouped_fp8_gemm_swiglu_keep(const uint8_t* A, const float* A_scale,
+                                 const int32_t* a_row_index, int64_t A_rows, const uint8_t* B,
+                                 const float* B_scale, const int32_t* group_offsets,
+                                 int32_t G, int64_t M_total, int64_t I, int64_t K,
+                                 uint8_t* H_e4m3, float* H_scale, void* GU_bf16, void* stream);
+
+/*
  * moe_combine - weighted combine plus shared expert (news.qq.com article,
  * section DeepSeekMoE 架构: shared experts are always on, routed experts are
  * weighted by their gates).

@@ -184,6 +184,16 @@ def test_router_backward_dense_validation():
     assert d(T=2000, wsb=16) == L.MOE_ERR_WORKSPACE
 
 
+def test_swiglu_keep_validation():
+    def k(I=256, GU=FAKE, M=100):
+        return rc("grouped_fp8_gemm_swiglu_keep", FAKE, FAKE, None, M, FAKE, FAKE, FAKE, 4, M, I,
+                  1024, FAKE, FAKE, GU, None)
+    assert k(I=200) == L.MOE_ERR_INVALID
+    assert k(GU=None) == L.MOE_ERR_INVALID and "GU" in L.last_error()
+    assert k(GU=ctypes.c_void_p(4104)) == L.MOE_ERR_INVALID
+    assert k(M=0, GU=None) == L.MOE_OK
+
+
 def test_route_group_size_two_is_valid_shape():
     # E=16 in 8 groups has group size 2: valid, but 2 is not 4 * 2^n
     assert rc("moe_route", FAKE, 8, 256, FAKE, FAKE, 16, 8, 2, 4, FAKE, FAKE, FAKE, FAKE, 1 << 30,

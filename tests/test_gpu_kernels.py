@@ -518,6 +518,43 @@ def test_gemm_swiglu_fused(sizes, I, K, with_index):
     check_fused_swiglu(q, s, exact, bound, I, f"fused swiglu {sizes} I={I} K={K}")
 
 
+# The fused gate+up that also keeps its bf16 outputs: codes and scales equal
+# the fused kernel's, the kept outputs equal the plain GEMM's, bit for bit
+# (256-row kernel: groups of >= 160 rows on average; smaller groups take the
+# fused kernel and the plain GEMM in turn).
+@pytest.mark.parametrize("sizes,with_index", [([1000, 0, 170, 400, 256, 513, 65], False),
+                                              ([1000, 0, 170, 400, 256, 513, 65], True),
+                                              ([5, 0, 300, 129], False)])
+def test_gemm_swiglu_keep(sizes, with_index):
+    import torch
+    I, K = 256, 1024
+    G = len(sizes)
+    offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    Mt = int(offsets[-1])
+    rng = np.random.default_rng(Mt + 5)
+    rows_src = 333 if with_index else Mt
+    qA, sA = OQ.quant_1x128(rng.standard_normal((rows_src, K)).astype(np.float32))
+    rowidx = rng.integers(0, rows_src, Mt).astype(np.int32) if with_index else None
+    qB = np.empty((G, 2 * I, K), np.uint8)
+    sB = np.empty((G, 2 * I // 128, K // 128), np.float32)
+    for g in range(G):
+        qB[g], sB[g] = OQ.quant_128x128((rng.standard_normal((2 * I, K)) * 0.05).astype(np.float32))
+    args = (dev(qA), dev(sA), None if rowidx is None else dev(rowidx), dev(qB), dev(sB),
+            dev(offsets.astype(np.int32)), G, Mt, I, K)
+    hq, hs = _u8((Mt, I)), _f32((Mt, I // 128))
+    M.grouped_fp8_gemm_swiglu(*args, hq, hs)
+    kq, ks = _u8((Mt, I)), _f32((Mt, I // 128))
+    gu = torch.full((Mt, 2 * I), float("nan"), dtype=torch.bfloat16, device="cuda")
+    M.grouped_fp8_gemm_swiglu_keep(*args, kq, ks, gu)
+    plain = torch.full((Mt, 2 * I), float("nan"), dtype=torch.bfloat16, device="cuda")
+    M.grouped_fp8_gemm(dev(qA), dev(sA), None if rowidx is None else dev(rowidx), dev(qB), dev(sB),
+                       dev(offsets.astype(np.int32)), G, Mt, 2 * I, K, plain)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(kq), host(hq)) and np.array_equal(host(ks).view(np.uint32),
+                                                                 host(hs).view(np.uint32))
+    assert torch.equal(gu.view(torch.int16), plain.view(torch.int16))
+
+
 # ------------------------------------------------------------------ combine
 @pytest.mark.parametrize("shared", [True, False])
 def test_combine(shared):

@@ -361,3 +361,41 @@ def test_layer_empty_batch():
         torch.cuda.synchronize()
         assert not host(bb.dW_gu).any() and not host(bb.dW_dn).any() and not host(bb.dC).any()
         assert tuple(bb.dx_total.shape) == (0, cfg.H)
+
+
+@pytest.mark.parametrize("T", [200, 2048])   # small-group fallback; the fused 256-row kernel
+def test_layer_backward_keep_gu_mid(T):
+    """forward(keep_gu=True): the fused gate+up kernel also writes its bf16
+    gate/up outputs and the backward reads them.  They are bit-identical to
+    the gate+up GEMM the backward would rerun, the layer's output equals the
+    plain forward's, and the gradients stay within the oracle bars."""
+    cfg = synth.MID.with_(T=T)
+    k, I, G = cfg.k, cfg.I, cfg.G
+    layer, C, b = build_layer(cfg)
+    x = synth.gen_x(cfg)
+    dy = synth.gen_dy(cfg)
+    log(f"[layer bwd keep_gu] mid: T={T}")
+    x_d = bf16_dev(x)
+    y = bf16_values_host(layer.forward(x_d, keep_gu=True))
+    bufs = layer.buffers(T)
+    bb = layer.backward(bf16_dev(dy), x_d)
+    torch.cuda.synchronize()
+    again = torch.empty_like(bufs.hgu)
+    M.grouped_fp8_gemm(bufs.xq, bufs.xs, bufs.perm_src, layer.w_gu, layer.w_gu_s, bufs.offsets, G,
+                       cfg.R, 2 * I, cfg.H, again)
+    torch.cuda.synchronize()
+    assert torch.equal(again.view(torch.int16), bufs.hgu.view(torch.int16))
+    # the layer's output is the fused kernel's, whether it keeps them or not
+    y_plain = bf16_values_host(layer.forward(x_d))
+    torch.cuda.synchronize()
+    assert np.array_equal(y, y_plain)
+    wts = oracle_weights(cfg)
+    fwd = OL.layer(x, C, b, wts, cfg.n_group, cfg.topk_group, k, I)
+    assert len(compare_routes(host(bufs.topk_idx), fwd["route"], "mid")) == 0
+    assert rel_l2(y, fwd["y"]) <= 2e-3
+    ref = OBK.layer_backward(dy, fwd, wts, x, C, T, k, I)
+    errs = dict(dx=rel_l2(bf16_values_host(bb.dx_total), ref["dx"]), dw=rel_l2(host(bb.dw), ref["dw"]),
+                dC=rel_l2(host(bb.dC), ref["dC"]), dW_gu=rel_l2(host(bb.dW_gu), ref["dW_gu"]),
+                dW_dn=rel_l2(host(bb.dW_dn), ref["dW_dn"]))
+    log(f"[layer bwd keep_gu] mid: end to end " + ", ".join(f"{k_} {v:.2e}" for k_, v in errs.items()))
+    assert max(errs.values()) <= 5e-3, errs

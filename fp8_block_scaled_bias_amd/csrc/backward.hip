@@ -175,8 +175,8 @@ template <int KMAX>
 __global__ __launch_bounds__(RB) void router_backward_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ C, const int32_t* __restrict__ idx,
     const float* __restrict__ dw, const int32_t* __restrict__ inv_perm,
-    const uint16_t* __restrict__ dx_in, int64_t H, int k, uint16_t* __restrict__ dx_out,
-    float* __restrict__ dlogit_rows) {
+    const uint16_t* __restrict__ dx_in, int64_t T, int64_t H, int E, int k,
+    uint16_t* __restrict__ dx_out, float* __restrict__ dlogit_rows) {
   __shared__ float s_part[RB / 64][KMAX];
   __shared__ float s_dl[KMAX];
   const int64_t t = blockIdx.x;
@@ -185,7 +185,8 @@ __global__ __launch_bounds__(RB) void router_backward_kernel(
   float dot[KMAX];
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) {
-    e[j] = j < k ? idx[t * k + j] : 0;
+    // ids outside [0, E) (not produced by the router) read expert E - 1
+    e[j] = j < k ? (int64_t)min((uint32_t)idx[t * k + j], (uint32_t)(E - 1)) : 0;
     dot[j] = 0.0f;
   }
   const uint16_t* xr = x + t * H;
@@ -230,7 +231,9 @@ __global__ __launch_bounds__(RB) void router_backward_kernel(
       if (j >= k) break;
       const float dl = (dw[t * k + j] - m) / S * s[j] * (1.0f - s[j]);
       s_dl[j] = dl;
-      dlogit_rows[inv_perm[t * k + j]] = dl;
+      // rows outside [0, T*k) (not produced by the permutation) are skipped
+      const uint32_t row = (uint32_t)inv_perm[t * k + j];
+      if (row < (uint32_t)(T * k)) dlogit_rows[row] = dl;
     }
   }
   __syncthreads();
@@ -265,7 +268,7 @@ __global__ __launch_bounds__(RB) void zero_f32_kernel(float* __restrict__ p, int
 
 __global__ __launch_bounds__(RB) void router_dcentroids_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ perm_src,
-    const int32_t* __restrict__ offs, const float* __restrict__ dlogit_rows, int64_t H,
+    const int32_t* __restrict__ offs, const float* __restrict__ dlogit_rows, int64_t T, int64_t H,
     float* __restrict__ dC) {
   const int e = blockIdx.y;
   const int64_t c = (int64_t)blockIdx.x * DC_COLS + threadIdx.x * 8;
@@ -275,7 +278,9 @@ __global__ __launch_bounds__(RB) void router_dcentroids_kernel(
   for (int r = r0; r < r1; ++r) {
     const float d = dlogit_rows[r];
     float xv[8];
-    bf16x8_to_f32(*reinterpret_cast<const uint4*>(x + (int64_t)perm_src[r] * H + c), xv);
+    // token ids outside [0, T) (not produced by the permutation) read token T - 1
+    const int64_t tok = min((uint32_t)perm_src[r], (uint32_t)(T - 1));
+    bf16x8_to_f32(*reinterpret_cast<const uint4*>(x + tok * H + c), xv);
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = fmaf(d, xv[i], acc[i]);
   }
@@ -306,7 +311,7 @@ extern "C" int moe_router_backward(const void* x_bf16, const float* centroids,
               "moe_router_backward: x, centroids, dx_in and dx_out must be 16-byte aligned");
   router_backward_kernel<8><<<dim3((unsigned)T), dim3(RB), 0, as_stream(stream)>>>(
       static_cast<const uint16_t*>(x_bf16), centroids, topk_idx, d_topk_w, inv_perm,
-      static_cast<const uint16_t*>(dx_in_bf16), H, k, static_cast<uint16_t*>(dx_out_bf16),
+      static_cast<const uint16_t*>(dx_in_bf16), T, H, E, k, static_cast<uint16_t*>(dx_out_bf16),
       dlogit_rows);
   return check_launch("moe_router_backward");
 }
@@ -332,6 +337,6 @@ extern "C" int moe_router_dcentroids(const void* x_bf16, const int32_t* perm_src
               "moe_router_dcentroids: x and d_centroids must be 16-byte aligned");
   router_dcentroids_kernel<<<dim3((unsigned)ceil_div(H, DC_COLS), (unsigned)E), dim3(RB), 0,
                              as_stream(stream)>>>(static_cast<const uint16_t*>(x_bf16), perm_src,
-                                                  group_offsets, dlogit_rows, H, d_centroids);
+                                                  group_offsets, dlogit_rows, T, H, d_centroids);
   return check_launch("moe_router_dcentroids");
 }

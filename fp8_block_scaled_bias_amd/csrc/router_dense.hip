@@ -71,7 +71,7 @@ __global__ __launch_bounds__(DT) void dense_dlogit_kernel(
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     if (j < k) {
-      ej[j] = idx[t * k + j];
+      ej[j] = (int)min((uint32_t)idx[t * k + j], (uint32_t)(E - 1));  // ids past E: E - 1
       sj[j] = scores[t * E + ej[j]];
       dwj[j] = dw[t * k + j];
       Ssel += sj[j];

@@ -334,7 +334,9 @@ int swiglu_backward(const void* gu_bf16, const void* dh_bf16, int64_t M, int64_t
  * x_bf16 [T, H]; centroids [E, H] fp32; topk_idx, d_topk_w, inv_perm [T*k];
  * dx_in_bf16 [T, H] or NULL (then 0); dx_out_bf16 (out) [T, H] (may equal
  * dx_in); dlogit_rows (out) [T*k] fp32.  Requirements: 1 <= k <= 8, k <= E,
- * H % 8 == 0; x, centroids, dx_in, dx_out 16-byte aligned.
+ * H % 8 == 0; x, centroids, dx_in, dx_out 16-byte aligned.  Expert ids
+ * outside [0, E) read centroid E - 1 and inv_perm rows outside [0, T*k) are
+ * not written (neither occurs for moe_route / moe_permute outputs).
  */
 int moe_router_backward(const void* x_bf16, const float* centroids, const int32_t* topk_idx,
                         const float* d_topk_w, const int32_t* inv_perm, const void* dx_in_bf16,
@@ -351,7 +353,8 @@ int moe_router_backward(const void* x_bf16, const float* centroids, const int32_
  * group_offsets [E+1] (the routed part of moe_permute's offsets, on the device);
  * d_centroids (out) [E, H] fp32.  Requirements: H % 8 == 0, 1 <= E <= 65535;
  * x and d_centroids 16-byte aligned.  T = 0 writes d_centroids = 0 (the other
- * pointers may then be NULL).
+ * pointers may then be NULL).  perm_src entries outside [0, T) read token
+ * T - 1; group_offsets must be moe_permute's.
  */
 int moe_router_dcentroids(const void* x_bf16, const int32_t* perm_src,
                           const int32_t* group_offsets, const float* dlogit_rows, int64_t T,
@@ -381,6 +384,7 @@ int moe_router_dcentroids(const void* x_bf16, const int32_t* perm_src,
  * Requirements: E % 16 == 0, 16 <= E <= 256, 1 <= k <= 8, H % 128 == 0,
  * 1 <= seq_len <= 65536; x, centroids, scores, seq_f, dx_in, dx_out,
  * d_centroids, dlogit 16-byte aligned.  T = 0 writes d_centroids = 0.
+ * Expert ids outside [0, E) count as expert E - 1.
  */
 size_t moe_router_backward_dense_workspace_bytes(int64_t T, int64_t H, int32_t E);
 int moe_router_backward_dense(const void* x_bf16, const float* centroids,

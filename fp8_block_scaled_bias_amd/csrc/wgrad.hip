@@ -12,8 +12,8 @@
 // whole 128-token chunks, so the 128 columns of one chunk that a tile reads
 // are one contiguous 16 KB block - and grouped_fp8_wgrad multiplies them
 // group by group:
-// each chunk is one FP8 MFMA partial in FP32, promoted into the FP32 total
-// with its two scales (the pages' accumulation at a fixed K interval).
+// each chunk is one FP8 MFMA partial in FP32, carried into the FP32 total at
+// its two scales (the pages' accumulation at a fixed K interval).
 #include "gemm_common.h"
 
 namespace moe {
@@ -93,11 +93,20 @@ __global__ __launch_bounds__(QT) void quant_128x1_grouped_kernel(
 // ---- weight-gradient GEMM ----------------------------------------------------
 // One workgroup (4 waves) per 128 (n) x 128 (k) tile of one group's dW; wave
 // (wm, wn) owns rows 64wm.. and columns 64wn.. as 2 x 2 blocks of
-// v_mfma_f32_32x32x64_f8f6f4.  The group's 128-token chunks stream through
-// two LDS stages (rows 128 B, 16 B chunks XOR-swizzled by row so the
-// fragment reads are conflict-free); chunk c+1 is loaded into registers while
-// chunk c is multiplied.  Per chunk: P = the two 64-token MFMA steps from
-// zero, then total += (sY[n, c] * sA[k, c]) * P.
+// v_mfma_f32_32x32x64_f8f6f4.  The group's 128-token chunks pass through one
+// LDS stage (rows 128 B, 16 B pieces XOR-swizzled by row so the fragment
+// reads are conflict-free); chunk c+1 is loaded into registers while chunk c
+// is multiplied.  One FP32 accumulator per element carries the sum in units
+// of the current chunk's scale product S_c = sY[n, c] sA[k, c]:
+//     acc = P_c0,   acc = acc * (S_{c-1} / S_c) + P_c,   dW = acc * S_last,
+// P_c the chunk's two 64-token MFMA steps (added by the MFMAs themselves).
+// The ratio is taken per operand, (sY_{c-1} / sY_c) (sA_{c-1} / sA_c), one
+// quotient per thread and chunk, shared through LDS.  Against a zero-started
+// partial per chunk promoted by FMA this halves the accumulator registers
+// (161 VGPRs: three waves per SIMD instead of two) and the single stage
+// halves the LDS (three workgroups per CU).  Scales are normal fp32 numbers
+// (amax/448 of finite data, 1 for an all-zero column); ratios beyond ~1e30
+// between consecutive chunks can overflow the rescaled accumulator.
 constexpr int WGT = 256;
 constexpr int TILE_B = 128 * 128;
 
@@ -109,18 +118,16 @@ __global__ __launch_bounds__(WGT) void wgrad_kernel(
     const uint8_t* __restrict__ yt, const float* __restrict__ ys, const uint8_t* __restrict__ at,
     const float* __restrict__ as, const int32_t* __restrict__ offs, int64_t N, int64_t K,
     float* __restrict__ dw) {
-  __shared__ __attribute__((aligned(16))) uint8_t s_y[2][TILE_B];
-  __shared__ __attribute__((aligned(16))) uint8_t s_a[2][TILE_B];
-  __shared__ __attribute__((aligned(16))) float s_sy[2][128];
-  __shared__ __attribute__((aligned(16))) float s_sa[2][128];
+  __shared__ __attribute__((aligned(16))) uint8_t s_y[TILE_B];
+  __shared__ __attribute__((aligned(16))) uint8_t s_a[TILE_B];
+  __shared__ __attribute__((aligned(16))) float s_r[2][256];   // ratios: [0..127] y, [128..255] a
+  __shared__ __attribute__((aligned(16))) float s_s[256];      // the current chunk's scales
   __shared__ int s_red[WGT / 64];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int wm = wv >> 1, wn = wv & 1, q = lane >> 5, l32 = lane & 31;
   const int g = blockIdx.y;
   const int64_t ktiles = K >> 7;
   const int64_t n0 = (int64_t)(blockIdx.x / ktiles) * 128, k0 = (int64_t)(blockIdx.x % ktiles) * 128;
-
-  // first chunk of group g: sum over the groups before it of ceil(rows / 128)
   int part = 0;
   for (int i = tid; i < g; i += WGT) part += (offs[i + 1] - offs[i] + 127) >> 7;
 #pragma unroll
@@ -129,43 +136,32 @@ __global__ __launch_bounds__(WGT) void wgrad_kernel(
   __syncthreads();
   const int c0 = s_red[0] + s_red[1] + s_red[2] + s_red[3];
   const int c1 = c0 + ((offs[g + 1] - offs[g] + 127) >> 7);
-
-  // chunk loads: thread -> rows (tid >> 3) + 32 i (i = 0..3), 16 B piece
-  // tid & 7; named registers (an indexed array here ends up in scratch)
   const int lrow = tid >> 3, lpc = tid & 7;
-  const int soff = lrow * 128 + ((lpc ^ (lrow & 7)) << 4);  // + 32 * 128 * i
+  const int soff = lrow * 128 + ((lpc ^ (lrow & 7)) << 4);
   uint4 y0, y1, y2, y3, a0, a1, a2, a3;
-  float rsc = 0.0f;
+  float rsc = 0.0f, rprev = 1.0f;
   auto ld16 = [](const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); };
   auto load = [&](int c) {
     const uint8_t* py = yt + ((int64_t)c * N + n0 + lrow) * 128 + lpc * 16;
     const uint8_t* pa = at + ((int64_t)c * K + k0 + lrow) * 128 + lpc * 16;
-    y0 = ld16(py);
-    y1 = ld16(py + 32 * 128);
-    y2 = ld16(py + 64 * 128);
-    y3 = ld16(py + 96 * 128);
-    a0 = ld16(pa);
-    a1 = ld16(pa + 32 * 128);
-    a2 = ld16(pa + 64 * 128);
-    a3 = ld16(pa + 96 * 128);
+    y0 = ld16(py); y1 = ld16(py + 32 * 128); y2 = ld16(py + 64 * 128); y3 = ld16(py + 96 * 128);
+    a0 = ld16(pa); a1 = ld16(pa + 32 * 128); a2 = ld16(pa + 64 * 128); a3 = ld16(pa + 96 * 128);
     rsc = tid < 128 ? ys[(int64_t)c * N + n0 + tid] : as[(int64_t)c * K + k0 + tid - 128];
   };
-  auto store = [&](int b) {
-    uint8_t* dy = s_y[b] + soff;
-    uint8_t* da = s_a[b] + soff;
-    *reinterpret_cast<uint4*>(dy) = y0;
-    *reinterpret_cast<uint4*>(dy + 32 * 128) = y1;
-    *reinterpret_cast<uint4*>(dy + 64 * 128) = y2;
-    *reinterpret_cast<uint4*>(dy + 96 * 128) = y3;
-    *reinterpret_cast<uint4*>(da) = a0;
-    *reinterpret_cast<uint4*>(da + 32 * 128) = a1;
-    *reinterpret_cast<uint4*>(da + 64 * 128) = a2;
-    *reinterpret_cast<uint4*>(da + 96 * 128) = a3;
-    if (tid < 128) s_sy[b][tid] = rsc;
-    else s_sa[b][tid - 128] = rsc;
+  // chunk into LDS; thread tid's scale and its ratio to the previous chunk's
+  auto store = [&](int slot) {
+    *reinterpret_cast<uint4*>(s_y + soff) = y0;
+    *reinterpret_cast<uint4*>(s_y + soff + 32 * 128) = y1;
+    *reinterpret_cast<uint4*>(s_y + soff + 64 * 128) = y2;
+    *reinterpret_cast<uint4*>(s_y + soff + 96 * 128) = y3;
+    *reinterpret_cast<uint4*>(s_a + soff) = a0;
+    *reinterpret_cast<uint4*>(s_a + soff + 32 * 128) = a1;
+    *reinterpret_cast<uint4*>(s_a + soff + 64 * 128) = a2;
+    *reinterpret_cast<uint4*>(s_a + soff + 96 * 128) = a3;
+    s_s[tid] = rsc;
+    s_r[slot][tid] = rprev / rsc;
+    rprev = rsc;
   };
-  // fragment of tile row `row` (l32 + a multiple of 32), step half h: its
-  // 16 B pieces 4h + 2q and 4h + 2q + 1
   auto frag = [&](const uint8_t* base, int row, int h) -> v8i {
     const int sw = row & 7;
     const uint4 lo = *reinterpret_cast<const uint4*>(base + row * 128 + (((4 * h + 2 * q) ^ sw) << 4));
@@ -175,7 +171,6 @@ __global__ __launch_bounds__(WGT) void wgrad_kernel(
     r[4] = hi.x; r[5] = hi.y; r[6] = hi.z; r[7] = hi.w;
     return r;
   };
-
   v16f tot[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -183,68 +178,64 @@ __global__ __launch_bounds__(WGT) void wgrad_kernel(
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) tot[i][j][r] = 0.0f;
-  v16f zero;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) zero[r] = 0.0f;
-
   if (c0 < c1) {
     load(c0);
     store(0);
   }
   __syncthreads();
   for (int c = c0; c < c1; ++c) {
-    const int b = (c - c0) & 1;
     const bool more = c + 1 < c1;
     if (more) load(c + 1);
-    // x = weights-side rows k (a_t), y = rows n (dy_t): lane holds row n =
-    // 64wm + 32j + l32 and, per x block i, columns k = 64wn + 32i + 8e + 4q
-    // + (0..3) for e = 0..3
-    v16f p[2][2];
+    if (c > c0) {  // into the units of this chunk's scales: tot *= (S_prev / S_c)
+      const int sl = (c - c0) & 1;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const float ry = s_r[sl][64 * wm + 32 * j + l32];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float4 ra = *reinterpret_cast<const float4*>(&s_r[sl][128 + 64 * wn + 32 * i + 8 * e + 4 * q]);
+            tot[i][j][4 * e + 0] *= ry * ra.x;
+            tot[i][j][4 * e + 1] *= ry * ra.y;
+            tot[i][j][4 * e + 2] *= ry * ra.z;
+            tot[i][j][4 * e + 3] *= ry * ra.w;
+          }
+      }
+    }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       v8i xa[2], yb[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) xa[i] = frag(s_a[b], 64 * wn + 32 * i + l32, h);
+      for (int i = 0; i < 2; ++i) xa[i] = frag(s_a, 64 * wn + 32 * i + l32, h);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) yb[j] = frag(s_y[b], 64 * wm + 32 * j + l32, h);
+      for (int j = 0; j < 2; ++j) yb[j] = frag(s_y, 64 * wm + 32 * j + l32, h);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          if (h == 0) p[i][j] = mfma32(xa[i], yb[j], zero);
-          else p[i][j] = mfma32(xa[i], yb[j], p[i][j]);
-        }
+        for (int j = 0; j < 2; ++j) tot[i][j] = mfma32(xa[i], yb[j], tot[i][j]);
     }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const float sy = s_sy[b][64 * wm + 32 * j + l32];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float4 sa = *reinterpret_cast<const float4*>(&s_sa[b][64 * wn + 32 * i + 8 * e + 4 * q]);
-          tot[i][j][4 * e + 0] = fmaf(sy * sa.x, p[i][j][4 * e + 0], tot[i][j][4 * e + 0]);
-          tot[i][j][4 * e + 1] = fmaf(sy * sa.y, p[i][j][4 * e + 1], tot[i][j][4 * e + 1]);
-          tot[i][j][4 * e + 2] = fmaf(sy * sa.z, p[i][j][4 * e + 2], tot[i][j][4 * e + 2]);
-          tot[i][j][4 * e + 3] = fmaf(sy * sa.w, p[i][j][4 * e + 3], tot[i][j][4 * e + 3]);
-        }
-      }
-    }
-    if (more) store(b ^ 1);
+    if (!more) break;
+    __syncthreads();
+    store((c + 1 - c0) & 1);
     __syncthreads();
   }
-
+  // result = tot * S_last
   float* out = dw + ((int64_t)g * N + n0) * K + k0;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int64_t n = 64 * wm + 32 * j + l32;
+    const float sy = c0 < c1 ? s_s[n] : 0.0f;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int k = 64 * wn + 32 * i + 8 * e + 4 * q;
+        float4 sa = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (c0 < c1) sa = *reinterpret_cast<const float4*>(&s_s[128 + k]);
         *reinterpret_cast<float4*>(out + n * K + k) =
-            make_float4(tot[i][j][4 * e], tot[i][j][4 * e + 1], tot[i][j][4 * e + 2], tot[i][j][4 * e + 3]);
+            make_float4(tot[i][j][4 * e] * (sy * sa.x), tot[i][j][4 * e + 1] * (sy * sa.y),
+                        tot[i][j][4 * e + 2] * (sy * sa.z), tot[i][j][4 * e + 3] * (sy * sa.w));
       }
   }
 }

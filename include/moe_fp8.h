@@ -271,8 +271,10 @@ int fp8_quant_128x1_grouped(const void* in_bf16, int64_t ld_in, const int32_t* r
  *                 * sum_{i<128} dy_c[c, n, i] * a_c[c, k, i]
  * with dy_c / a_c from fp8_quant_128x1_grouped of dY [M_total, N] and
  * A [M_total, K] on the same group_offsets.  Each chunk's 128-term FP8
- * partial is an FP32 MFMA sum that is scaled and added to an FP32 total.
- * A group without rows gets dW[g] = 0.
+ * partial is an FP32 MFMA sum added to one FP32 accumulator kept in units of
+ * the current chunk's scale product (rescaled by the ratio of consecutive
+ * chunks' scales, multiplied by the last one at the end).  A group without
+ * rows gets dW[g] = 0.
  *
  * dy_c [chunks_cap, N, 128], dy_scale_c [chunks_cap, N];
  * a_c  [chunks_cap, K, 128], a_scale_c  [chunks_cap, K]

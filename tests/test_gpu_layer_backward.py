@@ -225,12 +225,15 @@ def _logical(c, sc, nch):
 # 2^-13.3 on these weight-gradient operands (128x1 tiles of w * dy and of h:
 # a wide dynamic range within one tile), so the wgrad stage allows 2^-12.
 MFMA_REL_WGRAD = 2.0 ** -12
+# the rescaled accumulator's roundings per chunk (two scale quotients, their
+# product, the multiply, the MFMA's add) plus the final scaling
+WGRAD_ROUNDINGS = 6
 
 
 def _wgrad_bound(qY, sY, qA, sA, pref):
     S = OG.grouped_wgrad(np.asarray(qY) & 0x7F, sY, np.asarray(qA) & 0x7F, sA, pref)
     nch = np.diff(pref).astype(np.float64)[:, None, None]
-    return (MFMA_REL_WGRAD + 2 * (nch + 1) * 2.0 ** -24) * S
+    return (MFMA_REL_WGRAD + WGRAD_ROUNDINGS * (nch + 1) * 2.0 ** -24) * S
 
 
 @pytest.mark.parametrize("name", ["tiny", "mid"])

@@ -36,8 +36,11 @@ __global__ __launch_bounds__(QT) void quant_128x1_grouped_kernel(
     const uint16_t* __restrict__ in, int64_t ld_in, const int32_t* __restrict__ row_index,
     int64_t in_rows, const int32_t* __restrict__ offs, int G, int64_t C, uint8_t* __restrict__ out,
     float* __restrict__ scales) {
-  __shared__ int s_offs[gemm::MAXG + 1];
-  __shared__ int s_pref[gemm::MAXG + 1];
+  // the group tables take 2 (G + 1) ints of dynamic LDS (sized at launch),
+  // which keeps four workgroups per CU
+  extern __shared__ int s_tab[];
+  int* s_offs = s_tab;
+  int* s_pref = s_tab + (G + 1);
   __shared__ int s_red[QT / 64];
   __shared__ int s_carry;
   __shared__ float s_amax[128];
@@ -274,7 +277,8 @@ extern "C" int fp8_quant_128x1_grouped(const void* in_bf16, int64_t ld_in,
               "fp8_quant_128x1_grouped: in must be 16-byte aligned with ld_in %% 8 == 0, out 16-byte, "
               "scales 4-byte aligned");
   const int64_t chunks = chunks_needed(M_total, G);
-  quant_128x1_grouped_kernel<<<dim3((unsigned)chunks, (unsigned)(C / 128)), dim3(QT), 0, as_stream(stream)>>>(
+  quant_128x1_grouped_kernel<<<dim3((unsigned)chunks, (unsigned)(C / 128)), dim3(QT),
+                               2 * (G + 1) * sizeof(int), as_stream(stream)>>>(
       static_cast<const uint16_t*>(in_bf16), ld_in, row_index, in_rows, group_offsets, G, C, out_c,
       scales_c);
   return check_launch("fp8_quant_128x1_grouped");

@@ -496,6 +496,18 @@ def main():
     dbytes = (touched + 1) * (w_expert + sc_bytes) + 4 * dcfg.E * dcfg.H + 2 * 2 * dcfg.T * dcfg.H
     dgbs = dbytes / (dms * 1e-3) / 1e9
     log(f"[bench] decode per-kernel ms: " + ", ".join(f"{k} {v:.3f}" for k, v in dper.items()))
+    # the same decode step captured as one HIP graph and replayed
+    gdec = layer.capture(xd)
+    for _ in range(5):
+        gdec.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.decode_steps):
+        gdec.replay()
+    torch.cuda.synchronize()
+    gms = (time.perf_counter() - t0) / args.decode_steps * 1e3
+    del gdec
+    log(f"[bench] decode as a HIP graph: {gms:.3f} ms/step (eager {dms:.3f})")
 
     gg = bench_grouped_gemm(layer)
     bwd = bench_backward(layer, cfg.T) if not args.no_backward else None
@@ -531,7 +543,8 @@ def main():
                      "achieved": achieved_gu, "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved_gu / FP8_PEAK_TFLOPS, "traffic": traffic,
                      "algorithmic_flop_per_launch": flops_gu, "avg_launch_ms": gu_ms},
-        "decode": {"T": dcfg.T, "ms_per_step": dms, "touched_experts": touched,
+        "decode": {"T": dcfg.T, "ms_per_step": dms, "graph_ms_per_step": gms,
+                   "touched_experts": touched,
                    "algorithmic_bytes": dbytes, "GB_s": dgbs, "frac_hbm_peak": dgbs / HBM_PEAK_GBS,
                    "per_kernel_ms": dper},
         "grouped_gemm": gg,

@@ -297,6 +297,25 @@ class MoELayer:
         L.fp8_transpose_128x128(self.w_dn, self.w_dn_s, s.G, s.H, s.I, w["dn"], w["dn_s"], stream)
         return w
 
+    def capture(self, x_bf16: torch.Tensor, bufs: Buffers | None = None, **forward_kw):
+        """One forward captured as a HIP graph (torch.cuda.CUDAGraph); its
+        replay() reruns the whole layer on the same buffers - write the next
+        batch into x_bf16 first - with one launch.  The library only launches
+        kernels (no allocation, no memset, no host synchronisation), so every
+        step is capturable.  forward_kw as in forward (not events)."""
+        T = x_bf16.shape[0]
+        b = bufs or self.buffers(T)
+        side = torch.cuda.Stream()   # default priority
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            self.forward(x_bf16, b, stream=side, **forward_kw)   # warm-up outside the capture
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            self.forward(x_bf16, b, stream=torch.cuda.current_stream(), **forward_kw)
+        return graph
+
     def backward_buffers(self, T: int) -> BackwardBuffers:
         bb = self._bwd.get(T)
         if bb is None:

@@ -83,19 +83,26 @@ def layer(x_bits, centroids, bias, wts: ExpertWeights, n_group, topk_group, k, I
                 inv_perm=inv_perm, Hgu=Hgu, Hq=Hq, Hs=Hs, h=h, D=D, y=y, y64=y64)
 
 
-def expert_ffn(xq_row, xs_row, wts: ExpertWeights, e: int, I: int, fused: bool = True):
-    """One expert on quantised rows: gate+up GEMM, SwiGLU+requant, down GEMM."""
+def expert_ffn(xq_row, xs_row, wts: ExpertWeights, e: int, I: int, fused: bool = True,
+               keep: bool = False):
+    """One expert on quantised rows: gate+up GEMM, SwiGLU+requant, down GEMM.
+
+    Returns the bf16 values of the down projection; with keep, also the
+    exact gate/up sums (float64, before any rounding) as (D, hgu)."""
     qgu, sgu = wts.gu(e)
     qdn, sdn = wts.dn(e)
     hgu = block_scaled_matmul(xq_row, xs_row, qgu, sgu)
+    exact = hgu
     if not fused:
         hgu = bf16_round(hgu)
     hq, hs, _ = swiglu_quant(hgu, I)
-    return bf16_round(block_scaled_matmul(hq, hs, qdn, sdn))
+    D = bf16_round(block_scaled_matmul(hq, hs, qdn, sdn))
+    return (D, exact) if keep else D
 
 
 def layer_tokens(x_bits, centroids, bias, wts: ExpertWeights, n_group, topk_group, k, I,
-                 tokens, n_shared: int = 1, fused: bool = True):
+                 tokens, n_shared: int = 1, fused: bool = True, keep: bool = False,
+                 threads: int = 1):
     """Direct per-token form for the given token indices.
 
     Routing of a token only depends on that token (the counts are not an
@@ -103,7 +110,11 @@ def layer_tokens(x_bits, centroids, bias, wts: ExpertWeights, n_group, topk_grou
     batch.  Each expert is evaluated on the sampled tokens that chose it (its
     rows are independent of one another), then every token's output is the
     sum over its slots in slot order plus the shared expert(s).
-    Returns dict(idx, w32, margin, y (bf16 values), y64).
+    Returns dict(idx, w32, margin, y (bf16 values), y64); with keep also
+    hgu float64 [n, k + n_shared, 2I] (the exact gate/up sums of token i's
+    slot j, shared expert(s) last) and D [n, k + n_shared, H] (bf16 values of
+    the down projection).  threads > 1 evaluates the experts on a thread
+    pool (the result does not depend on it).
     """
     tokens = np.asarray(tokens, dtype=np.int64)
     E = centroids.shape[0]
@@ -114,17 +125,35 @@ def layer_tokens(x_bits, centroids, bias, wts: ExpertWeights, n_group, topk_grou
     xq, xsc = quant_1x128(bf16_value_from_bits(xs_bits).astype(np.float32))
     n = len(tokens)
     H = x_bits.shape[1]
-    out = {}                                   # (token row, slot) -> expert output
-    for e in sorted(set(idx.ravel().tolist())):
-        rows, slots = np.nonzero(idx == e)
-        d = expert_ffn(xq[rows], xsc[rows], wts, e, I, fused)
-        for r, j, dr in zip(rows, slots, d):
-            out[(int(r), int(j))] = dr
-    shared = [expert_ffn(xq, xsc, wts, E + sh, I, fused) for sh in range(n_shared)]
+
+    def run(e):
+        if e < E:
+            rows, slots = np.nonzero(idx == e)
+        else:
+            rows = np.arange(n)
+            slots = np.full(n, k + e - E)
+        return rows, slots, expert_ffn(xq[rows], xsc[rows], wts, e, I, fused, keep=True)
+
+    experts = sorted(set(idx.ravel().tolist())) + [E + sh for sh in range(n_shared)]
+    if threads > 1:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(threads) as ex:
+            results = list(ex.map(run, experts))
+    else:
+        results = [run(e) for e in experts]
+    D = np.zeros((n, k + n_shared, H), dtype=np.float64)
+    hgu = np.zeros((n, k + n_shared, 2 * I), dtype=np.float64) if keep else None
+    for rows, slots, (d, exact) in results:
+        D[rows, slots] = d
+        if keep:
+            hgu[rows, slots] = exact
     y64 = np.zeros((n, H), dtype=np.float64)
     for i in range(n):
         for j in range(k):
-            y64[i] += np.float64(w32[i, j]) * out[(i, j)]
+            y64[i] += np.float64(w32[i, j]) * D[i, j]
         for sh in range(n_shared):
-            y64[i] += shared[sh][i]
-    return dict(idx=idx, w32=w32, margin=margin, y=bf16_round(y64), y64=y64)
+            y64[i] += D[i, k + sh]
+    out = dict(idx=idx, w32=w32, margin=margin, y=bf16_round(y64), y64=y64)
+    if keep:
+        out.update(hgu=hgu, D=D, xq=xq, xs=xsc)
+    return out

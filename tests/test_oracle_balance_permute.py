@@ -157,3 +157,33 @@ def test_seq_balance_grad_is_the_derivative():
         fd = (BL.seq_balance(sig(lp), idx, L, 0.5)["loss"].sum()
               - BL.seq_balance(sig(lm), idx, L, 0.5)["loss"].sum()) / (2 * eps)
         assert abs(fd - g[t, e]) < 1e-9, (t, e, fd, g[t, e])
+
+
+def _bias_steps(b, steps, first):
+    """Route a fresh tiny batch (seed 1000 + step) with bias b, then update b
+    from that batch's counts; returns the bias after each step."""
+    import synth
+    from oracle import route as RT
+    cfg = synth.TINY
+    c = synth.gen_centroids(cfg)
+    out = []
+    for step in range(first, first + steps):
+        x = synth.gen_x(cfg, seed=1000 + step)
+        r = RT.route(x, c, b, cfg.n_group, cfg.topk_group, cfg.k)
+        b = BL.bias_update(r["counts"], b)
+        out.append(b)
+    return out
+
+
+def test_bias_save_resume_equals_straight_run(tmp_path):
+    """The layer's only state is the fp32 bias: 50 steps, save it to a file,
+    load it into a fresh run, 50 more steps - the same trajectory, bit for
+    bit, as 100 steps without the break."""
+    b0 = np.zeros(16, np.float32)
+    straight = _bias_steps(b0, 100, 0)
+    first = _bias_steps(b0, 50, 0)
+    np.save(tmp_path / "bias.npy", first[-1])
+    resumed = _bias_steps(np.load(tmp_path / "bias.npy"), 50, 50)
+    assert all(np.array_equal(a, b) for a, b in zip(first + resumed, straight))
+    assert straight[-1].dtype == np.float32
+    assert not np.array_equal(straight[49], straight[99])   # the bias did move

@@ -91,7 +91,7 @@ def _ties_rows():
             line = line.strip()
             if not line or line.startswith("#"):
                 continue
-            shape, biases, ids, ws = [p.strip() for p in line.split("|")]
+            shape, biases, ids, ws, margin = [p.strip() for p in line.split("|")]
             E, ng, tg, k = map(int, shape.split())
             b = np.zeros(E, np.float32)
             if biases != "-":
@@ -99,13 +99,13 @@ def _ties_rows():
                     e, v = item.split(":")
                     b[int(e)] = np.float32(float(v))
             rows.append((E, ng, tg, k, b, [int(i) for i in ids.split(",")],
-                         [float(w) for w in ws.split(",")]))
+                         [float(w) for w in ws.split(",")], float(margin)))
     return rows
 
 
 @pytest.mark.parametrize("row", _ties_rows())
 def test_hand_traced_ties(row):
-    E, ng, tg, k, b, ids, ws = row
+    E, ng, tg, k, b, ids, ws, margin = row
     H = 256
     x = np.zeros((3, H), np.uint16)              # bf16 zeros -> every s = 1/2
     c = synth.gen_centroids(synth.TINY.with_(E=E, H=H))
@@ -113,6 +113,7 @@ def test_hand_traced_ties(row):
     for t in range(3):
         assert r["idx"][t].tolist() == ids
         assert r["w"][t].tolist() == ws
+        assert r["margin"][t] == margin
     assert r["counts"].sum() == 3 * k
 
 
@@ -162,3 +163,54 @@ def test_bias_selects_but_does_not_weight():
         ssel = r1["s"][0, r1["idx"][0]]
         np.testing.assert_allclose(r1["w"][0], ssel / ssel.sum(), rtol=1e-15)
         assert r1["w"][0].max() < 0.99     # a biased expert is not weighted by its bias
+
+
+def _brute_force_margin(sb, n_group, topk_group, k):
+    """The gap that decided one token's choice, from explicit sorts.
+
+    Group gap: every group's score is its best pair sum (all pairs tried);
+    the scores are sorted in descending order, and the gap is the
+    topk_group-th minus the next one.  Expert gap: the groups kept are the
+    topk_group best by (score descending, index ascending); their experts'
+    biased scores are sorted in descending order and the gap is the k-th
+    minus the next one.  A gap with no next element is inf.
+    """
+    E = len(sb)
+    gs = E // n_group
+    gscore = [max(float(sb[g * gs + a]) + float(sb[g * gs + b])
+                  for a, b in itertools.combinations(range(gs), 2)) for g in range(n_group)]
+    ranked = sorted(range(n_group), key=lambda g: (-gscore[g], g))
+    if topk_group < n_group:
+        ggap = gscore[ranked[topk_group - 1]] - gscore[ranked[topk_group]]
+    else:
+        ggap = math.inf
+    kept = sorted(float(sb[g * gs + i]) for g in ranked[:topk_group] for i in range(gs))[::-1]
+    egap = kept[k - 1] - kept[k] if k < len(kept) else math.inf
+    return min(ggap, egap)
+
+
+@pytest.mark.parametrize("shape", [(16, 4, 2, 4), (24, 6, 3, 5), (16, 4, 4, 4), (16, 4, 2, 8),
+                                   (64, 8, 4, 8), (16, 1, 1, 3)])
+def test_margin_brute_force(shape):
+    """select()'s margin equals the brute-force gaps exactly on random scores
+    (distinct values, so an off-by-one in either gap, or a group gap taken
+    from the wrong pair, changes the number)."""
+    E, ng, tg, k = shape
+    cfg = synth.TINY.with_(E=E, n_group=ng, topk_group=tg, k=k)
+    x = synth.gen_x(cfg, seed=E + k, T=48)
+    c = synth.gen_centroids(cfg, seed=E + k) * 8
+    b = synth.gen_bias(cfg, seed=E + k)
+    r = RT.route(x, c, b, ng, tg, k)
+    forced = tg == ng and k == E
+    assert np.all(np.isfinite(r["margin"])) != forced
+    for t in range(48):
+        assert r["margin"][t] == _brute_force_margin(r["sb"][t], ng, tg, k), t
+
+
+def test_margin_forced_choice_is_inf():
+    """Every group kept and every expert chosen: nothing was decided."""
+    cfg = synth.TINY.with_(E=8, n_group=2, topk_group=2, k=8)
+    x = synth.gen_x(cfg, T=5)
+    r = RT.route(x, synth.gen_centroids(cfg), synth.gen_bias(cfg), 2, 2, 8)
+    assert np.all(np.isinf(r["margin"]))
+    assert np.array_equal(r["idx"], np.tile(np.arange(8, dtype=np.int32), (5, 1)))

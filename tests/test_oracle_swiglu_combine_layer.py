@@ -75,6 +75,17 @@ def test_layer_grouped_equals_direct_per_token_tiny():
     assert np.array_equal(out["route"]["idx"], direct["idx"])
     assert np.array_equal(out["y64"], direct["y64"])
     assert np.array_equal(out["y"], direct["y"])
+    # kept per-slot values (the form the full-size GPU checks read) are the
+    # grouped form's rows, and a thread pool changes nothing
+    kept = LY.layer_tokens(x, c, b, wts, cfg.n_group, cfg.topk_group, cfg.k, cfg.I,
+                           np.arange(cfg.T), keep=True, threads=4)
+    assert np.array_equal(kept["y"], direct["y"])
+    inv = out["inv_perm"].reshape(cfg.T, cfg.k)
+    for t in range(cfg.T):
+        rows = list(inv[t]) + [cfg.T * cfg.k + t]
+        assert np.array_equal(kept["hgu"][t], out["Hgu"][rows])
+        assert np.array_equal(kept["D"][t], out["D"][rows])
+    assert np.array_equal(kept["xq"], out["xq"]) and np.array_equal(kept["xs"], out["xs"])
     # the layer output is not trivially small or dominated by the shared expert
     ys = out["D"][cfg.T * cfg.k:]
     assert np.linalg.norm(out["y64"] - ys) > 0.3 * np.linalg.norm(out["y64"])

@@ -297,8 +297,8 @@ def bench_backward_step(layer, x, cfg, steps=3, warmup=1):
     log(f"[bench] backward step: {ms:.3f} ms ({out['TFLOPS']:.0f} TFLOP/s); " +
         ", ".join(f"{k} {v:.3f}" for k, v in per.items()))
     # a training step (forward + backward) both ways: the fused forward with
-    # the gate+up GEMM run again in the backward, or the unfused forward that
-    # keeps the bf16 gate/up outputs (1.2 GB) for the backward to read
+    # the gate+up GEMM run again in the backward, or the fused forward that
+    # also keeps its bf16 gate/up outputs (1.2 GB) for the backward to read
     for name, keep in (("train_step_recompute", False), ("train_step_keep_gu", True)):
         layer.forward(x, keep_gu=keep)
         layer.backward(dy, x)
@@ -413,38 +413,57 @@ def bench_skewed(layer, steps=100):
             "TFLOPS": flop / (ms * 1e-3) / 1e12}
 
 
-def cpu_baseline(cfg, n_tokens=32):
-    """The FP64 oracle on a bounded sample: the layer output of the first
-    n_tokens tokens of the same batch (their routes, the weights of every
-    expert they touch, and the shared expert), with the BLAS threads set to
-    the host cores this process may use (its CPU affinity, at most the
-    OMP_NUM_THREADS share when that is set)."""
+def cpu_baseline(cfg, dcfg, n_tokens=32, n_decode=8, decode_runs=3):
+    """The FP64 oracle on bounded samples, with the BLAS threads set to the
+    host cores this process may use (its CPU affinity, at most the
+    OMP_NUM_THREADS share when that is set).  Prefill: the layer output of
+    the first n_tokens tokens of the T=16384 batch, one run.  Decode: the
+    layer output of the first n_decode tokens of the T=128 batch, the median
+    of decode_runs runs.  Each sample covers the tokens' routes, the weights
+    of every expert they touch and the shared expert; the weights' 128x128
+    quantisation is setup, not timed (both workloads share the weights)."""
     import numpy as np
     import synth
     from threadpoolctl import threadpool_limits
     from oracle import layer as OL
     from oracle import route as OR
-    x = synth.gen_x(cfg)
-    C = synth.gen_centroids(cfg)
-    b = synth.gen_bias(cfg)
-    toks = np.arange(n_tokens)
     wts = OL.ExpertWeights(lambda e: synth.gen_expert_weight(cfg, "gu", e),
                            lambda e: synth.gen_expert_weight(cfg, "dn", e))
-    r = OR.route(x[toks], C, b, cfg.n_group, cfg.topk_group, cfg.k)
-    experts = set(r["idx"].ravel().tolist()) | {cfg.E}
-    t0 = time.time()
-    wts.prefetch(experts)   # weight quantisation is setup, not timed
-    log(f"[bench] cpu baseline setup: {len(experts)} experts quantised in {time.time() - t0:.1f}s")
     cores = len(os.sched_getaffinity(0))
     if os.environ.get("OMP_NUM_THREADS", "").isdigit():
         cores = max(1, min(cores, int(os.environ["OMP_NUM_THREADS"])))
-    with threadpool_limits(limits=cores):
-        t0 = time.perf_counter()
-        OL.layer_tokens(x, C, b, wts, cfg.n_group, cfg.topk_group, cfg.k, cfg.I, toks)
-        dt = time.perf_counter() - t0
+
+    def sample(c, n, runs):
+        x = synth.gen_x(c)
+        C = synth.gen_centroids(c)
+        b = synth.gen_bias(c)
+        toks = np.arange(n)
+        r = OR.route(x[toks], C, b, c.n_group, c.topk_group, c.k)
+        experts = set(r["idx"].ravel().tolist()) | {c.E}
+        t0 = time.time()
+        wts.prefetch(experts, threads=cores)
+        log(f"[bench] cpu baseline {c.name}: {len(experts)} experts quantised in "
+            f"{time.time() - t0:.1f}s (setup)")
+        times = []
+        with threadpool_limits(limits=cores):
+            for _ in range(runs):
+                t0 = time.perf_counter()
+                OL.layer_tokens(x, C, b, wts, c.n_group, c.topk_group, c.k, c.I, toks)
+                times.append(time.perf_counter() - t0)
+        return float(np.median(times)), len(experts), times
+
+    dt, ne, _ = sample(cfg, n_tokens, 1)
+    ddt, dne, dtimes = sample(dcfg, n_decode, decode_runs)
+    log(f"[bench] cpu baseline: prefill {n_tokens / dt:.2f} tokens/s, decode "
+        f"{n_decode / ddt:.2f} tokens/s ({cores} cores)")
     return {"value": n_tokens / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"FP64 oracle layer output for {n_tokens} of the {cfg.T} tokens "
-                      f"({len(experts)} experts incl. shared), {dt:.1f}s"}
+                      f"({ne} experts incl. shared), one run, {dt:.1f}s",
+            "decode": {"value": n_decode / ddt, "unit": "tokens/s", "cores": cores,
+                       "kind": "oracle",
+                       "sample": f"FP64 oracle layer output for {n_decode} of the {dcfg.T} "
+                                 f"decode tokens ({dne} experts incl. shared), median of "
+                                 f"{decode_runs} runs: " + ", ".join(f"{t:.1f}s" for t in dtimes)}}
 
 
 def main():
@@ -555,7 +574,7 @@ def main():
         "copy_probe": cp,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(cfg)
+        out["cpu_baseline"] = cpu_baseline(cfg, dcfg)
     print(json.dumps(out), flush=True)
 
 

@@ -38,7 +38,7 @@ namespace {
 constexpr int GM_THREADS = 256;
 constexpr int BN = 256;
 
-template <int BM, int WAVES_M, int STAGES, bool SWIGLU, bool GATHER>
+template <int BM, int WAVES_M, int STAGES, bool SWIGLU, bool GATHER, bool EXACT = false>
 struct Cfg {
   static constexpr int WAVES_N = 4 / WAVES_M;
   static constexpr int WTM = BM / WAVES_M;
@@ -70,9 +70,9 @@ struct Cfg {
 // tile are copied into LDS one tile ahead (every step of a tile repeats that
 // copy, so the table a new tile reads was written by a copy that has already
 // been waited for).
-template <int BM, int WAVES_M, int STAGES, bool SWIGLU, bool GATHER>
+template <int BM, int WAVES_M, int STAGES, bool SWIGLU, bool GATHER, bool EXACT>
 __global__ __launch_bounds__(GM_THREADS, 1) void grouped_gemm_kernel(GemmArgs args) {
-  using C_ = Cfg<BM, WAVES_M, STAGES, SWIGLU, GATHER>;
+  using C_ = Cfg<BM, WAVES_M, STAGES, SWIGLU, GATHER, EXACT>;
   __shared__ __attribute__((aligned(16))) uint8_t smem[C_::LDS];
   __shared__ int s_red[4];
   __shared__ int s_carry;
@@ -238,7 +238,12 @@ __global__ __launch_bounds__(GM_THREADS, 1) void grouped_gemm_kernel(GemmArgs ar
 
   const int nsteps32 = (int)nsteps;
   int c_ord = 0, c_kb = 0, slot = 0;  // consume position
+  int c_rows = 0;                     // rows of the tile being consumed
   for (int c = 0; c < nsteps32; ++c) {
+    if (c_kb == 0) {
+      const Tile tc = tile_of(c_ord);
+      c_rows = __builtin_amdgcn_readfirstlane(tc.m1 - tc.m0);
+    }
     const int after = min(STAGES - 2, nsteps32 - 1 - c);
     if (STAGES >= 4 && after >= 2) wait_vmcnt<(STAGES >= 4 ? 2 : 0) * C_::LOADS>();
     else if (after >= 1) wait_vmcnt<C_::LOADS>();
@@ -276,43 +281,87 @@ __global__ __launch_bounds__(GM_THREADS, 1) void grouped_gemm_kernel(GemmArgs ar
     v8i a[C_::SI];
 #pragma unroll
     for (int i = 0; i < C_::SI; ++i) a[i] = lds_frag(tA, wm * C_::WTM + i * 16 + (lane & 15), h);
-    // software pipeline over column subtiles: the MFMAs of subtile j and the
-    // LDS read of j+1 are issued before the promotion FMAs of subtile j-1
-    v8i bcur = lds_frag(tB, b_row_of(0), h);
-    v4f pprev[C_::SI];
+    if constexpr (EXACT) {
+      // exact sums: phase p of every (row block, column subtile) pair, the
+      // pairs' chains interleaved (independent accumulators), the step's
+      // copies spread over the phases; then one promotion FMA per output
+      v8i bb[C_::SJ];
 #pragma unroll
-    for (int j = 0; j < C_::SJ; ++j) {
-      v8i bnext = bcur;
-      if (j + 1 < C_::SJ) bnext = lds_frag(tB, b_row_of(j + 1), h);
-      v4f pcur[C_::SI];
+      for (int j = 0; j < C_::SJ; ++j) bb[j] = lds_frag(tB, b_row_of(j), h);
+      v4f pc[C_::SI][C_::SJ];
 #pragma unroll
-      for (int i = 0; i < C_::SI; ++i) pcur[i] = mfma_fp8_block(a[i], bcur);
-      if (do_issue) {
-        // copies k in [j*LOADS/SJ, (j+1)*LOADS/SJ) of the step STAGES-1 ahead
+      for (int i = 0; i < C_::SI; ++i)
 #pragma unroll
-        for (int k = (j * C_::LOADS) / C_::SJ; k < ((j + 1) * C_::LOADS) / C_::SJ; ++k) issue_op(k);
+        for (int j = 0; j < C_::SJ; ++j) pc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int p = 0; p < 8; ++p) {
+#pragma unroll
+        for (int i = 0; i < C_::SI; ++i) {
+          if (i > 0 && wm * C_::WTM + 16 * i >= c_rows) continue;
+          const v8i x = exact_phase(a[i], p);
+#pragma unroll
+          for (int j = 0; j < C_::SJ; ++j) pc[i][j] = mfma_fp8(x, bb[j], pc[i][j]);
+        }
+        if (do_issue) {
+#pragma unroll
+          for (int k = (p * C_::LOADS) / 8; k < ((p + 1) * C_::LOADS) / 8; ++k) issue_op(k);
+        }
       }
-      if (j > 0) {
-        const bool up = SWIGLU && (j - 1) >= SJH;
+      if (do_issue) issue_end();
+#pragma unroll
+      for (int j = 0; j < C_::SJ; ++j) {
+        const bool up = SWIGLU && j >= SJH;
 #pragma unroll
         for (int i = 0; i < C_::SI; ++i)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            acc[i][j - 1][r] = fmaf(up ? sc1[i][r] : sc0[i][r], pprev[i][r], acc[i][j - 1][r]);
+            acc[i][j][r] = fmaf(up ? sc1[i][r] : sc0[i][r], pc[i][j][r], acc[i][j][r]);
       }
+    } else {
+      // software pipeline over column subtiles: the MFMAs of subtile j and the
+      // LDS read of j+1 are issued before the promotion FMAs of subtile j-1
+      v8i bcur = lds_frag(tB, b_row_of(0), h);
+      v4f pprev[C_::SI];
 #pragma unroll
-      for (int i = 0; i < C_::SI; ++i) pprev[i] = pcur[i];
-      bcur = bnext;
-    }
-    if (do_issue) issue_end();
-    {
-      const bool up = SWIGLU && (C_::SJ - 1) >= SJH;
+      for (int j = 0; j < C_::SJ; ++j) {
+        v8i bnext = bcur;
+        if (j + 1 < C_::SJ) bnext = lds_frag(tB, b_row_of(j + 1), h);
+        // row blocks wholly past the group's end are never stored: no MFMAs
+        v4f pcur[C_::SI];
 #pragma unroll
-      for (int i = 0; i < C_::SI; ++i)
+        for (int i = 0; i < C_::SI; ++i) {
+          if (i == 0 || wm * C_::WTM + 16 * i < c_rows)
+            pcur[i] = mfma_fp8_block(a[i], bcur);
+          else
+            pcur[i] = v4f{0.f, 0.f, 0.f, 0.f};
+        }
+        if (do_issue) {
+          // copies k in [j*LOADS/SJ, (j+1)*LOADS/SJ) of the step STAGES-1 ahead
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          acc[i][C_::SJ - 1][r] =
-              fmaf(up ? sc1[i][r] : sc0[i][r], pprev[i][r], acc[i][C_::SJ - 1][r]);
+          for (int k = (j * C_::LOADS) / C_::SJ; k < ((j + 1) * C_::LOADS) / C_::SJ; ++k) issue_op(k);
+        }
+        if (j > 0) {
+          const bool up = SWIGLU && (j - 1) >= SJH;
+#pragma unroll
+          for (int i = 0; i < C_::SI; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              acc[i][j - 1][r] = fmaf(up ? sc1[i][r] : sc0[i][r], pprev[i][r], acc[i][j - 1][r]);
+        }
+#pragma unroll
+        for (int i = 0; i < C_::SI; ++i) pprev[i] = pcur[i];
+        bcur = bnext;
+      }
+      if (do_issue) issue_end();
+      {
+        const bool up = SWIGLU && (C_::SJ - 1) >= SJH;
+#pragma unroll
+        for (int i = 0; i < C_::SI; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            acc[i][C_::SJ - 1][r] =
+                fmaf(up ? sc1[i][r] : sc0[i][r], pprev[i][r], acc[i][C_::SJ - 1][r]);
+      }
     }
 
     const int ct = c_ord;
@@ -423,13 +472,15 @@ int num_cus() {
 
 namespace {
 
-template <int BM, int WAVES_M, int STAGES, bool SWIGLU>
+template <int BM, int WAVES_M, int STAGES, bool SWIGLU, bool EXACT = false>
 int launch(const GemmArgs& a, hipStream_t st) {
   const int grid = std::max(8, (num_cus() / 8) * 8);
   if (a.a_row_index)
-    grouped_gemm_kernel<BM, WAVES_M, STAGES, SWIGLU, true><<<dim3(grid), dim3(GM_THREADS), 0, st>>>(a);
+    grouped_gemm_kernel<BM, WAVES_M, STAGES, SWIGLU, true, EXACT>
+        <<<dim3(grid), dim3(GM_THREADS), 0, st>>>(a);
   else
-    grouped_gemm_kernel<BM, WAVES_M, STAGES, SWIGLU, false><<<dim3(grid), dim3(GM_THREADS), 0, st>>>(a);
+    grouped_gemm_kernel<BM, WAVES_M, STAGES, SWIGLU, false, EXACT>
+        <<<dim3(grid), dim3(GM_THREADS), 0, st>>>(a);
   return MOE_OK;
 }
 
@@ -451,12 +502,16 @@ template <bool SWIGLU>
 int dispatch(const GemmArgs& a, int64_t M_total, hipStream_t st) {
   // rows per group decide the M tile: 256 (the wide kernel) or 128 for
   // prefill-sized groups, 32 when groups hold a handful of rows (decode), 64
-  // in between
+  // in between.  The 32-row launches are bound by their weight stream (a few
+  // rows per 128x128 weight block); those feeding the SwiGLU requantisation
+  // take the exact-sum MFMA form (the truncation error of the gate/up sums
+  // would otherwise flip E4M3 codes of h), the plain bf16 ones the full-rate
+  // form.
   const int64_t avg = M_total / a.G;
   if (takes_wide<SWIGLU>(a, M_total)) return launch_wide(a, SWIGLU, st);
   if (avg >= 96) return launch<128, 2, 3, SWIGLU>(a, st);
   if (avg >= 40) return launch<64, 1, 3, SWIGLU>(a, st);
-  return launch<32, 1, 4, SWIGLU>(a, st);
+  return launch<32, 1, 4, SWIGLU, SWIGLU>(a, st);
 }
 
 int validate_common(const char* who, const uint8_t* A, const float* A_scale,

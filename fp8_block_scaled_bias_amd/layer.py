@@ -12,9 +12,7 @@ FP8 低精度训练):
   3. moe_permute       expert-major dispatch order (no copy: GEMM 1 gathers)
   4. grouped_fp8_gemm_swiglu
                        gate+up of the 256 routed experts and the shared one,
-                       SwiGLU and 1x128 requantisation in the epilogue (the
-                       unfused form - grouped_fp8_gemm to bf16, then
-                       fp8_quant_1x128 mode 1 - is kept behind fused=False)
+                       SwiGLU and 1x128 requantisation in the epilogue
   5. grouped_fp8_gemm  down projection
   6. moe_combine       gate-weighted sum of routed outputs + shared output
   7. moe_bias_update   (optional) aux-loss-free bias step for the next batch
@@ -117,7 +115,8 @@ class Buffers:
 
     @property
     def hgu(self):
-        """bf16 gate+up output of the unfused path (allocated on first use)."""
+        """bf16 gate+up outputs kept by forward(keep_gu=True) for the backward
+        (allocated on first use)."""
         if self._hgu is None:
             self._hgu = torch.empty((self.R, 2 * self._shape.I), dtype=torch.bfloat16,
                                     device=self._dev)
@@ -234,7 +233,7 @@ class MoELayer:
 
     def forward(self, x_bf16: torch.Tensor, bufs: Buffers | None = None, stream=None,
                 update_bias: bool = False, gamma: float = 0.001,
-                fused: bool = True, events: dict | None = None,
+                events: dict | None = None,
                 seq_len: int | None = None, alpha: float = 0.0001,
                 keep_gu: bool = False) -> torch.Tensor:
         """One layer forward.  With seq_len, also the sequence-wise balance
@@ -254,8 +253,8 @@ class MoELayer:
         R = b.R
         b.gu_kept = keep_gu
         if events is not None:
-            return self._forward_timed(x_bf16, b, stream, update_bias, gamma, fused, events,
-                                       seq_len, alpha)
+            return self._forward_timed(x_bf16, b, stream, update_bias, gamma, events, seq_len,
+                                       alpha)
         self._route(x_bf16, b, seq_len, stream)
         if seq_len is not None:
             self._seq_balance(b, seq_len, alpha, stream)
@@ -263,16 +262,12 @@ class MoELayer:
         L.moe_permute(b.topk_idx, b.counts, T, s.k, s.E, s.n_shared, b.offsets, b.perm_src,
                       b.inv_perm, None, None, s.H, None, None, b.perm_ws, b.perm_ws_bytes,
                       stream)
-        if fused and keep_gu:
+        if keep_gu:
             L.grouped_fp8_gemm_swiglu_keep(b.xq, b.xs, b.perm_src, self.w_gu, self.w_gu_s,
                                            b.offsets, s.G, R, s.I, s.H, b.hq, b.hs, b.hgu, stream)
-        elif fused:
+        else:
             L.grouped_fp8_gemm_swiglu(b.xq, b.xs, b.perm_src, self.w_gu, self.w_gu_s, b.offsets,
                                       s.G, R, s.I, s.H, b.hq, b.hs, stream)
-        else:
-            L.grouped_fp8_gemm(b.xq, b.xs, b.perm_src, self.w_gu, self.w_gu_s, b.offsets, s.G,
-                               R, 2 * s.I, s.H, b.hgu, stream)
-            L.fp8_quant_1x128(b.hgu, R, s.I, 2 * s.I, 1, b.hq, b.hs, stream)
         L.grouped_fp8_gemm(b.hq, b.hs, None, self.w_dn, self.w_dn_s, b.offsets, s.G, R, s.H,
                            s.I, b.d, stream)
         shared = b.d[T * s.k:T * s.k + T] if s.n_shared else None
@@ -424,8 +419,7 @@ class MoELayer:
         L.moe_seq_balance(b.scores, b.score_sums, b.topk_idx, b.T, s.E, s.k, seq_len, alpha,
                           b.seq_f, b.seq_p, b.seq_loss, b.seq_ws, b.seq_ws_bytes, stream)
 
-    def _forward_timed(self, x_bf16, b, stream, update_bias, gamma, fused, events, seq_len,
-                       alpha):
+    def _forward_timed(self, x_bf16, b, stream, update_bias, gamma, events, seq_len, alpha):
         s = self.shape
         T, R = x_bf16.shape[0], b.R
         st = stream if stream is not None else torch.cuda.current_stream()
@@ -445,19 +439,14 @@ class MoELayer:
         timed("permute", lambda: L.moe_permute(
             b.topk_idx, b.counts, T, s.k, s.E, s.n_shared, b.offsets, b.perm_src, b.inv_perm,
             None, None, s.H, None, None, b.perm_ws, b.perm_ws_bytes, st))
-        if fused and b.gu_kept:
+        if b.gu_kept:
             timed("gate_up", lambda: L.grouped_fp8_gemm_swiglu_keep(
                 b.xq, b.xs, b.perm_src, self.w_gu, self.w_gu_s, b.offsets, s.G, R, s.I, s.H,
                 b.hq, b.hs, b.hgu, st))
-        elif fused:
+        else:
             timed("gate_up", lambda: L.grouped_fp8_gemm_swiglu(
                 b.xq, b.xs, b.perm_src, self.w_gu, self.w_gu_s, b.offsets, s.G, R, s.I, s.H,
                 b.hq, b.hs, st))
-        else:
-            timed("gate_up", lambda: L.grouped_fp8_gemm(
-                b.xq, b.xs, b.perm_src, self.w_gu, self.w_gu_s, b.offsets, s.G, R, 2 * s.I,
-                s.H, b.hgu, st))
-            timed("swiglu", lambda: L.fp8_quant_1x128(b.hgu, R, s.I, 2 * s.I, 1, b.hq, b.hs, st))
         timed("down", lambda: L.grouped_fp8_gemm(
             b.hq, b.hs, None, self.w_dn, self.w_dn_s, b.offsets, s.G, R, s.H, s.I, b.d, st))
         shared = b.d[T * s.k:T * s.k + T] if s.n_shared else None

@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import synth
-from gpu_common import (bf16_dev, bf16_values_host, dev, host, log, rel_l2, compare_routes,
+from gpu_common import (bf16_dev, bf16_values_host, bf16_ulp, dev, host, log, rel_l2, compare_routes,
                         assert_within_one_bf16_ulp)
 from oracle import balance as OB
 from oracle import combine as OC
@@ -173,11 +173,13 @@ def _check_route(cfg, T, seed, label):
     ora = OR.route(bits, C, b, cfg.n_group, cfg.topk_group, cfg.k)
     mism = compare_routes(idx, ora, label)
     ok = np.setdiff1d(np.arange(T), mism)
-    # weights: fp32 sigmoid of fp32-accumulated logits vs float64; the logit
-    # error is bounded by a few 1e-6, so a weight moves by at most ~1e-6.
+    # weights: fp32 sigmoid of fp32-accumulated logits vs float64, checked
+    # relative to the oracle's weight (the bit-exact scope's reading: at most
+    # 1e-6 relative)
     err = np.abs(w[ok].astype(np.float64) - ora["w"][ok])
-    log(f"[route] {label}: max |w_gpu - w_oracle| = {err.max():.3e}")
-    assert err.max() <= 4e-6
+    rel = err / ora["w"][ok]
+    log(f"[route] {label}: max |w_gpu - w_oracle| = {err.max():.3e}, relative {rel.max():.3e}")
+    assert rel.max() <= 1e-6
     assert np.array_equal(cnt, np.bincount(idx.ravel(), minlength=cfg.E))
     if len(mism) == 0:
         assert np.array_equal(cnt, ora["counts"])
@@ -209,7 +211,7 @@ def test_route_large_batches():
 
 def test_route_hand_traced_ties():
     from test_oracle_route import _ties_rows
-    for E, ng, tg, k, b, ids, ws in _ties_rows():
+    for E, ng, tg, k, b, ids, ws, _margin in _ties_rows():
         H = 256
         bits = np.zeros((70, H), np.uint16)
         C = synth.gen_centroids(synth.TINY.with_(E=E, H=H))
@@ -286,9 +288,13 @@ def _gemm_gpu(qA, sA, rowidx, qB, sB, offsets, N, K):
 
 
 # Error of one FP8 MFMA 128-term partial relative to its absolute sum
-# sum|a b|: the gfx950 v_mfma_f32_16x16x128_f8f6f4 dot product is not
-# fp32-exact; over 1M random E4M3 sums its error reached 2^-15.6 of the
-# absolute sum (mean 2^-19.4).  2^-14 keeps a 3x margin over that maximum.
+# sum|a b|: gfx950's FP8 instructions truncate each product of a run of 8
+# consecutive K positions to 13 binades below the run's largest product
+# (pinned in test_gpu_mfma_precision).  On 1x128 tiles of Gaussian data and
+# of SwiGLU outputs against 128x128 Gaussian weight blocks (the operands of
+# these tests) the error reaches 2^-15.8 and 2^-14.1 of the absolute sum
+# (test_mfma_term_forward_operands asserts 2^-14); uniformly random codes,
+# which these tests never feed, reach 2^-12.2.
 MFMA_BLOCK_REL = 2.0 ** -14
 PROMO_ROUNDINGS = 5
 
@@ -413,6 +419,34 @@ def test_gemm_gather_index_clamped(sizes):
     clamped = np.where((rowidx < 0) | (rowidx >= rows_src), rows_src - 1, rowidx)
     ref = OG.to_bf16(OG.grouped_gemm(qA[clamped], sA[clamped], qB, sB, offsets))
     assert np.array_equal(got, ref), int((got != ref).sum())
+
+
+def test_gemm_swiglu_exact_sums_small_groups():
+    """Fused gate+up launches with a handful of rows per group (fewer than 40
+    on average: the decode regime, bound by the weight stream) take the
+    exact-sum MFMA form (eight instructions per K block, one K position of
+    every run of 8 in each): their fp32 gate/up totals are the exact
+    block-scaled sums up to fp32 roundings, so every E4M3 code of h is the
+    oracle's unless h lies within those roundings of a rounding midpoint
+    (check_fused_swiglu with the fp32-rounding bound in place of the MFMA
+    term: 8 phase additions and the promotion per K block)."""
+    sizes = [5, 0, 31, 1, 17, 3, 40, 9, 2, 12]
+    G, K, I = len(sizes), 1024, 256
+    N = 2 * I
+    offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    Mt = int(offsets[-1])
+    rng = np.random.default_rng(78)
+    qA, sA = OQ.quant_1x128(rng.standard_normal((Mt, K)).astype(np.float32))
+    qB = np.empty((G, N, K), np.uint8)
+    sB = np.empty((G, N // 128, K // 128), np.float32)
+    for g in range(G):
+        qB[g], sB[g] = OQ.quant_128x128((rng.standard_normal((N, K)) * 0.02).astype(np.float32))
+    exact = OG.grouped_gemm(qA, sA, qB, sB, offsets)
+    S = OG.grouped_gemm(qA & 0x7F, sA, [q & 0x7F for q in qB], sB, offsets)
+    bound = (10 * (K // 128) + 2) * 2.0 ** -24 * S
+    q, sc = _swiglu_gpu(qA, sA, None, qB, sB, offsets, I, K)
+    n = check_fused_swiglu(q, sc, exact, bound, I, "exact-sum SwiGLU")
+    log(f"[gemm exact] SwiGLU codes differing from the oracle: {n} of {q.size}")
 
 
 @pytest.mark.parametrize("sizes,N,K", [([5, 0, 300, 129], 384, 1024), ([1000], 256, 7168),

@@ -38,6 +38,8 @@ SIGNATURES = {
     "moe_permute_workspace_bytes": (_sz, [_i64, _i32, _i32]),
     "moe_permute": (ctypes.c_int, [_vp, _vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp,
                                    _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
+    "moe_permute_noalloc": (ctypes.c_int, [_vp, _vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp,
+                                           _vp, _vp, _i64, _vp, _vp, _vp]),
     "fp8_quant_1x128": (ctypes.c_int, [_vp, _i64, _i64, _i64, _i32, _vp, _vp, _vp]),
     "fp8_quant_128x128": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _vp, _vp]),
     "fp8_transpose_128x128": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp]),
@@ -179,6 +181,13 @@ def moe_permute(topk_idx, expert_counts, T, k, E, n_shared, offsets, perm_src, i
                  _dev(offsets), _dev(perm_src), _dev(inv_perm), _dev(xq), _dev(xs), H,
                  _dev(a_out), _dev(a_scale_out), _dev(workspace), workspace_bytes,
                  _stream(stream))
+
+
+def moe_permute_noalloc(topk_idx, expert_counts, T, k, E, n_shared, offsets, perm_src, inv_perm,
+                        xq, xs, H, a_out, a_scale_out, stream=None):
+    return _call("moe_permute_noalloc", _dev(topk_idx), _dev(expert_counts), T, k, E, n_shared,
+                 _dev(offsets), _dev(perm_src), _dev(inv_perm), _dev(xq), _dev(xs), H,
+                 _dev(a_out), _dev(a_scale_out), _stream(stream))
 
 
 def fp8_quant_1x128(in_bf16, M, K, ld_in, mode, out_e4m3, scales, stream=None):

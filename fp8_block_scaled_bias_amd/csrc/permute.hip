@@ -17,10 +17,42 @@
 // An optional gather copies the E4M3 rows and 1x128 scales into row order.
 #include "common.h"
 
+#include <mutex>
+
 namespace moe {
 namespace {
 
 constexpr int PM_TOK = 64;  // tokens per chunk
+
+// Scratch of moe_permute_noalloc: one copy per GPU, held until the process
+// ends.  Host code never passes the array's name to a kernel (on the host it
+// names a stand-in, not device memory); it uses the per-device address that
+// hipGetSymbolAddress returns, looked up once per device.
+static __device__ __align__(256) uint8_t scratch[MOE_PERMUTE_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+void* g_scratch_ptr[kMaxDevices] = {};
+std::mutex g_scratch_mu;
+
+// Device address of this device's scratch (NULL with the error set on failure).
+void* scratch_address() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    set_error("moe_permute_noalloc: no current device (or device id %d out of range)", dev);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) {
+      set_error("moe_permute_noalloc: hipGetSymbolAddress failed on device %d: %s", dev,
+                hipGetErrorString(e));
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
 
 __global__ __launch_bounds__(64) void permute_count_kernel(const int32_t* __restrict__ idx,
                                                            int64_t T, int k, int E,
@@ -214,4 +246,23 @@ extern "C" int moe_permute(const int32_t* topk_idx, const int32_t* expert_counts
     }
   }
   return check_launch("moe_permute");
+}
+
+extern "C" int moe_permute_noalloc(const int32_t* topk_idx, const int32_t* expert_counts,
+                                   int64_t T, int32_t k, int32_t E, int32_t n_shared,
+                                   int32_t* offsets, int32_t* perm_src, int32_t* inv_perm,
+                                   const uint8_t* xq, const float* xs, int64_t H,
+                                   uint8_t* a_out, float* a_scale_out, void* stream) {
+  clear_error();
+  MOE_INVALID(T >= 0 && E >= 1, "moe_permute_noalloc: T=%lld, E=%d", (long long)T, (int)E);
+  const size_t need = moe_permute_workspace_bytes(T, k, E);
+  MOE_REQUIRE(need <= MOE_PERMUTE_SCRATCH_BYTES, MOE_ERR_WORKSPACE,
+              "moe_permute_noalloc: T=%lld, E=%d needs %zu bytes of scratch, more than the "
+              "%zu of the static array (ceil(T/64) * E must be at most %zu)",
+              (long long)T, (int)E, need, (size_t)MOE_PERMUTE_SCRATCH_BYTES,
+              (size_t)MOE_PERMUTE_SCRATCH_BYTES / sizeof(int32_t));
+  void* ws = scratch_address();
+  if (ws == nullptr) return MOE_ERR_HIP;
+  return moe_permute(topk_idx, expert_counts, T, k, E, n_shared, offsets, perm_src, inv_perm,
+                     xq, xs, H, a_out, a_scale_out, ws, MOE_PERMUTE_SCRATCH_BYTES, stream);
 }

@@ -176,6 +176,27 @@ int moe_permute(const int32_t* topk_idx, const int32_t* expert_counts,
                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * moe_permute_noalloc - moe_permute for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments, outputs and errors as moe_permute minus
+ * the workspace: the per-chunk histograms live in a static device array of
+ * MOE_PERMUTE_SCRATCH_BYTES bytes that the library keeps on every GPU it
+ * runs on until the process ends (its address is looked up once per device,
+ * on the first call with that device current).  The call allocates nothing.
+ * Its scratch need is moe_permute_workspace_bytes(T, k, E); a larger need
+ * (ceil(T/64) * E > 262144, e.g. T > 65536 at E = 256) returns
+ * MOE_ERR_WORKSPACE without launching.  Every call on one GPU shares that
+ * GPU's array: calls that overlap on one GPU (different streams, or host
+ * threads without ordering) race; calls ordered on one stream do not.
+ */
+#define MOE_PERMUTE_SCRATCH_BYTES ((size_t)1 << 20)
+int moe_permute_noalloc(const int32_t* topk_idx, const int32_t* expert_counts,
+                        int64_t T, int32_t k, int32_t E, int32_t n_shared,
+                        int32_t* offsets, int32_t* perm_src, int32_t* inv_perm,
+                        const uint8_t* xq, const float* xs, int64_t H,
+                        uint8_t* a_out, float* a_scale_out, void* stream);
+
+/*
  * fp8_quant_1x128 - fine-grained activation quantisation (news.qq.com
  * article, section FP8 低精度训练 › 细粒度量化: 1x128 tiles for activations).
  *

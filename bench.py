@@ -266,25 +266,30 @@ def bench_backward_step(layer, x, cfg, steps=3, warmup=1):
     the same batch: combine backward, dgrad of down, the recomputed gate+up,
     SwiGLU backward, dgrad of gate+up, unpermute, both weight gradients and
     the router's backward (dx and the centroids' gradient); dy N(0,1) bf16
-    (synth.gen_dy).  The weight transposes are made once per weight update
-    (cached on the layer, timed under "backward").  Flops counted: the GEMMs
-    only, 2RHI for each of dgrad-down and wgrad-down, 4RHI for each of the
-    recomputed gate+up, dgrad-gate+up and wgrad-gate+up (34.6 TFLOP).  Then
-    a training step (forward + backward, wall clock) with the gate+up GEMM
-    rerun in the backward and with the forward keeping its outputs."""
+    (synth.gen_dy).  Every timed step starts as after a weight update
+    (mark_weights_changed), so the 128x128 weight transposes the input
+    gradient reads are made inside it ("transpose_weights" in the per-stage
+    times).  Flops counted: the GEMMs only, 2RHI for each of dgrad-down and
+    wgrad-down, 4RHI for each of the recomputed gate+up, dgrad-gate+up and
+    wgrad-gate+up (34.6 TFLOP).  Then a training step (forward + backward,
+    wall clock, with the same per-update transposes) with the gate+up GEMM
+    rerun in the backward and with the forward keeping its outputs; and the
+    128x128 requantisation of fp32 master weights (fp8_quant_128x128 over
+    both weight sets, the other per-update step), timed on its own."""
     import time
     import numpy as np
     import torch
     import synth
     dy = torch.from_numpy(synth.gen_dy(cfg).view(np.int16)).cuda().view(torch.bfloat16)
     layer.forward(x)
-    layer.transpose_weights()
     for _ in range(warmup):
+        layer.mark_weights_changed()
         layer.backward(dy, x)
     torch.cuda.synchronize()
     events = {}
     t0 = time.perf_counter()
     for _ in range(steps):
+        layer.mark_weights_changed()
         layer.backward(dy, x, events=events)
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) / steps * 1e3
@@ -301,16 +306,35 @@ def bench_backward_step(layer, x, cfg, steps=3, warmup=1):
     # also keeps its bf16 gate/up outputs (1.2 GB) for the backward to read
     for name, keep in (("train_step_recompute", False), ("train_step_keep_gu", True)):
         layer.forward(x, keep_gu=keep)
+        layer.mark_weights_changed()
         layer.backward(dy, x)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for _ in range(steps):
             layer.forward(x, keep_gu=keep)
+            layer.mark_weights_changed()
             layer.backward(dy, x)
         torch.cuda.synchronize()
         out[name + "_ms"] = (time.perf_counter() - t0) / steps * 1e3
     log(f"[bench] training step: {out['train_step_recompute_ms']:.3f} ms recomputing gate+up, "
         f"{out['train_step_keep_gu_ms']:.3f} ms keeping it")
+    # the per-update requantisation of fp32 master weights (expert by expert,
+    # from one fp32 buffer per weight set: the timing covers the quantiser)
+    s_ = layer.shape
+    gu32 = torch.randn((s_.G, 2 * s_.I, s_.H), dtype=torch.float32, device="cuda").mul_(0.006)
+    dn32 = torch.randn((s_.G, s_.H, s_.I), dtype=torch.float32, device="cuda").mul_(0.006)
+    wq = [t.clone() for t in (layer.w_gu, layer.w_gu_s, layer.w_dn, layer.w_dn_s)]
+    from fp8_block_scaled_bias_amd import _lib as L_
+    def requant():
+        L_.fp8_quant_128x128(gu32, s_.G, 2 * s_.I, s_.H, wq[0], wq[1])
+        L_.fp8_quant_128x128(dn32, s_.G, s_.H, s_.I, wq[2], wq[3])
+    q_ms = _median_ms(requant, 5, 1)
+    q_bytes = 4.0 * (gu32.numel() + dn32.numel()) + (gu32.numel() + dn32.numel()) * 1.0
+    out["requantize_weights_ms"] = q_ms
+    out["requantize_weights_GB_s"] = q_bytes / (q_ms * 1e-3) / 1e9
+    log(f"[bench] 128x128 requantisation of both fp32 weight sets: {q_ms:.3f} ms "
+        f"({out['requantize_weights_GB_s']:.0f} GB/s)")
+    del gu32, dn32, wq
     del dy
     return out
 

@@ -91,17 +91,32 @@ __global__ __launch_bounds__(GM_THREADS, 1) void grouped_gemm_kernel(GemmArgs ar
   build_group_tables<GM_THREADS, BM>(args.offs, G, s_offs, s_pref, s_red, &s_carry);
   const int64_t total = (int64_t)s_pref[G] * ntiles;
   // this workgroup's tiles: XCD x owns ids [x*chunk, (x+1)*chunk); its
-  // workgroups (blocks x, x+8, ...) take every (gridDim/8)-th of them
-  const int xcd = blockIdx.x & 7, jw = blockIdx.x >> 3, nper = gridDim.x >> 3;
+  // workgroups (blocks x, x+8, ...) take every (gridDim/8)-th of them.  The
+  // exact-sum launches (weight-stream bound, tiles of different cost: a
+  // group's 16-row blocks past its end skip their instructions) stride over
+  // the whole list instead, so no XCD holds all of a large group's tiles.
+  const int xcd = blockIdx.x & 7, jw = blockIdx.x >> 3;
+  const int nper = EXACT ? (int)gridDim.x : (int)(gridDim.x >> 3);
   const int64_t chunk = (total + 7) >> 3;
-  const int64_t tlo = xcd * chunk, thi = min(total, tlo + chunk);
-  const int64_t L0 = tlo + jw;
+  const int64_t tlo = EXACT ? 0 : xcd * chunk, thi = EXACT ? total : min(total, tlo + chunk);
+  const int64_t L0 = EXACT ? (int64_t)blockIdx.x : tlo + jw;
   if (L0 >= thi) return;
   const int64_t my_n = (thi - L0 + nper - 1) / nper;
   const int64_t nsteps = my_n * nkb;
+  // exact-sum launches: the tiles of more than 16 rows cost several times a
+  // 16-row one; in the MoE layer they are the last group's (the shared
+  // expert's rows follow the routed experts').  The strided list is rotated
+  // so that group's tiles sit at positions [rem, rem + n_last), rem = total
+  // mod grid: the workgroups taking them are not those that also take a tile
+  // of the last, partial round.
+  const int64_t n_last = (int64_t)(s_pref[G] - s_pref[G - 1]) * ntiles;
+  const int64_t rot =
+      EXACT ? (total - ((total % (int64_t)gridDim.x) + n_last) % total) % total : 0;
 
   auto tile_of = [&](int64_t ord) {
-    Tile t = decode_tile(s_pref, s_offs, G, ntiles, L0 + ord * nper, BM);
+    int64_t Lg = L0 + ord * nper;
+    if (EXACT) Lg = (Lg + rot) % total;
+    Tile t = decode_tile(s_pref, s_offs, G, ntiles, Lg, BM);
     t.g = __builtin_amdgcn_readfirstlane(t.g);
     t.m0 = __builtin_amdgcn_readfirstlane(t.m0);
     t.m1 = __builtin_amdgcn_readfirstlane(t.m1);
@@ -281,10 +296,13 @@ __global__ __launch_bounds__(GM_THREADS, 1) void grouped_gemm_kernel(GemmArgs ar
     v8i a[C_::SI];
 #pragma unroll
     for (int i = 0; i < C_::SI; ++i) a[i] = lds_frag(tA, wm * C_::WTM + i * 16 + (lane & 15), h);
-    if constexpr (EXACT) {
-      // exact sums: phase p of every (row block, column subtile) pair, the
-      // pairs' chains interleaved (independent accumulators), the step's
-      // copies spread over the phases; then one promotion FMA per output
+    if (EXACT && c_rows > 16) {
+      // exact sums, for tiles of more than one 16-row block (a tile of at
+      // most 16 rows streams its weights at full rate in the single-
+      // instruction form below): phase p of every (row block, column
+      // subtile) pair, the pairs' chains interleaved (independent
+      // accumulators), the step's copies spread over the phases; then one
+      // promotion FMA per output
       v8i bb[C_::SJ];
 #pragma unroll
       for (int j = 0; j < C_::SJ; ++j) bb[j] = lds_frag(tB, b_row_of(j), h);
@@ -503,10 +521,11 @@ int dispatch(const GemmArgs& a, int64_t M_total, hipStream_t st) {
   // rows per group decide the M tile: 256 (the wide kernel) or 128 for
   // prefill-sized groups, 32 when groups hold a handful of rows (decode), 64
   // in between.  The 32-row launches are bound by their weight stream (a few
-  // rows per 128x128 weight block); those feeding the SwiGLU requantisation
-  // take the exact-sum MFMA form (the truncation error of the gate/up sums
-  // would otherwise flip E4M3 codes of h), the plain bf16 ones the full-rate
-  // form.
+  // rows per 128x128 weight block); in those feeding the SwiGLU
+  // requantisation, tiles of more than 16 rows (at decode: the shared
+  // expert, which every token adds with weight one) take the exact-sum MFMA
+  // form, which removes the truncation error of their gate/up sums; tiles of
+  // at most 16 rows and the plain bf16 launches keep the full-rate form.
   const int64_t avg = M_total / a.G;
   if (takes_wide<SWIGLU>(a, M_total)) return launch_wide(a, SWIGLU, st);
   if (avg >= 96) return launch<128, 2, 3, SWIGLU>(a, st);

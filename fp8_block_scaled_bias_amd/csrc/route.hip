@@ -334,26 +334,23 @@ __global__ __launch_bounds__(256) void router_select_kernel(
   for (int64_t t = (int64_t)blockIdx.x * 4 + wv; t < T; t += (int64_t)gridDim.x * 4) {
     float lg[4] = {0.f, 0.f, 0.f, 0.f};
     if (active) {
-      // the split-K partials, in split order; up to 8 splits are requested
-      // before the first is added (one memory round trip per token)
-      float4 pv[8];
+      // the split-K partials, added in split order; eight splits are
+      // requested at a time before the first of them is added (one memory
+      // round trip per eight splits)
+      for (int k0 = 0; k0 < KS; k0 += 8) {
+        float4 pv[8];
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks)
-        if (ks < KS) pv[ks] = *reinterpret_cast<const float4*>(part + ((int64_t)ks * T + t) * E + ebase);
+        for (int u = 0; u < 8; ++u)
+          if (k0 + u < KS)
+            pv[u] = *reinterpret_cast<const float4*>(part + ((int64_t)(k0 + u) * T + t) * E + ebase);
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks)
-        if (ks < KS) {
-          lg[0] += pv[ks].x;
-          lg[1] += pv[ks].y;
-          lg[2] += pv[ks].z;
-          lg[3] += pv[ks].w;
-        }
-      for (int ks = 8; ks < KS; ++ks) {
-        const float4 v = *reinterpret_cast<const float4*>(part + ((int64_t)ks * T + t) * E + ebase);
-        lg[0] += v.x;
-        lg[1] += v.y;
-        lg[2] += v.z;
-        lg[3] += v.w;
+        for (int u = 0; u < 8; ++u)
+          if (k0 + u < KS) {
+            lg[0] += pv[u].x;
+            lg[1] += pv[u].y;
+            lg[2] += pv[u].z;
+            lg[3] += pv[u].w;
+          }
       }
     }
     float s[4], sb[4];
@@ -595,8 +592,7 @@ int route_impl(const void* x_bf16, int64_t T, int64_t H, const float* centroids,
                            dim3(256), 0, st>>>(static_cast<const uint16_t*>(x_bf16), T, H,
                                                centroids, E, sp.kper, part);
   }
-  // one wave per token (four per workgroup)
-  const int64_t sel_blocks = std::min<int64_t>(ceil_div(T, 4), 1 << 20);
+  const int64_t sel_blocks = std::min<int64_t>(ceil_div(T, 4), 2048);
   router_select_kernel<<<dim3((unsigned)sel_blocks), dim3(256), 0, st>>>(
       part, (int)sp.ks, T, bias, E, n_group, topk_group, k, lpg, topk_idx, topk_w,
       expert_counts, scores, score_sums);

@@ -36,8 +36,10 @@ backward-for-input and backward-for-weights chunks, section 工程 › DualPipe
      (with seq_len: moe_router_backward_dense - the balance term's gradient
      on every expert's logit joins the gate's, dx and dC as fp32 GEMMs)
 
-The weight transposes (fp8_transpose_128x128) are cached on the layer and
-redone by transpose_weights() when the weights change.
+The weight transposes (fp8_transpose_128x128) are cached on the layer; a
+backward after mark_weights_changed() (or any call that writes the weights
+through the layer) makes them again first, so stale transposes are never
+used.
 
 torch is only used to hold device memory and to name the stream; every step
 runs in the library's HIP kernels.
@@ -189,6 +191,8 @@ class MoELayer:
         self.bias = bias
         self.w_gu, self.w_gu_s, self.w_dn, self.w_dn_s = w_gu, w_gu_s, w_dn, w_dn_s
         self._wt = None          # transposed weight blocks, made on first backward
+        self._w_ver = 0          # bumped whenever the weights change
+        self._wt_ver = -1        # weight version the transposes were made from
         self._bwd = {}
         self._bufs = {}
 
@@ -276,9 +280,24 @@ class MoELayer:
             L.moe_bias_update(b.counts, self.bias, s.E, gamma, stream)
         return b.y
 
+    def mark_weights_changed(self):
+        """Record that w_gu / w_dn (or their scales) were written outside the
+        layer (an optimizer step followed by requantisation): the next backward
+        transposes them again before using them."""
+        self._w_ver += 1
+
+    def requantize_from_fp32(self, gu_fp32, dn_fp32, stream=None):
+        """Requantise both weight sets in place from fp32 master weights
+        ([G, 2I, H] and [G, H, I] device tensors) in 128x128 blocks, and mark
+        the transposes stale."""
+        s = self.shape
+        L.fp8_quant_128x128(gu_fp32, s.G, 2 * s.I, s.H, self.w_gu, self.w_gu_s, stream)
+        L.fp8_quant_128x128(dn_fp32, s.G, s.H, s.I, self.w_dn, self.w_dn_s, stream)
+        self.mark_weights_changed()
+
     def transpose_weights(self, stream=None):
-        """W^T of both weight sets in 128x128 blocks (the dgrad operands); call
-        again after the weights change."""
+        """W^T of both weight sets in 128x128 blocks (the dgrad operands), for
+        the current weights."""
         s = self.shape
         if self._wt is None:
             dev = self.w_gu.device
@@ -290,6 +309,7 @@ class MoELayer:
         w = self._wt
         L.fp8_transpose_128x128(self.w_gu, self.w_gu_s, s.G, 2 * s.I, s.H, w["gu"], w["gu_s"], stream)
         L.fp8_transpose_128x128(self.w_dn, self.w_dn_s, s.G, s.H, s.I, w["dn"], w["dn_s"], stream)
+        self._wt_ver = self._w_ver
         return w
 
     def capture(self, x_bf16: torch.Tensor, bufs: Buffers | None = None, **forward_kw):
@@ -336,11 +356,19 @@ class MoELayer:
         T = dy_bf16.shape[0]
         b = bufs or self.buffers(T)
         bb = bwd or self.backward_buffers(T)
-        if self._wt is None:
-            self.transpose_weights(stream)
-        w = self._wt
         R, G, H, I, k, cap = b.R, s.G, s.H, s.I, s.k, bb.cap
         st = stream if stream is not None else torch.cuda.current_stream()
+        if self._wt is None or self._wt_ver != self._w_ver:
+            if events is None:
+                self.transpose_weights(st)
+            else:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(st)
+                self.transpose_weights(st)
+                e1.record(st)
+                events.setdefault("transpose_weights", []).append((e0, e1))
+        w = self._wt
 
         def step(name, fn):
             if events is None:

@@ -423,15 +423,17 @@ def test_gemm_gather_index_clamped(sizes):
 
 def test_gemm_swiglu_exact_sums_small_groups():
     """Fused gate+up launches with a handful of rows per group (fewer than 40
-    on average: the decode regime, bound by the weight stream) take the
-    exact-sum MFMA form (eight instructions per K block, one K position of
-    every run of 8 in each): their fp32 gate/up totals are the exact
-    block-scaled sums up to fp32 roundings, so every E4M3 code of h is the
-    oracle's unless h lies within those roundings of a rounding midpoint
-    (check_fused_swiglu with the fp32-rounding bound in place of the MFMA
-    term: 8 phase additions and the promotion per K block)."""
+    on average: the decode regime, 32-row tiles, bound by the weight stream)
+    take the exact-sum MFMA form (eight instructions per K block, one K
+    position of every run of 8 in each) in tiles of more than 16 rows: their
+    fp32 gate/up totals are the exact block-scaled sums up to fp32
+    roundings, so every E4M3 code of h is the oracle's unless h lies within
+    those roundings of a rounding midpoint (check_fused_swiglu with the
+    fp32-rounding bound: 8 phase additions and the promotion per K block).
+    Rows of tiles of at most 16 rows (groups 5, 1, 3, 9, 2, 12 and the last
+    8 rows of the 40) keep the single-instruction form and its MFMA bound."""
     sizes = [5, 0, 31, 1, 17, 3, 40, 9, 2, 12]
-    G, K, I = len(sizes), 1024, 256
+    G, K, I, BM = len(sizes), 1024, 256, 32
     N = 2 * I
     offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
     Mt = int(offsets[-1])
@@ -443,10 +445,19 @@ def test_gemm_swiglu_exact_sums_small_groups():
         qB[g], sB[g] = OQ.quant_128x128((rng.standard_normal((N, K)) * 0.02).astype(np.float32))
     exact = OG.grouped_gemm(qA, sA, qB, sB, offsets)
     S = OG.grouped_gemm(qA & 0x7F, sA, [q & 0x7F for q in qB], sB, offsets)
-    bound = (10 * (K // 128) + 2) * 2.0 ** -24 * S
+    big = np.zeros(Mt, bool)
+    for g, m in enumerate(sizes):
+        for m0 in range(0, m, BM):
+            if min(BM, m - m0) > 16:
+                big[offsets[g] + m0:offsets[g] + min(m, m0 + BM)] = True
+    assert big.sum() == 31 + 17 + 32
+    bound = gemm_accumulation_bound(qA, sA, qB, sB, offsets, K)
+    bound[big] = (10 * (K // 128) + 2) * 2.0 ** -24 * S[big]
     q, sc = _swiglu_gpu(qA, sA, None, qB, sB, offsets, I, K)
-    n = check_fused_swiglu(q, sc, exact, bound, I, "exact-sum SwiGLU")
-    log(f"[gemm exact] SwiGLU codes differing from the oracle: {n} of {q.size}")
+    n = check_fused_swiglu(q[big], sc[big], exact[big], bound[big], I, "exact-sum SwiGLU")
+    check_fused_swiglu(q[~big], sc[~big], exact[~big], bound[~big], I, "single-form SwiGLU")
+    log(f"[gemm exact] SwiGLU codes of exact-form tiles differing from the oracle: {n} of "
+        f"{q[big].size}")
 
 
 @pytest.mark.parametrize("sizes,N,K", [([5, 0, 300, 129], 384, 1024), ([1000], 256, 7168),

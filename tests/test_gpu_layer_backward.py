@@ -402,3 +402,38 @@ def test_layer_backward_keep_gu_mid(T):
                 dW_dn=rel_l2(host(bb.dW_dn), ref["dW_dn"]))
     log(f"[layer bwd keep_gu] mid: end to end " + ", ".join(f"{k_} {v:.2e}" for k_, v in errs.items()))
     assert max(errs.values()) <= 5e-3, errs
+
+
+def test_layer_backward_after_weight_update():
+    """A weight update through the layer (requantize_from_fp32: 128x128
+    requantisation of new fp32 master weights) makes the next backward
+    transpose the weights again: forward and backward then equal those of a
+    fresh layer built from the new weights, bit for bit (the transposes made
+    for the old weights are never used)."""
+    cfg = synth.MID
+    layer, C, b = build_layer(cfg)
+    x = bf16_dev(synth.gen_x(cfg))
+    dy = bf16_dev(synth.gen_dy(cfg))
+    layer.forward(x)
+    layer.backward(dy, x)                       # transposes of the first weights
+    torch.cuda.synchronize()
+    seed = 5
+    gu = torch.stack([torch.from_numpy(synth.gen_expert_weight(cfg, "gu", e, seed=seed))
+                      for e in range(cfg.G)]).cuda()
+    dn = torch.stack([torch.from_numpy(synth.gen_expert_weight(cfg, "dn", e, seed=seed))
+                      for e in range(cfg.G)]).cuda()
+    layer.requantize_from_fp32(gu, dn)
+    y1 = bf16_values_host(layer.forward(x))
+    bb1 = layer.backward(dy, x)
+    out1 = [bf16_values_host(bb1.dx_total), host(bb1.dW_gu), host(bb1.dW_dn), host(bb1.dC)]
+    fresh = M.MoELayer.from_fp32_experts(
+        layer.shape, torch.from_numpy(C).cuda(), torch.from_numpy(b).cuda(),
+        ((e, synth.gen_expert_weight(cfg, "gu", e, seed=seed)) for e in range(cfg.G)),
+        ((e, synth.gen_expert_weight(cfg, "dn", e, seed=seed)) for e in range(cfg.G)))
+    y2 = bf16_values_host(fresh.forward(x))
+    bb2 = fresh.backward(dy, x)
+    out2 = [bf16_values_host(bb2.dx_total), host(bb2.dW_gu), host(bb2.dW_dn), host(bb2.dC)]
+    assert np.array_equal(y1, y2)
+    for name, a, c in zip(("dx", "dW_gu", "dW_dn", "dC"), out1, out2):
+        assert np.array_equal(a, c), name
+    log("[update] forward and backward after requantize_from_fp32 equal a fresh layer's")

@@ -3,6 +3,7 @@ sigmoid + bias group-limited routing, behind the C ABI of libmoe_fp8.so."""
 from . import _lib  # noqa: F401
 from ._lib import (MoEError, fp8_quant_1x128, fp8_quant_128x128,  # noqa: F401
                    fp8_quant_128x1_grouped, fp8_transpose_128x128, grouped_fp8_gemm,
+                   grouped_fp8_gemm_dgrad,
                    grouped_fp8_gemm_swiglu, grouped_fp8_gemm_swiglu_keep, grouped_fp8_wgrad, moe_bias_update, moe_combine,
                    moe_combine_backward, moe_permute, moe_permute_noalloc,
                    moe_permute_workspace_bytes, moe_route,

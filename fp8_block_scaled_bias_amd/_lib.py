@@ -59,6 +59,8 @@ SIGNATURES = {
                                          _vp, _vp]),
     "grouped_fp8_gemm": (ctypes.c_int, [_vp, _vp, _vp, _i64, _vp, _vp, _vp, _i32, _i64, _i64,
                                         _i64, _vp, _vp]),
+    "grouped_fp8_gemm_dgrad": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _vp,
+                                              _vp]),
     "grouped_fp8_gemm_swiglu": (ctypes.c_int, [_vp, _vp, _vp, _i64, _vp, _vp, _vp, _i32, _i64,
                                                _i64, _i64, _vp, _vp, _vp]),
     "grouped_fp8_gemm_swiglu_keep": (ctypes.c_int, [_vp, _vp, _vp, _i64, _vp, _vp, _vp, _i32, _i64,
@@ -266,6 +268,12 @@ def grouped_fp8_gemm(A, A_scale, a_row_index, B, B_scale, group_offsets, G, M_to
     return _call("grouped_fp8_gemm", _dev(A), _dev(A_scale), _dev(a_row_index), _rows(A), _dev(B),
                  _dev(B_scale), _dev(group_offsets), G, M_total, N, K, _dev(C_bf16),
                  _stream(stream))
+
+
+def grouped_fp8_gemm_dgrad(dC, dC_scale, W, W_scale, group_offsets, G, M_total, N, K, dA_bf16,
+                           stream=None):
+    return _call("grouped_fp8_gemm_dgrad", _dev(dC), _dev(dC_scale), _dev(W), _dev(W_scale),
+                 _dev(group_offsets), G, M_total, N, K, _dev(dA_bf16), _stream(stream))
 
 
 def grouped_fp8_gemm_swiglu(A, A_scale, a_row_index, B, B_scale, group_offsets, G, M_total, I,

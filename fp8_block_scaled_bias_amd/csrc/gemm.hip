@@ -583,6 +583,33 @@ extern "C" int grouped_fp8_gemm(const uint8_t* A, const float* A_scale, const in
   return check_launch("grouped_fp8_gemm");
 }
 
+extern "C" int grouped_fp8_gemm_dgrad(const uint8_t* dC, const float* dC_scale,
+                                      const uint8_t* W, const float* W_scale,
+                                      const int32_t* group_offsets, int32_t G, int64_t M_total,
+                                      int64_t N, int64_t K, void* dA_bf16, void* stream) {
+  clear_error();
+  // the kernel contracts over N (W's rows) and writes K columns
+  int rc = validate_common("grouped_fp8_gemm_dgrad", dC, dC_scale, nullptr, M_total, W, W_scale,
+                           group_offsets, G, M_total, K, N);
+  if (rc != MOE_OK || M_total == 0) return rc;
+  MOE_INVALID(dA_bf16 && ((uintptr_t)dA_bf16 & 15) == 0,
+              "grouped_fp8_gemm_dgrad: dA must be non-null and 16-byte aligned");
+  const int64_t lim = (int64_t)1 << 32;
+  MOE_UNSUPPORTED(K % 256 == 0 && K <= (1 << 21) && N % 256 == 0 && N >= 768 &&
+                      N <= (1 << 20) && N * K < lim && M_total * N < lim,
+                  "grouped_fp8_gemm_dgrad: N=%lld, K=%lld, M_total=%lld not supported (K a "
+                  "multiple of 256, N a multiple of 256 and >= 768, N*K and M_total*N below 2^32)",
+                  (long long)N, (long long)K, (long long)M_total);
+  GemmArgs a{};
+  a.A = dC; a.A_scale = dC_scale; a.a_row_index = nullptr; a.A_rows = M_total;
+  a.B = W; a.B_scale = W_scale;
+  a.offs = group_offsets; a.G = G; a.N = K; a.K = N; a.ntiles = K / BN; a.I = 0;
+  a.C = static_cast<uint16_t*>(dA_bf16);
+  rc = launch_wide_bt(a, as_stream(stream));
+  if (rc != MOE_OK) return rc;
+  return check_launch("grouped_fp8_gemm_dgrad");
+}
+
 extern "C" int grouped_fp8_gemm_swiglu(const uint8_t* A, const float* A_scale,
                                        const int32_t* a_row_index, int64_t A_rows, const uint8_t* B,
                                        const float* B_scale, const int32_t* group_offsets,

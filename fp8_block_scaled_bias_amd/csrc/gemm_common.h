@@ -196,5 +196,12 @@ int num_cus();
 // 32-bit copy offsets: N*K (one group's B) and A_rows*K below 2^32.
 int launch_wide(const GemmArgs& a, bool swiglu, hipStream_t st);
 
+// The same kernel, plain epilogue, with B given as W [G, K, N] (contraction
+// rows of N output bytes, the forward layout of the weights whose input
+// gradient this is) and scales [G, K/128, N/128]; the x operand is formed by
+// LDS transpose reads.  Requires what launch_wide requires of the plain form
+// and no row gather.
+int launch_wide_bt(const GemmArgs& a, hipStream_t st);
+
 }  // namespace gemm
 }  // namespace moe

@@ -54,6 +54,7 @@ namespace {
 
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
 
 constexpr int WT = 512;                  // 8 waves, 2 per SIMD
 constexpr int WBM = 256;                 // tile rows
@@ -166,7 +167,7 @@ __device__ __forceinline__ void build_cost_prefix(const int* s_offs, int G, int*
   }
 }
 
-template <bool SWIGLU, bool GATHER, bool KEEP = false>
+template <bool SWIGLU, bool GATHER, bool KEEP = false, bool BT = false>
 __global__ __launch_bounds__(WT, 1) void wide_gemm_kernel(GemmArgs args) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[LDS];
   __shared__ int s_red[8];
@@ -305,6 +306,15 @@ __global__ __launch_bounds__(WT, 1) void wide_gemm_kernel(GemmArgs args) {
     r.a_live = 32 * wv < t.m1 - t.m0;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
+      if (BT) {
+        // W in its forward layout: stage row = contraction index within the
+        // K block (this wave's rows 16wv + 4h + lane/16, and 8 further),
+        // 256 output bytes per row, 16 B chunk c of row r in slot c ^ (r & 7)
+        const int row = 16 * wv + 4 * h + (lane >> 4);
+        r.vb[h] = (uint32_t)row * (uint32_t)N + 256u * (uint32_t)t.nt +
+                  (uint32_t)(((lane & 15) ^ (row & 7)) << 4);
+        continue;
+      }
       const int row = crow(2 * h);
       uint32_t n;
       if (SWIGLU) n = (uint32_t)((row < 128 ? 0 : (int)args.I - 128) + 128 * (int)t.nt + row);
@@ -312,6 +322,7 @@ __global__ __launch_bounds__(WT, 1) void wide_gemm_kernel(GemmArgs args) {
       r.vb[h] = n * K + (uint32_t)((lane & 7) ^ swz(row)) * 16;
     }
     if (wv < 4) r.vs = a_row(t, ord, 64 * wv + lane) * (uint32_t)nkb * 4;
+    else if (BT) r.vs = (uint32_t)((t.g * nkb * nblk + nblk_of(t, lane == 1)) * 4);
     else r.vs = (uint32_t)((t.g * nblk + nblk_of(t, lane == 1)) * nkb * 4);
     return r;
   };
@@ -333,6 +344,9 @@ __global__ __launch_bounds__(WT, 1) void wide_gemm_kernel(GemmArgs args) {
   const uint32_t sc_w = (uint32_t)__builtin_amdgcn_readfirstlane(
       (int)(lds0 + OFF_SC + (wv < 4 ? (uint32_t)wv * 256 : 1024u)));
   const uint32_t k16 = (uint32_t)__builtin_amdgcn_readfirstlane((int)(16 * K));
+  // BT: a K block of B is 128 rows of N bytes; copies 6, 7 are 8 rows further
+  const uint32_t n128 = (uint32_t)__builtin_amdgcn_readfirstlane((int)(128 * N));
+  const uint32_t n8 = (uint32_t)__builtin_amdgcn_readfirstlane((int)(8 * N));
   // tile copy op of K block at global offset so into stage TST: 0..3 A
   // copies, 4..7 B copies
   auto tile_op = [&](auto TST_, const Srcs& r, int op, uint32_t so) __attribute__((always_inline)) {
@@ -341,6 +355,18 @@ __global__ __launch_bounds__(WT, 1) void wide_gemm_kernel(GemmArgs args) {
     // rows past the tile's end are never stored: their A copies are left out
     // (the stage keeps older bytes there)
     if (op < 4 && !r.a_live) return;
+    if (BT && op >= 4) {
+      // copy 4 + p: stage rows 16wv + 4p .. +3 (1 KB), from the K block's
+      // 128 W rows (so / 128 = the K block)
+      const uint32_t sob = (so >> 7) * n128;
+      switch (op) {
+        case 4: copy16<B0>(r.rb, r.vb[0], sob, m0_w); break;
+        case 5: copy16<B0 + 1024>(r.rb, r.vb[1], sob, m0_w); break;
+        case 6: copy16<B0 + 2048>(r.rb, r.vb[0], sob + n8, m0_w); break;
+        default: copy16<B0 + 3072>(r.rb, r.vb[1], sob + n8, m0_w); break;
+      }
+      return;
+    }
     switch (op) {
       case 0: copy16<A0>(ra, r.va[0], so, m0_w); break;
       case 1: copy16<A0 + 16 * 128>(ra, r.va[1], so, m0_w); break;
@@ -352,8 +378,10 @@ __global__ __launch_bounds__(WT, 1) void wide_gemm_kernel(GemmArgs args) {
       default: copy16<B0 + 24 * 128>(r.rb, r.vb[1], so + k16, m0_w); break;
     }
   };
+  // BT: the weight scales are [G, K/128, N/128] (the forward layout of W)
+  const uint32_t sstride = (uint32_t)__builtin_amdgcn_readfirstlane(BT && wv >= 4 ? nblk * 4 : 4);
   auto scale_copy = [&](const Srcs& r, int kb, int gslot) __attribute__((always_inline)) {
-    copy4(rs, r.vs, (uint32_t)kb * 4, sc_w + (uint32_t)gslot * SSLOT);
+    copy4(rs, r.vs, (uint32_t)kb * sstride, sc_w + (uint32_t)gslot * SSLOT);
   };
 
   // ---- prologue: table of tile 0, then its first K block and the scales
@@ -408,6 +436,25 @@ __global__ __launch_bounds__(WT, 1) void wide_gemm_kernel(GemmArgs args) {
     r[4] = b.x; r[5] = b.y; r[6] = b.z; r[7] = b.w;
     return r;
   };
+  // BT: the x operand of column block j from W's forward layout by LDS
+  // transpose reads.  Lane i of a 16-lane group addresses the 8 bytes at
+  // stage row n0 + i/2, output byte c0 + 8 (i & 1); the read hands lane l
+  // byte l % 8 of the group's chunks 2b + (l / 8) % 2, b = 0..7, i.e. the
+  // column c0 + l % 16 at rows n0 .. n0 + 7.  A group covers 16 columns
+  // (c0 = 128 wn + 32 j + 16 (group & 1)) and, with n0 = 64 h + 32 (group /
+  // 2) + 8 r for r = 0..3, its lanes' 32 contraction bytes in the order of
+  // the A operand's K bytes.  Rows n0 + b have (row & 7) = i / 2, which fixes
+  // the swizzled chunk per lane and column block.
+  typedef __attribute__((address_space(3))) v2i lds_v2i;
+  const __attribute__((address_space(3))) uint8_t* lds_b =
+      (const __attribute__((address_space(3))) uint8_t*)smem + OFF_B;
+  uint32_t o_tr[4];
+  {
+    const int grp = lane >> 4, li = lane & 15;
+    const int base = (32 * (grp >> 1) + (li >> 1)) * 256 + 8 * (li & 1) + 128 * wn;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o_tr[j] = (uint32_t)(base + (((2 * j + (grp & 1)) ^ (li >> 1)) << 4));
+  }
   // B stage row offset (from the wave's base row) of column block j
   auto b_roff = [&](int j) -> int { return SWIGLU ? (j < 2 ? 32 * j : 128 + 32 * (j - 2)) : 32 * j; };
   auto half_of = [&](int j) -> int { return SWIGLU ? (j >= 2) : wn; };
@@ -423,7 +470,17 @@ __global__ __launch_bounds__(WT, 1) void wide_gemm_kernel(GemmArgs args) {
       a[i] = read_frag(pa + o_lo[HH], pa + o_hi[HH], STG * ST_BYTES + i * 32 * 128);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      b[j] = read_frag(pb + o_lo[HH], pb + o_hi[HH], STG * ST_BYTES + b_roff(j) * 128);
+      if (BT) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const v2i t = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              (lds_v2i*)(lds_b + STG * ST_BYTES + (64 * HH + 8 * r) * 256 + o_tr[j]));
+          b[j][2 * r] = t[0];
+          b[j][2 * r + 1] = t[1];
+        }
+      } else {
+        b[j] = read_frag(pb + o_lo[HH], pb + o_hi[HH], STG * ST_BYTES + b_roff(j) * 128);
+      }
   };
   read_ops(ic<0>(), ic<0>());
 
@@ -807,6 +864,12 @@ int launch_wide(const GemmArgs& a, bool swiglu, hipStream_t st) {
     if (a.a_row_index) wide_gemm_kernel<false, true><<<dim3(grid), dim3(WT), 0, st>>>(a);
     else wide_gemm_kernel<false, false><<<dim3(grid), dim3(WT), 0, st>>>(a);
   }
+  return MOE_OK;
+}
+
+int launch_wide_bt(const GemmArgs& a, hipStream_t st) {
+  const int grid = std::max(8, (num_cus() / 8) * 8);
+  wide_gemm_kernel<false, false, false, true><<<dim3(grid), dim3(WT), 0, st>>>(a);
   return MOE_OK;
 }
 

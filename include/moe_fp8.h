@@ -451,6 +451,32 @@ int grouped_fp8_gemm(const uint8_t* A, const float* A_scale, const int32_t* a_ro
                      int64_t N, int64_t K, void* C_bf16, void* stream);
 
 /*
+ * grouped_fp8_gemm_dgrad - the input gradient of grouped_fp8_gemm, read
+ * from the weights in their forward layout (news.qq.com article, section
+ * FP8 低精度训练 › 细粒度量化: 1x128 activation tiles, 128x128 weight blocks;
+ * section 工程 › DualPipe 流水线并行: the backward-for-input chunks).  For
+ * the forward C = A W^T of group g (W [N, K]), the gradient is dA = dC W, a
+ * contraction over n:
+ *   dA[r, k] = bf16( sum_nb  sdc[r, nb] * W_scale[g, nb, k/128]
+ *                            * sum_{n in block nb} dC[r, n] * W[g, n, k] )
+ * with dC quantised by fp8_quant_1x128 along n.  Each 128-wide n block is one
+ * FP8 MFMA partial in FP32, as in grouped_fp8_gemm, whose result this equals
+ * bit for bit when given B = the fp8_transpose_128x128 of W; no transposed
+ * copy is made (the kernel forms its operand with LDS transpose reads).
+ *
+ * dC       [M_total, N] e4m3;  dC_scale [M_total, N/128] fp32
+ * W        [G, N, K] e4m3, W_scale [G, N/128, K/128] fp32: the forward B
+ * group_offsets [G+1] int32 on the device, as in grouped_fp8_gemm
+ * dA (out) [M_total, K] bf16
+ * Requirements: K % 256 == 0, N % 256 == 0 and N >= 768, N*K and M_total*N
+ * below 2^32 (otherwise MOE_ERR_UNSUPPORTED); G >= 1 (more than 1024 groups
+ * returns MOE_ERR_UNSUPPORTED).
+ */
+int grouped_fp8_gemm_dgrad(const uint8_t* dC, const float* dC_scale, const uint8_t* W,
+                           const float* W_scale, const int32_t* group_offsets, int32_t G,
+                           int64_t M_total, int64_t N, int64_t K, void* dA_bf16, void* stream);
+
+/*
  * grouped_fp8_gemm_swiglu - the gate+up GEMM of the experts with SwiGLU and
  * 1x128 requantisation fused into its epilogue (news.qq.com article, section
  * FP8 低精度训练: FP8 GEMM with fine-grained scales and FP32 accumulation,

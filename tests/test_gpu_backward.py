@@ -3,7 +3,9 @@
 fp8_transpose_128x128 moves bytes and scales only, so it must equal the
 oracle's block transpose bit for bit (random bytes, every code including
 NaN patterns).  The input gradient dA = dY W is grouped_fp8_gemm on the
-transposed blocks; with integer-valued E4M3 operands in [-2, 2] and
+transposed blocks, or grouped_fp8_gemm_dgrad on W in its forward layout
+(the same MFMA operand bytes in the same K positions, so the two agree bit
+for bit on any data); with integer-valued E4M3 operands in [-2, 2] and
 power-of-two scales 2^[-2, 2] every partial, scaled block and running sum is
 exact in fp32 (|sum| < 2^19 on a 2^-4 grid for contractions up to 7168), so
 the GPU's bf16 output must equal the oracle's bf16 rounding of the exact
@@ -15,7 +17,7 @@ import torch
 
 import synth
 import fp8_block_scaled_bias_amd as M
-from gpu_common import bf16_values_host, dev, host, log
+from gpu_common import bf16_bits_host, bf16_values_host, dev, host, log
 from oracle import formats as OF
 from oracle import gemm as OG
 
@@ -72,6 +74,16 @@ def test_transpose_full_shape_sampled(N, K):
     log(f"[transpose] full G={G} N={N} K={K}: scales whole and {len(picks)} blocks bit-exact")
 
 
+def _dgrad_dev(path, qY_d, sY_d, w_d, ws_d, offs_d, G, Mt, N, K):
+    out = torch.empty((Mt, K), dtype=torch.bfloat16, device="cuda")
+    if path == "forward_layout":
+        M.grouped_fp8_gemm_dgrad(qY_d, sY_d, w_d, ws_d, offs_d, G, Mt, N, K, out)
+    else:
+        wt, wts = _transpose_dev(w_d, ws_d, G, N, K)
+        M.grouped_fp8_gemm(qY_d, sY_d, None, wt, wts, offs_d, G, Mt, K, N, out)
+    return out
+
+
 @pytest.mark.parametrize("rows,N,K", [
     ([300, 0, 77, 513, 129], 384, 512),      # small-group kernel, ragged groups, an empty one
     ([700, 410, 905, 262], 1536, 512),        # 256x256-tile kernel (contraction 12 blocks)
@@ -95,12 +107,72 @@ def test_dgrad_exact(rows, N, K):
     assert np.array_equal(got, ref), int((got != ref).sum())
 
 
+@pytest.mark.parametrize("rows,N,K", [
+    ([300, 0, 77, 513, 129], 768, 512),      # ragged groups, an empty one, 6 contraction blocks
+    ([700, 410, 905, 262], 1536, 512),
+    ([5, 40, 1, 290], 1024, 768),             # groups far below one tile
+], ids=["ragged", "wide", "tiny_groups"])
+def test_dgrad_forward_layout_exact(rows, N, K):
+    """grouped_fp8_gemm_dgrad: dA = dY W read from W [N, K] as stored for the
+    forward (no transposed copy), against the oracle's block-scaled dgrad."""
+    G = len(rows)
+    offs = np.concatenate([[0], np.cumsum(rows)]).astype(np.int64)
+    Mt = int(offs[-1])
+    qY = _codes((Mt, N), 51 + N)
+    sY = synth.pow2_scales((Mt, N // 128), 52 + N, -2, 2)
+    qW = _codes((G, N, K), 53 + K)
+    sW = synth.pow2_scales((G, N // 128, K // 128), 54 + K, -2, 2)
+    log(f"[dgrad fwd-layout] rows {rows} N={N} K={K}")
+    out = _dgrad_dev("forward_layout", dev(qY), dev(sY), dev(qW), dev(sW),
+                     dev(offs.astype(np.int32)), G, Mt, N, K)
+    ref = OG.to_bf16(OG.grouped_dgrad(qY, sY, qW, sW, offs))
+    got = bf16_values_host(out)
+    assert np.array_equal(got, ref), int((got != ref).sum())
+
+
+def test_dgrad_forward_layout_equals_transposed_random():
+    """On Gaussian data quantised 1x128 / 128x128 (inexact sums), the
+    forward-layout dgrad and the grouped GEMM on the transposed blocks feed
+    the MFMAs the same bytes in the same K positions: equal bit for bit."""
+    from oracle import quant as OQ
+    rows, N, K = [700, 0, 410, 905, 262], 2048, 1024
+    G = len(rows)
+    offs = np.concatenate([[0], np.cumsum(rows)]).astype(np.int64)
+    Mt = int(offs[-1])
+    rng = np.random.default_rng(61)
+    qY, sY = OQ.quant_1x128(rng.standard_normal((Mt, N)).astype(np.float32))
+    qW = np.empty((G, N, K), np.uint8)
+    sW = np.empty((G, N // 128, K // 128), np.float32)
+    for g in range(G):
+        qW[g], sW[g] = OQ.quant_128x128((rng.standard_normal((N, K)) * 0.02).astype(np.float32))
+    args = (dev(qY), dev(sY), dev(qW), dev(sW), dev(offs.astype(np.int32)), G, Mt, N, K)
+    a = bf16_bits_host(_dgrad_dev("forward_layout", *args))
+    b = bf16_bits_host(_dgrad_dev("transposed", *args))
+    assert np.array_equal(a, b), int((a != b).sum())
+
+
+def test_dgrad_forward_layout_rejects_unsupported_shape():
+    """Shapes the forward-layout kernel does not take return MOE_ERR_UNSUPPORTED
+    before any launch (output columns not a multiple of 256)."""
+    G, Mt, N, K = 2, 64, 768, 384
+    y = torch.zeros((Mt, N), dtype=torch.uint8, device="cuda")
+    ys = torch.ones((Mt, N // 128), dtype=torch.float32, device="cuda")
+    w = torch.zeros((G, N, K), dtype=torch.uint8, device="cuda")
+    ws = torch.ones((G, N // 128, K // 128), dtype=torch.float32, device="cuda")
+    offs = torch.tensor([0, 32, 64], dtype=torch.int32, device="cuda")
+    out = torch.empty((Mt, K), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(M.MoEError) as e:
+        M.grouped_fp8_gemm_dgrad(y, ys, w, ws, offs, G, Mt, N, K, out)
+    assert e.value.code == M._lib.MOE_ERR_UNSUPPORTED
+
+
 def _group_w(base, g):
     return np.roll(base.ravel(), 7919 * g).reshape(base.shape)
 
 
+@pytest.mark.parametrize("path", ["transposed", "forward_layout"])
 @pytest.mark.parametrize("N,K", [(7168, 2048), (4096, 7168)], ids=["down", "gate_up"])
-def test_dgrad_full_shape_exact(N, K):
+def test_dgrad_full_shape_exact(N, K, path):
     """Input gradients of the layer's two expert GEMMs at T=16384 (147,456 rows
     in 257 groups: the routed counts of the prefill batch's multinomial stand-in
     plus the 16,384-row shared group): down's dH = dD W_dn (contraction 7168)
@@ -121,12 +193,10 @@ def test_dgrad_full_shape_exact(N, K):
     w_d = torch.empty((G, N, K), dtype=torch.uint8, device="cuda")
     for g in range(G):   # torch.roll matches np.roll (_group_w)
         w_d[g].copy_(torch.roll(base_d, 7919 * g).view(N, K))
-    wt, wts = _transpose_dev(w_d, dev(sW), G, N, K)
-    del w_d
-    out = torch.empty((R, K), dtype=torch.bfloat16, device="cuda")
-    log(f"[dgrad full] N={N} K={K}: launch")
-    M.grouped_fp8_gemm(qY_d, dev(sY), None, wt, wts, dev(offs.astype(np.int32)), G, R, K, N, out)
+    log(f"[dgrad full] N={N} K={K} {path}: launch")
+    out = _dgrad_dev(path, qY_d, dev(sY), w_d, dev(sW), dev(offs.astype(np.int32)), G, R, N, K)
     torch.cuda.synchronize()
+    del w_d
     checked = 0
     for g in list(range(0, G, 16)) + [G - 1]:
         r0, r1 = int(offs[g]), int(offs[g + 1])

@@ -12,8 +12,8 @@ Prints one JSON line (rank 0).  On the same weights it also reports: the
 decode batch (T=128, under "decode"), the standalone grouped GEMM over 256
 groups with Multinomial(65536) rows ("grouped_gemm") and the skewed-load
 layer (T=8192, Zipf(1.1) expert popularity, 100 steps of the bias update,
-"skewed"), the backward pieces of the two expert GEMMs at T=16384 (weight
-transposes, input and weight gradients: "backward") and the whole
+"skewed"), the backward pieces of the two expert GEMMs at T=16384 (input
+and weight gradients: "backward") and the whole
 expert-path backward step ("backward_step").
 """
 from __future__ import annotations
@@ -184,9 +184,8 @@ def _median_ms(run, reps, warmup):
 
 def bench_backward(layer, T, reps=10, warmup=3):
     """Backward of the two expert GEMMs at T=16384.  Input gradients (backward for input):
-    the 257 experts' weights transposed in 128x128 blocks (fp8_transpose_128x128,
-    HBM-bound: read + write of every code and scale), then grouped_fp8_gemm on
-    them.  Rows per group: Multinomial(T*k, uniform over E) at seed 0 plus the
+    grouped_fp8_gemm_dgrad on the 257 experts' weights as stored for the
+    forward.  Rows per group: Multinomial(T*k, uniform over E) at seed 0 plus the
     T-row shared group (R = 147,456); output gradients N(0,1) from a seeded
     device generator, quantised 1x128 along their contraction axis (untimed).
     down: dH [R, I] = dD [R, H] W_dn; gate+up: dX [R, H] = dGU [R, 2I] W_gu.
@@ -208,27 +207,21 @@ def bench_backward(layer, T, reps=10, warmup=3):
     for name, W, Ws, N, K in (("down", layer.w_dn, layer.w_dn_s, s.H, s.I),
                               ("gate_up", layer.w_gu, layer.w_gu_s, 2 * s.I, s.H)):
         # forward C = A W^T with W [G, N, K]; dA = dY W contracts over N
-        wt = torch.empty((G, K, N), dtype=torch.uint8, device="cuda")
-        wts = torch.empty((G, K // 128, N // 128), dtype=torch.float32, device="cuda")
-        t_ms = _median_ms(lambda: M.fp8_transpose_128x128(W, Ws, G, N, K, wt, wts), 5, 2)
-        t_bytes = 2 * (G * N * K + G * (N // 128) * (K // 128) * 4)
         dy = torch.randn((R, N), dtype=torch.float32, device="cuda", generator=gen).to(torch.bfloat16)
         dyq = torch.empty((R, N), dtype=torch.uint8, device="cuda")
         dys = torch.empty((R, N // 128), dtype=torch.float32, device="cuda")
         M.fp8_quant_1x128(dy, R, N, N, 0, dyq, dys)
         del dy
         da = torch.empty((R, K), dtype=torch.bfloat16, device="cuda")
-        g_ms = _median_ms(lambda: M.grouped_fp8_gemm(dyq, dys, None, wt, wts, offs, G, R, K, N, da),
+        g_ms = _median_ms(lambda: M.grouped_fp8_gemm_dgrad(dyq, dys, W, Ws, offs, G, R, N, K, da),
                           reps, warmup)
         flop = 2.0 * R * N * K
         tf = flop / (g_ms * 1e-3) / 1e12
-        out[name] = {"transpose_ms": t_ms, "transpose_GB_s": t_bytes / (t_ms * 1e-3) / 1e9,
-                     "transpose_frac_hbm": t_bytes / (t_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                     "dgrad_ms": g_ms, "dgrad_TFLOPS": tf, "dgrad_frac_fp8_peak": tf / FP8_PEAK_TFLOPS,
+        out[name] = {"dgrad_ms": g_ms, "dgrad_TFLOPS": tf, "dgrad_frac_fp8_peak": tf / FP8_PEAK_TFLOPS,
                      "contraction": N, "out_cols": K}
-        log(f"[bench] backward {name}: transpose {t_ms:.3f} ms ({out[name]['transpose_GB_s']:.0f} GB/s), "
-            f"dgrad {g_ms:.3f} ms ({tf:.0f} TFLOP/s)")
-        del wt, wts, dyq, dys, da
+        log(f"[bench] backward {name}: dgrad {g_ms:.3f} ms ({tf:.0f} TFLOP/s), weights read as "
+            f"stored for the forward")
+        del dyq, dys, da
         # weight gradient dW_g = dY_g^T A_g: both operands quantised 128x1 along the
         # tokens (transposed, chunk-padded), fp32 output [G, N, K]
         cap = M.wgrad_chunks(R, G)
@@ -266,16 +259,16 @@ def bench_backward_step(layer, x, cfg, steps=3, warmup=1):
     the same batch: combine backward, dgrad of down, the recomputed gate+up,
     SwiGLU backward, dgrad of gate+up, unpermute, both weight gradients and
     the router's backward (dx and the centroids' gradient); dy N(0,1) bf16
-    (synth.gen_dy).  Every timed step starts as after a weight update
-    (mark_weights_changed), so the 128x128 weight transposes the input
-    gradient reads are made inside it ("transpose_weights" in the per-stage
-    times).  Flops counted: the GEMMs only, 2RHI for each of dgrad-down and
-    wgrad-down, 4RHI for each of the recomputed gate+up, dgrad-gate+up and
-    wgrad-gate+up (34.6 TFLOP).  Then a training step (forward + backward,
-    wall clock, with the same per-update transposes) with the gate+up GEMM
-    rerun in the backward and with the forward keeping its outputs; and the
-    128x128 requantisation of fp32 master weights (fp8_quant_128x128 over
-    both weight sets, the other per-update step), timed on its own."""
+    (synth.gen_dy).  The input gradients read the weights as stored for the
+    forward, so the backward depends on nothing made from the weights
+    beforehand.  Flops counted: the GEMMs only, 2RHI for each of
+    dgrad-down and wgrad-down, 4RHI for each of the recomputed gate+up,
+    dgrad-gate+up and wgrad-gate+up (34.6 TFLOP).  Then a training step
+    (forward + backward, wall clock) with the gate+up GEMM rerun in the
+    backward and with the forward keeping its outputs; and the 128x128
+    requantisation of fp32 master weights (fp8_quant_128x128 over both
+    weight sets, the per-update cast after an optimizer step), timed on its
+    own."""
     import time
     import numpy as np
     import torch
@@ -283,13 +276,11 @@ def bench_backward_step(layer, x, cfg, steps=3, warmup=1):
     dy = torch.from_numpy(synth.gen_dy(cfg).view(np.int16)).cuda().view(torch.bfloat16)
     layer.forward(x)
     for _ in range(warmup):
-        layer.mark_weights_changed()
         layer.backward(dy, x)
     torch.cuda.synchronize()
     events = {}
     t0 = time.perf_counter()
     for _ in range(steps):
-        layer.mark_weights_changed()
         layer.backward(dy, x, events=events)
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) / steps * 1e3
@@ -306,13 +297,11 @@ def bench_backward_step(layer, x, cfg, steps=3, warmup=1):
     # also keeps its bf16 gate/up outputs (1.2 GB) for the backward to read
     for name, keep in (("train_step_recompute", False), ("train_step_keep_gu", True)):
         layer.forward(x, keep_gu=keep)
-        layer.mark_weights_changed()
         layer.backward(dy, x)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for _ in range(steps):
             layer.forward(x, keep_gu=keep)
-            layer.mark_weights_changed()
             layer.backward(dy, x)
         torch.cuda.synchronize()
         out[name + "_ms"] = (time.perf_counter() - t0) / steps * 1e3

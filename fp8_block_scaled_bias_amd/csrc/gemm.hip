@@ -70,8 +70,9 @@ struct Cfg {
 // tile are copied into LDS one tile ahead (every step of a tile repeats that
 // copy, so the table a new tile reads was written by a copy that has already
 // been waited for).
-template <int BM, int WAVES_M, int STAGES, bool SWIGLU, bool GATHER, bool EXACT>
+template <int BM, int WAVES_M, int STAGES, bool SWIGLU, bool GATHER, bool EXACT, bool BT = false>
 __global__ __launch_bounds__(GM_THREADS, 1) void grouped_gemm_kernel(GemmArgs args) {
+  static_assert(!BT || (!SWIGLU && !GATHER && !EXACT), "BT: plain epilogue, dense A rows");
   using C_ = Cfg<BM, WAVES_M, STAGES, SWIGLU, GATHER, EXACT>;
   __shared__ __attribute__((aligned(16))) uint8_t smem[C_::LDS];
   __shared__ int s_red[4];
@@ -135,6 +136,7 @@ __global__ __launch_bounds__(GM_THREADS, 1) void grouped_gemm_kernel(GemmArgs ar
   const uint8_t* b_src1 = nullptr;
   bool b_tail = false;
   const float* s_src = nullptr;
+  int s_kstride = 1;  // scale elements between consecutive K blocks
   const int32_t* r_src = nullptr;  // row-index copy source (next tile)
 
   auto row_src = [&](const Tile& t, int64_t ord, int row) -> int64_t {
@@ -149,13 +151,30 @@ __global__ __launch_bounds__(GM_THREADS, 1) void grouped_gemm_kernel(GemmArgs ar
       const int row = 8 * q + (lane >> 3);
       a_src[qi] = args.A + row_src(t, ord, row) * K + ((q & 1) ? chunk1 : chunk0) * 16;
     }
-    int64_t brow0;
-    if (SWIGLU) brow0 = ((wv < 2) ? 0 : args.I) + 128 * t.nt + 64 * (wv & 1) + (lane >> 3);
-    else brow0 = 256 * t.nt + 64 * wv + (lane >> 3);
-    const uint8_t* b_row = args.B + ((int64_t)t.g * N + min<int64_t>(brow0, N - 1)) * K;
-    b_src0 = b_row + chunk0 * 16;
-    b_src1 = b_row + chunk1 * 16;
-    b_tail = (brow0 - (lane >> 3)) + 64 > N;  // wave-uniform
+    if (BT) {
+      // W [K, N] as stored: stage row = contraction index in the K block,
+      // 256 output bytes per row, chunk c of row r in slot c ^ (r & 7).
+      // Copy qi covers rows 32wv + 4qi + lane/16 (slot lane%16); its source
+      // chunk depends on qi & 1 only.  A last tile of 128 columns (N not a
+      // multiple of 256) re-reads its valid chunks for the upper half.
+      const bool half = 256 * t.nt + 256 > N;  // wave-uniform
+      const uint8_t* w = args.B + (int64_t)t.g * K * N + 256 * t.nt;
+#pragma unroll
+      for (int o = 0; o < 2; ++o) {
+        const int row = 32 * wv + 4 * o + (lane >> 4);
+        int c = (lane & 15) ^ (row & 7);
+        if (half) c &= 7;
+        (o ? b_src1 : b_src0) = w + (int64_t)row * N + c * 16;
+      }
+    } else {
+      int64_t brow0;
+      if (SWIGLU) brow0 = ((wv < 2) ? 0 : args.I) + 128 * t.nt + 64 * (wv & 1) + (lane >> 3);
+      else brow0 = 256 * t.nt + 64 * wv + (lane >> 3);
+      const uint8_t* b_row = args.B + ((int64_t)t.g * N + min<int64_t>(brow0, N - 1)) * K;
+      b_src0 = b_row + chunk0 * 16;
+      b_src1 = b_row + chunk1 * 16;
+      b_tail = (brow0 - (lane >> 3)) + 64 > N;  // wave-uniform
+    }
     const int srow = 64 * wv + lane;
     if (srow < BM) {
       s_src = args.A_scale + row_src(t, ord, srow) * nkb;
@@ -163,7 +182,12 @@ __global__ __launch_bounds__(GM_THREADS, 1) void grouped_gemm_kernel(GemmArgs ar
       const int b = srow & 1;
       const int64_t nb = SWIGLU ? (b ? (args.I >> 7) + t.nt : t.nt)
                                 : min<int64_t>(2 * t.nt + b, (N >> 7) - 1);
-      s_src = args.B_scale + ((int64_t)t.g * (N >> 7) + nb) * nkb;
+      if (BT) {
+        s_src = args.B_scale + (int64_t)t.g * nkb * (N >> 7) + nb;  // [G, K/128, N/128]
+        s_kstride = (int)(N >> 7);
+      } else {
+        s_src = args.B_scale + ((int64_t)t.g * (N >> 7) + nb) * nkb;
+      }
     }
     if (GATHER) {
       const Tile tn = (ord + 1 < my_n) ? tile_of(ord + 1) : t;
@@ -174,6 +198,7 @@ __global__ __launch_bounds__(GM_THREADS, 1) void grouped_gemm_kernel(GemmArgs ar
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
   const int nkb32 = (int)nkb;
   const int64_t K8 = 8 * K;
+  const int64_t N8 = 8 * N, N128 = 128 * N;  // BT: 8 W rows, one K block of W rows
   // issue position (tile ordinal, K block, ring slot), advanced per step
   int iss_ord = 0, iss_kb = 0, iss_slot = 0;
   // One step's copies, split so they can be spread over the MFMA loop:
@@ -193,10 +218,14 @@ __global__ __launch_bounds__(GM_THREADS, 1) void grouped_gemm_kernel(GemmArgs ar
       dma16(a_src[k] + iss_ko, iss_st + (wv * C_::A_LOADS + k) * 1024);
     } else if (k < C_::A_LOADS + C_::B_LOADS) {
       const int qi = k - C_::A_LOADS;
-      dma16(((qi & 1) ? b_src1 : b_src0) + (b_tail ? 0 : qi * K8) + iss_ko,
-            iss_st + C_::A_BYTES + (wv * 8 + qi) * 1024);
+      if (BT)
+        dma16(((qi & 1) ? b_src1 : b_src0) + (qi >> 1) * N8 + (int64_t)iss_kb * N128,
+              iss_st + C_::A_BYTES + (wv * 8 + qi) * 1024);
+      else
+        dma16(((qi & 1) ? b_src1 : b_src0) + (b_tail ? 0 : qi * K8) + iss_ko,
+              iss_st + C_::A_BYTES + (wv * 8 + qi) * 1024);
     } else if (k == C_::A_LOADS + C_::B_LOADS) {
-      dma4(s_src + iss_kb, iss_st + C_::A_BYTES + C_::B_BYTES + wv * 256);
+      dma4(s_src + iss_kb * s_kstride, iss_st + C_::A_BYTES + C_::B_BYTES + wv * 256);
     } else {
       dma4(r_src, lds0 + C_::OFF_RIDX + (uint32_t)(((iss_ord + 1) & 1) * 1024 + wv * 256));
     }
@@ -249,6 +278,29 @@ __global__ __launch_bounds__(GM_THREADS, 1) void grouped_gemm_kernel(GemmArgs ar
   auto b_row_of = [&](int j) -> int {
     if (SWIGLU) return (j < SJH ? wn * WHN + 16 * j : 128 + wn * WHN + 16 * (j - SJH)) + (lane & 15);
     return wn * C_::WTN + 16 * j + (lane & 15);
+  };
+  // BT: column subtile j by LDS transpose reads.  Lane i of each 16-lane
+  // group addresses the 8 bytes at row 32 (lane/16) + 8r + i/2, output byte
+  // 16 chunk + 8 (i & 1); lane l receives byte l % 8 of the group's chunks
+  // 2b + (l / 8) % 2, i.e. column 16 chunk + l % 16 at the 8 rows from
+  // 32 (lane/16) + 8r: its 32 contraction bytes over r = 0..3, in the order
+  // of the A operand's K bytes.  (row & 7) = i / 2 fixes the swizzled slot.
+  typedef __attribute__((address_space(3))) v2i lds_v2i;
+  const int tli = lane & 15;
+  const uint32_t bt_lane = (uint32_t)((32 * (lane >> 4) + (tli >> 1)) * 256 + 8 * (tli & 1));
+  auto b_frag = [&](const uint8_t* tB, int j) -> v8i {
+    if (!BT) return lds_frag(tB, b_row_of(j), h);
+    const int chunk = (wn * C_::WTN + 16 * j) >> 4;
+    const __attribute__((address_space(3))) uint8_t* p =
+        (const __attribute__((address_space(3))) uint8_t*)tB + bt_lane + ((chunk ^ (tli >> 1)) << 4);
+    v8i x;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const v2i t = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(p + r * 8 * 256));
+      x[2 * r] = t[0];
+      x[2 * r + 1] = t[1];
+    }
+    return x;
   };
 
   const int nsteps32 = (int)nsteps;
@@ -305,7 +357,7 @@ __global__ __launch_bounds__(GM_THREADS, 1) void grouped_gemm_kernel(GemmArgs ar
       // promotion FMA per output
       v8i bb[C_::SJ];
 #pragma unroll
-      for (int j = 0; j < C_::SJ; ++j) bb[j] = lds_frag(tB, b_row_of(j), h);
+      for (int j = 0; j < C_::SJ; ++j) bb[j] = b_frag(tB, j);
       v4f pc[C_::SI][C_::SJ];
 #pragma unroll
       for (int i = 0; i < C_::SI; ++i)
@@ -338,12 +390,12 @@ __global__ __launch_bounds__(GM_THREADS, 1) void grouped_gemm_kernel(GemmArgs ar
     } else {
       // software pipeline over column subtiles: the MFMAs of subtile j and the
       // LDS read of j+1 are issued before the promotion FMAs of subtile j-1
-      v8i bcur = lds_frag(tB, b_row_of(0), h);
+      v8i bcur = b_frag(tB, 0);
       v4f pprev[C_::SI];
 #pragma unroll
       for (int j = 0; j < C_::SJ; ++j) {
         v8i bnext = bcur;
-        if (j + 1 < C_::SJ) bnext = lds_frag(tB, b_row_of(j + 1), h);
+        if (j + 1 < C_::SJ) bnext = b_frag(tB, j + 1);
         // row blocks wholly past the group's end are never stored: no MFMAs
         v4f pcur[C_::SI];
 #pragma unroll
@@ -502,6 +554,15 @@ int launch(const GemmArgs& a, hipStream_t st) {
   return MOE_OK;
 }
 
+// the input-gradient form (B = W in its forward layout): same tile shapes
+template <int BM, int WAVES_M, int STAGES>
+int launch_bt(const GemmArgs& a, hipStream_t st) {
+  const int grid = std::max(8, (num_cus() / 8) * 8);
+  grouped_gemm_kernel<BM, WAVES_M, STAGES, false, false, false, true>
+      <<<dim3(grid), dim3(GM_THREADS), 0, st>>>(a);
+  return MOE_OK;
+}
+
 // the 256x256 kernel: groups of at least 160 rows on average; it addresses
 // a tile's output, A and one group's B with 32-bit offsets, and takes an
 // even number of at least 6 K blocks
@@ -594,18 +655,21 @@ extern "C" int grouped_fp8_gemm_dgrad(const uint8_t* dC, const float* dC_scale,
   if (rc != MOE_OK || M_total == 0) return rc;
   MOE_INVALID(dA_bf16 && ((uintptr_t)dA_bf16 & 15) == 0,
               "grouped_fp8_gemm_dgrad: dA must be non-null and 16-byte aligned");
-  const int64_t lim = (int64_t)1 << 32;
-  MOE_UNSUPPORTED(K % 256 == 0 && K <= (1 << 21) && N % 256 == 0 && N >= 768 &&
-                      N <= (1 << 20) && N * K < lim && M_total * N < lim,
-                  "grouped_fp8_gemm_dgrad: N=%lld, K=%lld, M_total=%lld not supported (K a "
-                  "multiple of 256, N a multiple of 256 and >= 768, N*K and M_total*N below 2^32)",
-                  (long long)N, (long long)K, (long long)M_total);
   GemmArgs a{};
   a.A = dC; a.A_scale = dC_scale; a.a_row_index = nullptr; a.A_rows = M_total;
   a.B = W; a.B_scale = W_scale;
-  a.offs = group_offsets; a.G = G; a.N = K; a.K = N; a.ntiles = K / BN; a.I = 0;
+  a.offs = group_offsets; a.G = G; a.N = K; a.K = N; a.ntiles = ceil_div(K, BN); a.I = 0;
   a.C = static_cast<uint16_t*>(dA_bf16);
-  rc = launch_wide_bt(a, as_stream(stream));
+  // tile shape by rows per group, as in grouped_fp8_gemm; the 256x256 kernel
+  // also needs whole 256-column tiles and 32-bit copy offsets
+  hipStream_t st = as_stream(stream);
+  const int64_t avg = M_total / G, lim = (int64_t)1 << 32;
+  const bool wide_ok = K % 256 == 0 && K <= (1 << 21) && N % 256 == 0 && N >= 768 &&
+                       N <= (1 << 20) && N * K < lim && M_total * N < lim;
+  if (avg >= 160 && wide_ok) rc = launch_wide_bt(a, st);
+  else if (avg >= 96) rc = launch_bt<128, 2, 3>(a, st);
+  else if (avg >= 40) rc = launch_bt<64, 1, 3>(a, st);
+  else rc = launch_bt<32, 1, 4>(a, st);
   if (rc != MOE_OK) return rc;
   return check_launch("grouped_fp8_gemm_dgrad");
 }

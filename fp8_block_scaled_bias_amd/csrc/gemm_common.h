@@ -15,6 +15,7 @@ namespace moe {
 namespace gemm {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v2i __attribute__((ext_vector_type(2)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int MAXG = 1024;  // groups the LDS tile tables hold
@@ -200,7 +201,7 @@ int launch_wide(const GemmArgs& a, bool swiglu, hipStream_t st);
 // rows of N output bytes, the forward layout of the weights whose input
 // gradient this is) and scales [G, K/128, N/128]; the x operand is formed by
 // LDS transpose reads.  Requires what launch_wide requires of the plain form
-// and no row gather.
+// and no row gather (the small-tile kernel of gemm.hip has the same mode).
 int launch_wide_bt(const GemmArgs& a, hipStream_t st);
 
 }  // namespace gemm

@@ -54,7 +54,6 @@ namespace {
 
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef int v4i __attribute__((ext_vector_type(4)));
-typedef int v2i __attribute__((ext_vector_type(2)));
 
 constexpr int WT = 512;                  // 8 waves, 2 per SIMD
 constexpr int WBM = 256;                 // tile rows

@@ -23,11 +23,11 @@ backward-for-input and backward-for-weights chunks, section 工程 › DualPipe
 
   1. moe_combine_backward   dD = w * dy per routed row, dy for the shared rows;
                             dw = <dy, D> (the gate weights' gradient)
-  2. fp8_quant_1x128 + grouped_fp8_gemm on W_dn^T      dh = dD W_dn
+  2. fp8_quant_1x128 + grouped_fp8_gemm_dgrad on W_dn  dh = dD W_dn
   3. grouped_fp8_gemm       the gate+up outputs again (bf16; the fused
                             forward keeps none)
   4. swiglu_backward        dGU = [dg | du], h
-  5. fp8_quant_1x128 + grouped_fp8_gemm on W_gu^T      dX = dGU W_gu
+  5. fp8_quant_1x128 + grouped_fp8_gemm_dgrad on W_gu  dX = dGU W_gu
   6. moe_combine            dx = the sum of a token's rows of dX (unit weights)
   7. fp8_quant_128x1_grouped + grouped_fp8_wgrad       dW_dn = dD^T h,
                             dW_gu = dGU^T x (x gathered through the permutation)
@@ -36,10 +36,10 @@ backward-for-input and backward-for-weights chunks, section 工程 › DualPipe
      (with seq_len: moe_router_backward_dense - the balance term's gradient
      on every expert's logit joins the gate's, dx and dC as fp32 GEMMs)
 
-The weight transposes (fp8_transpose_128x128) are cached on the layer; a
-backward after mark_weights_changed() (or any call that writes the weights
-through the layer) makes them again first, so stale transposes are never
-used.
+The input gradients read the weights in their forward layout (LDS transpose
+reads inside the GEMM), so the backward keeps nothing derived from the
+weights: after a weight update (requantize_from_fp32, or any write to w_gu /
+w_dn) the next forward and backward use the new weights as they are.
 
 torch is only used to hold device memory and to name the stream; every step
 runs in the library's HIP kernels.
@@ -190,9 +190,6 @@ class MoELayer:
         self.centroids = centroids
         self.bias = bias
         self.w_gu, self.w_gu_s, self.w_dn, self.w_dn_s = w_gu, w_gu_s, w_dn, w_dn_s
-        self._wt = None          # transposed weight blocks, made on first backward
-        self._w_ver = 0          # bumped whenever the weights change
-        self._wt_ver = -1        # weight version the transposes were made from
         self._bwd = {}
         self._bufs = {}
 
@@ -280,37 +277,13 @@ class MoELayer:
             L.moe_bias_update(b.counts, self.bias, s.E, gamma, stream)
         return b.y
 
-    def mark_weights_changed(self):
-        """Record that w_gu / w_dn (or their scales) were written outside the
-        layer (an optimizer step followed by requantisation): the next backward
-        transposes them again before using them."""
-        self._w_ver += 1
-
     def requantize_from_fp32(self, gu_fp32, dn_fp32, stream=None):
         """Requantise both weight sets in place from fp32 master weights
-        ([G, 2I, H] and [G, H, I] device tensors) in 128x128 blocks, and mark
-        the transposes stale."""
+        ([G, 2I, H] and [G, H, I] device tensors) in 128x128 blocks (the
+        per-update cast after an optimizer step)."""
         s = self.shape
         L.fp8_quant_128x128(gu_fp32, s.G, 2 * s.I, s.H, self.w_gu, self.w_gu_s, stream)
         L.fp8_quant_128x128(dn_fp32, s.G, s.H, s.I, self.w_dn, self.w_dn_s, stream)
-        self.mark_weights_changed()
-
-    def transpose_weights(self, stream=None):
-        """W^T of both weight sets in 128x128 blocks (the dgrad operands), for
-        the current weights."""
-        s = self.shape
-        if self._wt is None:
-            dev = self.w_gu.device
-            self._wt = dict(
-                gu=torch.empty((s.G, s.H, 2 * s.I), dtype=torch.uint8, device=dev),
-                gu_s=torch.empty((s.G, s.H // 128, 2 * s.I // 128), dtype=torch.float32, device=dev),
-                dn=torch.empty((s.G, s.I, s.H), dtype=torch.uint8, device=dev),
-                dn_s=torch.empty((s.G, s.I // 128, s.H // 128), dtype=torch.float32, device=dev))
-        w = self._wt
-        L.fp8_transpose_128x128(self.w_gu, self.w_gu_s, s.G, 2 * s.I, s.H, w["gu"], w["gu_s"], stream)
-        L.fp8_transpose_128x128(self.w_dn, self.w_dn_s, s.G, s.H, s.I, w["dn"], w["dn_s"], stream)
-        self._wt_ver = self._w_ver
-        return w
 
     def capture(self, x_bf16: torch.Tensor, bufs: Buffers | None = None, **forward_kw):
         """One forward captured as a HIP graph (torch.cuda.CUDAGraph); its
@@ -358,17 +331,6 @@ class MoELayer:
         bb = bwd or self.backward_buffers(T)
         R, G, H, I, k, cap = b.R, s.G, s.H, s.I, s.k, bb.cap
         st = stream if stream is not None else torch.cuda.current_stream()
-        if self._wt is None or self._wt_ver != self._w_ver:
-            if events is None:
-                self.transpose_weights(st)
-            else:
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record(st)
-                self.transpose_weights(st)
-                e1.record(st)
-                events.setdefault("transpose_weights", []).append((e0, e1))
-        w = self._wt
 
         def step(name, fn):
             if events is None:
@@ -385,8 +347,8 @@ class MoELayer:
             dy_bf16, b.inv_perm, b.topk_w, b.d, T, k, H, s.n_shared, bb.dD, bb.dw, st))
         step("dgrad_down", lambda: (
             L.fp8_quant_1x128(bb.dD, R, H, H, 0, bb.dDq, bb.dDs, st),
-            L.grouped_fp8_gemm(bb.dDq, bb.dDs, None, w["dn"], w["dn_s"], b.offsets, G, R, I, H,
-                               bb.dh, st)))
+            L.grouped_fp8_gemm_dgrad(bb.dDq, bb.dDs, self.w_dn, self.w_dn_s, b.offsets, G, R, H,
+                                     I, bb.dh, st)))
         if getattr(b, "gu_kept", False):
             gu = b.hgu   # kept by the forward (keep_gu): the same bf16 GEMM output
         else:
@@ -397,8 +359,8 @@ class MoELayer:
         step("swiglu_bwd", lambda: L.swiglu_backward(gu, bb.dh, R, I, bb.dgu, bb.h, st))
         step("dgrad_gate_up", lambda: (
             L.fp8_quant_1x128(bb.dgu, R, 2 * I, 2 * I, 0, bb.dguq, bb.dgus, st),
-            L.grouped_fp8_gemm(bb.dguq, bb.dgus, None, w["gu"], w["gu_s"], b.offsets, G, R, H,
-                               2 * I, bb.dxp, st)))
+            L.grouped_fp8_gemm_dgrad(bb.dguq, bb.dgus, self.w_gu, self.w_gu_s, b.offsets, G, R,
+                                     2 * I, H, bb.dxp, st)))
         shared = bb.dxp[T * k:T * k + T] if s.n_shared else None
         step("unpermute", lambda: L.moe_combine(bb.dxp, b.inv_perm, bb.ones, shared, T, k, H,
                                                 bb.dx, st))

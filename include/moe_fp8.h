@@ -468,8 +468,7 @@ int grouped_fp8_gemm(const uint8_t* A, const float* A_scale, const int32_t* a_ro
  * W        [G, N, K] e4m3, W_scale [G, N/128, K/128] fp32: the forward B
  * group_offsets [G+1] int32 on the device, as in grouped_fp8_gemm
  * dA (out) [M_total, K] bf16
- * Requirements: K % 256 == 0, N % 256 == 0 and N >= 768, N*K and M_total*N
- * below 2^32 (otherwise MOE_ERR_UNSUPPORTED); G >= 1 (more than 1024 groups
+ * Requirements: N % 128 == 0, K % 128 == 0, G >= 1 (more than 1024 groups
  * returns MOE_ERR_UNSUPPORTED).
  */
 int grouped_fp8_gemm_dgrad(const uint8_t* dC, const float* dC_scale, const uint8_t* W,

@@ -108,13 +108,16 @@ def test_dgrad_exact(rows, N, K):
 
 
 @pytest.mark.parametrize("rows,N,K", [
-    ([300, 0, 77, 513, 129], 768, 512),      # ragged groups, an empty one, 6 contraction blocks
-    ([700, 410, 905, 262], 1536, 512),
-    ([5, 40, 1, 290], 1024, 768),             # groups far below one tile
-], ids=["ragged", "wide", "tiny_groups"])
+    ([300, 0, 77, 513, 129], 768, 512),      # 256x256 tiles: ragged groups, an empty one
+    ([700, 410, 905, 262], 1536, 512),        # 256x256 tiles, 12 contraction blocks
+    ([300, 0, 77, 513, 129], 384, 384),      # 128-row tiles; last column tile half full
+    ([5, 40, 1, 290], 1024, 768),             # 64-row tiles
+    ([3, 0, 17, 9, 30, 1], 256, 128),         # 32-row tiles; one half-full column tile
+], ids=["wide_ragged", "wide", "bm128_half_cols", "bm64", "bm32_half_cols"])
 def test_dgrad_forward_layout_exact(rows, N, K):
     """grouped_fp8_gemm_dgrad: dA = dY W read from W [N, K] as stored for the
-    forward (no transposed copy), against the oracle's block-scaled dgrad."""
+    forward (no transposed copy), against the oracle's block-scaled dgrad, in
+    every tile shape (rows per group choose it, as in grouped_fp8_gemm)."""
     G = len(rows)
     offs = np.concatenate([[0], np.cumsum(rows)]).astype(np.int64)
     Mt = int(offs[-1])
@@ -130,12 +133,13 @@ def test_dgrad_forward_layout_exact(rows, N, K):
     assert np.array_equal(got, ref), int((got != ref).sum())
 
 
-def test_dgrad_forward_layout_equals_transposed_random():
+@pytest.mark.parametrize("rows,N,K", [([700, 0, 410, 905, 262], 2048, 1024),
+                                      ([50, 7, 90, 33], 512, 640)], ids=["wide", "bm64"])
+def test_dgrad_forward_layout_equals_transposed_random(rows, N, K):
     """On Gaussian data quantised 1x128 / 128x128 (inexact sums), the
     forward-layout dgrad and the grouped GEMM on the transposed blocks feed
     the MFMAs the same bytes in the same K positions: equal bit for bit."""
     from oracle import quant as OQ
-    rows, N, K = [700, 0, 410, 905, 262], 2048, 1024
     G = len(rows)
     offs = np.concatenate([[0], np.cumsum(rows)]).astype(np.int64)
     Mt = int(offs[-1])
@@ -151,10 +155,10 @@ def test_dgrad_forward_layout_equals_transposed_random():
     assert np.array_equal(a, b), int((a != b).sum())
 
 
-def test_dgrad_forward_layout_rejects_unsupported_shape():
-    """Shapes the forward-layout kernel does not take return MOE_ERR_UNSUPPORTED
-    before any launch (output columns not a multiple of 256)."""
-    G, Mt, N, K = 2, 64, 768, 384
+def test_dgrad_forward_layout_rejects_bad_shape():
+    """Output columns that are not a multiple of 128 are rejected before any
+    launch with MOE_ERR_INVALID."""
+    G, Mt, N, K = 2, 64, 768, 200
     y = torch.zeros((Mt, N), dtype=torch.uint8, device="cuda")
     ys = torch.ones((Mt, N // 128), dtype=torch.float32, device="cuda")
     w = torch.zeros((G, N, K), dtype=torch.uint8, device="cuda")
@@ -163,7 +167,7 @@ def test_dgrad_forward_layout_rejects_unsupported_shape():
     out = torch.empty((Mt, K), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(M.MoEError) as e:
         M.grouped_fp8_gemm_dgrad(y, ys, w, ws, offs, G, Mt, N, K, out)
-    assert e.value.code == M._lib.MOE_ERR_UNSUPPORTED
+    assert e.value.code == M._lib.MOE_ERR_INVALID
 
 
 def _group_w(base, g):

@@ -406,16 +406,16 @@ def test_layer_backward_keep_gu_mid(T):
 
 def test_layer_backward_after_weight_update():
     """A weight update through the layer (requantize_from_fp32: 128x128
-    requantisation of new fp32 master weights) makes the next backward
-    transpose the weights again: forward and backward then equal those of a
-    fresh layer built from the new weights, bit for bit (the transposes made
-    for the old weights are never used)."""
+    requantisation of new fp32 master weights) after a forward and backward
+    on the old weights: the next forward and backward equal those of a fresh
+    layer built from the new weights, bit for bit (nothing derived from the
+    old weights survives the update)."""
     cfg = synth.MID
     layer, C, b = build_layer(cfg)
     x = bf16_dev(synth.gen_x(cfg))
     dy = bf16_dev(synth.gen_dy(cfg))
     layer.forward(x)
-    layer.backward(dy, x)                       # transposes of the first weights
+    layer.backward(dy, x)                       # on the first weights
     torch.cuda.synchronize()
     seed = 5
     gu = torch.stack([torch.from_numpy(synth.gen_expert_weight(cfg, "gu", e, seed=seed))

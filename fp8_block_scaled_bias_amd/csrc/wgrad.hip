@@ -179,7 +179,7 @@ __global__ __launch_bounds__(QT) void quant_128x1_direct_kernel(
 // The ratio is taken per operand, (sY_{c-1} / sY_c) (sA_{c-1} / sA_c), one
 // quotient per thread and chunk, shared through LDS.  Against a zero-started
 // partial per chunk promoted by FMA this halves the accumulator registers
-// (161 VGPRs: three waves per SIMD instead of two) and the single stage
+// (about 165 VGPRs: three waves per SIMD instead of two) and the single stage
 // halves the LDS (three workgroups per CU).  Scales are normal fp32 numbers
 // (amax/448 of finite data, 1 for an all-zero column); ratios beyond ~1e30
 // between consecutive chunks can overflow the rescaled accumulator.
@@ -296,23 +296,39 @@ __global__ __launch_bounds__(WGT) void wgrad_kernel(
     store((c + 1 - c0) & 1);
     __syncthreads();
   }
-  // result = tot * S_last
+  // result = tot * S_last, stored in whole 128 B lines: per column half i,
+  // each wave's 64 rows x 32 columns (8 KB) go through LDS (the operand
+  // stages, free once every wave is past the last chunk; 16 B chunk c of row
+  // r in slot c ^ (r & 7)) and come back 8 rows x 128 B per store
+  // instruction.  dW is written once and not read here: non-temporal stores.
   float* out = dw + ((int64_t)g * N + n0) * K + k0;
+  typedef float f4v __attribute__((ext_vector_type(4)));
+  __syncthreads();
+  uint8_t* stg = (wv < 2 ? s_y + wv * 8192 : s_a + (wv - 2) * 8192);
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int64_t n = 64 * wm + 32 * j + l32;
-    const float sy = c0 < c1 ? s_s[n] : 0.0f;
+  for (int i = 0; i < 2; ++i) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int j = 0; j < 2; ++j) {
+      const int r = 32 * j + l32;
+      const float sy = c0 < c1 ? s_s[64 * wm + r] : 0.0f;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int k = 64 * wn + 32 * i + 8 * e + 4 * q;
         float4 sa = make_float4(0.f, 0.f, 0.f, 0.f);
         if (c0 < c1) sa = *reinterpret_cast<const float4*>(&s_s[128 + k]);
-        *reinterpret_cast<float4*>(out + n * K + k) =
+        *reinterpret_cast<float4*>(stg + r * 128 + (((2 * e + q) ^ (r & 7)) << 4)) =
             make_float4(tot[i][j][4 * e] * (sy * sa.x), tot[i][j][4 * e + 1] * (sy * sa.y),
                         tot[i][j][4 * e + 2] * (sy * sa.z), tot[i][j][4 * e + 3] * (sy * sa.w));
       }
+    }
+#pragma unroll
+    for (int r8 = 0; r8 < 8; ++r8) {
+      const int r = 8 * r8 + (lane >> 3), ch = lane & 7;
+      const float4 v = *reinterpret_cast<const float4*>(stg + r * 128 + ((ch ^ (r & 7)) << 4));
+      const f4v w = {v.x, v.y, v.z, v.w};
+      __builtin_nontemporal_store(
+          w, reinterpret_cast<f4v*>(out + (int64_t)(64 * wm + r) * K + 64 * wn + 32 * i + 4 * ch));
+    }
   }
 }
 

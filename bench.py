@@ -331,9 +331,9 @@ def bench_backward_step(layer, x, cfg, steps=3, warmup=1):
 # HBM traffic of the gate+up kernel at T=16384, from two rocprofv3 --pmc runs
 # (FETCH_SIZE, WRITE_SIZE) of this script, each scaled by the same counter on
 # the 1 GiB copy probe.  Valid only for the kernel source with this digest.
-GATE_UP_TRAFFIC = {"gemm_src": "96416b49b44a1449",
-                   # FETCH_SIZE 9,133,671 KiB x 2.000 + WRITE_SIZE 311,311 KiB x 1.000
-                   "bytes": 9133671 * 1024 * 2 + 311311 * 1024}
+GATE_UP_TRAFFIC = {"gemm_src": "7f1794fed54dc23c",
+                   # FETCH_SIZE 9,126,703 KiB x 2.000 + WRITE_SIZE 311,385 KiB x 1.000
+                   "bytes": 9126703 * 1024 * 2 + 311385 * 1024}
 
 
 def bench_seq_balance(layer, x, cfg, seq_len=4096, steps=10, warmup=2, backward=True):

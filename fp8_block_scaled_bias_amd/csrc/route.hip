@@ -309,16 +309,14 @@ __global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
     p[i] = v;
 }
 
-__device__ __forceinline__ bool beats(float v, int e, float ov, int oe) {
-  return ov > v || (ov == v && oe < e);
-}
-
 __global__ __launch_bounds__(256) void router_select_kernel(
     const float* __restrict__ part, int KS, int64_t T, const float* __restrict__ bias, int E,
     int n_group, int topk_group, int k, int lpg, int32_t* __restrict__ topk_idx,
     float* __restrict__ topk_w, int32_t* __restrict__ counts, float* __restrict__ scores,
     float* __restrict__ score_sums) {
   __shared__ int hist[256];
+  __shared__ int s_sel_e[4][8];    // per wave: the token's selection in expert order
+  __shared__ float s_sel_s[4][8];
   for (int i = threadIdx.x; i < 256; i += 256) hist[i] = 0;
   __syncthreads();
 
@@ -390,77 +388,60 @@ __global__ __launch_bounds__(256) void router_select_kernel(
       rank += (sj > gscore || (sj == gscore && j < gid)) ? 1 : 0;
     }
     const bool kept = active && rank < topk_group;
-    float cand[4];
+    // top-k among the kept experts.  Every expert slot gets a unique 40-bit
+    // key: the order-preserving bits of its biased score above 255 - e (a
+    // tie goes to the lower expert id); slots outside the kept groups keep
+    // only the index part, below every kept one.  The k-th largest key is
+    // found bit by bit from the top: a bit stays set when at least k keys
+    // reach the prefix with it (counted by ballots), so the k selected slots
+    // are exactly the keys at or above it.
+    uint64_t key[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) cand[i] = kept ? sb[i] : -INFINITY;
-
-    int sel[8];
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t u = sb[i] == 0.0f ? 0u : __float_as_uint(sb[i]);  // -0 ties +0
+      const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+      key[i] = ((uint64_t)(kept ? ord : 0u) << 8) | (uint64_t)(255 - ((ebase + i) & 255));
+    }
+    uint64_t pre = 0;
+    for (int bit = 39; bit >= 0; --bit) {
+      const uint64_t c = pre | (1ull << bit);
+      int cnt = 0;
 #pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      if (it < k) {
-        float bv = cand[0];
-        int be = ebase;
+      for (int i = 0; i < 4; ++i) cnt += __popcll(__ballot(key[i] >= c));
+      if (cnt >= k) pre = c;
+    }
+    // ranks in ascending expert id (e = 4 lane + i): selected slots of the
+    // lanes below, then this lane's earlier slots; each selected slot puts
+    // (e, s) at its rank, and the wave reads the k entries back in order
+    uint64_t msk[4];
+    int below = 0;
 #pragma unroll
-        for (int i = 1; i < 4; ++i)
-          if (cand[i] > bv) {
-            bv = cand[i];
-            be = ebase + i;
-          }
+    for (int i = 0; i < 4; ++i) {
+      msk[i] = __ballot(key[i] >= pre);
+      below += __popcll(msk[i] & ((1ull << lane) - 1ull));
+    }
 #pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const float ov = __shfl_xor(bv, o, 64);
-          const int oe = __shfl_xor(be, o, 64);
-          if (beats(bv, be, ov, oe)) {
-            bv = ov;
-            be = oe;
-          }
-        }
-        sel[it] = be;
-        if ((be >> 2) == lane) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if ((be & 3) == i) cand[i] = -INFINITY;
-        }
-      } else {
-        sel[it] = 0x7FFFFFFF;
+    for (int i = 0; i < 4; ++i) {
+      if ((msk[i] >> lane) & 1ull) {
+        s_sel_e[wv][below] = ebase + i;
+        s_sel_s[wv][below] = s[i];
+        ++below;
       }
     }
-    // ascending expert id (uniform across the wave)
-#pragma unroll
-    for (int i = 1; i < 8; ++i) {
-#pragma unroll
-      for (int j = i; j > 0; --j) {
-        if (sel[j] < sel[j - 1]) {
-          const int tmp = sel[j];
-          sel[j] = sel[j - 1];
-          sel[j - 1] = tmp;
-        }
-      }
-    }
-    float sv[8];
     float sum = 0.f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (j < k) {
-        const int e = sel[j];
-        float mine = s[0];
-#pragma unroll
-        for (int i = 1; i < 4; ++i)
-          if ((e & 3) == i) mine = s[i];
-        sv[j] = __shfl(mine, e >> 2, 64);
-        sum += sv[j];
-      } else {
-        sv[j] = 0.f;
-      }
-    }
     int my_e = 0;
     float my_s = 0.f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (j == lane) {
-        my_e = sel[j];
-        my_s = sv[j];
+    for (int j = 0; j < 8; ++j) {
+      if (j < k) {
+        const float sj = s_sel_s[wv][j];
+        sum += sj;
+        if (j == lane) {
+          my_e = s_sel_e[wv][j];
+          my_s = sj;
+        }
       }
+    }
     my_e = min(my_e, E - 1);  // only reachable with NaN scores (unspecified input)
     if (lane < k) {
       topk_idx[t * k + lane] = my_e;

@@ -263,7 +263,9 @@ def bench_backward_step(layer, x, cfg, steps=3, warmup=1):
     forward, so the backward depends on nothing made from the weights
     beforehand.  Flops counted: the GEMMs only, 2RHI for each of
     dgrad-down and wgrad-down, 4RHI for each of the recomputed gate+up,
-    dgrad-gate+up and wgrad-gate+up (34.6 TFLOP).  Then a training step
+    dgrad-gate+up and wgrad-gate+up (34.6 TFLOP).  The same backward is also
+    timed after a forward that kept its gate/up outputs (ms_per_step_keep_gu:
+    no gate+up GEMM rerun).  Then a training step
     (forward + backward, wall clock) with the gate+up GEMM rerun in the
     backward and with the forward keeping its outputs; and the 128x128
     requantisation of fp32 master weights (fp8_quant_128x128 over both
@@ -292,6 +294,19 @@ def bench_backward_step(layer, x, cfg, steps=3, warmup=1):
            "flop_per_step": flop, "per_stage_ms": per}
     log(f"[bench] backward step: {ms:.3f} ms ({out['TFLOPS']:.0f} TFLOP/s); " +
         ", ".join(f"{k} {v:.3f}" for k, v in per.items()))
+    # the same backward after a forward that kept its gate/up outputs (the
+    # training configuration: the backward reads them instead of rerunning
+    # the gate+up GEMM)
+    layer.forward(x, keep_gu=True)
+    layer.backward(dy, x)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        layer.backward(dy, x)
+    torch.cuda.synchronize()
+    out["ms_per_step_keep_gu"] = (time.perf_counter() - t0) / steps * 1e3
+    log(f"[bench] backward step after a forward that kept gate/up: "
+        f"{out['ms_per_step_keep_gu']:.3f} ms")
     # a training step (forward + backward) both ways: the fused forward with
     # the gate+up GEMM run again in the backward, or the fused forward that
     # also keeps its bf16 gate/up outputs (1.2 GB) for the backward to read

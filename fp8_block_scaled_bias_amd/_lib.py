@@ -46,8 +46,8 @@ SIGNATURES = {
     "fp8_quant_128x1_grouped": (ctypes.c_int, [_vp, _i64, _vp, _i64, _vp, _i32, _i64, _i64, _vp,
                                                _vp, _i64, _vp]),
     "moe_combine_backward": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i32, _i64, _i32, _vp, _vp,
-                                            _vp]),
-    "swiglu_backward": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp, _vp, _vp]),
+                                            _vp, _vp, _vp]),
+    "swiglu_backward": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp]),
     "moe_router_backward": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i32, _i32,
                                            _vp, _vp, _vp]),
     "moe_router_dcentroids": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp]),
@@ -220,10 +220,11 @@ def fp8_quant_128x1_grouped(in_bf16, ld_in, row_index, group_offsets, G, M_total
 
 
 def moe_combine_backward(dy_bf16, inv_perm, topk_w, expert_out_bf16, T, k, H, n_shared,
-                         d_expert_out_bf16, d_topk_w, stream=None):
+                         d_expert_out_bf16, d_topk_w, stream=None, *, d_expert_out_e4m3=None,
+                         d_expert_out_scale=None):
     return _call("moe_combine_backward", _dev(dy_bf16), _dev(inv_perm), _dev(topk_w),
                  _dev(expert_out_bf16), T, k, H, n_shared, _dev(d_expert_out_bf16), _dev(d_topk_w),
-                 _stream(stream))
+                 _dev(d_expert_out_e4m3), _dev(d_expert_out_scale), _stream(stream))
 
 
 def moe_router_backward(x_bf16, centroids, topk_idx, d_topk_w, inv_perm, dx_in_bf16, T, H, E, k,
@@ -252,9 +253,10 @@ def moe_router_backward_dense(x_bf16, centroids, topk_idx, d_topk_w, scores, sco
                  _dev(workspace), workspace_bytes, _stream(stream))
 
 
-def swiglu_backward(gu_bf16, dh_bf16, M, I, dgu_bf16, h_bf16, stream=None):
+def swiglu_backward(gu_bf16, dh_bf16, M, I, dgu_bf16, h_bf16, stream=None, *, dgu_e4m3=None,
+                    dgu_scale=None):
     return _call("swiglu_backward", _dev(gu_bf16), _dev(dh_bf16), M, I, _dev(dgu_bf16),
-                 _dev(h_bf16), _stream(stream))
+                 _dev(h_bf16), _dev(dgu_e4m3), _dev(dgu_scale), _stream(stream))
 
 
 def grouped_fp8_wgrad(dy_c, dy_scale_c, a_c, a_scale_c, chunks_cap, group_offsets, G, M_total, N,

@@ -13,6 +13,11 @@
 //   s = 1 / (1 + exp(-g)),  dg = dh u s (1 + g (1 - s)),  du = dh g s,
 // plus h = g s u (the down projection's weight-gradient operand), in fp32,
 // stored as bf16.  HBM bound, grid-stride over 8-element vectors.
+//
+// Both kernels can also write the 1x128 E4M3 quantisation of their bf16
+// gradient rows (the input-gradient GEMM's operand), from the stored bf16
+// values with the quantiser's own tile routine: 16 consecutive lanes hold
+// one 128-column tile, so the rows are not read back from HBM.
 #include "common.h"
 
 namespace moe {
@@ -37,7 +42,8 @@ template <int KMAX>
 __global__ __launch_bounds__(CB) void combine_backward_kernel(
     const uint16_t* __restrict__ dy, const int32_t* __restrict__ inv_perm,
     const float* __restrict__ w, const uint16_t* __restrict__ D, int64_t T, int k, int64_t H,
-    int n_shared, uint16_t* __restrict__ dD, float* __restrict__ dw) {
+    int n_shared, uint16_t* __restrict__ dD, float* __restrict__ dw, uint8_t* __restrict__ dq,
+    float* __restrict__ dqs) {
   __shared__ float s_dot[CB / 64][KMAX];
   const int64_t t = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -64,9 +70,23 @@ __global__ __launch_bounds__(CB) void combine_backward_kernel(
         dot[j] = fmaf(g[i], d[i], dot[j]);
         o[i] = wt[j] * g[i];
       }
-      *reinterpret_cast<uint4*>(dD + rows[j] * H + c) = f32_to_bf16x8(o);
+      const uint4 ob = f32_to_bf16x8(o);
+      *reinterpret_cast<uint4*>(dD + rows[j] * H + c) = ob;
+      if (dq) {
+        float q[8], s;
+        bf16x8_to_f32(ob, q);
+        *reinterpret_cast<uint2*>(dq + rows[j] * H + c) = quant_tile_1x128(q, &s);
+        if ((tid & 15) == 0) dqs[rows[j] * (H >> 7) + (c >> 7)] = s;
+      }
     }
-    if (n_shared) *reinterpret_cast<uint4*>(dD + (T * k + t) * H + c) = v;
+    if (n_shared) {
+      *reinterpret_cast<uint4*>(dD + (T * k + t) * H + c) = v;
+      if (dq) {
+        float s;
+        *reinterpret_cast<uint2*>(dq + (T * k + t) * H + c) = quant_tile_1x128(g, &s);
+        if ((tid & 15) == 0) dqs[(T * k + t) * (H >> 7) + (c >> 7)] = s;
+      }
+    }
   }
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) {
@@ -81,7 +101,8 @@ __global__ __launch_bounds__(CB) void combine_backward_kernel(
 
 __global__ __launch_bounds__(256) void swiglu_backward_kernel(
     const uint16_t* __restrict__ gu, const uint16_t* __restrict__ dh, int64_t M, int64_t I,
-    uint16_t* __restrict__ dgu, uint16_t* __restrict__ h) {
+    uint16_t* __restrict__ dgu, uint16_t* __restrict__ h, uint8_t* __restrict__ dq,
+    float* __restrict__ dqs) {
   const int64_t per_row = I >> 3;
   const int64_t n = M * per_row;
   for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < n;
@@ -99,9 +120,21 @@ __global__ __launch_bounds__(256) void swiglu_backward_kernel(
       du[i] = d[i] * gs;
       hv[i] = gs * u[i];
     }
-    *reinterpret_cast<uint4*>(dgu + m * 2 * I + c) = f32_to_bf16x8(dg);
-    *reinterpret_cast<uint4*>(dgu + m * 2 * I + I + c) = f32_to_bf16x8(du);
+    const uint4 dgb = f32_to_bf16x8(dg), dub = f32_to_bf16x8(du);
+    *reinterpret_cast<uint4*>(dgu + m * 2 * I + c) = dgb;
+    *reinterpret_cast<uint4*>(dgu + m * 2 * I + I + c) = dub;
     *reinterpret_cast<uint4*>(h + m * I + c) = f32_to_bf16x8(hv);
+    if (dq) {
+      float q[8], s0, s1;
+      bf16x8_to_f32(dgb, q);
+      *reinterpret_cast<uint2*>(dq + m * 2 * I + c) = quant_tile_1x128(q, &s0);
+      bf16x8_to_f32(dub, q);
+      *reinterpret_cast<uint2*>(dq + m * 2 * I + I + c) = quant_tile_1x128(q, &s1);
+      if ((threadIdx.x & 15) == 0) {
+        dqs[m * (I >> 6) + (c >> 7)] = s0;
+        dqs[m * (I >> 6) + ((I + c) >> 7)] = s1;
+      }
+    }
   }
 }
 
@@ -113,7 +146,8 @@ using namespace moe;
 extern "C" int moe_combine_backward(const void* dy_bf16, const int32_t* inv_perm,
                                     const float* topk_w, const void* expert_out_bf16, int64_t T,
                                     int32_t k, int64_t H, int32_t n_shared, void* d_expert_out_bf16,
-                                    float* d_topk_w, void* stream) {
+                                    float* d_topk_w, uint8_t* d_expert_out_e4m3,
+                                    float* d_expert_out_scale, void* stream) {
   clear_error();
   MOE_INVALID(T >= 0 && T < (1ll << 31), "moe_combine_backward: T=%lld out of range", (long long)T);
   MOE_INVALID(k >= 1 && k <= 8, "moe_combine_backward: k=%d must be in [1, 8]", (int)k);
@@ -128,15 +162,24 @@ extern "C" int moe_combine_backward(const void* dy_bf16, const int32_t* inv_perm
                   ((uintptr_t)d_expert_out_bf16 & 15) == 0,
               "moe_combine_backward: dy, D and dD must be 16-byte aligned");
   MOE_INVALID(d_expert_out_bf16 != expert_out_bf16, "moe_combine_backward: dD must not alias D");
+  MOE_INVALID((d_expert_out_e4m3 == nullptr) == (d_expert_out_scale == nullptr),
+              "moe_combine_backward: dD codes and scales are given together or not at all");
+  if (d_expert_out_e4m3) {
+    MOE_INVALID(H % 128 == 0, "moe_combine_backward: quantised dD needs H %% 128 == 0, got %lld",
+                (long long)H);
+    MOE_INVALID(((uintptr_t)d_expert_out_e4m3 & 7) == 0 && ((uintptr_t)d_expert_out_scale & 3) == 0,
+                "moe_combine_backward: dD codes must be 8-byte, scales 4-byte aligned");
+  }
   combine_backward_kernel<8><<<dim3((unsigned)T), dim3(CB), 0, as_stream(stream)>>>(
       static_cast<const uint16_t*>(dy_bf16), inv_perm, topk_w,
       static_cast<const uint16_t*>(expert_out_bf16), T, k, H, n_shared,
-      static_cast<uint16_t*>(d_expert_out_bf16), d_topk_w);
+      static_cast<uint16_t*>(d_expert_out_bf16), d_topk_w, d_expert_out_e4m3, d_expert_out_scale);
   return check_launch("moe_combine_backward");
 }
 
 extern "C" int swiglu_backward(const void* gu_bf16, const void* dh_bf16, int64_t M, int64_t I,
-                               void* dgu_bf16, void* h_bf16, void* stream) {
+                               void* dgu_bf16, void* h_bf16, uint8_t* dgu_e4m3, float* dgu_scale,
+                               void* stream) {
   clear_error();
   MOE_INVALID(M >= 0, "swiglu_backward: M=%lld < 0", (long long)M);
   MOE_INVALID(I > 0 && I % 8 == 0, "swiglu_backward: I=%lld must be a positive multiple of 8",
@@ -146,11 +189,19 @@ extern "C" int swiglu_backward(const void* gu_bf16, const void* dh_bf16, int64_t
   MOE_INVALID(((uintptr_t)gu_bf16 & 15) == 0 && ((uintptr_t)dh_bf16 & 15) == 0 &&
                   ((uintptr_t)dgu_bf16 & 15) == 0 && ((uintptr_t)h_bf16 & 15) == 0,
               "swiglu_backward: all tensors must be 16-byte aligned");
+  MOE_INVALID((dgu_e4m3 == nullptr) == (dgu_scale == nullptr),
+              "swiglu_backward: dGU codes and scales are given together or not at all");
+  if (dgu_e4m3) {
+    MOE_INVALID(I % 128 == 0, "swiglu_backward: quantised dGU needs I %% 128 == 0, got %lld",
+                (long long)I);
+    MOE_INVALID(((uintptr_t)dgu_e4m3 & 7) == 0 && ((uintptr_t)dgu_scale & 3) == 0,
+                "swiglu_backward: dGU codes must be 8-byte, scales 4-byte aligned");
+  }
   const int64_t n = M * (I / 8);
   const int64_t blocks = std::min<int64_t>(ceil_div(n, 256), 256 * 64);
   swiglu_backward_kernel<<<dim3((unsigned)blocks), dim3(256), 0, as_stream(stream)>>>(
       static_cast<const uint16_t*>(gu_bf16), static_cast<const uint16_t*>(dh_bf16), M, I,
-      static_cast<uint16_t*>(dgu_bf16), static_cast<uint16_t*>(h_bf16));
+      static_cast<uint16_t*>(dgu_bf16), static_cast<uint16_t*>(h_bf16), dgu_e4m3, dgu_scale);
   return check_launch("swiglu_backward");
 }
 

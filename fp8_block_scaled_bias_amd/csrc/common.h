@@ -94,4 +94,20 @@ __device__ __forceinline__ float wave_max_xor(float v, int width) {
   return v;
 }
 
+// 1x128 E4M3 quantisation of one tile spread over 16 consecutive lanes (lane
+// l % 16 holds elements 8 (l % 16) .. + 7; all 16 lanes must call it
+// together): scale = amax / 448 (1 for an all-zero tile), codes = E4M3 of
+// v / scale (round to nearest even, saturating).  Returns the lane's 8
+// codes; *scale gets the tile's scale.
+__device__ __forceinline__ uint2 quant_tile_1x128(const float* v, float* scale) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  amax = wave_max_xor(amax, 16);
+  const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+  *scale = s;
+  return make_uint2(f32x4_to_e4m3x4(v[0] / s, v[1] / s, v[2] / s, v[3] / s),
+                    f32x4_to_e4m3x4(v[4] / s, v[5] / s, v[6] / s, v[7] / s));
+}
+
 }  // namespace moe

@@ -51,14 +51,8 @@ __global__ __launch_bounds__(256) void quant_1x128_kernel(
         }
       }
     }
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
-    amax = wave_max_xor(amax, 16);
-    const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
-    const uint32_t lo = f32x4_to_e4m3x4(v[0] / s, v[1] / s, v[2] / s, v[3] / s);
-    const uint32_t hi = f32x4_to_e4m3x4(v[4] / s, v[5] / s, v[6] / s, v[7] / s);
-    *reinterpret_cast<uint2*>(out + row * K + tc * 128 + l16 * 8) = make_uint2(lo, hi);
+    float s;
+    *reinterpret_cast<uint2*>(out + row * K + tc * 128 + l16 * 8) = quant_tile_1x128(v, &s);
     if (l16 == 0) scales[row * tpr + tc] = s;
   }
 }

@@ -21,13 +21,14 @@ MoELayer.backward runs the backward of the expert path in FP8 (the pages'
 backward-for-input and backward-for-weights chunks, section 工程 › DualPipe
 流水线并行, with the FP8 formats of section FP8 低精度训练):
 
-  1. moe_combine_backward   dD = w * dy per routed row, dy for the shared rows;
+  1. moe_combine_backward   dD = w * dy per routed row, dy for the shared rows
+                            (bf16, and its 1x128 E4M3 codes in the same pass);
                             dw = <dy, D> (the gate weights' gradient)
-  2. fp8_quant_1x128 + grouped_fp8_gemm_dgrad on W_dn  dh = dD W_dn
+  2. grouped_fp8_gemm_dgrad on W_dn                   dh = dD W_dn
   3. grouped_fp8_gemm       the gate+up outputs again (bf16; the fused
                             forward keeps none)
-  4. swiglu_backward        dGU = [dg | du], h
-  5. fp8_quant_1x128 + grouped_fp8_gemm_dgrad on W_gu  dX = dGU W_gu
+  4. swiglu_backward        dGU = [dg | du] (bf16 and 1x128 codes), h
+  5. grouped_fp8_gemm_dgrad on W_gu                   dX = dGU W_gu
   6. moe_combine            dx = the sum of a token's rows of dX (unit weights)
   7. fp8_quant_128x1_grouped + grouped_fp8_wgrad       dW_dn = dD^T h,
                             dW_gu = dGU^T x (x gathered through the permutation)
@@ -343,12 +344,13 @@ class MoELayer:
             e1.record(st)
             events.setdefault(name, []).append((e0, e1))
 
+        # the combine and SwiGLU backward also write the 1x128 quantisation of
+        # their bf16 gradients (the input-gradient GEMMs' operands)
         step("combine_bwd", lambda: L.moe_combine_backward(
-            dy_bf16, b.inv_perm, b.topk_w, b.d, T, k, H, s.n_shared, bb.dD, bb.dw, st))
-        step("dgrad_down", lambda: (
-            L.fp8_quant_1x128(bb.dD, R, H, H, 0, bb.dDq, bb.dDs, st),
-            L.grouped_fp8_gemm_dgrad(bb.dDq, bb.dDs, self.w_dn, self.w_dn_s, b.offsets, G, R, H,
-                                     I, bb.dh, st)))
+            dy_bf16, b.inv_perm, b.topk_w, b.d, T, k, H, s.n_shared, bb.dD, bb.dw, st,
+            d_expert_out_e4m3=bb.dDq, d_expert_out_scale=bb.dDs))
+        step("dgrad_down", lambda: L.grouped_fp8_gemm_dgrad(
+            bb.dDq, bb.dDs, self.w_dn, self.w_dn_s, b.offsets, G, R, H, I, bb.dh, st))
         if getattr(b, "gu_kept", False):
             gu = b.hgu   # kept by the forward (keep_gu): the same bf16 GEMM output
         else:
@@ -356,11 +358,10 @@ class MoELayer:
             step("recompute_gate_up", lambda: L.grouped_fp8_gemm(
                 b.xq, b.xs, b.perm_src, self.w_gu, self.w_gu_s, b.offsets, G, R, 2 * I, H, gu,
                 st))
-        step("swiglu_bwd", lambda: L.swiglu_backward(gu, bb.dh, R, I, bb.dgu, bb.h, st))
-        step("dgrad_gate_up", lambda: (
-            L.fp8_quant_1x128(bb.dgu, R, 2 * I, 2 * I, 0, bb.dguq, bb.dgus, st),
-            L.grouped_fp8_gemm_dgrad(bb.dguq, bb.dgus, self.w_gu, self.w_gu_s, b.offsets, G, R,
-                                     2 * I, H, bb.dxp, st)))
+        step("swiglu_bwd", lambda: L.swiglu_backward(gu, bb.dh, R, I, bb.dgu, bb.h, st,
+                                                     dgu_e4m3=bb.dguq, dgu_scale=bb.dgus))
+        step("dgrad_gate_up", lambda: L.grouped_fp8_gemm_dgrad(
+            bb.dguq, bb.dgus, self.w_gu, self.w_gu_s, b.offsets, G, R, 2 * I, H, bb.dxp, st))
         shared = bb.dxp[T * k:T * k + T] if s.n_shared else None
         step("unpermute", lambda: L.moe_combine(bb.dxp, b.inv_perm, bb.ones, shared, T, k, H,
                                                 bb.dx, st))

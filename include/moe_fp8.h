@@ -321,13 +321,20 @@ int grouped_fp8_wgrad(const uint8_t* dy_c, const float* dy_scale_c, const uint8_
  *                            summed in a fixed order)
  * dy_bf16 [T, H]; inv_perm [T*k] (a permutation of [0, T*k)); topk_w [T*k];
  * expert_out_bf16 D [T*k + n_shared*T, H]; d_expert_out_bf16 (out) like D;
- * d_topk_w (out) [T*k] fp32.  Requirements: 1 <= k <= 8, H % 8 == 0,
- * n_shared in {0, 1}; dy, D, dD 16-byte aligned, dD not aliasing D.
+ * d_topk_w (out) [T*k] fp32.
+ * d_expert_out_e4m3, d_expert_out_scale (out, both or neither; NULL: not
+ * written) [T*k + n_shared*T, H] e4m3 and [.., H/128] fp32: the 1x128
+ * quantisation of dD as stored (bit for bit what fp8_quant_1x128 mode 0
+ * writes for d_expert_out_bf16), formed in the same pass so the input-
+ * gradient GEMM's operand needs no second read of dD (section FP8 低精度训练
+ * › 细粒度量化); requires H % 128 == 0, codes 8-byte and scales 4-byte aligned.
+ * Requirements: 1 <= k <= 8, H % 8 == 0, n_shared in {0, 1}; dy, D, dD
+ * 16-byte aligned, dD not aliasing D.
  */
 int moe_combine_backward(const void* dy_bf16, const int32_t* inv_perm, const float* topk_w,
                          const void* expert_out_bf16, int64_t T, int32_t k, int64_t H,
                          int32_t n_shared, void* d_expert_out_bf16, float* d_topk_w,
-                         void* stream);
+                         uint8_t* d_expert_out_e4m3, float* d_expert_out_scale, void* stream);
 
 /*
  * swiglu_backward - backward of h = silu(g) * u (the experts' SwiGLU, see
@@ -337,9 +344,14 @@ int moe_combine_backward(const void* dy_bf16, const int32_t* inv_perm, const flo
  * gu_bf16 [M, 2I] = [g | u]; dh_bf16 [M, I]; dgu_bf16 (out) [M, 2I] = [dg | du];
  * h_bf16 (out) [M, I] (the down projection's weight-gradient operand); all
  * stored as bf16 (round to nearest even), 16-byte aligned.  I % 8 == 0.
+ * dgu_e4m3, dgu_scale (out, both or neither; NULL: not written) [M, 2I] e4m3
+ * and [M, 2I/128] fp32: the 1x128 quantisation of dGU as stored (bit for
+ * bit what fp8_quant_1x128 mode 0 writes for dgu_bf16), in the same pass;
+ * requires I % 128 == 0, codes 8-byte and scales 4-byte aligned.
  */
 int swiglu_backward(const void* gu_bf16, const void* dh_bf16, int64_t M, int64_t I,
-                    void* dgu_bf16, void* h_bf16, void* stream);
+                    void* dgu_bf16, void* h_bf16, uint8_t* dgu_e4m3, float* dgu_scale,
+                    void* stream);
 
 /*
  * moe_router_backward - backward of the gate weights to the router's input and

@@ -88,7 +88,8 @@ def test_wgrad_validation():
 
 def test_backward_elementwise_validation():
     def c(T=4, k=2, H=256, ns=1, dD=ctypes.c_void_p(8192)):
-        return rc("moe_combine_backward", FAKE, FAKE, FAKE, FAKE, T, k, H, ns, dD, FAKE, None)
+        return rc("moe_combine_backward", FAKE, FAKE, FAKE, FAKE, T, k, H, ns, dD, FAKE, None, None,
+                  None)
     assert c(k=9) == L.MOE_ERR_INVALID and "k=9" in L.last_error()
     assert c(H=100) == L.MOE_ERR_INVALID
     assert c(ns=2) == L.MOE_ERR_INVALID
@@ -96,10 +97,17 @@ def test_backward_elementwise_validation():
     assert c(dD=None) == L.MOE_ERR_INVALID
     assert c(T=0, dD=None) == L.MOE_OK
     def g(M=4, I=128, out=FAKE):
-        return rc("swiglu_backward", FAKE, FAKE, M, I, out, FAKE, None)
+        return rc("swiglu_backward", FAKE, FAKE, M, I, out, FAKE, None, None, None)
     assert g(I=100) == L.MOE_ERR_INVALID and "I=100" in L.last_error()
     assert g(out=None) == L.MOE_ERR_INVALID
     assert g(out=ctypes.c_void_p(4104)) == L.MOE_ERR_INVALID and "aligned" in L.last_error()
+    # the fused 1x128 codes: both or neither, whole 128-column tiles
+    assert rc("swiglu_backward", FAKE, FAKE, 4, 128, FAKE, FAKE, FAKE, None, None) == L.MOE_ERR_INVALID
+    assert "together" in L.last_error()
+    assert rc("swiglu_backward", FAKE, FAKE, 4, 136, FAKE, FAKE, FAKE, FAKE, None) == L.MOE_ERR_INVALID
+    assert "I % 128" in L.last_error()
+    assert rc("moe_combine_backward", FAKE, FAKE, FAKE, ctypes.c_void_p(8192), 4, 2, 136, 1, FAKE, FAKE,
+              FAKE, FAKE, None) == L.MOE_ERR_INVALID and "H % 128" in L.last_error()
     assert g(M=0, out=None) == L.MOE_OK
     def r(T=4, H=256, E=16, k=4, dx=FAKE):
         return rc("moe_router_backward", FAKE, FAKE, FAKE, FAKE, FAKE, None, T, H, E, k, dx, FAKE, None)

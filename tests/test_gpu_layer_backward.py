@@ -76,6 +76,56 @@ def test_swiglu_backward_kernel(M_, I):
         assert (d <= bf16_ulp(np.maximum(np.abs(got), np.abs(ref))) + 1e-30).all(), what
 
 
+@pytest.mark.parametrize("T,k,H,ns", [(37, 8, 1024, 1), (5, 3, 256, 0), (64, 4, 7168, 1)])
+def test_combine_backward_writes_1x128_codes(T, k, H, ns):
+    """The 1x128 codes and scales moe_combine_backward writes with dD equal
+    the oracle's quant_1x128 of dD as stored, and fp8_quant_1x128 of the same
+    bf16 rows, bit for bit (rows of both kinds: routed w*dy and shared dy)."""
+    rng = np.random.default_rng([T, k, H, 1])
+    R = T * k + ns * T
+    dy = rng.standard_normal((T, H)).astype(np.float32)
+    dy[0, :128] = 0.0                                   # an all-zero tile
+    dy = synth.f32_to_bf16_bits(dy)
+    D = synth.f32_to_bf16_bits(rng.standard_normal((R, H)).astype(np.float32))
+    inv_perm = rng.permutation(T * k).astype(np.int32)
+    w = rng.random((T, k)).astype(np.float32)
+    dD = torch.empty((R, H), dtype=torch.bfloat16, device="cuda")
+    dw = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    q = torch.empty((R, H), dtype=torch.uint8, device="cuda")
+    sc = torch.empty((R, H // 128), dtype=torch.float32, device="cuda")
+    M.moe_combine_backward(bf16_dev(dy), dev(inv_perm), dev(w), bf16_dev(D), T, k, H, ns, dD, dw,
+                           d_expert_out_e4m3=q, d_expert_out_scale=sc)
+    oq, os_ = OQ.quant_1x128(bf16_values_host(dD).astype(np.float32))
+    assert np.array_equal(host(q), oq) and np.array_equal(host(sc), os_)
+    q2 = torch.empty_like(q)
+    s2 = torch.empty_like(sc)
+    M.fp8_quant_1x128(dD, R, H, H, 0, q2, s2)
+    assert torch.equal(q, q2) and torch.equal(sc, s2)
+
+
+@pytest.mark.parametrize("M_,I", [(300, 128), (7, 2048)])
+def test_swiglu_backward_writes_1x128_codes(M_, I):
+    """The 1x128 codes and scales swiglu_backward writes with dGU equal the
+    oracle's quant_1x128 of dGU as stored, and fp8_quant_1x128 of the same
+    bf16 rows, bit for bit (dg and du halves)."""
+    rng = np.random.default_rng([M_, I, 1])
+    gub = synth.f32_to_bf16_bits(rng.standard_normal((M_, 2 * I)).astype(np.float32) * 3.0)
+    dh = rng.standard_normal((M_, I)).astype(np.float32)
+    dh[1, :] = 0.0                                      # zero tiles in both halves
+    dh = synth.f32_to_bf16_bits(dh)
+    dgu = torch.empty((M_, 2 * I), dtype=torch.bfloat16, device="cuda")
+    h = torch.empty((M_, I), dtype=torch.bfloat16, device="cuda")
+    q = torch.empty((M_, 2 * I), dtype=torch.uint8, device="cuda")
+    sc = torch.empty((M_, 2 * I // 128), dtype=torch.float32, device="cuda")
+    M.swiglu_backward(bf16_dev(gub), bf16_dev(dh), M_, I, dgu, h, dgu_e4m3=q, dgu_scale=sc)
+    oq, os_ = OQ.quant_1x128(bf16_values_host(dgu).astype(np.float32))
+    assert np.array_equal(host(q), oq) and np.array_equal(host(sc), os_)
+    q2 = torch.empty_like(q)
+    s2 = torch.empty_like(sc)
+    M.fp8_quant_1x128(dgu, M_, 2 * I, 2 * I, 0, q2, s2)
+    assert torch.equal(q, q2) and torch.equal(sc, s2)
+
+
 def _expert_rows(idx, E):
     """perm_src, inv_perm [T*k] and offsets [E+1] in moe_permute's layout: rows
     grouped by expert, each expert's tokens in ascending order."""

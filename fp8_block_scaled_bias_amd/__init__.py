@@ -10,5 +10,5 @@ from ._lib import (MoEError, fp8_quant_1x128, fp8_quant_128x128,  # noqa: F401
                    moe_route_scores, moe_route_workspace_bytes, moe_router_backward,
                    moe_router_backward_dense, moe_router_backward_dense_workspace_bytes,
                    moe_router_dcentroids, moe_seq_balance, moe_seq_balance_workspace_bytes,
-                   swiglu_backward, wgrad_chunks)
+                   swiglu_backward, swiglu_backward_grouped, wgrad_chunks)
 from .layer import BackwardBuffers, Buffers, LayerShape, MoELayer  # noqa: F401

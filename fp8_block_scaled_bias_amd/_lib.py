@@ -48,6 +48,8 @@ SIGNATURES = {
     "moe_combine_backward": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i32, _i64, _i32, _vp, _vp,
                                             _vp, _vp, _vp]),
     "swiglu_backward": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp]),
+    "swiglu_backward_grouped": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i64, _i64, _vp, _vp, _vp,
+                                               _vp, _i64, _vp, _vp, _vp, _vp, _vp]),
     "moe_router_backward": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i32, _i32,
                                            _vp, _vp, _vp]),
     "moe_router_dcentroids": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp]),
@@ -257,6 +259,15 @@ def swiglu_backward(gu_bf16, dh_bf16, M, I, dgu_bf16, h_bf16, stream=None, *, dg
                     dgu_scale=None):
     return _call("swiglu_backward", _dev(gu_bf16), _dev(dh_bf16), M, I, _dev(dgu_bf16),
                  _dev(h_bf16), _dev(dgu_e4m3), _dev(dgu_scale), _stream(stream))
+
+
+def swiglu_backward_grouped(gu_bf16, dh_bf16, group_offsets, G, M_total, I, dgu_bf16, h_bf16,
+                            dgu_e4m3, dgu_scale, chunks_cap, dgu_c, dgu_scale_c, h_c, h_scale_c,
+                            stream=None):
+    return _call("swiglu_backward_grouped", _dev(gu_bf16), _dev(dh_bf16), _dev(group_offsets), G,
+                 M_total, I, _dev(dgu_bf16), _dev(h_bf16), _dev(dgu_e4m3), _dev(dgu_scale),
+                 chunks_cap, _dev(dgu_c), _dev(dgu_scale_c), _dev(h_c), _dev(h_scale_c),
+                 _stream(stream))
 
 
 def grouped_fp8_wgrad(dy_c, dy_scale_c, a_c, a_scale_c, chunks_cap, group_offsets, G, M_total, N,

@@ -113,13 +113,7 @@ __global__ __launch_bounds__(256) void swiglu_backward_kernel(
     bf16x8_to_f32(*reinterpret_cast<const uint4*>(gu + m * 2 * I + I + c), u);
     bf16x8_to_f32(*reinterpret_cast<const uint4*>(dh + m * I + c), d);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float s = 1.0f / (1.0f + expf(-g[i]));
-      const float gs = g[i] * s;
-      dg[i] = d[i] * u[i] * s * (1.0f + g[i] * (1.0f - s));
-      du[i] = d[i] * gs;
-      hv[i] = gs * u[i];
-    }
+    for (int i = 0; i < 8; ++i) swiglu_bwd_elem(g[i], u[i], d[i], &dg[i], &du[i], &hv[i]);
     const uint4 dgb = f32_to_bf16x8(dg), dub = f32_to_bf16x8(du);
     *reinterpret_cast<uint4*>(dgu + m * 2 * I + c) = dgb;
     *reinterpret_cast<uint4*>(dgu + m * 2 * I + I + c) = dub;

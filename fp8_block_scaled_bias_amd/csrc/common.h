@@ -94,6 +94,18 @@ __device__ __forceinline__ float wave_max_xor(float v, int width) {
   return v;
 }
 
+// SwiGLU backward of one element (fp32): s = 1 / (1 + exp(-g)),
+// dg = dh u s (1 + g (1 - s)), du = dh g s, h = g s u.  Every kernel that
+// forms these values calls this, so they agree bit for bit.
+__device__ __forceinline__ void swiglu_bwd_elem(float g, float u, float d, float* dg, float* du,
+                                                float* h) {
+  const float s = 1.0f / (1.0f + expf(-g));
+  const float gs = g * s;
+  *dg = d * u * s * (1.0f + g * (1.0f - s));
+  *du = d * gs;
+  *h = gs * u;
+}
+
 // 1x128 E4M3 quantisation of one tile spread over 16 consecutive lanes (lane
 // l % 16 holds elements 8 (l % 16) .. + 7; all 16 lanes must call it
 // together): scale = amax / 448 (1 for an all-zero tile), codes = E4M3 of

@@ -166,6 +166,150 @@ __global__ __launch_bounds__(QT) void quant_128x1_direct_kernel(
   }
 }
 
+// ---- SwiGLU backward in the chunk layout -----------------------------------
+// The SwiGLU backward (swiglu_bwd_elem, the arithmetic of swiglu_backward)
+// over each group's 128-token chunks, writing besides dGU = [dg | du] and h
+// as bf16 the codes the next steps read: dGU's 1x128 codes (the input-
+// gradient GEMM's operand) and the 128x1 chunk-major codes of dGU and h (the
+// two weight gradients' operands, the layout of fp8_quant_128x1_grouped), all
+// from the stored bf16 values, so neither is read back.  One workgroup per
+// (chunk, 128 columns of I).  Lane l of wave w owns columns 8 (l % 16) .. +7
+// of rows 32w + 8 (l / 16) .. +7: a row's 1x128 tile is 16 lanes (xor 1..8),
+// a column's 32 rows in a wave are 4 lanes (xor 16, 32) whose 8 codes each
+// are contiguous in the chunk layout, and the four waves meet in LDS.
+__global__ __launch_bounds__(QT) void swiglu_backward_grouped_kernel(
+    const uint16_t* __restrict__ gu, const uint16_t* __restrict__ dh,
+    const int32_t* __restrict__ offs, int G, int64_t I, uint16_t* __restrict__ dgu,
+    uint16_t* __restrict__ h, uint8_t* __restrict__ dgu_q, float* __restrict__ dgu_qs,
+    uint8_t* __restrict__ dgu_c, float* __restrict__ dgu_cs, uint8_t* __restrict__ h_c,
+    float* __restrict__ h_cs) {
+  extern __shared__ int s_tab[];
+  int* s_offs = s_tab;
+  int* s_pref = s_tab + (G + 1);
+  __shared__ int s_red[QT / 64];
+  __shared__ int s_carry;
+  __shared__ float s_am[4][128];
+  gemm::build_group_tables<QT, 128>(offs, G, s_offs, s_pref, s_red, &s_carry);
+  const int64_t L = blockIdx.x;  // chunk
+  if (L >= s_pref[G]) return;
+  const gemm::Tile t = gemm::decode_tile(s_pref, s_offs, G, 1, L, 128);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int cg = lane & 15, rs = lane >> 4;
+  const int64_t c0 = (int64_t)blockIdx.y * 128, I2 = 2 * I;
+  const int64_t col = c0 + 8 * cg;          // this lane's first column of I
+  const int row0 = 32 * w + 8 * rs;         // its first row of the chunk
+  // bf16 values of dg, du, h: [row i][4 words of 2 columns]
+  uint4 pg[8], pu[8], ph[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t r = t.m0 + row0 + i;
+    const bool ok = r < t.m1;
+    const int64_t rr = ok ? r : t.m0;       // a valid row; values zeroed below
+    const uint4 gv = *reinterpret_cast<const uint4*>(gu + rr * I2 + col);
+    const uint4 uv = *reinterpret_cast<const uint4*>(gu + rr * I2 + I + col);
+    const uint4 dv = *reinterpret_cast<const uint4*>(dh + rr * I + col);
+    const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w}, uw[4] = {uv.x, uv.y, uv.z, uv.w},
+                   dw_[4] = {dv.x, dv.y, dv.z, dv.w};
+    uint32_t og[4], ou[4], oh[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float dg0, du0, h0, dg1, du1, h1;
+      swiglu_bwd_elem(bf16_to_f32(gw[q] & 0xFFFFu), bf16_to_f32(uw[q] & 0xFFFFu),
+                      bf16_to_f32(dw_[q] & 0xFFFFu), &dg0, &du0, &h0);
+      swiglu_bwd_elem(bf16_to_f32(gw[q] >> 16), bf16_to_f32(uw[q] >> 16), bf16_to_f32(dw_[q] >> 16),
+                      &dg1, &du1, &h1);
+      og[q] = ok ? f32x2_to_bf16x2(dg0, dg1) : 0u;
+      ou[q] = ok ? f32x2_to_bf16x2(du0, du1) : 0u;
+      oh[q] = ok ? f32x2_to_bf16x2(h0, h1) : 0u;
+    }
+    pg[i] = make_uint4(og[0], og[1], og[2], og[3]);
+    pu[i] = make_uint4(ou[0], ou[1], ou[2], ou[3]);
+    ph[i] = make_uint4(oh[0], oh[1], oh[2], oh[3]);
+    if (ok) {
+      *reinterpret_cast<uint4*>(dgu + r * I2 + col) = pg[i];
+      *reinterpret_cast<uint4*>(dgu + r * I2 + I + col) = pu[i];
+      *reinterpret_cast<uint4*>(h + r * I + col) = ph[i];
+    }
+  }
+  auto unpack = [](const uint4& p, float* v) {
+    const uint32_t x[4] = {p.x, p.y, p.z, p.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v[2 * q] = bf16_to_f32(x[q] & 0xFFFFu);
+      v[2 * q + 1] = bf16_to_f32(x[q] >> 16);
+    }
+  };
+  // dGU's 1x128 codes: a row's tile is the 16 lanes of one rs (all valid or
+  // all past the group's end together)
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t r = t.m0 + row0 + i;
+    float v[8], s;
+    unpack(pg[i], v);
+    const uint2 qg = quant_tile_1x128(v, &s);
+    if (r < t.m1) {
+      *reinterpret_cast<uint2*>(dgu_q + r * I2 + col) = qg;
+      if (cg == 0) dgu_qs[r * (I2 >> 7) + (c0 >> 7)] = s;
+    }
+    unpack(pu[i], v);
+    const uint2 qu = quant_tile_1x128(v, &s);
+    if (r < t.m1) {
+      *reinterpret_cast<uint2*>(dgu_q + r * I2 + I + col) = qu;
+      if (cg == 0) dgu_qs[r * (I2 >> 7) + ((I + c0) >> 7)] = s;
+    }
+  }
+  // 128x1 codes of one output: a column's maximum over the lane's 8 rows,
+  // the wave's 4 row groups (xor 16, 32) and the four waves (LDS); rows past
+  // the group's end are the chunk's zero padding
+  auto col_codes = [&](const uint4* p, uint8_t* out, float* scl, int64_t C, int64_t cbase) {
+    float m[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m[j] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float v[8];
+      unpack(p[i], v);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) m[j] = fmaxf(m[j], fabsf(v[j]));
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      m[j] = fmaxf(m[j], __shfl_xor(m[j], 16, 64));
+      m[j] = fmaxf(m[j], __shfl_xor(m[j], 32, 64));
+    }
+    if (rs == 0) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) s_am[w][8 * cg + j] = m[j];
+    }
+    __syncthreads();
+    float sc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int cc = 8 * cg + j;
+      const float a = fmaxf(fmaxf(s_am[0][cc], s_am[1][cc]), fmaxf(s_am[2][cc], s_am[3][cc]));
+      sc[j] = a > 0.0f ? a / 448.0f : 1.0f;
+    }
+    __syncthreads();  // s_am is reused by the next output
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float v[8];  // column j of this lane's 8 rows
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t x[4] = {p[i].x, p[i].y, p[i].z, p[i].w};
+        const uint32_t b = (j & 1) ? (x[j >> 1] >> 16) : (x[j >> 1] & 0xFFFFu);
+        v[i] = bf16_to_f32(b);
+      }
+      const uint2 qc = make_uint2(f32x4_to_e4m3x4(v[0] / sc[j], v[1] / sc[j], v[2] / sc[j], v[3] / sc[j]),
+                                  f32x4_to_e4m3x4(v[4] / sc[j], v[5] / sc[j], v[6] / sc[j], v[7] / sc[j]));
+      *reinterpret_cast<uint2*>(out + (L * C + cbase + 8 * cg + j) * 128 + row0) = qc;
+      if (w == 0 && rs == 0) scl[L * C + cbase + 8 * cg + j] = sc[j];
+    }
+  };
+  col_codes(pg, dgu_c, dgu_cs, I2, c0);
+  col_codes(pu, dgu_c, dgu_cs, I2, I + c0);
+  col_codes(ph, h_c, h_cs, I, c0);
+}
+
 // ---- weight-gradient GEMM ----------------------------------------------------
 // One workgroup (4 waves) per 128 (n) x 128 (k) tile of one group's dW; wave
 // (wm, wn) owns rows 64wm.. and columns 64wn.. as 2 x 2 blocks of
@@ -372,6 +516,40 @@ extern "C" int fp8_quant_128x1_grouped(const void* in_bf16, int64_t ld_in,
       static_cast<const uint16_t*>(in_bf16), ld_in, row_index, in_rows, group_offsets, G, C, out_c,
       scales_c);
   return check_launch("fp8_quant_128x1_grouped");
+}
+
+extern "C" int swiglu_backward_grouped(const void* gu_bf16, const void* dh_bf16,
+                                       const int32_t* group_offsets, int32_t G, int64_t M_total,
+                                       int64_t I, void* dgu_bf16, void* h_bf16, uint8_t* dgu_e4m3,
+                                       float* dgu_scale, int64_t chunks_cap, uint8_t* dgu_c,
+                                       float* dgu_scale_c, uint8_t* h_c, float* h_scale_c,
+                                       void* stream) {
+  clear_error();
+  MOE_INVALID(G >= 1, "swiglu_backward_grouped: G=%d < 1", (int)G);
+  MOE_UNSUPPORTED(G <= gemm::MAXG, "swiglu_backward_grouped: G=%d > %d", (int)G, gemm::MAXG);
+  MOE_INVALID(M_total >= 0 && M_total < (1ll << 31),
+              "swiglu_backward_grouped: M_total=%lld out of range", (long long)M_total);
+  MOE_INVALID(I > 0 && I % 128 == 0 && I / 128 <= 65535,
+              "swiglu_backward_grouped: I=%lld must be a positive multiple of 128", (long long)I);
+  if (M_total == 0) return MOE_OK;
+  MOE_INVALID(chunks_cap >= chunks_needed(M_total, G),
+              "swiglu_backward_grouped: chunks_cap=%lld < ceil(M_total/128) + G = %lld",
+              (long long)chunks_cap, (long long)chunks_needed(M_total, G));
+  MOE_INVALID(gu_bf16 && dh_bf16 && group_offsets && dgu_bf16 && h_bf16 && dgu_e4m3 && dgu_scale &&
+                  dgu_c && dgu_scale_c && h_c && h_scale_c,
+              "swiglu_backward_grouped: null pointer");
+  MOE_INVALID(((uintptr_t)gu_bf16 & 15) == 0 && ((uintptr_t)dh_bf16 & 15) == 0 &&
+                  ((uintptr_t)dgu_bf16 & 15) == 0 && ((uintptr_t)h_bf16 & 15) == 0 &&
+                  ((uintptr_t)dgu_e4m3 & 15) == 0 && ((uintptr_t)dgu_c & 15) == 0 &&
+                  ((uintptr_t)h_c & 15) == 0 && ((uintptr_t)dgu_scale & 3) == 0 &&
+                  ((uintptr_t)dgu_scale_c & 3) == 0 && ((uintptr_t)h_scale_c & 3) == 0,
+              "swiglu_backward_grouped: tensors and codes must be 16-byte, scales 4-byte aligned");
+  swiglu_backward_grouped_kernel<<<dim3((unsigned)chunks_needed(M_total, G), (unsigned)(I / 128)),
+                                   dim3(QT), 2 * (G + 1) * sizeof(int), as_stream(stream)>>>(
+      static_cast<const uint16_t*>(gu_bf16), static_cast<const uint16_t*>(dh_bf16), group_offsets,
+      G, I, static_cast<uint16_t*>(dgu_bf16), static_cast<uint16_t*>(h_bf16), dgu_e4m3, dgu_scale,
+      dgu_c, dgu_scale_c, h_c, h_scale_c);
+  return check_launch("swiglu_backward_grouped");
 }
 
 extern "C" int grouped_fp8_wgrad(const uint8_t* dy_c, const float* dy_scale_c, const uint8_t* a_c,

@@ -27,10 +27,12 @@ backward-for-input and backward-for-weights chunks, section 工程 › DualPipe
   2. grouped_fp8_gemm_dgrad on W_dn                   dh = dD W_dn
   3. grouped_fp8_gemm       the gate+up outputs again (bf16; the fused
                             forward keeps none)
-  4. swiglu_backward        dGU = [dg | du] (bf16 and 1x128 codes), h
+  4. swiglu_backward_grouped  dGU = [dg | du] and h (bf16), dGU's 1x128
+                            codes, the 128x1 chunk codes of dGU and h
   5. grouped_fp8_gemm_dgrad on W_gu                   dX = dGU W_gu
   6. moe_combine            dx = the sum of a token's rows of dX (unit weights)
-  7. fp8_quant_128x1_grouped + grouped_fp8_wgrad       dW_dn = dD^T h,
+  7. fp8_quant_128x1_grouped (dD, gathered x) + grouped_fp8_wgrad
+                            dW_dn = dD^T h,
                             dW_gu = dGU^T x (x gathered through the permutation)
   8. moe_router_backward    dw -> the gate logits' gradient, dx += its part
      moe_router_dcentroids  the centroids' gradient (the bias has none)
@@ -358,8 +360,11 @@ class MoELayer:
             step("recompute_gate_up", lambda: L.grouped_fp8_gemm(
                 b.xq, b.xs, b.perm_src, self.w_gu, self.w_gu_s, b.offsets, G, R, 2 * I, H, gu,
                 st))
-        step("swiglu_bwd", lambda: L.swiglu_backward(gu, bb.dh, R, I, bb.dgu, bb.h, st,
-                                                     dgu_e4m3=bb.dguq, dgu_scale=bb.dgus))
+        # the SwiGLU backward also writes dGU's 1x128 codes and the 128x1 chunk
+        # codes of dGU and h that the input and weight gradients read
+        step("swiglu_bwd", lambda: L.swiglu_backward_grouped(
+            gu, bb.dh, b.offsets, G, R, I, bb.dgu, bb.h, bb.dguq, bb.dgus, cap, bb.c_dgu,
+            bb.s_dgu, bb.c_h, bb.s_h, st))
         step("dgrad_gate_up", lambda: L.grouped_fp8_gemm_dgrad(
             bb.dguq, bb.dgus, self.w_gu, self.w_gu_s, b.offsets, G, R, 2 * I, H, bb.dxp, st))
         shared = bb.dxp[T * k:T * k + T] if s.n_shared else None
@@ -367,12 +372,9 @@ class MoELayer:
                                                 bb.dx, st))
         step("wgrad_down", lambda: (
             L.fp8_quant_128x1_grouped(bb.dD, H, None, b.offsets, G, R, H, bb.c_dD, bb.s_dD, cap, st),
-            L.fp8_quant_128x1_grouped(bb.h, I, None, b.offsets, G, R, I, bb.c_h, bb.s_h, cap, st),
             L.grouped_fp8_wgrad(bb.c_dD, bb.s_dD, bb.c_h, bb.s_h, cap, b.offsets, G, R, H, I,
                                 bb.dW_dn, st)))
         step("wgrad_gate_up", lambda: (
-            L.fp8_quant_128x1_grouped(bb.dgu, 2 * I, None, b.offsets, G, R, 2 * I, bb.c_dgu,
-                                      bb.s_dgu, cap, st),
             L.fp8_quant_128x1_grouped(x_bf16, H, b.perm_src, b.offsets, G, R, H, bb.c_x, bb.s_x,
                                       cap, st),
             L.grouped_fp8_wgrad(bb.c_dgu, bb.s_dgu, bb.c_x, bb.s_x, cap, b.offsets, G, R, 2 * I, H,

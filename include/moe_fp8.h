@@ -354,6 +354,30 @@ int swiglu_backward(const void* gu_bf16, const void* dh_bf16, int64_t M, int64_t
                     void* stream);
 
 /*
+ * swiglu_backward_grouped - swiglu_backward over the rows of G groups (the
+ * experts' permuted rows) that also writes the FP8 operands the backward's
+ * GEMMs read, from the stored bf16 values, in the same pass (news.qq.com
+ * article, section FP8 低精度训练 › 细粒度量化; section 工程 › DualPipe
+ * 流水线并行: backward-for-input and backward-for-weights chunks):
+ *   dgu_bf16, h_bf16 (out): as swiglu_backward, bit for bit;
+ *   dgu_e4m3 [M_total, 2I], dgu_scale [M_total, 2I/128] (out): what
+ *     fp8_quant_1x128 mode 0 writes for dgu_bf16;
+ *   dgu_c, dgu_scale_c (out, C = 2I) and h_c, h_scale_c (out, C = I): what
+ *     fp8_quant_128x1_grouped writes for dgu_bf16 and h_bf16 with the same
+ *     group_offsets and chunks_cap (chunk-major, zero-padded chunks).
+ * gu_bf16 [M_total, 2I] = [g | u]; dh_bf16 [M_total, I]; group_offsets [G+1]
+ * int32 on the device (non-decreasing, [0] == 0, [G] == M_total).
+ * Requirements: I % 128 == 0, 1 <= G <= 1024, chunks_cap >= ceil(M_total/128)
+ * + G; tensors and codes 16-byte aligned, scales 4-byte aligned.  M_total ==
+ * 0 is a no-op.
+ */
+int swiglu_backward_grouped(const void* gu_bf16, const void* dh_bf16,
+                            const int32_t* group_offsets, int32_t G, int64_t M_total, int64_t I,
+                            void* dgu_bf16, void* h_bf16, uint8_t* dgu_e4m3, float* dgu_scale,
+                            int64_t chunks_cap, uint8_t* dgu_c, float* dgu_scale_c, uint8_t* h_c,
+                            float* h_scale_c, void* stream);
+
+/*
  * moe_router_backward - backward of the gate weights to the router's input and
  * the per-expert logits (news.qq.com article: section 无额外损耗的负载均衡 - the
  * bias only selects, so neither it nor the choice of experts has a gradient;

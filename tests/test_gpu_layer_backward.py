@@ -126,6 +126,55 @@ def test_swiglu_backward_writes_1x128_codes(M_, I):
     assert torch.equal(q, q2) and torch.equal(sc, s2)
 
 
+@pytest.mark.parametrize("sizes,I", [([300, 0, 1, 129, 128, 77], 256), ([40, 2, 250], 2048)],
+                         ids=["ragged", "wide_I"])
+def test_swiglu_backward_grouped_equals_unfused(sizes, I):
+    """swiglu_backward_grouped writes what swiglu_backward, fp8_quant_1x128 and
+    fp8_quant_128x1_grouped write on the same rows, bit for bit (groups that are
+    empty, one row, exactly one chunk, ragged), and its 128x1 codes of dGU and
+    h equal the oracle's grouped quantiser of the stored bf16 values."""
+    from test_gpu_wgrad import _to_logical
+    G = len(sizes)
+    offs = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    Mt = int(offs[-1])
+    rng = np.random.default_rng([Mt, I])
+    gu = rng.standard_normal((Mt, 2 * I)).astype(np.float32) * 3.0
+    dh = rng.standard_normal((Mt, I)).astype(np.float32)
+    dh[5, :] = 0.0                                      # zero tiles, both layouts
+    gub, dhb = bf16_dev(synth.f32_to_bf16_bits(gu)), bf16_dev(synth.f32_to_bf16_bits(dh))
+    offs_d = dev(offs.astype(np.int32))
+    cap = M.wgrad_chunks(Mt, G)
+    u8, f32, bf = torch.uint8, torch.float32, torch.bfloat16
+    dgu = torch.empty((Mt, 2 * I), dtype=bf, device="cuda")
+    h = torch.empty((Mt, I), dtype=bf, device="cuda")
+    q = torch.empty((Mt, 2 * I), dtype=u8, device="cuda")
+    qs = torch.empty((Mt, 2 * I // 128), dtype=f32, device="cuda")
+    cg, sg = (torch.zeros((cap, 2 * I, 128), dtype=u8, device="cuda"),
+              torch.zeros((cap, 2 * I), dtype=f32, device="cuda"))
+    ch, sh = (torch.zeros((cap, I, 128), dtype=u8, device="cuda"),
+              torch.zeros((cap, I), dtype=f32, device="cuda"))
+    log(f"[swiglu bwd grouped] sizes {sizes} I={I}")
+    M.swiglu_backward_grouped(gub, dhb, offs_d, G, Mt, I, dgu, h, q, qs, cap, cg, sg, ch, sh)
+    # the unfused chain on the same inputs
+    dgu2, h2 = torch.empty_like(dgu), torch.empty_like(h)
+    M.swiglu_backward(gub, dhb, Mt, I, dgu2, h2)
+    q2, qs2 = torch.empty_like(q), torch.empty_like(qs)
+    M.fp8_quant_1x128(dgu2, Mt, 2 * I, 2 * I, 0, q2, qs2)
+    cg2, sg2, ch2, sh2 = (torch.zeros_like(t) for t in (cg, sg, ch, sh))
+    M.fp8_quant_128x1_grouped(dgu2, 2 * I, None, offs_d, G, Mt, 2 * I, cg2, sg2, cap)
+    M.fp8_quant_128x1_grouped(h2, I, None, offs_d, G, Mt, I, ch2, sh2, cap)
+    nch = int(OQ.chunk_prefix(offs)[-1])
+    assert torch.equal(dgu.view(torch.int16), dgu2.view(torch.int16))
+    assert torch.equal(h.view(torch.int16), h2.view(torch.int16))
+    assert torch.equal(q, q2) and torch.equal(qs, qs2)
+    assert torch.equal(cg[:nch], cg2[:nch]) and torch.equal(sg[:nch], sg2[:nch])
+    assert torch.equal(ch[:nch], ch2[:nch]) and torch.equal(sh[:nch], sh2[:nch])
+    for c, sc, ref in ((cg, sg, dgu), (ch, sh, h)):
+        qo, so = OQ.quant_128x1_grouped(bf16_values_host(ref).astype(np.float32), offs)
+        ql, sl = _to_logical(host(c), host(sc), qo.shape[1] // 128)
+        assert np.array_equal(ql, qo) and np.array_equal(sl, so)
+
+
 def _expert_rows(idx, E):
     """perm_src, inv_perm [T*k] and offsets [E+1] in moe_permute's layout: rows
     grouped by expert, each expert's tokens in ascending order."""

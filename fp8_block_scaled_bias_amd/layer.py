@@ -195,6 +195,7 @@ class MoELayer:
         self.w_gu, self.w_gu_s, self.w_dn, self.w_dn_s = w_gu, w_gu_s, w_dn, w_dn_s
         self._bwd = {}
         self._bufs = {}
+        self._side = None   # stream for x's quantisation beside the router (lazily made)
 
     @staticmethod
     def empty_weights(shape: LayerShape, device="cuda"):
@@ -250,34 +251,60 @@ class MoELayer:
         given, maps a step name ("route", "seq_balance", "quant", "permute",
         "gate_up", "down", "combine", "bias") to a list that receives a
         (start, end) pair of torch.cuda.Event recorded on the launch stream
-        around that step."""
+        around that step (quant: on the side stream it runs on); a dict that
+        already holds keys times only those steps (each event pair adds a few
+        microseconds to the step).
+
+        x's 1x128 quantisation does not depend on the routing: it runs on a
+        side stream (default priority) that forks from the launch stream
+        before the router and joins it before the first expert GEMM, so the
+        two overlap."""
         s = self.shape
         T = x_bf16.shape[0]
         b = bufs or self.buffers(T)
         R = b.R
         b.gu_kept = keep_gu
-        if events is not None:
-            return self._forward_timed(x_bf16, b, stream, update_bias, gamma, events, seq_len,
-                                       alpha)
-        self._route(x_bf16, b, seq_len, stream)
+        st = stream if stream is not None else torch.cuda.current_stream()
+        if self._side is None:
+            self._side = torch.cuda.Stream(device=st.device)
+        side = self._side
+        only = set(events) if events else None
+
+        def step(name, on, fn):
+            if events is None or (only is not None and name not in only):
+                fn()
+                return
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(on)
+            fn()
+            e1.record(on)
+            events.setdefault(name, []).append((e0, e1))
+
+        side.wait_stream(st)
+        step("quant", side, lambda: L.fp8_quant_1x128(x_bf16, T, s.H, s.H, 0, b.xq, b.xs, side))
+        step("route", st, lambda: self._route(x_bf16, b, seq_len, st))
         if seq_len is not None:
-            self._seq_balance(b, seq_len, alpha, stream)
-        L.fp8_quant_1x128(x_bf16, T, s.H, s.H, 0, b.xq, b.xs, stream)
-        L.moe_permute(b.topk_idx, b.counts, T, s.k, s.E, s.n_shared, b.offsets, b.perm_src,
-                      b.inv_perm, None, None, s.H, None, None, b.perm_ws, b.perm_ws_bytes,
-                      stream)
+            step("seq_balance", st, lambda: self._seq_balance(b, seq_len, alpha, st))
+        step("permute", st, lambda: L.moe_permute(
+            b.topk_idx, b.counts, T, s.k, s.E, s.n_shared, b.offsets, b.perm_src, b.inv_perm,
+            None, None, s.H, None, None, b.perm_ws, b.perm_ws_bytes, st))
+        st.wait_stream(side)
         if keep_gu:
-            L.grouped_fp8_gemm_swiglu_keep(b.xq, b.xs, b.perm_src, self.w_gu, self.w_gu_s,
-                                           b.offsets, s.G, R, s.I, s.H, b.hq, b.hs, b.hgu, stream)
+            step("gate_up", st, lambda: L.grouped_fp8_gemm_swiglu_keep(
+                b.xq, b.xs, b.perm_src, self.w_gu, self.w_gu_s, b.offsets, s.G, R, s.I, s.H,
+                b.hq, b.hs, b.hgu, st))
         else:
-            L.grouped_fp8_gemm_swiglu(b.xq, b.xs, b.perm_src, self.w_gu, self.w_gu_s, b.offsets,
-                                      s.G, R, s.I, s.H, b.hq, b.hs, stream)
-        L.grouped_fp8_gemm(b.hq, b.hs, None, self.w_dn, self.w_dn_s, b.offsets, s.G, R, s.H,
-                           s.I, b.d, stream)
+            step("gate_up", st, lambda: L.grouped_fp8_gemm_swiglu(
+                b.xq, b.xs, b.perm_src, self.w_gu, self.w_gu_s, b.offsets, s.G, R, s.I, s.H,
+                b.hq, b.hs, st))
+        step("down", st, lambda: L.grouped_fp8_gemm(
+            b.hq, b.hs, None, self.w_dn, self.w_dn_s, b.offsets, s.G, R, s.H, s.I, b.d, st))
         shared = b.d[T * s.k:T * s.k + T] if s.n_shared else None
-        L.moe_combine(b.d, b.inv_perm, b.topk_w, shared, T, s.k, s.H, b.y, stream)
+        step("combine", st, lambda: L.moe_combine(b.d, b.inv_perm, b.topk_w, shared, T, s.k,
+                                                  s.H, b.y, st))
         if update_bias:
-            L.moe_bias_update(b.counts, self.bias, s.E, gamma, stream)
+            step("bias", st, lambda: L.moe_bias_update(b.counts, self.bias, s.E, gamma, st))
         return b.y
 
     def requantize_from_fp32(self, gu_fp32, dn_fp32, stream=None):
@@ -412,39 +439,3 @@ class MoELayer:
         L.moe_seq_balance(b.scores, b.score_sums, b.topk_idx, b.T, s.E, s.k, seq_len, alpha,
                           b.seq_f, b.seq_p, b.seq_loss, b.seq_ws, b.seq_ws_bytes, stream)
 
-    def _forward_timed(self, x_bf16, b, stream, update_bias, gamma, events, seq_len, alpha):
-        s = self.shape
-        T, R = x_bf16.shape[0], b.R
-        st = stream if stream is not None else torch.cuda.current_stream()
-
-        def timed(name, fn):
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(st)
-            fn()
-            e1.record(st)
-            events.setdefault(name, []).append((e0, e1))
-
-        timed("route", lambda: self._route(x_bf16, b, seq_len, st))
-        if seq_len is not None:
-            timed("seq_balance", lambda: self._seq_balance(b, seq_len, alpha, st))
-        timed("quant", lambda: L.fp8_quant_1x128(x_bf16, T, s.H, s.H, 0, b.xq, b.xs, st))
-        timed("permute", lambda: L.moe_permute(
-            b.topk_idx, b.counts, T, s.k, s.E, s.n_shared, b.offsets, b.perm_src, b.inv_perm,
-            None, None, s.H, None, None, b.perm_ws, b.perm_ws_bytes, st))
-        if b.gu_kept:
-            timed("gate_up", lambda: L.grouped_fp8_gemm_swiglu_keep(
-                b.xq, b.xs, b.perm_src, self.w_gu, self.w_gu_s, b.offsets, s.G, R, s.I, s.H,
-                b.hq, b.hs, b.hgu, st))
-        else:
-            timed("gate_up", lambda: L.grouped_fp8_gemm_swiglu(
-                b.xq, b.xs, b.perm_src, self.w_gu, self.w_gu_s, b.offsets, s.G, R, s.I, s.H,
-                b.hq, b.hs, st))
-        timed("down", lambda: L.grouped_fp8_gemm(
-            b.hq, b.hs, None, self.w_dn, self.w_dn_s, b.offsets, s.G, R, s.H, s.I, b.d, st))
-        shared = b.d[T * s.k:T * s.k + T] if s.n_shared else None
-        timed("combine", lambda: L.moe_combine(b.d, b.inv_perm, b.topk_w, shared, T, s.k, s.H,
-                                               b.y, st))
-        if update_bias:
-            timed("bias", lambda: L.moe_bias_update(b.counts, self.bias, s.E, gamma, st))
-        return b.y

@@ -309,6 +309,7 @@ __global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
     p[i] = v;
 }
 
+template <bool PF>
 __global__ __launch_bounds__(256) void router_select_kernel(
     const float* __restrict__ part, int KS, int64_t T, const float* __restrict__ bias, int E,
     int n_group, int topk_group, int k, int lpg, int32_t* __restrict__ topk_idx,
@@ -329,12 +330,35 @@ __global__ __launch_bounds__(256) void router_select_kernel(
 #pragma unroll
   for (int i = 0; i < 4; ++i) b[i] = active ? bias[ebase + i] : 0.f;
 
-  for (int64_t t = (int64_t)blockIdx.x * 4 + wv; t < T; t += (int64_t)gridDim.x * 4) {
+  // PF (at most 8 split-K partials): a wave requests its next token's
+  // partials before the current token's selection runs, so their memory
+  // round trip overlaps it; otherwise eight splits at a time are requested
+  // before the first of them is added.  Either way they are added in split
+  // order.
+  const int64_t tstride = (int64_t)gridDim.x * 4;
+  float4 nx[8];
+  auto fetch = [&](int64_t tt) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (u < KS && tt < T && active)
+        nx[u] = *reinterpret_cast<const float4*>(part + ((int64_t)u * T + tt) * E + ebase);
+  };
+  if (PF) fetch((int64_t)blockIdx.x * 4 + wv);
+  for (int64_t t = (int64_t)blockIdx.x * 4 + wv; t < T; t += tstride) {
     float lg[4] = {0.f, 0.f, 0.f, 0.f};
-    if (active) {
-      // the split-K partials, added in split order; eight splits are
-      // requested at a time before the first of them is added (one memory
-      // round trip per eight splits)
+    if (PF) {
+      if (active) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (u < KS) {
+            lg[0] += nx[u].x;
+            lg[1] += nx[u].y;
+            lg[2] += nx[u].z;
+            lg[3] += nx[u].w;
+          }
+      }
+      fetch(t + tstride);
+    } else if (active) {
       for (int k0 = 0; k0 < KS; k0 += 8) {
         float4 pv[8];
 #pragma unroll
@@ -573,10 +597,17 @@ int route_impl(const void* x_bf16, int64_t T, int64_t H, const float* centroids,
                            dim3(256), 0, st>>>(static_cast<const uint16_t*>(x_bf16), T, H,
                                                centroids, E, sp.kper, part);
   }
-  const int64_t sel_blocks = std::min<int64_t>(ceil_div(T, 4), 2048);
-  router_select_kernel<<<dim3((unsigned)sel_blocks), dim3(256), 0, st>>>(
-      part, (int)sp.ks, T, bias, E, n_group, topk_group, k, lpg, topk_idx, topk_w,
-      expert_counts, scores, score_sums);
+  // four tokens per workgroup per round; 1024 workgroups (four per CU at
+  // 96 VGPRs: one round of residency) give a prefetching wave several tokens
+  const int64_t sel_blocks = std::min<int64_t>(ceil_div(T, 4), 1024);
+  if (sp.ks <= 8)
+    router_select_kernel<true><<<dim3((unsigned)sel_blocks), dim3(256), 0, st>>>(
+        part, (int)sp.ks, T, bias, E, n_group, topk_group, k, lpg, topk_idx, topk_w,
+        expert_counts, scores, score_sums);
+  else
+    router_select_kernel<false><<<dim3((unsigned)sel_blocks), dim3(256), 0, st>>>(
+        part, (int)sp.ks, T, bias, E, n_group, topk_group, k, lpg, topk_idx, topk_w,
+        expert_counts, scores, score_sums);
   return check_launch("moe_route");
 }
 

@@ -106,6 +106,21 @@ __device__ __forceinline__ void swiglu_bwd_elem(float g, float u, float d, float
   *h = gs * u;
 }
 
+// The quotients x / s of the quantisers with one division per scale instead
+// of one per element: with y the correctly rounded 1/s, q = x*y lies within
+// an ulp of x/s, the residual x - q*s is exact as one FMA, and q + (x -
+// q*s)*y rounded once is the correctly rounded quotient (Markstein's theorem
+// on division through a correctly rounded reciprocal), so the codes equal
+// those of x / s bit for bit; a zero quotient keeps the sign of x.  This
+// needs y finite and no underflow in the residual wherever a code depends on
+// the quotient (|x/s| >= 2^-10): scales in [2^-90, 2^100] (recip_ok); the
+// quantisers divide for any other scale.
+__device__ __forceinline__ bool recip_ok(float s) { return s >= 0x1p-90f && s <= 0x1p100f; }
+__device__ __forceinline__ float div_recip(float x, float s, float y) {
+  const float q = x * y;
+  return copysignf(fmaf(fmaf(-q, s, x), y, q), q);
+}
+
 // 1x128 E4M3 quantisation of one tile spread over 16 consecutive lanes (lane
 // l % 16 holds elements 8 (l % 16) .. + 7; all 16 lanes must call it
 // together): scale = amax / 448 (1 for an all-zero tile), codes = E4M3 of
@@ -118,6 +133,13 @@ __device__ __forceinline__ uint2 quant_tile_1x128(const float* v, float* scale) 
   amax = wave_max_xor(amax, 16);
   const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
   *scale = s;
+  if (recip_ok(s)) {
+    const float y = 1.0f / s;
+    return make_uint2(f32x4_to_e4m3x4(div_recip(v[0], s, y), div_recip(v[1], s, y),
+                                      div_recip(v[2], s, y), div_recip(v[3], s, y)),
+                      f32x4_to_e4m3x4(div_recip(v[4], s, y), div_recip(v[5], s, y),
+                                      div_recip(v[6], s, y), div_recip(v[7], s, y)));
+  }
   return make_uint2(f32x4_to_e4m3x4(v[0] / s, v[1] / s, v[2] / s, v[3] / s),
                     f32x4_to_e4m3x4(v[4] / s, v[5] / s, v[6] / s, v[7] / s));
 }

@@ -81,10 +81,18 @@ __global__ __launch_bounds__(256) void quant_128x128_kernel(
   __syncthreads();
   amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
-  for (int r = r0; r < 128; r += 8) {
-    const float4 v = *reinterpret_cast<const float4*>(base + (int64_t)r * K + c4);
-    const uint32_t q = f32x4_to_e4m3x4(v.x / s, v.y / s, v.z / s, v.w / s);
-    *reinterpret_cast<uint32_t*>(obase + (int64_t)r * K + c4) = q;
+  auto emit = [&](auto dv) __attribute__((always_inline)) {
+    for (int r = r0; r < 128; r += 8) {
+      const float4 v = *reinterpret_cast<const float4*>(base + (int64_t)r * K + c4);
+      *reinterpret_cast<uint32_t*>(obase + (int64_t)r * K + c4) =
+          f32x4_to_e4m3x4(dv(v.x), dv(v.y), dv(v.z), dv(v.w));
+    }
+  };
+  if (recip_ok(s)) {
+    const float y = 1.0f / s;
+    emit([&](float x) { return div_recip(x, s, y); });
+  } else {
+    emit([&](float x) { return x / s; });
   }
   if (threadIdx.x == 0) scales[(g * (N >> 7) + nb) * nkb + kb] = s;
 }

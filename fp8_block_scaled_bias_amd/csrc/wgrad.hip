@@ -81,14 +81,22 @@ __global__ __launch_bounds__(QT) void quant_128x1_grouped_kernel(
   amax = s_amax[col];
   const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
   uint8_t* dst = out + (L * C + c0 + col) * 128 + 64 * half;
+  auto emit = [&](auto dv) __attribute__((always_inline)) {
 #pragma unroll
-  for (int i = 0; i < 64; i += 16) {
-    uint4 w;
-    w.x = f32x4_to_e4m3x4(v[i] / s, v[i + 1] / s, v[i + 2] / s, v[i + 3] / s);
-    w.y = f32x4_to_e4m3x4(v[i + 4] / s, v[i + 5] / s, v[i + 6] / s, v[i + 7] / s);
-    w.z = f32x4_to_e4m3x4(v[i + 8] / s, v[i + 9] / s, v[i + 10] / s, v[i + 11] / s);
-    w.w = f32x4_to_e4m3x4(v[i + 12] / s, v[i + 13] / s, v[i + 14] / s, v[i + 15] / s);
-    *reinterpret_cast<uint4*>(dst + i) = w;
+    for (int i = 0; i < 64; i += 16) {
+      uint4 w;
+      w.x = f32x4_to_e4m3x4(dv(v[i]), dv(v[i + 1]), dv(v[i + 2]), dv(v[i + 3]));
+      w.y = f32x4_to_e4m3x4(dv(v[i + 4]), dv(v[i + 5]), dv(v[i + 6]), dv(v[i + 7]));
+      w.z = f32x4_to_e4m3x4(dv(v[i + 8]), dv(v[i + 9]), dv(v[i + 10]), dv(v[i + 11]));
+      w.w = f32x4_to_e4m3x4(dv(v[i + 12]), dv(v[i + 13]), dv(v[i + 14]), dv(v[i + 15]));
+      *reinterpret_cast<uint4*>(dst + i) = w;
+    }
+  };
+  if (recip_ok(s)) {
+    const float y = 1.0f / s;
+    emit([&](float x) { return div_recip(x, s, y); });
+  } else {
+    emit([&](float x) { return x / s; });
   }
   if (!half) scales[L * C + c0 + col] = s;
 }
@@ -146,19 +154,27 @@ __global__ __launch_bounds__(QT) void quant_128x1_direct_kernel(
   const float s1 = a1 > 0.0f ? a1 / 448.0f : 1.0f;
   uint8_t* dst0 = out + (L * C + c0 + 2 * lane) * 128 + 32 * w;
   uint8_t* dst1 = dst0 + 128;
+  auto emit = [&](auto d0, auto d1) __attribute__((always_inline)) {
 #pragma unroll
-  for (int i = 0; i < 32; i += 16) {
-    uint4 q0, q1;
-    q0.x = f32x4_to_e4m3x4(v0[i] / s0, v0[i + 1] / s0, v0[i + 2] / s0, v0[i + 3] / s0);
-    q0.y = f32x4_to_e4m3x4(v0[i + 4] / s0, v0[i + 5] / s0, v0[i + 6] / s0, v0[i + 7] / s0);
-    q0.z = f32x4_to_e4m3x4(v0[i + 8] / s0, v0[i + 9] / s0, v0[i + 10] / s0, v0[i + 11] / s0);
-    q0.w = f32x4_to_e4m3x4(v0[i + 12] / s0, v0[i + 13] / s0, v0[i + 14] / s0, v0[i + 15] / s0);
-    q1.x = f32x4_to_e4m3x4(v1[i] / s1, v1[i + 1] / s1, v1[i + 2] / s1, v1[i + 3] / s1);
-    q1.y = f32x4_to_e4m3x4(v1[i + 4] / s1, v1[i + 5] / s1, v1[i + 6] / s1, v1[i + 7] / s1);
-    q1.z = f32x4_to_e4m3x4(v1[i + 8] / s1, v1[i + 9] / s1, v1[i + 10] / s1, v1[i + 11] / s1);
-    q1.w = f32x4_to_e4m3x4(v1[i + 12] / s1, v1[i + 13] / s1, v1[i + 14] / s1, v1[i + 15] / s1);
-    *reinterpret_cast<uint4*>(dst0 + i) = q0;
-    *reinterpret_cast<uint4*>(dst1 + i) = q1;
+    for (int i = 0; i < 32; i += 16) {
+      uint4 q0, q1;
+      q0.x = f32x4_to_e4m3x4(d0(v0[i]), d0(v0[i + 1]), d0(v0[i + 2]), d0(v0[i + 3]));
+      q0.y = f32x4_to_e4m3x4(d0(v0[i + 4]), d0(v0[i + 5]), d0(v0[i + 6]), d0(v0[i + 7]));
+      q0.z = f32x4_to_e4m3x4(d0(v0[i + 8]), d0(v0[i + 9]), d0(v0[i + 10]), d0(v0[i + 11]));
+      q0.w = f32x4_to_e4m3x4(d0(v0[i + 12]), d0(v0[i + 13]), d0(v0[i + 14]), d0(v0[i + 15]));
+      q1.x = f32x4_to_e4m3x4(d1(v1[i]), d1(v1[i + 1]), d1(v1[i + 2]), d1(v1[i + 3]));
+      q1.y = f32x4_to_e4m3x4(d1(v1[i + 4]), d1(v1[i + 5]), d1(v1[i + 6]), d1(v1[i + 7]));
+      q1.z = f32x4_to_e4m3x4(d1(v1[i + 8]), d1(v1[i + 9]), d1(v1[i + 10]), d1(v1[i + 11]));
+      q1.w = f32x4_to_e4m3x4(d1(v1[i + 12]), d1(v1[i + 13]), d1(v1[i + 14]), d1(v1[i + 15]));
+      *reinterpret_cast<uint4*>(dst0 + i) = q0;
+      *reinterpret_cast<uint4*>(dst1 + i) = q1;
+    }
+  };
+  if (recip_ok(s0) && recip_ok(s1)) {
+    const float y0 = 1.0f / s0, y1 = 1.0f / s1;
+    emit([&](float x) { return div_recip(x, s0, y0); }, [&](float x) { return div_recip(x, s1, y1); });
+  } else {
+    emit([&](float x) { return x / s0; }, [&](float x) { return x / s1; });
   }
   if (w == 0) {
     scales[L * C + c0 + 2 * lane] = s0;
@@ -299,8 +315,17 @@ __global__ __launch_bounds__(QT) void swiglu_backward_grouped_kernel(
         const uint32_t b = (j & 1) ? (x[j >> 1] >> 16) : (x[j >> 1] & 0xFFFFu);
         v[i] = bf16_to_f32(b);
       }
-      const uint2 qc = make_uint2(f32x4_to_e4m3x4(v[0] / sc[j], v[1] / sc[j], v[2] / sc[j], v[3] / sc[j]),
-                                  f32x4_to_e4m3x4(v[4] / sc[j], v[5] / sc[j], v[6] / sc[j], v[7] / sc[j]));
+      uint2 qc;
+      if (recip_ok(sc[j])) {
+        const float y = 1.0f / sc[j];
+        qc = make_uint2(f32x4_to_e4m3x4(div_recip(v[0], sc[j], y), div_recip(v[1], sc[j], y),
+                                        div_recip(v[2], sc[j], y), div_recip(v[3], sc[j], y)),
+                        f32x4_to_e4m3x4(div_recip(v[4], sc[j], y), div_recip(v[5], sc[j], y),
+                                        div_recip(v[6], sc[j], y), div_recip(v[7], sc[j], y)));
+      } else {
+        qc = make_uint2(f32x4_to_e4m3x4(v[0] / sc[j], v[1] / sc[j], v[2] / sc[j], v[3] / sc[j]),
+                        f32x4_to_e4m3x4(v[4] / sc[j], v[5] / sc[j], v[6] / sc[j], v[7] / sc[j]));
+      }
       *reinterpret_cast<uint2*>(out + (L * C + cbase + 8 * cg + j) * 128 + row0) = qc;
       if (w == 0 && rs == 0) scl[L * C + cbase + 8 * cg + j] = sc[j];
     }

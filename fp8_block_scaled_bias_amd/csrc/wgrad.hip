@@ -241,7 +241,7 @@ __global__ __launch_bounds__(QT) void swiglu_backward_grouped_kernel(
     pg[i] = make_uint4(og[0], og[1], og[2], og[3]);
     pu[i] = make_uint4(ou[0], ou[1], ou[2], ou[3]);
     ph[i] = make_uint4(oh[0], oh[1], oh[2], oh[3]);
-    if (ok) {
+    if (ok && dgu) {  // the bf16 values are optional (only their codes feed the GEMMs)
       *reinterpret_cast<uint4*>(dgu + r * I2 + col) = pg[i];
       *reinterpret_cast<uint4*>(dgu + r * I2 + I + col) = pu[i];
       *reinterpret_cast<uint4*>(h + r * I + col) = ph[i];
@@ -560,9 +560,11 @@ extern "C" int swiglu_backward_grouped(const void* gu_bf16, const void* dh_bf16,
   MOE_INVALID(chunks_cap >= chunks_needed(M_total, G),
               "swiglu_backward_grouped: chunks_cap=%lld < ceil(M_total/128) + G = %lld",
               (long long)chunks_cap, (long long)chunks_needed(M_total, G));
-  MOE_INVALID(gu_bf16 && dh_bf16 && group_offsets && dgu_bf16 && h_bf16 && dgu_e4m3 && dgu_scale &&
-                  dgu_c && dgu_scale_c && h_c && h_scale_c,
+  MOE_INVALID(gu_bf16 && dh_bf16 && group_offsets && dgu_e4m3 && dgu_scale && dgu_c &&
+                  dgu_scale_c && h_c && h_scale_c,
               "swiglu_backward_grouped: null pointer");
+  MOE_INVALID((dgu_bf16 == nullptr) == (h_bf16 == nullptr),
+              "swiglu_backward_grouped: dgu_bf16 and h_bf16 are given together or not at all");
   MOE_INVALID(((uintptr_t)gu_bf16 & 15) == 0 && ((uintptr_t)dh_bf16 & 15) == 0 &&
                   ((uintptr_t)dgu_bf16 & 15) == 0 && ((uintptr_t)h_bf16 & 15) == 0 &&
                   ((uintptr_t)dgu_e4m3 & 15) == 0 && ((uintptr_t)dgu_c & 15) == 0 &&

@@ -141,6 +141,15 @@ class BackwardBuffers:
             self.dense_ws = torch.empty((self.dense_ws_bytes,), dtype=torch.uint8, device=self._dev)
         return self
 
+    def intermediates(self):
+        """Allocate the bf16 dGU [R, 2I] and h [R, I] that a backward with
+        keep_intermediates writes (the GEMMs read only their FP8 codes)."""
+        if self.dgu is None:
+            I = self._shape.I
+            self.dgu = torch.empty((self.R, 2 * I), dtype=torch.bfloat16, device=self._dev)
+            self.h = torch.empty((self.R, I), dtype=torch.bfloat16, device=self._dev)
+        return self
+
     def __init__(self, shape: LayerShape, T: int, device="cuda"):
         s = shape
         R = T * s.k + s.n_shared * T
@@ -154,8 +163,7 @@ class BackwardBuffers:
         self.dDs = torch.empty((R, H // 128), dtype=f32, device=dev)
         self.dh = torch.empty((R, I), dtype=bf, device=dev)
         self.gu = torch.empty((R, 2 * I), dtype=bf, device=dev)
-        self.dgu = torch.empty((R, 2 * I), dtype=bf, device=dev)
-        self.h = torch.empty((R, I), dtype=bf, device=dev)
+        self.dgu = self.h = None   # bf16 dGU and h: only with keep_intermediates
         self.dguq = torch.empty((R, 2 * I), dtype=u8, device=dev)
         self.dgus = torch.empty((R, 2 * I // 128), dtype=f32, device=dev)
         self.dxp = torch.empty((R, H), dtype=bf, device=dev)
@@ -342,7 +350,8 @@ class MoELayer:
 
     def backward(self, dy_bf16: torch.Tensor, x_bf16: torch.Tensor, bufs: Buffers | None = None,
                  bwd: BackwardBuffers | None = None, stream=None, events: dict | None = None,
-                 seq_len: int | None = None, alpha: float = 0.0001):
+                 seq_len: int | None = None, alpha: float = 0.0001,
+                 keep_intermediates: bool = False):
         """Backward of the layer for the output gradient dy, after a forward of
         x on `bufs` (its routing, permutation, quantised x and D).  With
         seq_len (the forward's, which left the scores and f in `bufs`), the
@@ -352,6 +361,8 @@ class MoELayer:
         bufs.hgu; otherwise the gate+up GEMM runs again (into bwd.gu).
         Returns the BackwardBuffers: dx_total (the input gradient), dx (its
         expert-path part), dw (gate weights), dC (centroids), dW_gu, dW_dn.
+        keep_intermediates: also write the bf16 dGU and h (bwd.dgu, bwd.h),
+        which the step itself does not need (its GEMMs read their codes).
         `events` as in forward, keys "combine_bwd", "dgrad_down",
         "recompute_gate_up", "swiglu_bwd", "dgrad_gate_up", "unpermute",
         "wgrad_down", "wgrad_gate_up", "router_bwd"."""
@@ -359,6 +370,8 @@ class MoELayer:
         T = dy_bf16.shape[0]
         b = bufs or self.buffers(T)
         bb = bwd or self.backward_buffers(T)
+        if keep_intermediates:
+            bb.intermediates()
         R, G, H, I, k, cap = b.R, s.G, s.H, s.I, s.k, bb.cap
         st = stream if stream is not None else torch.cuda.current_stream()
 
@@ -390,7 +403,8 @@ class MoELayer:
         # the SwiGLU backward also writes dGU's 1x128 codes and the 128x1 chunk
         # codes of dGU and h that the input and weight gradients read
         step("swiglu_bwd", lambda: L.swiglu_backward_grouped(
-            gu, bb.dh, b.offsets, G, R, I, bb.dgu, bb.h, bb.dguq, bb.dgus, cap, bb.c_dgu,
+            gu, bb.dh, b.offsets, G, R, I, bb.dgu if keep_intermediates else None,
+            bb.h if keep_intermediates else None, bb.dguq, bb.dgus, cap, bb.c_dgu,
             bb.s_dgu, bb.c_h, bb.s_h, st))
         step("dgrad_gate_up", lambda: L.grouped_fp8_gemm_dgrad(
             bb.dguq, bb.dgus, self.w_gu, self.w_gu_s, b.offsets, G, R, 2 * I, H, bb.dxp, st))

@@ -359,7 +359,8 @@ int swiglu_backward(const void* gu_bf16, const void* dh_bf16, int64_t M, int64_t
  * GEMMs read, from the stored bf16 values, in the same pass (news.qq.com
  * article, section FP8 低精度训练 › 细粒度量化; section 工程 › DualPipe
  * 流水线并行: backward-for-input and backward-for-weights chunks):
- *   dgu_bf16, h_bf16 (out): as swiglu_backward, bit for bit;
+ *   dgu_bf16, h_bf16 (out, optional: both NULL to skip them): as
+ *     swiglu_backward, bit for bit (the codes below do not depend on them);
  *   dgu_e4m3 [M_total, 2I], dgu_scale [M_total, 2I/128] (out): what
  *     fp8_quant_1x128 mode 0 writes for dgu_bf16;
  *   dgu_c, dgu_scale_c (out, C = 2I) and h_c, h_scale_c (out, C = I): what

@@ -108,14 +108,16 @@ def test_backward_elementwise_validation():
     assert "I % 128" in L.last_error()
     assert rc("moe_combine_backward", FAKE, FAKE, FAKE, ctypes.c_void_p(8192), 4, 2, 136, 1, FAKE, FAKE,
               FAKE, FAKE, None) == L.MOE_ERR_INVALID and "H % 128" in L.last_error()
-    def sg(G=2, M_=300, I=256, cap=100, out=FAKE):
-        return rc("swiglu_backward_grouped", FAKE, FAKE, FAKE, G, M_, I, out, FAKE, FAKE, FAKE, cap,
+    def sg(G=2, M_=300, I=256, cap=100, out=FAKE, codes=FAKE):
+        return rc("swiglu_backward_grouped", FAKE, FAKE, FAKE, G, M_, I, out, FAKE, codes, FAKE, cap,
                   FAKE, FAKE, FAKE, FAKE, None)
     assert sg(I=200) == L.MOE_ERR_INVALID and "I=200" in L.last_error()
     assert sg(G=0) == L.MOE_ERR_INVALID
     assert sg(G=2000) == L.MOE_ERR_UNSUPPORTED
     assert sg(cap=3) == L.MOE_ERR_INVALID and "chunks_cap" in L.last_error()
-    assert sg(out=None) == L.MOE_ERR_INVALID and "null" in L.last_error()
+    assert sg(codes=None) == L.MOE_ERR_INVALID and "null" in L.last_error()
+    # the bf16 dGU and h are optional, but only together
+    assert sg(out=None) == L.MOE_ERR_INVALID and "together" in L.last_error()
     assert sg(out=ctypes.c_void_p(4104)) == L.MOE_ERR_INVALID and "aligned" in L.last_error()
     assert sg(M_=0, out=None) == L.MOE_OK
     assert g(M=0, out=None) == L.MOE_OK

@@ -173,6 +173,12 @@ def test_swiglu_backward_grouped_equals_unfused(sizes, I):
         qo, so = OQ.quant_128x1_grouped(bf16_values_host(ref).astype(np.float32), offs)
         ql, sl = _to_logical(host(c), host(sc), qo.shape[1] // 128)
         assert np.array_equal(ql, qo) and np.array_equal(sl, so)
+    # without the optional bf16 outputs: the same codes and scales
+    q3, qs3 = torch.empty_like(q), torch.empty_like(qs)
+    cg3, sg3, ch3, sh3 = (torch.zeros_like(t) for t in (cg, sg, ch, sh))
+    M.swiglu_backward_grouped(gub, dhb, offs_d, G, Mt, I, None, None, q3, qs3, cap, cg3, sg3, ch3, sh3)
+    assert torch.equal(q3, q) and torch.equal(qs3, qs)
+    assert torch.equal(cg3, cg) and torch.equal(sg3, sg) and torch.equal(ch3, ch) and torch.equal(sh3, sh)
 
 
 def _expert_rows(idx, E):
@@ -350,7 +356,7 @@ def test_layer_backward_small(name):
     x_d = bf16_dev(x)
     layer.forward(x_d)
     bufs = layer.buffers(T)
-    bb = layer.backward(bf16_dev(dy), x_d)
+    bb = layer.backward(bf16_dev(dy), x_d, keep_intermediates=True)
     torch.cuda.synchronize()
     wts = oracle_weights(cfg)
     fwd = OL.layer(x, C, b, wts, cfg.n_group, cfg.topk_group, k, I)

@@ -28,9 +28,9 @@ SIGNATURES = {
     "moe_version": (ctypes.c_char_p, []),
     "moe_route_workspace_bytes": (_sz, [_i64, _i64, _i32]),
     "moe_route": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _i32, _i32, _i32, _i32,
-                                 _vp, _vp, _vp, _vp, _sz, _vp]),
+                                 _vp, _vp, _vp, _vp, _sz, _vp, _vp]),
     "moe_route_scores": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _i32, _i32, _i32, _i32,
-                                        _vp, _vp, _vp, _vp, _sz, _vp, _vp, _vp]),
+                                        _vp, _vp, _vp, _vp, _sz, _vp, _vp, _vp, _vp]),
     "moe_seq_balance_workspace_bytes": (_sz, [_i64, _i32, _i64]),
     "moe_seq_balance": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i32, _i32, _i64, _f32, _vp, _vp, _vp,
                                        _vp, _sz, _vp]),
@@ -51,7 +51,7 @@ SIGNATURES = {
     "swiglu_backward_grouped": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i64, _i64, _vp, _vp, _vp,
                                                _vp, _i64, _vp, _vp, _vp, _vp, _vp]),
     "moe_router_backward": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i32, _i32,
-                                           _vp, _vp, _vp]),
+                                           _vp, _vp, _vp, _vp]),
     "moe_router_dcentroids": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp]),
     "moe_router_backward_dense_workspace_bytes": (_sz, [_i64, _i64, _i32]),
     "moe_router_backward_dense": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i32,
@@ -151,17 +151,20 @@ def moe_permute_workspace_bytes(T, k, E) -> int:
 
 
 def moe_route(x_bf16, T, H, centroids, bias, E, n_group, topk_group, k,
-              topk_idx, topk_w, expert_counts, workspace, workspace_bytes, stream=None):
+              topk_idx, topk_w, expert_counts, workspace, workspace_bytes, stream=None, *,
+              topk_s=None):
     return _call("moe_route", _dev(x_bf16), T, H, _dev(centroids), _dev(bias), E, n_group,
                  topk_group, k, _dev(topk_idx), _dev(topk_w), _dev(expert_counts),
-                 _dev(workspace), workspace_bytes, _stream(stream))
+                 _dev(workspace), workspace_bytes, _dev(topk_s), _stream(stream))
 
 
 def moe_route_scores(x_bf16, T, H, centroids, bias, E, n_group, topk_group, k, topk_idx, topk_w,
-                     expert_counts, workspace, workspace_bytes, scores, score_sums, stream=None):
+                     expert_counts, workspace, workspace_bytes, scores, score_sums, stream=None, *,
+                     topk_s=None):
     return _call("moe_route_scores", _dev(x_bf16), T, H, _dev(centroids), _dev(bias), E, n_group,
                  topk_group, k, _dev(topk_idx), _dev(topk_w), _dev(expert_counts),
-                 _dev(workspace), workspace_bytes, _dev(scores), _dev(score_sums), _stream(stream))
+                 _dev(workspace), workspace_bytes, _dev(scores), _dev(score_sums), _dev(topk_s),
+                 _stream(stream))
 
 
 def moe_seq_balance_workspace_bytes(T, E, seq_len) -> int:
@@ -230,10 +233,10 @@ def moe_combine_backward(dy_bf16, inv_perm, topk_w, expert_out_bf16, T, k, H, n_
 
 
 def moe_router_backward(x_bf16, centroids, topk_idx, d_topk_w, inv_perm, dx_in_bf16, T, H, E, k,
-                        dx_out_bf16, dlogit_rows, stream=None):
+                        dx_out_bf16, dlogit_rows, stream=None, *, topk_s=None):
     return _call("moe_router_backward", _dev(x_bf16), _dev(centroids), _dev(topk_idx),
                  _dev(d_topk_w), _dev(inv_perm), _dev(dx_in_bf16), T, H, E, k, _dev(dx_out_bf16),
-                 _dev(dlogit_rows), _stream(stream))
+                 _dev(dlogit_rows), _dev(topk_s), _stream(stream))
 
 
 def moe_router_dcentroids(x_bf16, perm_src, group_offsets, dlogit_rows, T, H, E, d_centroids,

@@ -221,7 +221,8 @@ __global__ __launch_bounds__(RB) void router_backward_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ C, const int32_t* __restrict__ idx,
     const float* __restrict__ dw, const int32_t* __restrict__ inv_perm,
     const uint16_t* __restrict__ dx_in, int64_t T, int64_t H, int E, int k,
-    uint16_t* __restrict__ dx_out, float* __restrict__ dlogit_rows) {
+    uint16_t* __restrict__ dx_out, float* __restrict__ dlogit_rows,
+    const float* __restrict__ topk_s) {
   __shared__ float s_part[RB / 64][KMAX];
   __shared__ float s_dl[KMAX];
   const int64_t t = blockIdx.x;
@@ -235,7 +236,8 @@ __global__ __launch_bounds__(RB) void router_backward_kernel(
     dot[j] = 0.0f;
   }
   const uint16_t* xr = x + t * H;
-  for (int64_t c = (int64_t)tid * 8; c < H; c += RB * 8) {
+  // without the forward's scores, the selected experts' logits again
+  for (int64_t c = topk_s ? H : (int64_t)tid * 8; c < H; c += RB * 8) {
     float xv[8];
     bf16x8_to_f32(*reinterpret_cast<const uint4*>(xr + c), xv);
 #pragma unroll
@@ -261,8 +263,12 @@ __global__ __launch_bounds__(RB) void router_backward_kernel(
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
       if (j >= k) break;
-      const float l = (s_part[0][j] + s_part[1][j]) + (s_part[2][j] + s_part[3][j]);
-      s[j] = 1.0f / (1.0f + expf(-l));
+      if (topk_s) {
+        s[j] = topk_s[t * k + j];
+      } else {
+        const float l = (s_part[0][j] + s_part[1][j]) + (s_part[2][j] + s_part[3][j]);
+        s[j] = 1.0f / (1.0f + expf(-l));
+      }
       S += s[j];
     }
     float m = 0.0f;
@@ -341,7 +347,7 @@ extern "C" int moe_router_backward(const void* x_bf16, const float* centroids,
                                    const int32_t* topk_idx, const float* d_topk_w,
                                    const int32_t* inv_perm, const void* dx_in_bf16, int64_t T,
                                    int64_t H, int32_t E, int32_t k, void* dx_out_bf16,
-                                   float* dlogit_rows, void* stream) {
+                                   float* dlogit_rows, const float* topk_s, void* stream) {
   clear_error();
   MOE_INVALID(T >= 0 && T < (1ll << 31), "moe_router_backward: T=%lld out of range", (long long)T);
   MOE_INVALID(k >= 1 && k <= 8, "moe_router_backward: k=%d must be in [1, 8]", (int)k);
@@ -354,10 +360,11 @@ extern "C" int moe_router_backward(const void* x_bf16, const float* centroids,
   MOE_INVALID(((uintptr_t)x_bf16 & 15) == 0 && ((uintptr_t)centroids & 15) == 0 &&
                   ((uintptr_t)dx_out_bf16 & 15) == 0 && ((uintptr_t)dx_in_bf16 & 15) == 0,
               "moe_router_backward: x, centroids, dx_in and dx_out must be 16-byte aligned");
+  MOE_INVALID(((uintptr_t)topk_s & 3) == 0, "moe_router_backward: topk_s must be 4-byte aligned");
   router_backward_kernel<8><<<dim3((unsigned)T), dim3(RB), 0, as_stream(stream)>>>(
       static_cast<const uint16_t*>(x_bf16), centroids, topk_idx, d_topk_w, inv_perm,
       static_cast<const uint16_t*>(dx_in_bf16), T, H, E, k, static_cast<uint16_t*>(dx_out_bf16),
-      dlogit_rows);
+      dlogit_rows, topk_s);
   return check_launch("moe_router_backward");
 }
 

@@ -314,7 +314,8 @@ __global__ __launch_bounds__(256) void router_select_kernel(
     const float* __restrict__ part, int KS, int64_t T, const float* __restrict__ bias, int E,
     int n_group, int topk_group, int k, int lpg, int32_t* __restrict__ topk_idx,
     float* __restrict__ topk_w, int32_t* __restrict__ counts, float* __restrict__ scores,
-    float* __restrict__ score_sums) {
+    float* __restrict__ score_sums,
+    float* __restrict__ topk_s) {
   __shared__ int hist[256];
   __shared__ int s_sel_e[4][8];    // per wave: the token's selection in expert order
   __shared__ float s_sel_s[4][8];
@@ -470,6 +471,7 @@ __global__ __launch_bounds__(256) void router_select_kernel(
     if (lane < k) {
       topk_idx[t * k + lane] = my_e;
       topk_w[t * k + lane] = my_s / sum;
+      if (topk_s) topk_s[t * k + lane] = my_s;
       atomicAdd(&hist[my_e], 1);
     }
   }
@@ -548,7 +550,8 @@ namespace {
 int route_impl(const void* x_bf16, int64_t T, int64_t H, const float* centroids,
                const float* bias, int32_t E, int32_t n_group, int32_t topk_group, int32_t k,
                int32_t* topk_idx, float* topk_w, int32_t* expert_counts, void* workspace,
-               size_t workspace_bytes, float* scores, float* score_sums, void* stream) {
+               size_t workspace_bytes, float* scores, float* score_sums, float* topk_s,
+               void* stream) {
   MOE_INVALID(T >= 0, "moe_route: T=%lld < 0", (long long)T);
   MOE_INVALID(H > 0 && H % 128 == 0, "moe_route: H=%lld must be a positive multiple of 128",
               (long long)H);
@@ -573,6 +576,7 @@ int route_impl(const void* x_bf16, int64_t T, int64_t H, const float* centroids,
     return check_launch("moe_route(fill)");
   }
   MOE_INVALID(x_bf16 && centroids && bias && topk_idx && topk_w, "moe_route: null pointer");
+  MOE_INVALID(((uintptr_t)topk_s & 3) == 0, "moe_route: topk_s must be 4-byte aligned");
   MOE_INVALID(((uintptr_t)x_bf16 & 15) == 0 && ((uintptr_t)centroids & 15) == 0,
               "moe_route: x and centroids must be 16-byte aligned");
   const size_t need = moe_route_workspace_bytes(T, H, E);
@@ -603,11 +607,11 @@ int route_impl(const void* x_bf16, int64_t T, int64_t H, const float* centroids,
   if (sp.ks <= 8)
     router_select_kernel<true><<<dim3((unsigned)sel_blocks), dim3(256), 0, st>>>(
         part, (int)sp.ks, T, bias, E, n_group, topk_group, k, lpg, topk_idx, topk_w,
-        expert_counts, scores, score_sums);
+        expert_counts, scores, score_sums, topk_s);
   else
     router_select_kernel<false><<<dim3((unsigned)sel_blocks), dim3(256), 0, st>>>(
         part, (int)sp.ks, T, bias, E, n_group, topk_group, k, lpg, topk_idx, topk_w,
-        expert_counts, scores, score_sums);
+        expert_counts, scores, score_sums, topk_s);
   return check_launch("moe_route");
 }
 
@@ -616,10 +620,10 @@ int route_impl(const void* x_bf16, int64_t T, int64_t H, const float* centroids,
 extern "C" int moe_route(const void* x_bf16, int64_t T, int64_t H, const float* centroids,
                          const float* bias, int32_t E, int32_t n_group, int32_t topk_group,
                          int32_t k, int32_t* topk_idx, float* topk_w, int32_t* expert_counts,
-                         void* workspace, size_t workspace_bytes, void* stream) {
+                         void* workspace, size_t workspace_bytes, float* topk_s, void* stream) {
   clear_error();
   return route_impl(x_bf16, T, H, centroids, bias, E, n_group, topk_group, k, topk_idx, topk_w,
-                    expert_counts, workspace, workspace_bytes, nullptr, nullptr, stream);
+                    expert_counts, workspace, workspace_bytes, nullptr, nullptr, topk_s, stream);
 }
 
 extern "C" int moe_route_scores(const void* x_bf16, int64_t T, int64_t H,
@@ -627,12 +631,12 @@ extern "C" int moe_route_scores(const void* x_bf16, int64_t T, int64_t H,
                                 int32_t n_group, int32_t topk_group, int32_t k,
                                 int32_t* topk_idx, float* topk_w, int32_t* expert_counts,
                                 void* workspace, size_t workspace_bytes, float* scores,
-                                float* score_sums, void* stream) {
+                                float* score_sums, float* topk_s, void* stream) {
   clear_error();
   MOE_INVALID(T == 0 || (scores && score_sums), "moe_route_scores: scores or score_sums is null");
   MOE_INVALID(((uintptr_t)scores & 15) == 0, "moe_route_scores: scores must be 16-byte aligned");
   return route_impl(x_bf16, T, H, centroids, bias, E, n_group, topk_group, k, topk_idx, topk_w,
-                    expert_counts, workspace, workspace_bytes, scores, score_sums, stream);
+                    expert_counts, workspace, workspace_bytes, scores, score_sums, topk_s, stream);
 }
 
 extern "C" int moe_bias_update(const int32_t* expert_counts, float* bias, int32_t E, float gamma,

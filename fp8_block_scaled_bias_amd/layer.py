@@ -82,6 +82,7 @@ class Buffers:
         self.T, self.R = T, R
         self.topk_idx = torch.empty((T, s.k), dtype=i32, device=dev)
         self.topk_w = torch.empty((T, s.k), dtype=f32, device=dev)
+        self.topk_s = torch.empty((T, s.k), dtype=f32, device=dev)   # the chosen experts' scores
         self.counts = torch.empty((s.E,), dtype=i32, device=dev)
         self.route_ws_bytes = max(16, L.moe_route_workspace_bytes(T, s.H, s.E))
         self.route_ws = torch.empty((self.route_ws_bytes,), dtype=u8, device=dev)
@@ -423,7 +424,8 @@ class MoELayer:
         if seq_len is None:
             step("router_bwd", lambda: (
                 L.moe_router_backward(x_bf16, self.centroids, b.topk_idx, bb.dw, b.inv_perm, bb.dx,
-                                      T, H, s.E, k, bb.dx_total, bb.dlogit_rows, st),
+                                      T, H, s.E, k, bb.dx_total, bb.dlogit_rows, st,
+                                      topk_s=b.topk_s),
                 L.moe_router_dcentroids(x_bf16, b.perm_src, b.offsets, bb.dlogit_rows, T, H, s.E,
                                         bb.dC, st)))
         else:
@@ -441,12 +443,13 @@ class MoELayer:
         T = x_bf16.shape[0]
         if seq_len is None:
             L.moe_route(x_bf16, T, s.H, self.centroids, self.bias, s.E, s.n_group, s.topk_group,
-                        s.k, b.topk_idx, b.topk_w, b.counts, b.route_ws, b.route_ws_bytes, stream)
+                        s.k, b.topk_idx, b.topk_w, b.counts, b.route_ws, b.route_ws_bytes, stream,
+                        topk_s=b.topk_s)
         else:
             b.balance(seq_len)
             L.moe_route_scores(x_bf16, T, s.H, self.centroids, self.bias, s.E, s.n_group,
                                s.topk_group, s.k, b.topk_idx, b.topk_w, b.counts, b.route_ws,
-                               b.route_ws_bytes, b.scores, b.score_sums, stream)
+                               b.route_ws_bytes, b.scores, b.score_sums, stream, topk_s=b.topk_s)
 
     def _seq_balance(self, b, seq_len, alpha, stream):
         s = self.shape

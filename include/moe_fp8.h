@@ -83,6 +83,10 @@ const char* moe_version(void);
  * expert_counts (out) [E] int32
  * workspace       device scratch of at least moe_route_workspace_bytes(T, H, E)
  *                 bytes (partial logits); contents on entry are ignored.
+ * topk_s    (out, optional: NULL skips it) [T, k] fp32, 4-byte aligned: the
+ *                 unbiased scores s[e_j] of the chosen experts (w[j] times
+ *                 their sum), which moe_router_backward can take instead of
+ *                 computing the logits again.
  * Requirements: H % 128 == 0; 2 <= E <= 256; E % n_group == 0; the group
  * size E/n_group is 4 times a power of two (4 .. 256); 1 <= topk_group <=
  * n_group; 1 <= k <= 8; k <= topk_group * E / n_group.
@@ -92,7 +96,7 @@ int moe_route(const void* x_bf16, int64_t T, int64_t H,
               const float* centroids, const float* bias,
               int32_t E, int32_t n_group, int32_t topk_group, int32_t k,
               int32_t* topk_idx, float* topk_w, int32_t* expert_counts,
-              void* workspace, size_t workspace_bytes, void* stream);
+              void* workspace, size_t workspace_bytes, float* topk_s, void* stream);
 
 /*
  * moe_route_scores - moe_route that also writes what the sequence-wise
@@ -106,7 +110,7 @@ int moe_route_scores(const void* x_bf16, int64_t T, int64_t H,
                      int32_t E, int32_t n_group, int32_t topk_group, int32_t k,
                      int32_t* topk_idx, float* topk_w, int32_t* expert_counts,
                      void* workspace, size_t workspace_bytes, float* scores,
-                     float* score_sums, void* stream);
+                     float* score_sums, float* topk_s, void* stream);
 
 /*
  * moe_seq_balance - sequence-wise balance statistic (news.qq.com article,
@@ -385,8 +389,9 @@ int swiglu_backward_grouped(const void* gu_bf16, const void* dh_bf16,
  * section FP8 低精度训练 - the gating stays in FP32).
  *
  * For token t with selected experts e_j = topk_idx[t, j] and the unbiased
- * scores s_j = sigmoid(x[t] . C[e_j]) recomputed here in fp32 (S = sum_j s_j,
- * w_j = s_j / S, the forward's gate weights):
+ * scores s_j = sigmoid(x[t] . C[e_j]) - the forward's (topk_s as moe_route
+ * wrote it), or recomputed here in fp32 when topk_s is NULL - (S = sum_j
+ * s_j in slot order, w_j = s_j / S, the forward's gate weights):
  *   dlogit_j = (dw_j - sum_i dw_i w_i) / S * s_j * (1 - s_j)
  *   dx_out[t, :] = bf16( dx_in[t, :] + sum_j dlogit_j * C[e_j, :] )   (fp32 sums)
  *   dlogit_rows[inv_perm[t*k + j]] = dlogit_j   (expert-row order, for the
@@ -401,7 +406,7 @@ int swiglu_backward_grouped(const void* gu_bf16, const void* dh_bf16,
 int moe_router_backward(const void* x_bf16, const float* centroids, const int32_t* topk_idx,
                         const float* d_topk_w, const int32_t* inv_perm, const void* dx_in_bf16,
                         int64_t T, int64_t H, int32_t E, int32_t k, void* dx_out_bf16,
-                        float* dlogit_rows, void* stream);
+                        float* dlogit_rows, const float* topk_s, void* stream);
 
 /*
  * moe_router_dcentroids - gradient of the router centroids (same sections):

@@ -121,11 +121,13 @@ def test_backward_elementwise_validation():
     assert sg(out=ctypes.c_void_p(4104)) == L.MOE_ERR_INVALID and "aligned" in L.last_error()
     assert sg(M_=0, out=None) == L.MOE_OK
     assert g(M=0, out=None) == L.MOE_OK
-    def r(T=4, H=256, E=16, k=4, dx=FAKE):
-        return rc("moe_router_backward", FAKE, FAKE, FAKE, FAKE, FAKE, None, T, H, E, k, dx, FAKE, None)
+    def r(T=4, H=256, E=16, k=4, dx=FAKE, ts=None):
+        return rc("moe_router_backward", FAKE, FAKE, FAKE, FAKE, FAKE, None, T, H, E, k, dx, FAKE, ts,
+                  None)
     assert r(k=9) == L.MOE_ERR_INVALID and r(E=2) == L.MOE_ERR_INVALID
     assert r(H=100) == L.MOE_ERR_INVALID and r(dx=None) == L.MOE_ERR_INVALID
     assert r(dx=ctypes.c_void_p(4104)) == L.MOE_ERR_INVALID and "aligned" in L.last_error()
+    assert r(ts=ctypes.c_void_p(4098)) == L.MOE_ERR_INVALID and "topk_s" in L.last_error()
     assert r(T=0, dx=None) == L.MOE_OK
     def d(E=16, H=256, out=FAKE):
         return rc("moe_router_dcentroids", FAKE, FAKE, FAKE, FAKE, 4, H, E, out, None)
@@ -150,8 +152,9 @@ def test_gemm_validation():
 
 
 def test_route_validation():
-    def f(T=64, H=256, E=16, ng=4, tg=2, k=4, ws=FAKE, wsb=1 << 30):
-        return rc("moe_route", FAKE, T, H, FAKE, FAKE, E, ng, tg, k, FAKE, FAKE, FAKE, ws, wsb, None)
+    def f(T=64, H=256, E=16, ng=4, tg=2, k=4, ws=FAKE, wsb=1 << 30, ts=None):
+        return rc("moe_route", FAKE, T, H, FAKE, FAKE, E, ng, tg, k, FAKE, FAKE, FAKE, ws, wsb, ts,
+                  None)
     assert f(H=200) == L.MOE_ERR_INVALID
     assert f(E=18, ng=4) == L.MOE_ERR_INVALID and "n_group" in L.last_error()
     assert f(tg=5) == L.MOE_ERR_INVALID
@@ -162,12 +165,13 @@ def test_route_validation():
     assert f(E=16, ng=16, tg=2, k=2) == L.MOE_ERR_INVALID      # group size 1: no top-2 sum
     assert f(wsb=16) == L.MOE_ERR_WORKSPACE
     assert f(ws=None) == L.MOE_ERR_WORKSPACE
+    assert f(ts=ctypes.c_void_p(4098)) == L.MOE_ERR_INVALID and "topk_s" in L.last_error()
 
 
 def test_route_scores_and_seq_balance_validation():
     def r(T=64, sc=FAKE, ss=FAKE, k=4):
         return rc("moe_route_scores", FAKE, T, 256, FAKE, FAKE, 16, 4, 2, k, FAKE, FAKE, FAKE, FAKE,
-                  1 << 30, sc, ss, None)
+                  1 << 30, sc, ss, None, None)
     assert r(sc=None) == L.MOE_ERR_INVALID and "scores" in L.last_error()
     assert r(ss=None) == L.MOE_ERR_INVALID
     assert r(sc=ctypes.c_void_p(4100)) == L.MOE_ERR_INVALID and "aligned" in L.last_error()
@@ -217,7 +221,7 @@ def test_swiglu_keep_validation():
 def test_route_group_size_two_is_valid_shape():
     # E=16 in 8 groups has group size 2: valid, but 2 is not 4 * 2^n
     assert rc("moe_route", FAKE, 8, 256, FAKE, FAKE, 16, 8, 2, 4, FAKE, FAKE, FAKE, FAKE, 1 << 30,
-              None) == L.MOE_ERR_UNSUPPORTED
+              None, None) == L.MOE_ERR_UNSUPPORTED
 
 
 def test_permute_and_combine_and_bias_validation():

@@ -158,18 +158,24 @@ def test_e4m3_conversion_every_boundary():
 # ------------------------------------------------------------------- router
 def _route_gpu(bits, C, b, E, ng, tg, k):
     T, H = bits.shape
-    idx, w, cnt = _i32((T, k)), _f32((T, k)), _i32((E,))
+    idx, w, cnt, ts = _i32((T, k)), _f32((T, k)), _i32((E,)), _f32((T, k))
     wsb = max(16, M.moe_route_workspace_bytes(T, H, E))
     ws = _u8((wsb,))
-    M.moe_route(bf16_dev(bits), T, H, dev(C), dev(b), E, ng, tg, k, idx, w, cnt, ws, wsb)
-    return host(idx), host(w), host(cnt)
+    M.moe_route(bf16_dev(bits), T, H, dev(C), dev(b), E, ng, tg, k, idx, w, cnt, ws, wsb, topk_s=ts)
+    ts = host(ts)
+    # the weights are the chosen scores over their fp32 sum in slot order
+    S = ts[:, 0].copy()
+    for j in range(1, k):
+        S = (S + ts[:, j]).astype(np.float32)
+    assert np.array_equal(host(w), (ts / S[:, None]).astype(np.float32))
+    return host(idx), host(w), host(cnt), ts
 
 
 def _check_route(cfg, T, seed, label):
     bits = synth.gen_x(cfg, seed=seed, T=T)
     C = synth.gen_centroids(cfg, seed=seed)
     b = synth.gen_bias(cfg, seed=seed)
-    idx, w, cnt = _route_gpu(bits, C, b, cfg.E, cfg.n_group, cfg.topk_group, cfg.k)
+    idx, w, cnt, ts = _route_gpu(bits, C, b, cfg.E, cfg.n_group, cfg.topk_group, cfg.k)
     ora = OR.route(bits, C, b, cfg.n_group, cfg.topk_group, cfg.k)
     mism = compare_routes(idx, ora, label)
     ok = np.setdiff1d(np.arange(T), mism)
@@ -180,6 +186,9 @@ def _check_route(cfg, T, seed, label):
     rel = err / ora["w"][ok]
     log(f"[route] {label}: max |w_gpu - w_oracle| = {err.max():.3e}, relative {rel.max():.3e}")
     assert rel.max() <= 1e-6
+    # the chosen experts' unbiased scores (topk_s) to the same bar
+    s_ref = np.take_along_axis(ora["s"][ok], idx[ok].astype(np.int64), axis=1)
+    assert (np.abs(ts[ok].astype(np.float64) - s_ref) / s_ref).max() <= 1e-6
     assert np.array_equal(cnt, np.bincount(idx.ravel(), minlength=cfg.E))
     if len(mism) == 0:
         assert np.array_equal(cnt, ora["counts"])
@@ -215,7 +224,7 @@ def test_route_hand_traced_ties():
         H = 256
         bits = np.zeros((70, H), np.uint16)
         C = synth.gen_centroids(synth.TINY.with_(E=E, H=H))
-        idx, w, cnt = _route_gpu(bits, C, b, E, ng, tg, k)
+        idx, w, cnt, _ = _route_gpu(bits, C, b, E, ng, tg, k)
         assert np.all(idx == np.array(ids)), (idx[0], ids)
         assert np.all(w == np.array(ws, np.float32))
         exp = np.zeros(E, np.int64)

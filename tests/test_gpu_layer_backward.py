@@ -237,9 +237,15 @@ def check_router_stage(xbits, C, idx, dw32, inv_perm, perm_src, offs, dx_in, dl_
     assert rel_l2(dC, ref["dC"]) <= 1e-4, (label, rel_l2(dC, ref["dC"]))
 
 
-@pytest.mark.parametrize("T,H,E,k,mode", [(37, 1024, 64, 8, "dx_in"), (5, 256, 16, 3, "none"),
-                                          (64, 7168, 256, 8, "in_place")])
-def test_router_backward_kernel(T, H, E, k, mode):
+@pytest.mark.parametrize("T,H,E,k,mode,given", [(37, 1024, 64, 8, "dx_in", False),
+                                                (5, 256, 16, 3, "none", False),
+                                                (64, 7168, 256, 8, "in_place", False),
+                                                (37, 1024, 64, 8, "dx_in", True),
+                                                (64, 7168, 256, 8, "in_place", True)])
+def test_router_backward_kernel(T, H, E, k, mode, given):
+    """given: the chosen experts' scores come in as topk_s (the fp64 scores
+    rounded to fp32, as the forward's fp32 scores are within an ulp of them)
+    instead of being computed again from x and C."""
     rng = np.random.default_rng([T, H, E, k])
     xbits = synth.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
     C = (rng.standard_normal((E, H)) * 0.02).astype(np.float32)
@@ -255,8 +261,13 @@ def test_router_backward_kernel(T, H, E, k, mode):
                                                           device="cuda")
     dl_rows = torch.full((T * k,), float("nan"), dtype=torch.float32, device="cuda")
     dC = torch.full((E, H), float("nan"), dtype=torch.float32, device="cuda")
+    ts = None
+    if given:
+        lg = np.einsum("th,tkh->tk", OF.bf16_value_from_bits(xbits),
+                       C.astype(np.float64)[idx.astype(np.int64)])
+        ts = dev((1.0 / (1.0 + np.exp(-lg))).astype(np.float32))
     M.moe_router_backward(x_d, C_d, dev(idx), dev(dw), dev(inv_perm), dx_in_d, T, H, E, k, dx_out,
-                          dl_rows)
+                          dl_rows, topk_s=ts)
     M.moe_router_dcentroids(x_d, dev(perm_src), dev(offs), dl_rows, T, H, E, dC)
     torch.cuda.synchronize()
     check_router_stage(xbits, C, idx, dw, inv_perm, perm_src, offs,
@@ -282,7 +293,9 @@ def test_router_backward_v3_prefill_sampled():
     w_d = torch.empty((T, k), dtype=torch.float32, device="cuda")
     cnt_d = torch.empty((E,), dtype=torch.int32, device="cuda")
     x_d, C_d = bf16_dev(x), dev(C)
-    M.moe_route(x_d, T, H, C_d, dev(b), E, cfg.n_group, cfg.topk_group, k, idx_d, w_d, cnt_d, ws, wsb)
+    ts_d = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    M.moe_route(x_d, T, H, C_d, dev(b), E, cfg.n_group, cfg.topk_group, k, idx_d, w_d, cnt_d, ws, wsb,
+                topk_s=ts_d)
     idx = host(idx_d)
     offs, perm_src, inv_perm = _permute_gpu(idx, E, 0)
     dw = np.random.default_rng(8).standard_normal((T, k)).astype(np.float32)
@@ -291,7 +304,7 @@ def test_router_backward_v3_prefill_sampled():
     dl_rows = torch.empty((T * k,), dtype=torch.float32, device="cuda")
     dC = torch.empty((E, H), dtype=torch.float32, device="cuda")
     M.moe_router_backward(x_d, C_d, idx_d, dev(dw), dev(inv_perm), bf16_dev(dx_in), T, H, E, k,
-                          dx_out, dl_rows)
+                          dx_out, dl_rows, topk_s=ts_d)   # the forward's scores, as the layer
     M.moe_router_dcentroids(x_d, dev(perm_src), dev(offs), dl_rows, T, H, E, dC)
     torch.cuda.synchronize()
     rng = np.random.default_rng(9)

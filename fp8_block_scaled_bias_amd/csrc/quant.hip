@@ -67,14 +67,20 @@ __global__ __launch_bounds__(256) void quant_128x128_kernel(
   const int64_t g = blockIdx.z;
   const float* base = w + (g * N + nb * 128) * K + kb * 128;
   uint8_t* obase = out + (g * N + nb * 128) * K + kb * 128;
-  // thread layout: 32 threads per row (4 floats each), 8 rows per pass
+  // thread layout: 32 threads per row (4 floats each), 8 rows per pass; the
+  // block stays in registers (16 float4 per thread) between the maximum and
+  // the codes, so it is read from memory once
   const int c4 = (threadIdx.x & 31) * 4;
   const int r0 = threadIdx.x >> 5;
+  typedef float f4v __attribute__((ext_vector_type(4)));
+  f4v v[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    v[i] = __builtin_nontemporal_load(reinterpret_cast<const f4v*>(base + (int64_t)(r0 + 8 * i) * K + c4));
   float amax = 0.0f;
-  for (int r = r0; r < 128; r += 8) {
-    const float4 v = *reinterpret_cast<const float4*>(base + (int64_t)r * K + c4);
-    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
-  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w))));
   amax = wave_max_xor(amax, 64);
   __shared__ float red[4];
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
@@ -82,11 +88,10 @@ __global__ __launch_bounds__(256) void quant_128x128_kernel(
   amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
   auto emit = [&](auto dv) __attribute__((always_inline)) {
-    for (int r = r0; r < 128; r += 8) {
-      const float4 v = *reinterpret_cast<const float4*>(base + (int64_t)r * K + c4);
-      *reinterpret_cast<uint32_t*>(obase + (int64_t)r * K + c4) =
-          f32x4_to_e4m3x4(dv(v.x), dv(v.y), dv(v.z), dv(v.w));
-    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      *reinterpret_cast<uint32_t*>(obase + (int64_t)(r0 + 8 * i) * K + c4) =
+          f32x4_to_e4m3x4(dv(v[i].x), dv(v[i].y), dv(v[i].z), dv(v[i].w));
   };
   if (recip_ok(s)) {
     const float y = 1.0f / s;

@@ -309,6 +309,21 @@ __global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
     p[i] = v;
 }
 
+// The value of the lane paired with this one in the merge round of width o
+// (o = 1, 2, 4, 8): quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror,
+// row_mirror.
+__device__ __forceinline__ float dpp_pair(float v, int o) {
+  const int x = __float_as_int(v);
+  int r;
+  switch (o) {
+    case 1: r = __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false); break;
+    case 2: r = __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false); break;
+    case 4: r = __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, false); break;
+    default: r = __builtin_amdgcn_mov_dpp(x, 0x140, 0xF, 0xF, false); break;
+  }
+  return __int_as_float(r);
+}
+
 template <bool PF>
 __global__ __launch_bounds__(256) void router_select_kernel(
     const float* __restrict__ part, int KS, int64_t T, const float* __restrict__ bias, int E,
@@ -338,11 +353,14 @@ __global__ __launch_bounds__(256) void router_select_kernel(
   // order.
   const int64_t tstride = (int64_t)gridDim.x * 4;
   float4 nx[8];
+  const int64_t kstride = T * E;  // between split-K partials
   auto fetch = [&](int64_t tt) {
+    if (tt < T && active) {
+      const float* p = part + tt * E + ebase;
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-      if (u < KS && tt < T && active)
-        nx[u] = *reinterpret_cast<const float4*>(part + ((int64_t)u * T + tt) * E + ebase);
+      for (int u = 0; u < 8; ++u)
+        if (u < KS) nx[u] = *reinterpret_cast<const float4*>(p + u * kstride);
+    }
   };
   if (PF) fetch((int64_t)blockIdx.x * 4 + wv);
   for (int64_t t = (int64_t)blockIdx.x * 4 + wv; t < T; t += tstride) {
@@ -400,51 +418,92 @@ __global__ __launch_bounds__(256) void router_select_kernel(
       t2 = fmaxf(t2, fminf(t1, v));
       t1 = fmaxf(t1, v);
     }
+    // merge rounds pair each lane with one holding the top-2 of a disjoint
+    // set of the group's lanes: xor 1 and xor 2 within a quad, then the
+    // mirror lane in a half row (i <-> 7 - i) and in a row (i <-> 15 - i),
+    // all lane moves within the row (DPP); wider groups exchange by xor
     for (int o = 1; o < lpg; o <<= 1) {
-      const float o1 = __shfl_xor(t1, o, 64);
-      const float o2 = __shfl_xor(t2, o, 64);
+      float o1, o2;
+      if (o <= 8) {
+        o1 = dpp_pair(t1, o);
+        o2 = dpp_pair(t2, o);
+      } else {
+        o1 = __shfl_xor(t1, o, 64);
+        o2 = __shfl_xor(t2, o, 64);
+      }
       t2 = fmaxf(fminf(t1, o1), fmaxf(t2, o2));
       t1 = fmaxf(t1, o1);
     }
     const float gscore = t1 + t2;
+    // group j's score sits in lane j * lpg (read as a scalar)
     int rank = 0;
     for (int j = 0; j < n_group; ++j) {
-      const float sj = __shfl(gscore, j * lpg, 64);
+      const float sj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gscore), j * lpg));
       rank += (sj > gscore || (sj == gscore && j < gid)) ? 1 : 0;
     }
     const bool kept = active && rank < topk_group;
-    // top-k among the kept experts.  Every expert slot gets a unique 40-bit
-    // key: the order-preserving bits of its biased score above 255 - e (a
-    // tie goes to the lower expert id); slots outside the kept groups keep
-    // only the index part, below every kept one.  The k-th largest key is
-    // found bit by bit from the top: a bit stays set when at least k keys
-    // reach the prefix with it (counted by ballots), so the k selected slots
-    // are exactly the keys at or above it.
-    uint64_t key[4];
+    // top-k among the kept experts, in the order (biased score descending,
+    // expert id ascending).  Each slot's key is the order-preserving bits
+    // of its biased score (-0 as +0), 0 for slots outside the kept groups
+    // (below every kept one).  A threshold is built bit by bit from the top:
+    // a bit stays set when at least k keys reach the prefix with it (counted
+    // by ballots), so the keys at or above the prefix always include the k
+    // largest; as soon as exactly k keys reach it they are the selection and
+    // the search stops.  Otherwise it ends on the k-th largest key itself,
+    // shared by several slots: every slot above it is taken, and of those
+    // equal to it the ones with the lowest expert ids, as many as are left.
+    uint32_t key[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t u = sb[i] == 0.0f ? 0u : __float_as_uint(sb[i]);  // -0 ties +0
       const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-      key[i] = ((uint64_t)(kept ? ord : 0u) << 8) | (uint64_t)(255 - ((ebase + i) & 255));
+      key[i] = kept ? ord : 0u;
     }
-    uint64_t pre = 0;
-    for (int bit = 39; bit >= 0; --bit) {
-      const uint64_t c = pre | (1ull << bit);
+    uint32_t pre = 0;
+    bool exact = false;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t c = pre | (1u << bit);
       int cnt = 0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) cnt += __popcll(__ballot(key[i] >= c));
-      if (cnt >= k) pre = c;
+      if (cnt >= k) {
+        pre = c;
+        if (cnt == k) {
+          exact = true;
+          break;
+        }
+      }
+    }
+    const uint64_t lanes_below = (1ull << lane) - 1ull;
+    uint64_t msk[4];
+    if (exact) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) msk[i] = __ballot(key[i] >= pre);
+    } else {
+      // slots equal to the k-th key, ranked by expert id (e = 4 lane + i):
+      // equal slots of the lanes below, then this lane's earlier ones
+      uint64_t eq[4];
+      int left = k, tie = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        msk[i] = __ballot(key[i] > pre);
+        eq[i] = __ballot(key[i] == pre);
+        left -= __popcll(msk[i]);
+        tie += __popcll(eq[i] & lanes_below);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool mine = (eq[i] >> lane) & 1ull;
+        msk[i] |= __ballot(mine && tie < left);
+        tie += mine ? 1 : 0;
+      }
     }
     // ranks in ascending expert id (e = 4 lane + i): selected slots of the
     // lanes below, then this lane's earlier slots; each selected slot puts
     // (e, s) at its rank, and the wave reads the k entries back in order
-    uint64_t msk[4];
     int below = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      msk[i] = __ballot(key[i] >= pre);
-      below += __popcll(msk[i] & ((1ull << lane) - 1ull));
-    }
+    for (int i = 0; i < 4; ++i) below += __popcll(msk[i] & lanes_below);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if ((msk[i] >> lane) & 1ull) {

@@ -1,6 +1,8 @@
 """Helpers shared by the GPU parity tests (host <-> device marshalling and
 comparisons).  No method arithmetic lives here."""
+import os
 import sys
+import time
 
 import numpy as np
 import torch
@@ -10,9 +12,22 @@ from oracle.formats import bf16_value_from_bits
 NEAR_TIE = 1e-6   # routing margin below which a mismatch is logged, not failed
 
 
+# Progress lines also go to a file under the repository's gpurun_out/ (the
+# folder a GPU run hands back), so that a long test shows signs of life even
+# while pytest captures its output.
+_PROGRESS = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                         "gpurun_out", "gpu_tests_progress.log")
+
+
 def log(*a):
     print(*a, flush=True)
     sys.stdout.flush()
+    try:
+        os.makedirs(os.path.dirname(_PROGRESS), exist_ok=True)
+        with open(_PROGRESS, "a") as f:
+            f.write(time.strftime("%H:%M:%S ") + " ".join(str(x) for x in a) + "\n")
+    except OSError:
+        pass
 
 
 def dev(a):

@@ -266,18 +266,19 @@ def bench_backward(layer, T, reps=10, warmup=3):
 
 def bench_backward_step(layer, x, cfg, steps=3, warmup=1):
     """The layer's backward (MoELayer.backward) at T=16384 after a forward of
-    the same batch: combine backward, dgrad of down, the recomputed gate+up,
-    SwiGLU backward, dgrad of gate+up, unpermute, both weight gradients and
-    the router's backward (dx and the centroids' gradient); dy N(0,1) bf16
-    (synth.gen_dy).  The input gradients read the weights as stored for the
-    forward, so the backward depends on nothing made from the weights
-    beforehand.  Flops counted: the GEMMs only, 2RHI for each of
-    dgrad-down and wgrad-down, 4RHI for each of the recomputed gate+up,
-    dgrad-gate+up and wgrad-gate+up (34.6 TFLOP).  The same backward is also
-    timed after a forward that kept its gate/up outputs (ms_per_step_keep_gu:
-    no gate+up GEMM rerun).  Then a training step
-    (forward + backward, wall clock) with the gate+up GEMM rerun in the
-    backward and with the forward keeping its outputs; and the 128x128
+    the same batch that kept its bf16 gate/up outputs (the pages recompute
+    only RMSNorm and MLA's up-projection in the backward and store the other
+    activations in FP8/BF16): combine backward, dgrad of down, SwiGLU
+    backward from the stored gate/up, dgrad of gate+up, unpermute, both
+    weight gradients and the router's backward (dx and the centroids'
+    gradient); dy N(0,1) bf16 (synth.gen_dy).  The input gradients read the
+    weights as stored for the forward, so the backward depends on nothing
+    made from the weights beforehand.  Flops counted: the GEMMs only, 2RHI
+    for each of dgrad-down and wgrad-down, 4RHI for each of dgrad-gate+up
+    and wgrad-gate+up (26.0 TFLOP).  The same backward is also timed after a
+    forward that kept nothing (ms_per_step_recompute_gu: the gate+up GEMM
+    runs again in the backward, 34.6 TFLOP).  Then a training step
+    (forward + backward, wall clock) both ways; and the 128x128
     requantisation of fp32 master weights (fp8_quant_128x128 over both
     weight sets, the per-update cast after an optimizer step), timed on its
     own."""
@@ -286,37 +287,36 @@ def bench_backward_step(layer, x, cfg, steps=3, warmup=1):
     import torch
     import synth
     dy = torch.from_numpy(synth.gen_dy(cfg).view(np.int16)).cuda().view(torch.bfloat16)
-    layer.forward(x)
-    for _ in range(warmup):
-        layer.backward(dy, x)
-    torch.cuda.synchronize()
-    events = {}
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        layer.backward(dy, x, events=events)
-    torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) / steps * 1e3
-    per = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in events.items()}
     R = cfg.R
-    flop = 2.0 * R * cfg.H * cfg.I * (1 + 1 + 2 + 2 + 2)
-    out = {"workload": "layer backward (experts + router), T=16384, V3 shapes", "ms_per_step": ms,
+    unit = 2.0 * R * cfg.H * cfg.I
+
+    def timed(keep):
+        layer.forward(x, keep_gu=keep)
+        for _ in range(warmup):
+            layer.backward(dy, x)
+        torch.cuda.synchronize()
+        events = {}
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            layer.backward(dy, x, events=events)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) / steps * 1e3
+        per = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in events.items()}
+        return ms, per
+
+    ms, per = timed(True)
+    flop = unit * (1 + 1 + 2 + 2)
+    out = {"workload": "layer backward (experts + router), T=16384, V3 shapes, after a forward "
+                       "that stored its bf16 gate/up outputs", "ms_per_step": ms,
            "tokens_per_s": cfg.T / (ms * 1e-3), "TFLOPS": flop / (ms * 1e-3) / 1e12,
            "flop_per_step": flop, "per_stage_ms": per}
-    log(f"[bench] backward step: {ms:.3f} ms ({out['TFLOPS']:.0f} TFLOP/s); " +
-        ", ".join(f"{k} {v:.3f}" for k, v in per.items()))
-    # the same backward after a forward that kept its gate/up outputs (the
-    # training configuration: the backward reads them instead of rerunning
-    # the gate+up GEMM)
-    layer.forward(x, keep_gu=True)
-    layer.backward(dy, x)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        layer.backward(dy, x)
-    torch.cuda.synchronize()
-    out["ms_per_step_keep_gu"] = (time.perf_counter() - t0) / steps * 1e3
-    log(f"[bench] backward step after a forward that kept gate/up: "
-        f"{out['ms_per_step_keep_gu']:.3f} ms")
+    log(f"[bench] backward step (gate/up stored by the forward): {ms:.3f} ms "
+        f"({out['TFLOPS']:.0f} TFLOP/s); " + ", ".join(f"{k} {v:.3f}" for k, v in per.items()))
+    ms_r, per_r = timed(False)
+    out["ms_per_step_recompute_gu"] = ms_r
+    out["per_stage_ms_recompute_gu"] = per_r
+    log(f"[bench] backward step rerunning the gate+up GEMM: {ms_r:.3f} ms; " +
+        ", ".join(f"{k} {v:.3f}" for k, v in per_r.items()))
     # a training step (forward + backward) both ways: the fused forward with
     # the gate+up GEMM run again in the backward, or the fused forward that
     # also keeps its bf16 gate/up outputs (1.2 GB) for the backward to read

@@ -216,8 +216,15 @@ def _v3_check(v3_layer, wts, cfg, tokens, label):
 
     tokens = np.array([t for t in tokens if t not in set(mism.tolist())], np.int64)
     t0 = time.time()
-    ref = OL.layer_tokens(x, C, b, wts, cfg.n_group, cfg.topk_group, k, I, tokens, keep=True,
-                          threads=THREADS)
+    # the oracle runs on slices of the tokens (every result is per token), so
+    # that progress is logged while it works
+    parts = []
+    for i0 in range(0, len(tokens), 64):
+        parts.append(OL.layer_tokens(x, C, b, wts, cfg.n_group, cfg.topk_group, k, I,
+                                     tokens[i0:i0 + 64], keep=True, threads=THREADS))
+        log(f"[layer] {label}: oracle on {min(i0 + 64, len(tokens))} of {len(tokens)} tokens "
+            f"({time.time() - t0:.0f} s)")
+    ref = {key: np.concatenate([np.atleast_1d(p_[key]) for p_ in parts]) for key in parts[0]}
     assert np.array_equal(ref["idx"], idx[tokens])
     log(f"[layer] {label}: oracle on {len(tokens)} tokens in {time.time() - t0:.0f} s")
     rows = _slot_rows(inv, tokens, T, k)
@@ -226,6 +233,7 @@ def _v3_check(v3_layer, wts, cfg, tokens, label):
     hs = host(bufs.hs.index_select(0, rr))
     d = bf16_values_host(bufs.d.index_select(0, rr)).reshape(len(tokens), k + 1, cfg.H)
     bound = _accumulation_bounds(ref, idx[tokens], wts, cfg, THREADS)
+    log(f"[layer] {label}: accumulation bounds of the tokens' gate/up sums ({time.time() - t0:.0f} s)")
     nflip = check_fused_swiglu(hq, hs, ref["hgu"].reshape(-1, 2 * I), bound.reshape(-1, 2 * I), I,
                                f"{label} gate+up+SwiGLU")
     log(f"[layer] {label}: rel L2 of D over the tokens' {rows.size} rows = "

@@ -175,9 +175,12 @@ def _accumulation_bounds(ref, idx, wts, cfg, threads):
         return rows, slots, gemm_accumulation_bound(qa[rows], sa[rows], [qB], [sB], off, cfg.H)
 
     out = np.zeros((n, k + 1, 2 * cfg.I))
+    experts = sorted(set(idx.ravel().tolist())) + [E]
     with ThreadPoolExecutor(threads) as ex:
-        for rows, slots, bnd in ex.map(run, sorted(set(idx.ravel().tolist())) + [E]):
+        for i, (rows, slots, bnd) in enumerate(ex.map(run, experts)):
             out[rows, slots] = bnd
+            if (i + 1) % 64 == 0:
+                log(f"[layer] accumulation bounds: {i + 1} of {len(experts)} experts")
     return out
 
 

@@ -106,8 +106,24 @@ def copy_probe(gib=1, reps=5):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps
+    out = {"bytes_per_copy": 2 * n, "ms": ms, "GB_s": 2 * n / (ms * 1e-3) / 1e9}
+    # the read and write ceilings on their own: torch's int64 sum (reads
+    # only) and zero_ (writes only) over 4 GiB, the practical bounds for the
+    # weight-streaming decode GEMMs and for the stores of the weight gradient
     del src, dst
-    return {"bytes_per_copy": 2 * n, "ms": ms, "GB_s": 2 * n / (ms * 1e-3) / 1e9}
+    big = torch.empty(4 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+    for name, fn in (("read", lambda: big.view(torch.int64).sum()), ("write", lambda: big.zero_())):
+        fn()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms_ = e0.elapsed_time(e1) / reps
+        out[name + "_GB_s"] = big.numel() / (ms_ * 1e-3) / 1e9
+    del big
+    return out
 
 
 def gemm_source_digest():
@@ -529,7 +545,8 @@ def main():
     x = x_device(cfg)
 
     cp = copy_probe()
-    log(f"[bench] copy probe: {cp['GB_s']:.0f} GB/s")
+    log(f"[bench] copy probe: {cp['GB_s']:.0f} GB/s; read alone {cp['read_GB_s']:.0f} GB/s, "
+        f"write alone {cp['write_GB_s']:.0f} GB/s")
     log(f"[bench] prefill T={cfg.T}: warmup {args.warmup}, steps {args.steps}")
     wall, per, gu_live = run_steps(layer, x, args.steps, args.warmup, update_bias=True)
     ms = wall / args.steps * 1e3

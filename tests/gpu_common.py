@@ -12,9 +12,8 @@ from oracle.formats import bf16_value_from_bits
 NEAR_TIE = 1e-6   # routing margin below which a mismatch is logged, not failed
 
 
-# Progress lines also go to a file under the repository's gpurun_out/ (the
-# folder a GPU run hands back), so that a long test shows signs of life even
-# while pytest captures its output.
+# Progress lines also go to a file in the repository's output folder, so that
+# a long test shows signs of life even while pytest captures its output.
 _PROGRESS = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
                          "gpurun_out", "gpu_tests_progress.log")
 

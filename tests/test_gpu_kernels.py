@@ -232,6 +232,27 @@ def test_route_hand_traced_ties():
         assert np.array_equal(cnt, exp)
 
 
+def test_route_hand_traced_ties_large_batch():
+    """The 256-expert hand-traced rows again on 2100 tokens of width 7168: the
+    wide logits kernel with several K splits and the selection that prefetches
+    the next token's partials.  Every score is exactly 1/2, so the threshold
+    search ends on a shared score and the lowest expert ids fill the rest."""
+    from test_oracle_route import _ties_rows
+    T, H = 2100, 7168
+    bits = np.zeros((T, H), np.uint16)
+    for E, ng, tg, k, b, ids, ws, _margin in _ties_rows():
+        if E != 256:
+            continue
+        C = synth.gen_centroids(synth.TINY.with_(E=E, H=H))
+        idx, w, cnt, _ = _route_gpu(bits, C, b, E, ng, tg, k)
+        assert np.all(idx == np.array(ids)), (idx[0], ids)
+        assert np.all(w == np.array(ws, np.float32))
+        exp = np.zeros(E, np.int64)
+        exp[ids] = T
+        assert np.array_equal(cnt, exp)
+    log(f"[route] hand-traced ties on {T} tokens of width {H}: every token as traced")
+
+
 def test_bias_update():
     rng = np.random.default_rng(4)
     for E, T, k in [(256, 4096, 8), (16, 64, 4), (256, 128, 8)]:

@@ -188,6 +188,44 @@ def bench_grouped_gemm(layer, reps=20, warmup=5):
             f"{out[name]['GB_s']:.0f} GB/s, {out[name]['frac_of_bound']:.2f} of the "
             f"{out[name]['bound']} roof")
         del aq, asc, c
+    out["dense_reference"] = dense_reference(s)
+    return out
+
+
+def dense_reference(s, reps=5, warmup=2):
+    """Context for the GEMM rows: the 256x256 kernel on ONE dense group of the
+    gate+up size (R = 9T rows x N = 2I x K = H, no ragged tiles, no gather,
+    bf16 out; random E4M3 codes, scales in [0.5, 1.5)), and torch._scaled_mm
+    (hipBLASLt) on the same codes with per-tensor scales - a plain FP8 GEMM
+    without the 128-element block scales, so not the same arithmetic."""
+    import numpy as np
+    import torch
+    import fp8_block_scaled_bias_amd as M
+    R, N, K = 9 * 16384, 2 * s.I, s.H
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    A = torch.randint(0, 256, (R, K), dtype=torch.uint8, device="cuda", generator=gen) & 0x77
+    As = torch.rand((R, K // 128), device="cuda", generator=gen) + 0.5
+    B = torch.randint(0, 256, (1, N, K), dtype=torch.uint8, device="cuda", generator=gen) & 0x77
+    Bs = torch.rand((1, N // 128, K // 128), device="cuda", generator=gen) + 0.5
+    C = torch.empty((R, N), dtype=torch.bfloat16, device="cuda")
+    o1 = torch.tensor([0, R], dtype=torch.int32, device="cuda")
+    flop = 2.0 * R * N * K
+    ms = _median_ms(lambda: M.grouped_fp8_gemm(A, As, None, B, Bs, o1, 1, R, N, K, C), reps, warmup)
+    out = {"R": R, "N": N, "K": K, "block_scaled_one_group_ms": ms,
+           "block_scaled_one_group_TFLOPS": flop / (ms * 1e-3) / 1e12}
+    try:
+        one = torch.tensor(1.0, device="cuda")
+        a8, b8 = A.view(torch.float8_e4m3fn), B[0].view(torch.float8_e4m3fn).t()
+        hb = _median_ms(lambda: torch._scaled_mm(a8, b8, scale_a=one, scale_b=one,
+                                                 out_dtype=torch.bfloat16), reps, warmup)
+        out["hipblaslt_per_tensor_ms"] = hb
+        out["hipblaslt_per_tensor_TFLOPS"] = flop / (hb * 1e-3) / 1e12
+    except Exception as e:  # the vendor library is context only
+        out["hipblaslt_per_tensor_error"] = f"{type(e).__name__}: {str(e)[:120]}"
+    log(f"[bench] dense reference {R}x{N}x{K}: block-scaled, one group {ms:.3f} ms; "
+        f"hipBLASLt per-tensor {out.get('hipblaslt_per_tensor_ms', float('nan')):.3f} ms")
+    del A, As, B, Bs, C
+    torch.cuda.empty_cache()
     return out
 
 

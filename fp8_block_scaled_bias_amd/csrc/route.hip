@@ -8,20 +8,25 @@
 // routed experts per token), 节点限制路由 (at most 4 nodes per token) and
 // 无额外损耗的负载均衡 (bias update speed 0.001).
 //
-// Two kernels:
-//  1. router_logits: l = x * C^T on bf16 MFMA.  x is bf16 (exact); each fp32
+// Kernels:
+//  1. router logits: l = x * C^T on bf16 MFMA.  x is bf16 (exact); each fp32
 //     centroid is split exactly into three bf16 pieces (hi + mid + lo), so
-//     every product is exact and only the fp32 accumulation rounds.  Partial
-//     sums are kept per 512-wide K chunk and then added, which keeps the
-//     accumulator's rounding error near that of a short fp32 sum.  A 64-token
-//     x 64-expert tile per workgroup; for small T the K range is split over
-//     workgroups and the partials are added in fixed order by kernel 2.
+//     every product is exact and only the fp32 accumulation rounds.  Small
+//     batches (router_logits_kernel): a 64-token x 64-expert tile per
+//     workgroup, partial sums kept per 512-wide K chunk; large batches
+//     (router_logits_wide_kernel): the planes split once per call into the
+//     workspace, 256 tokens x 256 experts per workgroup.  Either way the K
+//     range may be split over workgroups; the partials are added in fixed
+//     order by kernel 2.
 //  2. router_select: one wave per token, 4 experts per lane (lane l owns
-//     experts 4l..4l+3).  Group top-2 sums are butterflies over the lanes of a
-//     group, group ranks are counted over shuffled group scores, and the k
-//     winners are k wave-wide argmax rounds.  The histogram is built with LDS
-//     atomics and flushed with one global integer atomic per expert and
-//     workgroup (integer adds: order-independent, so deterministic).
+//     experts 4l..4l+3).  Group top-2 sums by merge rounds over the lanes of
+//     a group, group ranks from each group's score read as a scalar, and the
+//     top-k as a threshold on the biased scores' order-preserving bits built
+//     from ballot counts (ties to the lower expert id).  The histogram is
+//     built with LDS atomics and flushed with one global integer atomic per
+//     expert and workgroup (integer adds: order-independent, so
+//     deterministic).
+//  3. bias_update: the +-gamma rule on the counts.
 #include "common.h"
 
 namespace moe {
@@ -459,9 +464,26 @@ __global__ __launch_bounds__(256) void router_select_kernel(
       const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
       key[i] = kept ? ord : 0u;
     }
-    uint32_t pre = 0;
+    // every kept key shares the bits above the highest bit where the largest
+    // and the smallest kept key differ: the search would set exactly those
+    // (at least k keys reach each of them, no key reaches a zero one), so it
+    // starts below them
+    uint32_t kmax = 0u, kmin = 0xFFFFFFFFu;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      kmax = max(kmax, key[i]);
+      if (kept) kmin = min(kmin, key[i]);
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
+      kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
+    }
+    const uint32_t diff = kmax ^ kmin;
+    const int top = diff ? 31 - __builtin_clz(diff) : -1;  // highest differing bit
+    uint32_t pre = top < 0 ? kmax : top >= 31 ? 0u : kmax & ~((2u << top) - 1u);
     bool exact = false;
-    for (int bit = 31; bit >= 0; --bit) {
+    for (int bit = top; bit >= 0; --bit) {
       const uint32_t c = pre | (1u << bit);
       int cnt = 0;
 #pragma unroll

@@ -1,7 +1,8 @@
 """Host check of the selection rule the router's select kernel applies (its
 top-k among the kept experts), written out on the CPU: a threshold on the
 order-preserving 32-bit keys of the biased scores, built bit by bit from
-counts, stopping as soon as exactly k keys reach it; when it ends on a key
+counts (from the top bit, or from below the bits every kept key shares),
+stopping as soon as exactly k keys reach it; when it ends on a key
 shared by several slots, every slot above it is taken and, of the equal ones,
 the lowest expert ids.  Compared with a stable sort (score descending, id
 ascending) on random scores, on scores forced into ties, and with dropped
@@ -18,9 +19,15 @@ def _ord_keys(sb, kept):
     return np.where(kept, ordk, 0).astype(np.uint32)
 
 
-def _select_threshold(key, k):
-    pre, exact = 0, False
-    for bit in range(31, -1, -1):
+def _select_threshold(key, k, kept=None):
+    pre, exact, top = 0, False, 31
+    if kept is not None:
+        # the kernel starts below the bits that every kept key shares
+        kmax, kmin = int(key.max()), int(key[kept].min())
+        diff = kmax ^ kmin
+        top = diff.bit_length() - 1
+        pre = kmax if top < 0 else kmax & ~((2 << top) - 1)
+    for bit in range(top, -1, -1):
         c = pre | (1 << bit)
         cnt = int((key >= c).sum())
         if cnt >= k:
@@ -59,6 +66,12 @@ def test_threshold_rule_matches_sorted_choice():
         sb = sb.astype(np.float32)
         groups = rng.choice(8, int(rng.integers(4, 9)), replace=False)
         kept = np.isin(np.arange(E) // 32, groups)
-        got = _select_threshold(_ord_keys(sb, kept), k)
+        if trial % 7 == 6:     # exactly k candidates
+            kept = np.zeros(E, bool)
+            kept[rng.choice(E, k, replace=False)] = True
+        key = _ord_keys(sb, kept)
         exp = _select_sort(sb, kept, k)
+        got = _select_threshold(key, k)
         assert np.array_equal(got, exp), (trial, k, got, exp)
+        got = _select_threshold(key, k, kept)
+        assert np.array_equal(got, exp), (trial, k, "prefix start", got, exp)
